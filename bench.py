@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode-phase weight-only-quantized GEMM on one MI355X.
+
+A step is one call of the hot path (dispatch, weight stream, activation staging,
+dequant, matrix-core inner product, stream-K scheduling, epilogue) on one batch:
+by default the FP8 block-scaled FFN gate/up projection, N=17408, K=5120, M=16,
+BF16 activations.  Inputs are synthetic and seeded (synth/), already resident in
+HBM before timing starts.  Each step reads a different copy of the packed
+weight matrix, and the copies together exceed the 256 MB Infinity Cache, so the
+weight bytes of every step come from HBM.
+
+Reported value: weight-stream GB/s = (packed code bytes + scale bytes) per step
+divided by the time per step (the pages count stored weight bytes, see
+the design doc).  The JSON line also carries the dominant kernel's roofline (bytes
+per launch over the mean launch duration, from HIP events on the library's
+stream), the CPU oracle timed on the host as a baseline, and (with --all) the
+other workloads' numbers.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "weight-stream GB/s (% of HBM peak) for quantized GEMM at M=1/8/16/32"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+ROTATE_TARGET_BYTES = 1 << 30
+
+
+def weight_bytes(fmt: str, N: int, K: int) -> int:
+    if fmt == "fp8":
+        return N * K + 4 * (N // 128) * (K // 128)
+    return N * K // 2 + 2 * N * (K // 128) + 16
+
+
+def algorithmic_bytes(fmt: str, N: int, K: int, M: int) -> int:
+    """Bytes a launch must move: weight stream + activations in + outputs out."""
+    return weight_bytes(fmt, N, K) + 2 * M * K + 2 * M * N
+
+
+def kernel_src_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("wq_kernels.hip", "wq_device.hpp", "wq_internal.h", "wq_api.cpp"):
+        with open(os.path.join(ROOT, "weight_only_quantized_fp8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_key: str):
+    """HBM traffic per launch measured with rocprofv3 PMC counters for this kernel
+    source (profiles/traffic.json); None when absent or the kernel changed."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d.get(workload_key)
+        if not e or e.get("kernel_src_sha") != kernel_src_sha():
+            return None
+        return float(e["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+class Workload:
+    def __init__(self, name: str, M: int, copies: int | None = None):
+        import numpy as np
+        import torch
+        import synth
+        from weight_only_quantized_fp8_amd import wq
+
+        self.name, self.M = name, M
+        self.fmt, self.N, self.K, _ = synth.CONFIGS[name]
+        N, K = self.N, self.K
+        seed = synth.SEEDS[name]
+        dev = "cuda:0"
+        self.wbytes = weight_bytes(self.fmt, N, K)
+        self.abytes = algorithmic_bytes(self.fmt, N, K, M)
+        if copies is None:
+            copies = max(2, math.ceil(ROTATE_TARGET_BYTES / self.wbytes))
+        self.copies = copies
+        if self.fmt == "fp8":
+            codes, scales = synth.fp8_weights(N, K, seed)
+            p0 = wq.pack_fp8(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev))
+            x = synth.x_bf16(M, K, seed + 100)
+            self.x = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+            self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            self.ws = wq.workspace(wq.WQ_FMT_FP8_BLOCK, N, K, dev)
+            self._call = lambda p: wq.wq_gemm_fp8_block(p, N, K, self.x, self.y, M, self.ws)
+        else:
+            codes, qmap, g = synth.lut3_weights(N, K, seed)
+            t16 = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16)
+            p0 = wq.pack_lut3(torch.from_numpy(codes).to(dev), t16(qmap), t16(g))
+            x = synth.x_f16(M, K, seed + 100)
+            self.x = t16(x)
+            self.y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            self.ws = wq.workspace(wq.WQ_FMT_LUT3, N, K, dev)
+            self._call = lambda p: wq.wq_gemm_lut3(p, N, K, self.x, self.y, M, self.ws)
+        self.packed = [p0] + [p0.clone() for _ in range(copies - 1)]
+        torch.cuda.synchronize()
+        self.i = 0
+
+    def step(self):
+        self._call(self.packed[self.i % self.copies])
+        self.i += 1
+
+    def launches_per_step(self) -> int:
+        return 1 if self.M <= 16 else 2
+
+
+def time_workload(w: Workload, steps: int, warmup: int):
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        w.step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        w.step()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    total_ms = t_begin.elapsed_time(t_end)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    mean_step_ms = sum(per) / len(per)
+    return {
+        "ms_per_step": total_ms / steps,
+        "host_ms_per_step": host_s * 1e3 / steps,
+        "launch_ms_mean": mean_step_ms / w.launches_per_step(),
+        "step_ms_p10": per[int(0.1 * (len(per) - 1))],
+        "step_ms_p50": per[int(0.5 * (len(per) - 1))],
+        "step_ms_p90": per[int(0.9 * (len(per) - 1))],
+    }
+
+
+def cpu_baseline(name: str, M: int):
+    """The oracle as it stands, on the host cores, over the whole workload."""
+    import numpy as np
+    import oracle
+    import synth
+    fmt, N, K, _ = synth.CONFIGS[name]
+    seed = synth.SEEDS[name]
+    threads = oracle.default_threads()
+    if fmt == "fp8":
+        codes, scales = synth.fp8_weights(N, K, seed)
+        x = synth.x_bf16(M, K, seed + 100)
+        t0 = time.perf_counter()
+        oracle.gemm_fp8(x, codes, scales, nthreads=threads)
+    else:
+        codes, qmap, g = synth.lut3_weights(N, K, seed)
+        x = synth.x_f16(M, K, seed + 100)
+        t0 = time.perf_counter()
+        oracle.gemm_lut3(x, codes, qmap, g, nthreads=threads)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": weight_bytes(fmt, N, K) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "whole %s workload N=%d K=%d M=%d, all outputs, one pass (%.2f s wall)" % (name, N, K, M, dt),
+            "seconds": dt}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="gate_up")
+    ap.add_argument("--M", type=int, default=16)
+    ap.add_argument("--all", action="store_true", help="also time every other workload and M")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the kernel is "
+              "sized for one GPU's share; see DESIGN.md for how it would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    import synth
+    print("bench: preparing %s M=%d" % (args.config, args.M), file=sys.stderr, flush=True)
+    w = Workload(args.config, args.M)
+    r = time_workload(w, args.steps, args.warmup)
+    value = w.wbytes / (r["ms_per_step"] * 1e-3) / 1e9
+    achieved = w.abytes / (r["launch_ms_mean"] * 1e-3) / 1e9
+    key = "%s_M%d" % (args.config, args.M)
+    traffic = load_traffic(key)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.fmt == "fp8" else "f16",
+        "data": "synthetic",
+        "config": {"workload": "%s %s N=%d K=%d M=%d" % (args.config, w.fmt, w.N, w.K, args.M),
+                   "format": "fp8_e4m3_block128x128" if w.fmt == "fp8" else "lut3_group128",
+                   "N": w.N, "K": w.K, "M": args.M, "weight_bytes_per_step": w.wbytes,
+                   "weight_copies_rotated": w.copies, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": w.abytes,
+                     "launch_us_mean": round(r["launch_ms_mean"] * 1e3, 3)},
+        "timing": {k: round(v * 1e3, 3) for k, v in r.items()},
+    }
+    out["timing"] = {"us_" + k.replace("_ms", ""): v for k, v in out["timing"].items()}
+    del w
+    torch.cuda.empty_cache()
+
+    if args.all:
+        extra = {}
+        for name, (fmt, N, K, Ms) in synth.CONFIGS.items():
+            if name == "tiny":
+                continue
+            for M in Ms:
+                if name == args.config and M == args.M:
+                    continue
+                print("bench: %s M=%d" % (name, M), file=sys.stderr, flush=True)
+                wk = Workload(name, M)
+                rk = time_workload(wk, max(20, args.steps // 4), max(5, args.warmup // 4))
+                gbs = wk.wbytes * wk.launches_per_step() / (rk["ms_per_step"] * 1e-3) / 1e9
+                extra["%s_M%d" % (name, M)] = {
+                    "us_per_call": round(rk["ms_per_step"] * 1e3, 2),
+                    "us_launch_mean": round(rk["launch_ms_mean"] * 1e3, 2),
+                    "stream_GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                    "passes": wk.launches_per_step()}
+                del wk
+                torch.cuda.empty_cache()
+        out["extra"] = extra
+
+    if not args.no_cpu:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cb = cpu_baseline(args.config, args.M)
+        out["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cb.items()
+                               if k != "seconds"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,183 @@
+/*
+ * libwq -- decode-phase weight-only-quantized GEMM for AMD Instinct MI355X (gfx950).
+ *
+ *     y[M, N] = x[M, K] . dequant(W)[N, K]^T ,   M = 1 .. 32
+ *
+ * Two weight formats:
+ *
+ *   FP8 block-scaled: E4M3 codes with one FP32 scale per 128x128 block of W.
+ *     The GEMM takes each 128-wide K block's partial sum in FP32 and folds it
+ *     once onto an FP32 outer accumulator times the block's scale (the
+ *     "two-level fold" of the atlas "Module m16_tc" docs, section NUMERICS;
+ *     block geometry [128, 128] from the arc PR "FP8 bank conflict + the
+ *     dispatch threshold's provenance", section "The threshold").  Activations
+ *     and outputs are BF16.  The E4M3 flavour is OCP E4M3FN (max 448, NaN =
+ *     S.1111.111, no infinity).
+ *
+ *   3-bit LUT: codes 0..7 looked up in an 8-entry learned FP16 map, times an
+ *     FP16 scale per (row, 128-wide K group); each dequantised weight is
+ *     rounded to FP16 before it is accumulated (FLUTE PR "Add optimized_w3:
+ *     3-bit LUT GEMM on a new mainloop", "Core contributions" item 1 and
+ *     "Results").  Activations and outputs are FP16.
+ *
+ * Work flow (FLUTE PR, "Core contributions" item 2: pack once, offline):
+ *   1. wq_pack_* reorders canonical row-major [N, K] codes (plus scales and
+ *      map) into the library's packed layout, once per matrix.
+ *   2. wq_gemm_* runs the decode GEMM on the packed matrix for each batch.
+ *
+ * Conventions for every call:
+ *   - Pointers named as device pointers must point to memory of the current
+ *     HIP device; the caller owns all memory.  The library allocates nothing
+ *     and keeps no per-call state (only cached device properties and the
+ *     options read once from the environment, see below).
+ *   - Arguments are validated synchronously before any work is queued; an
+ *     invalid call returns an error code and queues nothing.  No C++
+ *     exception crosses this interface.
+ *   - Work is queued asynchronously on `hip_stream` (a hipStream_t; NULL is
+ *     the default stream).  Results are valid once the stream reaches them.
+ *   - Calls are thread-safe.  Calls that share a workspace must be ordered
+ *     (same stream, or synchronised): concurrent calls on one workspace race.
+ *
+ * Environment options, read once at the first call that needs them:
+ *   WQ_FORCE_PATH = auto | gemv | mfma   path for wq_gemm_fp8_block (default auto)
+ *   WQ_NT         = 2 | 4 | 8            16-column MFMA tiles per wave (default 4)
+ *   WQ_WG_PER_CU  = 1 .. 8               persistent work-groups per compute unit
+ */
+#ifndef WQ_H_
+#define WQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WQ_OK = 0,
+    WQ_ERR_NULL = 1,       /* a required pointer is NULL                              */
+    WQ_ERR_SHAPE = 2,      /* M, N or K outside what the format/path supports         */
+    WQ_ERR_LD = 3,         /* a leading dimension is smaller than the row length      */
+    WQ_ERR_WORKSPACE = 4,  /* workspace smaller than wq_gemm_workspace_bytes()        */
+    WQ_ERR_CODE = 5,       /* wq_pack_lut3 found a code > 7 (packed buffer not valid) */
+    WQ_ERR_DEVICE = 6,     /* current device is not gfx950                            */
+    WQ_ERR_HIP = 7,        /* a HIP runtime call failed (includes: no device)         */
+    WQ_ERR_ALIGN = 8,      /* pointer or leading dimension breaks a 16-byte alignment */
+    WQ_ERR_PATH = 9        /* requested path cannot serve this format / M             */
+} wq_status;
+
+typedef enum { WQ_FMT_FP8_BLOCK = 0, WQ_FMT_LUT3 = 1 } wq_format;
+
+/* Kernel path for the GEMM.  AUTO follows the batch ladder of the atlas
+ * "Module m16_tc" docs (section ARM ORDER): FP8 uses the strict-K-order GEMV
+ * for M <= 4 and the 16-row MFMA tile for M = 5..16; the LUT format uses the
+ * MFMA tile for every M = 1..16 (one mainloop across the decode band, as in
+ * the FLUTE PR's "Results").  M = 17..32 always runs the MFMA tile twice, on
+ * rows 0..15 and 16..M-1 ("ARM ORDER": two contiguous row halves). */
+typedef enum { WQ_PATH_AUTO = 0, WQ_PATH_GEMV = 1, WQ_PATH_MFMA = 2 } wq_path;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* wq_status_str(wq_status s);
+
+/* Version of the packed layouts written by wq_pack_*; a packed buffer is a
+ * deterministic, byte-for-byte function of the pack inputs and this number. */
+int wq_packed_format_version(void);
+
+/* ------------------------------------------------------------ FP8 block */
+
+/* Bytes of the packed FP8 matrix: N*K code bytes + 4*(N/128)*(K/128) scale
+ * bytes.  Returns 0 for an unsupported shape (N or K not a positive multiple
+ * of 128). */
+size_t wq_fp8_block_packed_bytes(int64_t N, int64_t K);
+
+/* Pack an FP8 weight matrix.
+ *   w_e4m3  device, [N][ldw] bytes, row-major E4M3FN codes, ldw >= K
+ *   scales  device, [N/128][K/128] FP32, row-major, contiguous
+ *   packed  device, wq_fp8_block_packed_bytes(N, K) bytes, 16-byte aligned
+ * N and K must be positive multiples of 128.  Every byte value is accepted
+ * (NaN codes decode to NaN).  Asynchronous on hip_stream. */
+wq_status wq_pack_fp8_block(const uint8_t* w_e4m3, int64_t ldw, const float* scales,
+                            int64_t N, int64_t K, void* packed, void* hip_stream);
+
+/* y = x . dequant(W)^T for a packed FP8 matrix.
+ *   packed     device, from wq_pack_fp8_block with the same N, K
+ *   x          device, [M][ldx] BF16 bits; ldx >= K, ldx % 8 == 0, x 16-byte aligned
+ *   y          device, [M][ldy] BF16 bits (RNE); ldy >= N; only columns < N are written
+ *   M          0 .. 32; M == 0 queues nothing and returns WQ_OK
+ *   workspace  device, >= wq_gemm_workspace_bytes(WQ_FMT_FP8_BLOCK, M, N, K) bytes,
+ *              zero-filled before its first use; every call leaves it zero-filled again
+ * Numerics: every output is within 2 BF16 ULP of the exact result rounded to
+ * BF16, or within 1e-3*sqrt(K)*max|x|*max|w| of the exact result.  Results are
+ * deterministic, and row r of an M-row call equals row r of any other call on
+ * the same path with the same row r of x, bit for bit. */
+wq_status wq_gemm_fp8_block(const void* packed, int64_t N, int64_t K,
+                            const uint16_t* x, int64_t ldx,
+                            uint16_t* y, int64_t ldy, int64_t M,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Same as wq_gemm_fp8_block with an explicit path (WQ_PATH_GEMV serves
+ * M <= 4 only; WQ_PATH_MFMA serves M <= 32; AUTO as above).  Used to sweep
+ * the GEMV/MFMA crossover (arc PR, section "The threshold": one binary, arms
+ * toggled without a rebuild). */
+wq_status wq_gemm_fp8_block_path(const void* packed, int64_t N, int64_t K,
+                                 const uint16_t* x, int64_t ldx,
+                                 uint16_t* y, int64_t ldy, int64_t M,
+                                 void* workspace, size_t workspace_bytes,
+                                 int path, void* hip_stream);
+
+/* ----------------------------------------------------------------- LUT3 */
+
+/* Bytes of the packed LUT matrix: N*K/2 nibble bytes + 2*N*(K/128) scale
+ * bytes + 32 bytes (map and pack status).  Returns 0 for an unsupported
+ * shape (N not a positive multiple of 16 or K not of 128). */
+size_t wq_lut3_packed_bytes(int64_t N, int64_t K);
+
+/* Pack a 3-bit LUT weight matrix.
+ *   codes   device, [N][ldc] bytes, one code 0..7 per byte, ldc >= K
+ *   qmap    device, FP16 bits [8] (the learned map; entry c serves code c)
+ *   scales  device, FP16 bits [N][K/128], row-major, contiguous
+ *   packed  device, wq_lut3_packed_bytes(N, K) bytes, 16-byte aligned
+ * This call synchronises hip_stream: it reads back whether any code exceeded
+ * 7 and then returns WQ_ERR_CODE (the packed buffer is then not valid). */
+wq_status wq_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* qmap,
+                       const uint16_t* scales, int64_t N, int64_t K,
+                       void* packed, void* hip_stream);
+
+/* y = x . dequant(W)^T for a packed LUT matrix.
+ *   x  device, [M][ldx] FP16 bits; ldx >= K, ldx % 8 == 0, x 16-byte aligned
+ *   y  device, [M][ldy] FP16 bits (RNE); ldy >= N
+ * Other arguments, limits and guarantees as wq_gemm_fp8_block (the ULP
+ * criterion is applied after rounding the FP16 result to BF16). */
+wq_status wq_gemm_lut3(const void* packed, int64_t N, int64_t K,
+                       const uint16_t* x, int64_t ldx,
+                       uint16_t* y, int64_t ldy, int64_t M,
+                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------ workspace */
+
+/* Workspace bytes a GEMM of this format and shape needs on the current
+ * device (the same for every M and path, so one buffer serves all of them).
+ * Returns 0 if the shape is unsupported or the device cannot be queried. */
+size_t wq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
+
+/* ----------------------------------------------------------- test hooks */
+/* Decode a packed matrix back to canonical row-major [N][K] with the same
+ * device dequant code the GEMM runs.  Asynchronous on hip_stream. */
+
+/* out[n][k] = BF16(e4m3(code)) -- unscaled; the MFMA path's converter. */
+wq_status wq_unpack_fp8_block(const void* packed, int64_t N, int64_t K,
+                              uint16_t* w_bf16, void* hip_stream);
+
+/* out[n][k] = FP32(e4m3(code)) -- unscaled; the GEMV path's converter. */
+wq_status wq_unpack_fp8_block_f32(const void* packed, int64_t N, int64_t K,
+                                  float* w_f32, void* hip_stream);
+
+/* out[n][k] = fp16_rne(qmap[code] * scale[n][k/128]) */
+wq_status wq_unpack_lut3(const void* packed, int64_t N, int64_t K,
+                         uint16_t* w_f16, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H_ */

@@ -21,16 +21,19 @@ maps the pages measure on, none of which are available):
   scales ~ U(0.005, 0.02) per (row, 128-wide K group).
 * Activations x ~ N(0,1) in float32, rounded to BF16 (FP8 path) or FP16 (LUT path).
 
-Random numbers come from ``numpy.random.Generator(PCG64(seed))``.  Stored dtypes
-are produced with library conversions (torch's float8_e4m3fn / bfloat16 casts and
-numpy's float16 cast), all round-to-nearest-even.
+Random numbers come from ``numpy.random.Generator(PCG64(.))``: a matrix is drawn
+in fixed chunks of 1024 rows, chunk i from ``SeedSequence(seed).spawn(...)[i]``,
+so the values depend only on the seed and the shape (never on the thread count)
+and large matrices can be drawn in parallel.  Stored dtypes are produced with
+library conversions (torch's float8_e4m3fn / bfloat16 casts and numpy's float16
+cast), all round-to-nearest-even.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = [
-    "SEEDS", "CONFIGS", "fp8_weights", "lut3_weights", "x_bf16", "x_f16",
+    "SEEDS", "CONFIGS", "normal_matrix", "fp8_weights", "lut3_weights", "x_bf16", "x_f16",
     "bits_to_torch",
 ]
 
@@ -56,8 +59,36 @@ _BLOCK = 128
 _E4M3_MAX = 448.0
 
 
+_CHUNK_ROWS = 1024
+
+
 def _rng(seed: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(seed))
+
+
+def _chunked(seed: int, rows: int, fill) -> None:
+    """Call fill(generator, r0, r1) for each 1024-row chunk, in parallel threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    n = (rows + _CHUNK_ROWS - 1) // _CHUNK_ROWS
+    seqs = np.random.SeedSequence(seed).spawn(n)
+    jobs = [(np.random.Generator(np.random.PCG64(seqs[i])), i * _CHUNK_ROWS, min(rows, (i + 1) * _CHUNK_ROWS))
+            for i in range(n)]
+    workers = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda j: fill(*j), jobs))
+
+
+def normal_matrix(rows: int, cols: int, seed: int, std: float = 1.0) -> np.ndarray:
+    """float32 [rows, cols] ~ N(0, std^2), chunk-seeded (see module doc)."""
+    out = np.empty((rows, cols), dtype=np.float32)
+
+    def fill(g, r0, r1):
+        g.standard_normal((r1 - r0, cols), dtype=np.float32, out=out[r0:r1])
+        if std != 1.0:
+            out[r0:r1] *= np.float32(std)
+    _chunked(seed, rows, fill)
+    return out
 
 
 def _to_e4m3_codes(a: np.ndarray) -> np.ndarray:
@@ -75,21 +106,17 @@ def fp8_weights(N: int, K: int, seed: int, std: float = 0.02, w: np.ndarray | No
     """
     if N % _BLOCK or K % _BLOCK:
         raise ValueError("N and K must be multiples of 128 for 128x128 block scales")
+    import torch
     if w is None:
-        w = _rng(seed).standard_normal((N, K), dtype=np.float32) * np.float32(std)
+        w = normal_matrix(N, K, seed, std)
     w = np.asarray(w, dtype=np.float32)
     nb, kb = N // _BLOCK, K // _BLOCK
-    blocks = w.reshape(nb, _BLOCK, kb, _BLOCK)
-    amax = np.abs(blocks).max(axis=(1, 3)).astype(np.float32)          # [nb, kb]
-    scales = np.where(amax > 0, amax / np.float32(_E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    codes = np.empty((N, K), dtype=np.uint8)
-    # Quantise one block-row at a time to bound temporary memory.
-    for i in range(nb):
-        rows = w[i * _BLOCK:(i + 1) * _BLOCK].reshape(_BLOCK, kb, _BLOCK)
-        q = rows / scales[i][None, :, None]
-        q = np.clip(q, -_E4M3_MAX, _E4M3_MAX).astype(np.float32)
-        codes[i * _BLOCK:(i + 1) * _BLOCK] = _to_e4m3_codes(q).reshape(_BLOCK, K)
-    return codes, scales
+    wt = torch.from_numpy(w)
+    amax = wt.view(nb, _BLOCK, kb, _BLOCK).abs().amax(dim=(1, 3))                  # [nb, kb] float32
+    scales = torch.where(amax > 0, amax / _E4M3_MAX, torch.ones_like(amax))        # float32 division
+    q = (wt.view(nb, _BLOCK, kb, _BLOCK) / scales[:, None, :, None]).clamp_(-_E4M3_MAX, _E4M3_MAX)
+    codes = q.reshape(N, K).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scales.numpy().astype(np.float32)
 
 
 def lut3_weights(N: int, K: int, seed: int, g_lo: float = 0.005, g_hi: float = 0.02):
@@ -97,9 +124,13 @@ def lut3_weights(N: int, K: int, seed: int, g_lo: float = 0.005, g_hi: float = 0
     if N % 16 or K % _BLOCK:
         raise ValueError("N must be a multiple of 16 and K of 128")
     r = _rng(seed)
-    codes = r.integers(0, 8, size=(N, K), dtype=np.uint8)
     qmap = np.sort(r.standard_normal(8, dtype=np.float32).astype(np.float16))
     scales = r.uniform(g_lo, g_hi, size=(N, K // _BLOCK)).astype(np.float32).astype(np.float16)
+    codes = np.empty((N, K), dtype=np.uint8)
+
+    def fill(g, r0, r1):
+        codes[r0:r1] = g.integers(0, 8, size=(r1 - r0, K), dtype=np.uint8)
+    _chunked(seed + 7919, N, fill)
     return codes, qmap.view(np.uint16).copy(), scales.view(np.uint16).copy()
 
 
@@ -107,7 +138,7 @@ def x_bf16(M: int, K: int, seed: int, ld: int | None = None) -> np.ndarray:
     """BF16 bits uint16 [M, ld] (columns >= K are padding filled with a canary pattern)."""
     import torch
     ld = K if ld is None else ld
-    x = _rng(seed).standard_normal((M, K), dtype=np.float32)
+    x = normal_matrix(M, K, seed)
     bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     out = np.full((M, ld), 0x7FC1, dtype=np.uint16)   # canary: a NaN payload
     out[:, :K] = bits
@@ -117,7 +148,7 @@ def x_bf16(M: int, K: int, seed: int, ld: int | None = None) -> np.ndarray:
 def x_f16(M: int, K: int, seed: int, ld: int | None = None) -> np.ndarray:
     """FP16 bits uint16 [M, ld] (padding columns hold a NaN canary)."""
     ld = K if ld is None else ld
-    x = _rng(seed).standard_normal((M, K), dtype=np.float32).astype(np.float16)
+    x = normal_matrix(M, K, seed).astype(np.float16)
     out = np.full((M, ld), 0x7E01, dtype=np.uint16)
     out[:, :K] = x.view(np.uint16)
     return out

@@ -1,0 +1,154 @@
+"""Helpers shared by the GPU tests: run the HIP path through the C ABI on seeded
+inputs and grade it against the CPU oracle.  Nothing here computes results:
+the device side is libwq, the reference side is oracle/."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from oracle import compare
+
+DEV = "cuda:0"
+
+
+def wqmod():
+    from weight_only_quantized_fp8_amd import wq
+    return wq
+
+
+def note(msg: str) -> None:
+    """Print and flush what names the case before GPU work, so a failure that
+    takes the process down still leaves the case on record."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def t_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(DEV)
+
+
+def t_u16(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(DEV).view(dtype)
+
+
+def t_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def bits_of(t) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------------ FP8
+
+def pack_fp8(codes, scales, ldw=None):
+    wq = wqmod()
+    N, K = codes.shape
+    if ldw is not None and ldw > K:
+        wide = np.zeros((N, ldw), dtype=np.uint8)
+        wide[:, :K] = codes
+        wide[:, K:] = 0x7F
+        src = t_u8(wide)[:, :K]
+    else:
+        src = t_u8(codes)
+    packed = torch.empty(wq.wq_fp8_block_packed_bytes(N, K), dtype=torch.uint8, device=DEV)
+    wq.wq_pack_fp8_block(src, t_f32(scales), N, K, packed)
+    return packed
+
+
+def run_fp8(packed, N, K, xbits, M=None, path=0, ws=None, ldy=None, y_init=None):
+    """xbits: uint16 [M, ldx] (ldx >= K).  Returns (y bits [M, N], full y buffer bits)."""
+    wq = wqmod()
+    M = xbits.shape[0] if M is None else M
+    x = t_u16(xbits, torch.bfloat16)
+    ldy = N if ldy is None else ldy
+    y = torch.empty((max(M, 1), ldy), dtype=torch.bfloat16, device=DEV)
+    if y_init is not None:
+        y.copy_(t_u16(y_init, torch.bfloat16))
+    ws = wq.workspace(wq.WQ_FMT_FP8_BLOCK, N, K, DEV) if ws is None else ws
+    wq.wq_gemm_fp8_block_path(packed, N, K, x, y, M, ws, path)
+    torch.cuda.synchronize()
+    full = bits_of(y)
+    return full[:M, :N], full
+
+
+def floor_fp8(xbits, codes, scales, K):
+    mx = float(np.abs(oracle.bf16_value(xbits[:, :K])).max())
+    mw = 0.0
+    for r0 in range(0, codes.shape[0], 2048):
+        w = oracle.dequant_fp8(codes[r0:r0 + 2048], scales[r0 // 128:(r0 + 2048) // 128])
+        mw = max(mw, float(np.nanmax(np.abs(w))))
+    return compare.abs_floor(K, mx, mw)
+
+
+def grade_fp8(ybits, xbits, codes, scales, K, cols=None, floor=None):
+    y64 = oracle.gemm_fp8(xbits, codes, scales, K=K, cols=cols)
+    if floor is None:
+        floor = floor_fp8(xbits, codes, scales, K)
+    yb = ybits if cols is None else ybits[:, cols]
+    return compare.grade(yb, y64, floor, "bf16")
+
+
+# ------------------------------------------------------------------ LUT3
+
+def pack_lut3(codes, qmap, scales):
+    wq = wqmod()
+    N, K = codes.shape
+    packed = torch.empty(wq.wq_lut3_packed_bytes(N, K), dtype=torch.uint8, device=DEV)
+    wq.wq_pack_lut3(t_u8(codes), t_u16(qmap, torch.float16), t_u16(scales, torch.float16), N, K, packed)
+    return packed
+
+
+def run_lut3(packed, N, K, xbits, M=None, ws=None, ldy=None, y_init=None):
+    wq = wqmod()
+    M = xbits.shape[0] if M is None else M
+    x = t_u16(xbits, torch.float16)
+    ldy = N if ldy is None else ldy
+    y = torch.empty((max(M, 1), ldy), dtype=torch.float16, device=DEV)
+    if y_init is not None:
+        y.copy_(t_u16(y_init, torch.float16))
+    ws = wq.workspace(wq.WQ_FMT_LUT3, N, K, DEV) if ws is None else ws
+    wq.wq_gemm_lut3(packed, N, K, x, y, M, ws)
+    torch.cuda.synchronize()
+    full = bits_of(y)
+    return full[:M, :N], full
+
+
+def floor_lut3(xbits, codes, qmap, scales, K):
+    mx = float(np.abs(oracle.f16_value(xbits[:, :K])).max())
+    mw = 0.0
+    for r0 in range(0, codes.shape[0], 2048):
+        w = oracle.dequant_lut3(codes[r0:r0 + 2048], qmap, scales[r0:r0 + 2048])
+        mw = max(mw, float(np.abs(w).max()))
+    return compare.abs_floor(K, mx, mw)
+
+
+def grade_lut3(ybits, xbits, codes, qmap, scales, K, cols=None, floor=None):
+    y64 = oracle.gemm_lut3(xbits, codes, qmap, scales, K=K, cols=cols)
+    if floor is None:
+        floor = floor_lut3(xbits, codes, qmap, scales, K)
+    yb = ybits if cols is None else ybits[:, cols]
+    return compare.grade(yb, y64, floor, "f16")
+
+
+def sample_cols(N: int, seed: int, n: int = 768) -> np.ndarray:
+    """Every column of the first and last 128, plus n random ones in between."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    mid = rng.choice(np.arange(128, max(128, N - 128)), size=min(n, max(0, N - 256)), replace=False)
+    return np.unique(np.concatenate([np.arange(min(128, N)), np.arange(max(0, N - 128), N), mid]))
+
+
+@functools.lru_cache(maxsize=4)
+def config_inputs(name: str):
+    fmt, N, K, Ms = synth.CONFIGS[name]
+    seed = synth.SEEDS[name]
+    if fmt == "fp8":
+        codes, scales = synth.fp8_weights(N, K, seed)
+        return fmt, N, K, Ms, (codes, scales)
+    codes, qmap, g = synth.lut3_weights(N, K, seed)
+    return fmt, N, K, Ms, (codes, qmap, g)

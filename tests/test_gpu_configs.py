@@ -1,0 +1,45 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times.  The oracle computes every column of the first and last 128 and 768
+random columns in between (all M rows each); the comparison rule is the same
+as at small sizes."""
+import numpy as np
+import pytest
+
+import synth
+import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+CASES = [(name, M) for name, (fmt, N, K, Ms) in synth.CONFIGS.items() for M in Ms]
+
+
+@pytest.mark.parametrize("name,M", CASES, ids=["%s-M%d" % c for c in CASES])
+def test_config_parity(name, M):
+    fmt, N, K, Ms, data = U.config_inputs(name)
+    U.note("config %s %s N=%d K=%d M=%d" % (name, fmt, N, K, M))
+    cols = U.sample_cols(N, 7 + M)
+    if fmt == "fp8":
+        codes, scales = data
+        xbits = synth.x_bf16(M, K, synth.SEEDS[name] + 100)
+        packed = _packed(name, lambda: U.pack_fp8(codes, scales))
+        y, _ = U.run_fp8(packed, N, K, xbits)
+        r = U.grade_fp8(y, xbits, codes, scales, K, cols=cols)
+    else:
+        codes, qmap, g = data
+        xbits = synth.x_f16(M, K, synth.SEEDS[name] + 100)
+        packed = _packed(name, lambda: U.pack_lut3(codes, qmap, g))
+        y, _ = U.run_lut3(packed, N, K, xbits)
+        r = U.grade_lut3(y, xbits, codes, qmap, g, K, cols=cols)
+    U.note("  %s" % r)
+    assert r.ok, str(r)
+    assert np.isfinite(r.rel_rms) and r.rel_rms < 4e-3
+
+
+_PACKED = {}
+
+
+def _packed(name, make):
+    if name not in _PACKED:
+        _PACKED.clear()            # keep one packed matrix resident at a time
+        _PACKED[name] = make()
+    return _PACKED[name]

@@ -1,0 +1,245 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle.
+
+* dequant: the unpack hooks run the GEMM's own device dequant and must match the
+  oracle bit for bit (every E4M3 code, every LUT code, FP16-subnormal products);
+* GEMM: every output within 2 BF16 ULP of the oracle rounded to BF16, or within
+  1e-3*sqrt(K)*max|x|*max|w| of it, on shapes that span several tiles and column
+  groups with ragged tails, every M from 1 to 32, both FP8 paths;
+* integer-exact inputs: the GPU result equals the exact integer rounded to BF16;
+* invariants: power-of-two scale linearity, M=32 = two M=16 halves, GEMV rows =
+  M=1 calls, MFMA rows = the M=16 call, determinism over repeats, strides and
+  canaries, workspace left zeroed, pack determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+AUTO, GEMV, MFMA = 0, 1, 2
+
+
+# ---------------------------------------------------------------- dequant
+
+def test_unpack_fp8_every_code_bit_exact():
+    wq = U.wqmod()
+    N, K = 256, 512
+    U.note("unpack fp8 %dx%d" % (N, K))
+    codes = (np.arange(N * K, dtype=np.int64) * 7 % 256).astype(np.uint8).reshape(N, K)
+    scales = np.full((N // 128, K // 128), 3.0, dtype=np.float32)
+    packed = U.pack_fp8(codes, scales)
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=U.DEV)
+    wq.wq_unpack_fp8_block(packed, N, K, out)
+    out32 = torch.empty((N, K), dtype=torch.float32, device=U.DEV)
+    wq.wq_unpack_fp8_block_f32(packed, N, K, out32)
+    torch.cuda.synchronize()
+    ref = oracle.e4m3_value(codes)
+    got = U.bits_of(out)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * N * K // 256
+    assert np.array_equal(got[~nan], oracle.bf16_rne(ref[~nan]))
+    assert np.all(np.isnan(oracle.bf16_value(got[nan])))
+    g32 = out32.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(g32), nan)
+    assert np.array_equal(g32[~nan], ref[~nan]) and np.array_equal(np.signbit(g32[~nan]), np.signbit(ref[~nan]))
+
+
+def test_unpack_lut3_bit_exact_including_subnormal_products():
+    wq = U.wqmod()
+    N, K = 48, 512                       # 3 tiles: a ragged column group for 4-tile groups
+    U.note("unpack lut3 %dx%d" % (N, K))
+    rng = np.random.Generator(np.random.PCG64(5))
+    codes = rng.integers(0, 8, size=(N, K), dtype=np.uint8)
+    codes[0, :8] = np.arange(8)
+    qmap = np.sort(rng.standard_normal(8).astype(np.float16))
+    qmap[2] = np.float16(0.0)
+    g = (rng.uniform(0.5, 1.0, size=(N, K // 128)) * np.ldexp(1.0, rng.integers(-20, 3, size=(N, K // 128))))
+    g = g.astype(np.float16)
+    packed = U.pack_lut3(codes, qmap.view(np.uint16), g.view(np.uint16))
+    out = torch.empty((N, K), dtype=torch.float16, device=U.DEV)
+    wq.wq_unpack_lut3(packed, N, K, out)
+    torch.cuda.synchronize()
+    ref = oracle.f16_rne(oracle.dequant_lut3(codes, qmap.view(np.uint16), g.view(np.uint16)))
+    got = U.bits_of(out)
+    assert np.array_equal(got, ref)
+    assert np.sum((np.abs(ref.view(np.float16)) < np.float16(2.0 ** -14)) & (ref & 0x7FFF != 0)) > 0
+
+
+def test_pack_is_deterministic_and_stride_free():
+    N, K = 384, 640
+    U.note("pack determinism")
+    codes, scales = synth.fp8_weights(N, K, 41)
+    a = U.pack_fp8(codes, scales).cpu().numpy()
+    b = U.pack_fp8(codes, scales, ldw=K + 96).cpu().numpy()
+    assert np.array_equal(a, b)
+    assert np.array_equal(a[N * K:].view(np.float32).reshape(scales.shape), scales)
+    c, q, g = synth.lut3_weights(80, 384, 42)
+    p1 = U.pack_lut3(c, q, g).cpu().numpy()
+    p2 = U.pack_lut3(c, q, g).cpu().numpy()
+    assert np.array_equal(p1, p2)
+
+
+def test_pack_lut3_rejects_code_above_7():
+    wq = U.wqmod()
+    U.note("pack lut3 bad code")
+    c, q, g = synth.lut3_weights(32, 256, 43)
+    c[17, 200] = 9
+    with pytest.raises(wq.WqError) as e:
+        U.pack_lut3(c, q, g)
+    assert e.value.status == 5
+
+
+# ------------------------------------------------------------------- GEMM
+
+FP8_SHAPES = [(256, 512), (384, 1024), (1024, 640), (640, 2048)]
+
+
+@pytest.mark.parametrize("N,K", FP8_SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 13, 16, 17, 24, 32])
+def test_gemm_fp8_parity(N, K, M):
+    U.note("fp8 parity N=%d K=%d M=%d" % (N, K, M))
+    codes, scales = synth.fp8_weights(N, K, 100 + N + K)
+    xbits = synth.x_bf16(M, K, 200 + M)
+    packed = U.pack_fp8(codes, scales)
+    paths = [AUTO, MFMA] + ([GEMV] if M <= 4 else [])
+    for path in paths:
+        y, _ = U.run_fp8(packed, N, K, xbits, path=path)
+        r = U.grade_fp8(y, xbits, codes, scales, K)
+        assert r.ok, "path %d: %s" % (path, r)
+        assert r.rel_rms < 4e-3, r
+
+
+LUT_SHAPES = [(48, 256), (272, 1024), (1024, 384), (528, 2048)]
+
+
+@pytest.mark.parametrize("N,K", LUT_SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 4, 7, 16, 20, 32])
+def test_gemm_lut3_parity(N, K, M):
+    U.note("lut3 parity N=%d K=%d M=%d" % (N, K, M))
+    c, q, g = synth.lut3_weights(N, K, 300 + N + K)
+    xbits = synth.x_f16(M, K, 400 + M)
+    packed = U.pack_lut3(c, q, g)
+    y, _ = U.run_lut3(packed, N, K, xbits)
+    r = U.grade_lut3(y, xbits, c, q, g, K)
+    assert r.ok, str(r)
+    assert r.rel_rms < 4e-3, r
+
+
+def test_integer_exact_results_are_exact():
+    U.note("integer exact")
+    rng = np.random.Generator(np.random.PCG64(44))
+    N, K, M = 256, 1024, 16
+    wi = rng.integers(-8, 9, size=(N, K))
+    xi = rng.integers(-2, 3, size=(M, K))
+    codes = torch.from_numpy(wi.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    scales = np.ones((N // 128, K // 128), dtype=np.float32)
+    xbits = torch.from_numpy(xi.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    exact = oracle.bf16_rne((xi @ wi.T).astype(np.float64))
+    packed = U.pack_fp8(codes, scales)
+    for M_ in (1, 4, 16):
+        for path in ([GEMV, MFMA] if M_ <= 4 else [MFMA]):
+            y, _ = U.run_fp8(packed, N, K, xbits[:M_], path=path)
+            assert np.array_equal(y, exact[:M_]), (M_, path)
+    ci = rng.integers(0, 8, size=(N, K)).astype(np.uint8)
+    qmap = np.arange(-4, 4).astype(np.float16).view(np.uint16)
+    g = np.ones((N, K // 128), dtype=np.float16).view(np.uint16)
+    xh = xi.astype(np.float16).view(np.uint16)
+    exact_l = oracle.f16_rne((xi @ (ci.astype(np.int64) - 4).T).astype(np.float64))
+    yl, _ = U.run_lut3(U.pack_lut3(ci, qmap, g), N, K, xh)
+    assert np.array_equal(yl, exact_l)
+
+
+def test_invariants_fp8():
+    U.note("invariants fp8")
+    N, K = 640, 1280
+    codes, scales = synth.fp8_weights(N, K, 45)
+    x32 = synth.x_bf16(32, K, 46)
+    packed = U.pack_fp8(codes, scales)
+    packed2 = U.pack_fp8(codes, scales * np.float32(2.0))
+    y32, _ = U.run_fp8(packed, N, K, x32, path=MFMA)
+    # scale linearity (bitwise): doubling every block scale doubles every output
+    y32b, _ = U.run_fp8(packed2, N, K, x32, path=MFMA)
+    v1, v2 = oracle.bf16_value(y32), oracle.bf16_value(y32b)
+    assert np.array_equal(v2, 2 * v1)
+    # M=32 is two M=16 halves
+    ya, _ = U.run_fp8(packed, N, K, x32[:16], path=MFMA)
+    yb, _ = U.run_fp8(packed, N, K, x32[16:], path=MFMA)
+    assert np.array_equal(np.vstack([ya, yb]), y32)
+    # MFMA rows of an M-call equal those rows of the M=16 call
+    for M in (5, 9, 13):
+        yM, _ = U.run_fp8(packed, N, K, x32[:M], path=MFMA)
+        assert np.array_equal(yM, ya[:M]), M
+    # GEMV rows of an M-call equal the M=1 calls of those rows
+    ones = [U.run_fp8(packed, N, K, x32[m:m + 1], path=GEMV)[0] for m in range(4)]
+    for M in (2, 3, 4):
+        yM, _ = U.run_fp8(packed, N, K, x32[:M], path=GEMV)
+        assert np.array_equal(yM, np.vstack(ones[:M])), M
+    # determinism over repeats, sharing one workspace across paths
+    wq = U.wqmod()
+    ws = wq.workspace(wq.WQ_FMT_FP8_BLOCK, N, K, U.DEV)
+    for i in range(20):
+        path = (MFMA, GEMV)[i % 2]
+        xs = x32[:16] if path == MFMA else x32[:4]
+        yr, _ = U.run_fp8(packed, N, K, xs, path=path, ws=ws)
+        assert np.array_equal(yr, ya if path == MFMA else np.vstack(ones[:4])), i
+    # the arrival counters at the head of the workspace are back to zero
+    head = ws[: (N // 16) * 4].cpu().numpy()
+    assert not head.any()
+
+
+def test_invariants_lut3():
+    U.note("invariants lut3")
+    N, K = 528, 1024
+    c, q, g = synth.lut3_weights(N, K, 47)
+    x32 = synth.x_f16(32, K, 48)
+    packed = U.pack_lut3(c, q, g)
+    g2 = (g.view(np.float16).astype(np.float32) * 2).astype(np.float16).view(np.uint16)
+    y32, _ = U.run_lut3(packed, N, K, x32)
+    y32b, _ = U.run_lut3(U.pack_lut3(c, q, g2), N, K, x32)
+    assert np.array_equal(oracle.f16_value(y32b), 2 * oracle.f16_value(y32))
+    ya, _ = U.run_lut3(packed, N, K, x32[:16])
+    yb, _ = U.run_lut3(packed, N, K, x32[16:])
+    assert np.array_equal(np.vstack([ya, yb]), y32)
+    for M in (1, 2, 7, 15):
+        yM, _ = U.run_lut3(packed, N, K, x32[:M])
+        assert np.array_equal(yM, ya[:M]), M
+    wq = U.wqmod()
+    ws = wq.workspace(wq.WQ_FMT_LUT3, N, K, U.DEV)
+    for i in range(20):
+        yr, _ = U.run_lut3(packed, N, K, x32[:16], ws=ws)
+        assert np.array_equal(yr, ya), i
+
+
+def test_strides_and_canaries():
+    U.note("strides and canaries")
+    N, K, M = 384, 768, 20
+    codes, scales = synth.fp8_weights(N, K, 49)
+    packed = U.pack_fp8(codes, scales)
+    xs = synth.x_bf16(M, K, 50, ld=K + 40)            # NaN canaries in the x padding
+    ldy = N + 24
+    canary = np.full((M, ldy), 0x7FAB, dtype=np.uint16)
+    for path in (AUTO, MFMA):
+        y, full = U.run_fp8(packed, N, K, xs, path=path, ldy=ldy, y_init=canary)
+        assert U.grade_fp8(y, xs, codes, scales, K).ok
+        assert np.all(full[:, N:] == 0x7FAB)
+    y4, full4 = U.run_fp8(packed, N, K, xs[:4], path=GEMV, ldy=ldy, y_init=canary[:4])
+    assert U.grade_fp8(y4, xs[:4], codes, scales, K).ok and np.all(full4[:, N:] == 0x7FAB)
+    c, q, g = synth.lut3_weights(N, K, 51)
+    xh = synth.x_f16(M, K, 52, ld=K + 8)
+    yl, fl = U.run_lut3(U.pack_lut3(c, q, g), N, K, xh, ldy=ldy, y_init=canary)
+    assert U.grade_lut3(yl, xh, c, q, g, K).ok and np.all(fl[:, N:] == 0x7FAB)
+
+
+def test_zero_rows_and_zero_matrix():
+    U.note("degenerate inputs")
+    N, K = 256, 512
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.ones((N // 128, K // 128), dtype=np.float32)
+    xbits = synth.x_bf16(8, K, 53)
+    for path in (MFMA, GEMV):
+        y, _ = U.run_fp8(U.pack_fp8(codes, scales), N, K, xbits[: (8 if path == MFMA else 4)], path=path)
+        assert not (y & 0x7FFF).any()

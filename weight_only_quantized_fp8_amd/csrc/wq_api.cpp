@@ -1,0 +1,403 @@
+// Host side of libwq: argument validation, device properties, options,
+// per-shape plan and the C ABI declared in include/wq.h.
+#include "wq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "wq_internal.h"
+
+namespace {
+
+using wq::GemmArgs;
+
+constexpr int kPackedFormatVersion = 1;
+constexpr int kMaxDevices = 64;
+
+// ----------------------------------------------------------------- options
+struct Options {
+    int force_path = WQ_PATH_AUTO;
+    int nt = 4;
+    int wg_per_cu = 2;
+};
+
+const Options& options()
+{
+    static Options o;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        if (const char* p = std::getenv("WQ_FORCE_PATH")) {
+            if (!std::strcmp(p, "gemv")) o.force_path = WQ_PATH_GEMV;
+            else if (!std::strcmp(p, "mfma")) o.force_path = WQ_PATH_MFMA;
+        }
+        if (const char* p = std::getenv("WQ_NT")) {
+            int v = std::atoi(p);
+            if (v == 2 || v == 4 || v == 8) o.nt = v;
+        }
+        if (const char* p = std::getenv("WQ_WG_PER_CU")) {
+            int v = std::atoi(p);
+            if (v >= 1 && v <= 8) o.wg_per_cu = v;
+        }
+    });
+    return o;
+}
+
+// -------------------------------------------------------- device properties
+struct DevInfo {
+    bool ok = false;
+    bool gfx950 = false;
+    int cu = 0;
+};
+
+std::mutex g_dev_mu;
+DevInfo g_dev[kMaxDevices];
+
+// Returns WQ_OK and fills *info for the current device.
+wq_status current_device(DevInfo* info, int* dev_out = nullptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return WQ_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DevInfo& d = g_dev[dev];
+    if (!d.ok) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return WQ_ERR_HIP;
+        }
+        d.cu = prop.multiProcessorCount;
+        d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.ok = true;
+    }
+    *info = d;
+    if (dev_out) *dev_out = dev;
+    return d.gfx950 ? WQ_OK : WQ_ERR_DEVICE;
+}
+
+// --------------------------------------------------------------------- plan
+struct Plan {
+    int kind = 0;
+    int nt = 4;
+    int n_tiles = 0, n_cg = 0, KB = 0, G = 0;
+    int64_t U = 0;
+    int slots = 0;          // column groups one work-group can touch
+    size_t lds = 0;
+    size_t partial_floats = 0;
+};
+
+int64_t range_begin(int64_t U, int G, int g) { return (U * g) / G; }
+
+Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
+{
+    Plan p;
+    p.kind = kind;
+    // The GEMV keeps its accumulators and x slice for up to 4 rows in VGPRs;
+    // two tiles per wave keep it at two waves per SIMD.  Its tile count must
+    // not depend on M (batch invariance), so it is fixed.
+    p.nt = kind == wq::KIND_GEMV_FP8 ? 2 : o.nt;
+    p.n_tiles = (int)(N / 16);
+    p.n_cg = (p.n_tiles + p.nt - 1) / p.nt;
+    p.KB = (int)(K / 128);
+    p.U = (int64_t)p.n_cg * p.KB;
+    int64_t g = (int64_t)cu * o.wg_per_cu;
+    p.G = (int)std::max<int64_t>(1, std::min<int64_t>(p.U, g));
+    int slots = 1;
+    for (int i = 0; i < p.G; ++i) {
+        int64_t b = range_begin(p.U, p.G, i), e = range_begin(p.U, p.G, i + 1);
+        slots = std::max<int>(slots, (int)((e - 1) / p.KB - b / p.KB + 1));
+    }
+    p.slots = slots;
+    const size_t slot_floats = (size_t)16 * 16 * p.nt;
+    p.lds = (size_t)slots * wq::kWavesPerWG * slot_floats * sizeof(float);
+    p.partial_floats = (size_t)p.G * 2 * slot_floats;
+    return p;
+}
+
+// Plans depend only on (kind, N, K, CU count, options); cache them so the
+// per-call host work is a lookup.
+struct PlanKey {
+    int kind;
+    int64_t N, K;
+    int cu;
+    bool operator==(const PlanKey& o) const { return kind == o.kind && N == o.N && K == o.K && cu == o.cu; }
+};
+
+constexpr int kPlanCache = 64;
+std::mutex g_plan_mu;
+PlanKey g_plan_keys[kPlanCache];
+Plan g_plans[kPlanCache];
+int g_plan_count = 0, g_plan_next = 0;
+
+Plan cached_plan(int kind, int64_t N, int64_t K, int cu)
+{
+    const PlanKey key{kind, N, K, cu};
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    for (int i = 0; i < g_plan_count; ++i)
+        if (g_plan_keys[i] == key) return g_plans[i];
+    Plan p = make_plan(kind, N, K, cu, options());
+    g_plan_keys[g_plan_next] = key;
+    g_plans[g_plan_next] = p;
+    g_plan_next = (g_plan_next + 1) % kPlanCache;
+    g_plan_count = std::min(g_plan_count + 1, kPlanCache);
+    return p;
+}
+
+constexpr size_t kCounterBytesAlign = 256;
+
+// Workspace = [arrival counters][partial tiles].  The counter region is sized
+// by the number of 16-column tiles, which bounds the column-group count of
+// every plan, so calls on different paths can share one workspace: each
+// leaves every counter at zero and the partial region always starts at the
+// same offset.
+size_t counters_bytes(int n_tiles)
+{
+    size_t b = (size_t)n_tiles * sizeof(uint32_t);
+    return (b + kCounterBytesAlign - 1) / kCounterBytesAlign * kCounterBytesAlign;
+}
+
+size_t workspace_for(const Plan& p) { return counters_bytes(p.n_tiles) + p.partial_floats * sizeof(float); }
+
+bool shape_ok(int fmt, int64_t N, int64_t K)
+{
+    if (N <= 0 || K <= 0 || K % 128) return false;
+    if (N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return false;
+    if (fmt == WQ_FMT_FP8_BLOCK) return N % 128 == 0;
+    if (fmt == WQ_FMT_LUT3) return N % 16 == 0;
+    return false;
+}
+
+// Kinds whose workspace a (fmt, N, K) GEMM may need.
+size_t workspace_max(int fmt, int64_t N, int64_t K, int cu)
+{
+    if (fmt == WQ_FMT_LUT3) return workspace_for(cached_plan(wq::KIND_MFMA_LUT, N, K, cu));
+    return std::max(workspace_for(cached_plan(wq::KIND_MFMA_FP8, N, K, cu)),
+                    workspace_for(cached_plan(wq::KIND_GEMV_FP8, N, K, cu)));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Shared front end of the two GEMMs.
+wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                      uint16_t* y, int64_t ldy, int64_t M, void* workspace, size_t workspace_bytes, int path,
+                      void* stream)
+{
+    // ---- validation that needs no HIP call
+    if (M < 0 || M > 32) return WQ_ERR_SHAPE;
+    if (!shape_ok(fmt, N, K)) return WQ_ERR_SHAPE;
+    if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_ERR_PATH;
+    if (M == 0) return WQ_OK;
+    if (!packed || !x || !y || !workspace) return WQ_ERR_NULL;
+    if (ldx < K || ldy < N) return WQ_ERR_LD;
+    if (!aligned16(packed) || !aligned16(x) || ldx % 8) return WQ_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15) || (reinterpret_cast<uintptr_t>(y) & 1)) return WQ_ERR_ALIGN;
+
+    const Options& o = options();
+    int kind;
+    if (fmt == WQ_FMT_LUT3) {
+        if (path == WQ_PATH_GEMV) return WQ_ERR_PATH;
+        kind = wq::KIND_MFMA_LUT;
+    } else {
+        int eff = path == WQ_PATH_AUTO ? o.force_path : path;
+        if (eff == WQ_PATH_AUTO) eff = M <= 4 ? WQ_PATH_GEMV : WQ_PATH_MFMA;
+        if (eff == WQ_PATH_GEMV && M > 4) {
+            if (path == WQ_PATH_GEMV) return WQ_ERR_PATH;
+            eff = WQ_PATH_MFMA;   // a forced GEMV lever only applies where it can run
+        }
+        kind = eff == WQ_PATH_GEMV ? wq::KIND_GEMV_FP8 : wq::KIND_MFMA_FP8;
+    }
+
+    // ---- device and workspace
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    const Plan p = cached_plan(kind, N, K, dev.cu);
+    if (workspace_bytes < workspace_max(fmt, N, K, dev.cu)) return WQ_ERR_WORKSPACE;
+
+    GemmArgs a{};
+    const uint8_t* base = static_cast<const uint8_t*>(packed);
+    a.codes = base;
+    if (fmt == WQ_FMT_FP8_BLOCK) {
+        a.scales = base + N * K;
+        a.qmap = nullptr;
+    } else {
+        a.scales = base + N * K / 2;
+        a.qmap = reinterpret_cast<const uint16_t*>(base + N * K / 2 + 2 * N * (K / 128));
+    }
+    a.N = (int)N;
+    a.KB = p.KB;
+    a.n_tiles = p.n_tiles;
+    a.n_cg = p.n_cg;
+    a.G = p.G;
+    a.U = p.U;
+    a.counters = static_cast<uint32_t*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(p.n_tiles));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    // rows 0..15, then (for M > 16) rows 16..M-1 as a second pass
+    for (int64_t r0 = 0; r0 < M; r0 += 16) {
+        const int rows = (int)std::min<int64_t>(16, M - r0);
+        a.x = x + r0 * ldx;
+        a.ldx = ldx;
+        a.y = y + r0 * ldy;
+        a.ldy = ldy;
+        a.rows = rows;
+        hipError_t e = wq::launch_gemm(kind, p.nt, kind == wq::KIND_GEMV_FP8 ? rows : 0, a, p.lds, s);
+        if (e != hipSuccess) return WQ_ERR_HIP;
+    }
+    return WQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wq_status_str(wq_status s)
+{
+    switch (s) {
+    case WQ_OK: return "WQ_OK";
+    case WQ_ERR_NULL: return "WQ_ERR_NULL: required pointer is NULL";
+    case WQ_ERR_SHAPE: return "WQ_ERR_SHAPE: unsupported M, N or K";
+    case WQ_ERR_LD: return "WQ_ERR_LD: leading dimension smaller than the row";
+    case WQ_ERR_WORKSPACE: return "WQ_ERR_WORKSPACE: workspace too small";
+    case WQ_ERR_CODE: return "WQ_ERR_CODE: a 3-bit code exceeds 7";
+    case WQ_ERR_DEVICE: return "WQ_ERR_DEVICE: current device is not gfx950";
+    case WQ_ERR_HIP: return "WQ_ERR_HIP: HIP runtime call failed";
+    case WQ_ERR_ALIGN: return "WQ_ERR_ALIGN: pointer or leading dimension misaligned";
+    case WQ_ERR_PATH: return "WQ_ERR_PATH: path cannot serve this format or M";
+    }
+    return "WQ_ERR_UNKNOWN";
+}
+
+int wq_packed_format_version(void) { return kPackedFormatVersion; }
+
+size_t wq_fp8_block_packed_bytes(int64_t N, int64_t K)
+{
+    if (!shape_ok(WQ_FMT_FP8_BLOCK, N, K)) return 0;
+    return (size_t)(N * K) + 4 * (size_t)(N / 128) * (size_t)(K / 128);
+}
+
+size_t wq_lut3_packed_bytes(int64_t N, int64_t K)
+{
+    if (!shape_ok(WQ_FMT_LUT3, N, K)) return 0;
+    return (size_t)(N * K / 2) + 2 * (size_t)N * (size_t)(K / 128) + 32;
+}
+
+wq_status wq_pack_fp8_block(const uint8_t* w_e4m3, int64_t ldw, const float* scales, int64_t N, int64_t K,
+                            void* packed, void* hip_stream)
+{
+    if (!shape_ok(WQ_FMT_FP8_BLOCK, N, K)) return WQ_ERR_SHAPE;
+    if (!w_e4m3 || !scales || !packed) return WQ_ERR_NULL;
+    if (ldw < K) return WQ_ERR_LD;
+    if (!aligned16(packed) || (reinterpret_cast<uintptr_t>(scales) & 3)) return WQ_ERR_ALIGN;
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    hipError_t e = wq::launch_pack_fp8(w_e4m3, ldw, scales, N, K, static_cast<uint8_t*>(packed),
+                                       static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
+}
+
+wq_status wq_gemm_fp8_block(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, uint16_t* y,
+                            int64_t ldy, int64_t M, void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    return gemm_common(WQ_FMT_FP8_BLOCK, packed, N, K, x, ldx, y, ldy, M, workspace, workspace_bytes,
+                       WQ_PATH_AUTO, hip_stream);
+}
+
+wq_status wq_gemm_fp8_block_path(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                                 uint16_t* y, int64_t ldy, int64_t M, void* workspace, size_t workspace_bytes,
+                                 int path, void* hip_stream)
+{
+    return gemm_common(WQ_FMT_FP8_BLOCK, packed, N, K, x, ldx, y, ldy, M, workspace, workspace_bytes, path,
+                       hip_stream);
+}
+
+wq_status wq_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* qmap, const uint16_t* scales, int64_t N,
+                       int64_t K, void* packed, void* hip_stream)
+{
+    if (!shape_ok(WQ_FMT_LUT3, N, K)) return WQ_ERR_SHAPE;
+    if (!codes || !qmap || !scales || !packed) return WQ_ERR_NULL;
+    if (ldc < K) return WQ_ERR_LD;
+    if (!aligned16(packed) || (reinterpret_cast<uintptr_t>(scales) & 1) || (reinterpret_cast<uintptr_t>(qmap) & 1))
+        return WQ_ERR_ALIGN;
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    uint8_t* pk = static_cast<uint8_t*>(packed);
+    uint32_t* status = reinterpret_cast<uint32_t*>(pk + N * K / 2 + 2 * N * (K / 128) + 16);
+    if (wq::launch_pack_lut3(codes, ldc, qmap, scales, N, K, pk, status, s) != hipSuccess) return WQ_ERR_HIP;
+    uint32_t host_status = 0;
+    if (hipMemcpyAsync(&host_status, status, sizeof(host_status), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return WQ_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return WQ_ERR_HIP;
+    return host_status ? WQ_ERR_CODE : WQ_OK;
+}
+
+wq_status wq_gemm_lut3(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, uint16_t* y,
+                       int64_t ldy, int64_t M, void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    return gemm_common(WQ_FMT_LUT3, packed, N, K, x, ldx, y, ldy, M, workspace, workspace_bytes, WQ_PATH_AUTO,
+                       hip_stream);
+}
+
+size_t wq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K)
+{
+    (void)M;
+    if (!shape_ok(fmt, N, K)) return 0;
+    DevInfo dev;
+    if (current_device(&dev) != WQ_OK) return 0;
+    return workspace_max(fmt, N, K, dev.cu);
+}
+
+wq_status wq_unpack_fp8_block(const void* packed, int64_t N, int64_t K, uint16_t* w_bf16, void* hip_stream)
+{
+    if (!shape_ok(WQ_FMT_FP8_BLOCK, N, K)) return WQ_ERR_SHAPE;
+    if (!packed || !w_bf16) return WQ_ERR_NULL;
+    if (!aligned16(packed) || !aligned16(w_bf16)) return WQ_ERR_ALIGN;
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    return wq::launch_unpack_fp8(static_cast<const uint8_t*>(packed), N, K, w_bf16, false,
+                                 static_cast<hipStream_t>(hip_stream)) == hipSuccess
+               ? WQ_OK
+               : WQ_ERR_HIP;
+}
+
+wq_status wq_unpack_fp8_block_f32(const void* packed, int64_t N, int64_t K, float* w_f32, void* hip_stream)
+{
+    if (!shape_ok(WQ_FMT_FP8_BLOCK, N, K)) return WQ_ERR_SHAPE;
+    if (!packed || !w_f32) return WQ_ERR_NULL;
+    if (!aligned16(packed) || !aligned16(w_f32)) return WQ_ERR_ALIGN;
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    return wq::launch_unpack_fp8(static_cast<const uint8_t*>(packed), N, K, w_f32, true,
+                                 static_cast<hipStream_t>(hip_stream)) == hipSuccess
+               ? WQ_OK
+               : WQ_ERR_HIP;
+}
+
+wq_status wq_unpack_lut3(const void* packed, int64_t N, int64_t K, uint16_t* w_f16, void* hip_stream)
+{
+    if (!shape_ok(WQ_FMT_LUT3, N, K)) return WQ_ERR_SHAPE;
+    if (!packed || !w_f16) return WQ_ERR_NULL;
+    if (!aligned16(packed) || !aligned16(w_f16)) return WQ_ERR_ALIGN;
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    return wq::launch_unpack_lut3(static_cast<const uint8_t*>(packed), N, K, w_f16,
+                                  static_cast<hipStream_t>(hip_stream)) == hipSuccess
+               ? WQ_OK
+               : WQ_ERR_HIP;
+}
+
+}  // extern "C"

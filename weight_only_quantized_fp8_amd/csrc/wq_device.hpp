@@ -1,0 +1,144 @@
+// Device primitives for the gfx950 weight-only-quantized decode GEMM.
+//
+// Everything here runs inside the GEMM, pack and unpack kernels; the unpack
+// test hooks call the very same dequant functions as the GEMM so that a
+// bit-exact unpack proves the GEMM's dequant.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 128;      // K extent of one scale block / group
+constexpr int kTileN = 16;       // MFMA tile width along N (and along the batch M)
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------- FP8 -> BF16
+// E4M3FN -> BF16 is exact: every E4M3 value (including subnormals down to
+// 2^-9) is a normal BF16 value, and NaN stays NaN.  gfx950's scaled converter
+// with a unit scale performs exactly that conversion for two bytes at a time.
+// HI selects bytes 2..3 of the word instead of bytes 0..1.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t word)
+{
+    bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight consecutive codes (two dwords, bytes in memory order) -> eight BF16.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1)
+{
+    u32x4_t r;
+    r[0] = e4m3x2_to_bf16x2<false>(w0);
+    r[1] = e4m3x2_to_bf16x2<true>(w0);
+    r[2] = e4m3x2_to_bf16x2<false>(w1);
+    r[3] = e4m3x2_to_bf16x2<true>(w1);
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// E4M3FN pair -> FP32 pair (exact), used by the strict-order GEMV.
+template <bool HI>
+__device__ __forceinline__ f32x2_t e4m3x2_to_f32x2(uint32_t word)
+{
+    return __builtin_amdgcn_cvt_pk_f32_fp8(word, HI);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
+{
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// ------------------------------------------------------- 3-bit LUT decode
+// The learned 8-entry FP16 map is scaled by the row's group scale (one RNE
+// FP16 multiply per entry, identical to rounding each dequantised weight) and
+// split into two byte planes: LO holds the low bytes of entries 0..7, HI the
+// high bytes.  A code word whose bytes are 0..7 is then a byte-permute
+// selector into each plane.
+struct LutPlanes {
+    uint32_t lo0, lo1;   // low bytes of entries 0..3 / 4..7
+    uint32_t hi0, hi1;   // high bytes of entries 0..3 / 4..7
+};
+
+// q[i] holds map entries (2i, 2i+1) as an FP16 pair; g is the group scale.
+__device__ __forceinline__ LutPlanes lut_scaled_planes(const uint32_t q[4], _Float16 g)
+{
+    f16x2_t gg = {g, g};
+    uint32_t e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        e[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, q[i]) * gg);
+    LutPlanes p;
+    // v_perm pool = {S0 (bytes 4..7), S1 (bytes 0..3)}
+    p.lo0 = __builtin_amdgcn_perm(e[1], e[0], 0x06040200u);
+    p.hi0 = __builtin_amdgcn_perm(e[1], e[0], 0x07050301u);
+    p.lo1 = __builtin_amdgcn_perm(e[3], e[2], 0x06040200u);
+    p.hi1 = __builtin_amdgcn_perm(e[3], e[2], 0x07050301u);
+    return p;
+}
+
+// One packed dword = eight 3-bit codes: byte b carries code e=b in its low
+// nibble and code e=b+4 in its high nibble.  Returns the eight FP16 weights in
+// order e = 0..7.
+__device__ __forceinline__ f16x8_t lut_decode8(uint32_t word, const LutPlanes& p)
+{
+    uint32_t sl = word & 0x07070707u;
+    uint32_t sh = (word >> 4) & 0x07070707u;
+    uint32_t l0 = __builtin_amdgcn_perm(p.lo1, p.lo0, sl);
+    uint32_t h0 = __builtin_amdgcn_perm(p.hi1, p.hi0, sl);
+    uint32_t l1 = __builtin_amdgcn_perm(p.lo1, p.lo0, sh);
+    uint32_t h1 = __builtin_amdgcn_perm(p.hi1, p.hi0, sh);
+    u32x4_t r;
+    r[0] = __builtin_amdgcn_perm(h0, l0, 0x05010400u);
+    r[1] = __builtin_amdgcn_perm(h0, l0, 0x07030602u);
+    r[2] = __builtin_amdgcn_perm(h1, l1, 0x05010400u);
+    r[3] = __builtin_amdgcn_perm(h1, l1, 0x07030602u);
+    return __builtin_bit_cast(f16x8_t, r);
+}
+
+// ------------------------------------------------------------------ MFMA
+// D(16x16) += A(16x32) * B(32x16).  Lane l supplies A row (l % 16) and B
+// column (l % 16), eight K values each at K group (l / 16); lane l receives
+// D rows 4*(l/16) .. 4*(l/16)+3 of column (l % 16).
+__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// --------------------------------------------------------------- epilogue
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float v)
+{
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Streaming 16-byte load for single-use weight bytes.
+__device__ __forceinline__ uint4 load_stream16(const void* p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint4 load16(const void* p)
+{
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+}  // namespace wq

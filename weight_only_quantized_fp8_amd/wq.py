@@ -1,0 +1,196 @@
+"""ctypes binding of include/wq.h.
+
+Every ``wq_*`` function here has the name, argument order and meaning of the C
+function it wraps; tensors stand in for device pointers and their leading
+dimensions, and a non-OK status raises :class:`WqError`.  A few helpers
+(``alloc_*``, ``workspace``, ``pack_*``/``gemm_*``) allocate outputs with torch.
+Nothing here computes: every step runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "WqError", "LIB_PATH", "lib",
+    "WQ_OK", "WQ_FMT_FP8_BLOCK", "WQ_FMT_LUT3", "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA",
+    "wq_status_str", "wq_packed_format_version",
+    "wq_fp8_block_packed_bytes", "wq_pack_fp8_block", "wq_gemm_fp8_block", "wq_gemm_fp8_block_path",
+    "wq_lut3_packed_bytes", "wq_pack_lut3", "wq_gemm_lut3",
+    "wq_gemm_workspace_bytes", "wq_unpack_fp8_block", "wq_unpack_fp8_block_f32", "wq_unpack_lut3",
+    "workspace", "pack_fp8", "pack_lut3", "gemm_fp8", "gemm_lut3",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwq.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libwq.so is not built (%s); run __graft_entry__.build() or "
+                      "python weight_only_quantized_fp8_amd/build.py" % LIB_PATH)
+lib = ctypes.CDLL(LIB_PATH)
+
+WQ_OK = 0
+WQ_FMT_FP8_BLOCK, WQ_FMT_LUT3 = 0, 1
+WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
+
+_P, _I64, _SZ, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+_SIGS = {
+    "wq_status_str": (ctypes.c_char_p, [_INT]),
+    "wq_packed_format_version": (_INT, []),
+    "wq_fp8_block_packed_bytes": (_SZ, [_I64, _I64]),
+    "wq_pack_fp8_block": (_INT, [_P, _I64, _P, _I64, _I64, _P, _P]),
+    "wq_gemm_fp8_block": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
+    "wq_gemm_fp8_block_path": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _INT, _P]),
+    "wq_lut3_packed_bytes": (_SZ, [_I64, _I64]),
+    "wq_pack_lut3": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _P]),
+    "wq_gemm_lut3": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
+    "wq_gemm_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
+    "wq_unpack_fp8_block": (_INT, [_P, _I64, _I64, _P, _P]),
+    "wq_unpack_fp8_block_f32": (_INT, [_P, _I64, _I64, _P, _P]),
+    "wq_unpack_lut3": (_INT, [_P, _I64, _I64, _P, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class WqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, wq_status_str(status)))
+
+
+def _check(st: int, where: str) -> None:
+    if st != WQ_OK:
+        raise WqError(st, where)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+# ------------------------------------------------------------- raw C calls
+
+def wq_status_str(status: int) -> str:
+    return lib.wq_status_str(int(status)).decode()
+
+
+def wq_packed_format_version() -> int:
+    return lib.wq_packed_format_version()
+
+
+def wq_fp8_block_packed_bytes(N: int, K: int) -> int:
+    return lib.wq_fp8_block_packed_bytes(N, K)
+
+
+def wq_lut3_packed_bytes(N: int, K: int) -> int:
+    return lib.wq_lut3_packed_bytes(N, K)
+
+
+def wq_gemm_workspace_bytes(fmt: int, M: int, N: int, K: int) -> int:
+    return lib.wq_gemm_workspace_bytes(fmt, M, N, K)
+
+
+def wq_pack_fp8_block(w_e4m3, scales, N: int, K: int, packed, stream=None) -> None:
+    _check(lib.wq_pack_fp8_block(_ptr(w_e4m3), _ld(w_e4m3), _ptr(scales), N, K, _ptr(packed), _stream(stream)),
+           "wq_pack_fp8_block")
+
+
+def wq_gemm_fp8_block(packed, N: int, K: int, x, y, M: int, workspace, stream=None) -> None:
+    _check(lib.wq_gemm_fp8_block(_ptr(packed), N, K, _ptr(x), _ld(x), _ptr(y), _ld(y), M, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "wq_gemm_fp8_block")
+
+
+def wq_gemm_fp8_block_path(packed, N: int, K: int, x, y, M: int, workspace, path: int, stream=None) -> None:
+    _check(lib.wq_gemm_fp8_block_path(_ptr(packed), N, K, _ptr(x), _ld(x), _ptr(y), _ld(y), M, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), path, _stream(stream)),
+           "wq_gemm_fp8_block_path")
+
+
+def wq_pack_lut3(codes, qmap, scales, N: int, K: int, packed, stream=None) -> None:
+    _check(lib.wq_pack_lut3(_ptr(codes), _ld(codes), _ptr(qmap), _ptr(scales), N, K, _ptr(packed),
+                            _stream(stream)), "wq_pack_lut3")
+
+
+def wq_gemm_lut3(packed, N: int, K: int, x, y, M: int, workspace, stream=None) -> None:
+    _check(lib.wq_gemm_lut3(_ptr(packed), N, K, _ptr(x), _ld(x), _ptr(y), _ld(y), M, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream)), "wq_gemm_lut3")
+
+
+def wq_unpack_fp8_block(packed, N: int, K: int, w_bf16, stream=None) -> None:
+    _check(lib.wq_unpack_fp8_block(_ptr(packed), N, K, _ptr(w_bf16), _stream(stream)), "wq_unpack_fp8_block")
+
+
+def wq_unpack_fp8_block_f32(packed, N: int, K: int, w_f32, stream=None) -> None:
+    _check(lib.wq_unpack_fp8_block_f32(_ptr(packed), N, K, _ptr(w_f32), _stream(stream)),
+           "wq_unpack_fp8_block_f32")
+
+
+def wq_unpack_lut3(packed, N: int, K: int, w_f16, stream=None) -> None:
+    _check(lib.wq_unpack_lut3(_ptr(packed), N, K, _ptr(w_f16), _stream(stream)), "wq_unpack_lut3")
+
+
+# -------------------------------------------------------- torch helpers
+
+def workspace(fmt: int, N: int, K: int, device="cuda"):
+    """Zero-filled workspace for GEMMs of this format and shape (any M, any path)."""
+    import torch
+    nbytes = wq_gemm_workspace_bytes(fmt, 1, N, K)
+    if nbytes == 0:
+        raise WqError(2, "wq_gemm_workspace_bytes")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def pack_fp8(codes, scales, stream=None):
+    """Pack E4M3 codes [N, K] (uint8, cuda) and FP32 block scales into a new buffer."""
+    import torch
+    N, K = codes.shape[0], codes.shape[1]
+    packed = torch.empty(wq_fp8_block_packed_bytes(N, K), dtype=torch.uint8, device=codes.device)
+    wq_pack_fp8_block(codes, scales, N, K, packed, stream)
+    return packed
+
+
+def pack_lut3(codes, qmap, scales, stream=None):
+    """Pack 3-bit codes [N, K] (uint8), FP16 map [8] and FP16 group scales into a new buffer."""
+    import torch
+    N, K = codes.shape[0], codes.shape[1]
+    packed = torch.empty(wq_lut3_packed_bytes(N, K), dtype=torch.uint8, device=codes.device)
+    wq_pack_lut3(codes, qmap, scales, N, K, packed, stream)
+    return packed
+
+
+def gemm_fp8(packed, N: int, K: int, x, ws, path: int = WQ_PATH_AUTO, stream=None):
+    """y [M, N] (bfloat16) = x [M, K] (bfloat16) . dequant(W)^T."""
+    import torch
+    M = x.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    wq_gemm_fp8_block_path(packed, N, K, x, y, M, ws, path, stream)
+    return y
+
+
+def gemm_lut3(packed, N: int, K: int, x, ws, stream=None):
+    """y [M, N] (float16) = x [M, K] (float16) . dequant(W)^T."""
+    import torch
+    M = x.shape[0]
+    y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    wq_gemm_lut3(packed, N, K, x, y, M, ws, stream)
+    return y
