@@ -38,10 +38,12 @@
  *   - Calls are thread-safe.  Calls that share a workspace must be ordered
  *     (same stream, or synchronised): concurrent calls on one workspace race.
  *
- * Environment options, read once at the first call that needs them:
- *   WQ_FORCE_PATH = auto | gemv | mfma   path for wq_gemm_fp8_block (default auto)
- *   WQ_NT         = 2 | 4 | 8            16-column MFMA tiles per wave (default 4)
- *   WQ_WG_PER_CU  = 1 .. 8               persistent work-groups per compute unit
+ * Environment options, read once at the first call that needs them (for
+ * sweeps without a rebuild; the defaults are the per-shape plan):
+ *   WQ_FORCE_PATH   = auto | gemv | mfma  path for wq_gemm_fp8_block (default auto)
+ *   WQ_NT           = 1 | 2 | 4           16-column MFMA tiles per wave
+ *   WQ_SPLIT        = 1 .. 16             waves splitting K inside a work-group
+ *   WQ_WAVES_PER_CU = 1 .. 32             resident waves per CU the plan aims for (4)
  */
 #ifndef WQ_H_
 #define WQ_H_
@@ -58,7 +60,7 @@ typedef enum {
     WQ_ERR_NULL = 1,       /* a required pointer is NULL                              */
     WQ_ERR_SHAPE = 2,      /* M, N or K outside what the format/path supports         */
     WQ_ERR_LD = 3,         /* a leading dimension is smaller than the row length      */
-    WQ_ERR_WORKSPACE = 4,  /* workspace smaller than wq_gemm_workspace_bytes()        */
+    WQ_ERR_WORKSPACE = 4,  /* workspace smaller than wq_gemm_workspace_bytes() (unused) */
     WQ_ERR_CODE = 5,       /* wq_pack_lut3 found a code > 7 (packed buffer not valid) */
     WQ_ERR_DEVICE = 6,     /* current device is not gfx950                            */
     WQ_ERR_HIP = 7,        /* a HIP runtime call failed (includes: no device)         */
@@ -104,8 +106,9 @@ wq_status wq_pack_fp8_block(const uint8_t* w_e4m3, int64_t ldw, const float* sca
  *   x          device, [M][ldx] BF16 bits; ldx >= K, ldx % 8 == 0, x 16-byte aligned
  *   y          device, [M][ldy] BF16 bits (RNE); ldy >= N; only columns < N are written
  *   M          0 .. 32; M == 0 queues nothing and returns WQ_OK
- *   workspace  device, >= wq_gemm_workspace_bytes(WQ_FMT_FP8_BLOCK, M, N, K) bytes,
- *              zero-filled before its first use; every call leaves it zero-filled again
+ *   workspace  device scratch of wq_gemm_workspace_bytes(...) bytes; that size is 0
+ *              in this version (every output is reduced inside one work-group), so
+ *              NULL is accepted.  Kept in the interface for schedules that need one.
  * Numerics: every output is within 2 BF16 ULP of the exact result rounded to
  * BF16, or within 1e-3*sqrt(K)*max|x|*max|w| of the exact result.  Results are
  * deterministic, and row r of an M-row call equals row r of any other call on
@@ -155,9 +158,8 @@ wq_status wq_gemm_lut3(const void* packed, int64_t N, int64_t K,
 
 /* ------------------------------------------------------------ workspace */
 
-/* Workspace bytes a GEMM of this format and shape needs on the current
- * device (the same for every M and path, so one buffer serves all of them).
- * Returns 0 if the shape is unsupported or the device cannot be queried. */
+/* Workspace bytes a GEMM of this format and shape needs (the same for every M
+ * and path).  0 for every shape in this version. */
 size_t wq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* ----------------------------------------------------------- test hooks */

@@ -22,8 +22,9 @@ constexpr int kMaxDevices = 64;
 // ----------------------------------------------------------------- options
 struct Options {
     int force_path = WQ_PATH_AUTO;
-    int nt = 4;
-    int wg_per_cu = 2;
+    int nt = 0;              // 0 = per-shape choice
+    int split = 0;           // 0 = per-shape choice
+    int waves_per_cu = 4;    // target resident waves per compute unit
 };
 
 const Options& options()
@@ -37,11 +38,15 @@ const Options& options()
         }
         if (const char* p = std::getenv("WQ_NT")) {
             int v = std::atoi(p);
-            if (v == 2 || v == 4 || v == 8) o.nt = v;
+            if (v == 1 || v == 2 || v == 4) o.nt = v;
         }
-        if (const char* p = std::getenv("WQ_WG_PER_CU")) {
+        if (const char* p = std::getenv("WQ_SPLIT")) {
             int v = std::atoi(p);
-            if (v >= 1 && v <= 8) o.wg_per_cu = v;
+            if (v >= 1 && v <= 16) o.split = v;
+        }
+        if (const char* p = std::getenv("WQ_WAVES_PER_CU")) {
+            int v = std::atoi(p);
+            if (v >= 1 && v <= 32) o.waves_per_cu = v;
         }
     });
     return o;
@@ -83,41 +88,38 @@ wq_status current_device(DevInfo* info, int* dev_out = nullptr)
 }
 
 // --------------------------------------------------------------------- plan
+// One work-group per column group of NT 16-column tiles; its S waves split
+// the K blocks.  NT and S are chosen so that about `waves_per_cu` waves per
+// compute unit are resident: wide tiles (NT = 4, each activation fragment
+// feeds four MFMAs) where N allows, narrower tiles and a deeper K split for
+// the low-N projections.
 struct Plan {
     int kind = 0;
     int nt = 4;
-    int n_tiles = 0, n_cg = 0, KB = 0, G = 0;
-    int64_t U = 0;
-    int slots = 0;          // column groups one work-group can touch
-    size_t lds = 0;
-    size_t partial_floats = 0;
+    int split = 1;
+    int n_tiles = 0, n_cg = 0, KB = 0;
 };
-
-int64_t range_begin(int64_t U, int G, int g) { return (U * g) / G; }
 
 Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
 {
     Plan p;
     p.kind = kind;
-    // The GEMV keeps its accumulators and x slice for up to 4 rows in VGPRs;
-    // two tiles per wave keep it at two waves per SIMD.  Its tile count must
-    // not depend on M (batch invariance), so it is fixed.
-    p.nt = kind == wq::KIND_GEMV_FP8 ? 2 : o.nt;
     p.n_tiles = (int)(N / 16);
-    p.n_cg = (p.n_tiles + p.nt - 1) / p.nt;
     p.KB = (int)(K / 128);
-    p.U = (int64_t)p.n_cg * p.KB;
-    int64_t g = (int64_t)cu * o.wg_per_cu;
-    p.G = (int)std::max<int64_t>(1, std::min<int64_t>(p.U, g));
-    int slots = 1;
-    for (int i = 0; i < p.G; ++i) {
-        int64_t b = range_begin(p.U, p.G, i), e = range_begin(p.U, p.G, i + 1);
-        slots = std::max<int>(slots, (int)((e - 1) / p.KB - b / p.KB + 1));
+    const int target = std::max(1, cu * o.waves_per_cu);
+    // The GEMV always covers 4 tiles per wave (one column per lane); its plan
+    // must not depend on M (batch invariance), and it does not.
+    int nt = 4;
+    if (kind != wq::KIND_GEMV_FP8) {
+        if (o.nt) nt = o.nt;
+        else
+            while (nt > 1 && (int64_t)((p.n_tiles + nt - 1) / nt) * wq::max_split(kind, nt) < target) nt /= 2;
     }
-    p.slots = slots;
-    const size_t slot_floats = (size_t)16 * 16 * p.nt;
-    p.lds = (size_t)slots * wq::kWavesPerWG * slot_floats * sizeof(float);
-    p.partial_floats = (size_t)p.G * 2 * slot_floats;
+    p.nt = nt;
+    p.n_cg = (p.n_tiles + nt - 1) / nt;
+    int s = o.split ? o.split : (int)std::lround((double)target / p.n_cg);
+    s = std::max(1, std::min(s, std::min(wq::max_split(kind, nt), p.KB)));
+    p.split = s;
     return p;
 }
 
@@ -150,21 +152,6 @@ Plan cached_plan(int kind, int64_t N, int64_t K, int cu)
     return p;
 }
 
-constexpr size_t kCounterBytesAlign = 256;
-
-// Workspace = [arrival counters][partial tiles].  The counter region is sized
-// by the number of 16-column tiles, which bounds the column-group count of
-// every plan, so calls on different paths can share one workspace: each
-// leaves every counter at zero and the partial region always starts at the
-// same offset.
-size_t counters_bytes(int n_tiles)
-{
-    size_t b = (size_t)n_tiles * sizeof(uint32_t);
-    return (b + kCounterBytesAlign - 1) / kCounterBytesAlign * kCounterBytesAlign;
-}
-
-size_t workspace_for(const Plan& p) { return counters_bytes(p.n_tiles) + p.partial_floats * sizeof(float); }
-
 bool shape_ok(int fmt, int64_t N, int64_t K)
 {
     if (N <= 0 || K <= 0 || K % 128) return false;
@@ -172,14 +159,6 @@ bool shape_ok(int fmt, int64_t N, int64_t K)
     if (fmt == WQ_FMT_FP8_BLOCK) return N % 128 == 0;
     if (fmt == WQ_FMT_LUT3) return N % 16 == 0;
     return false;
-}
-
-// Kinds whose workspace a (fmt, N, K) GEMM may need.
-size_t workspace_max(int fmt, int64_t N, int64_t K, int cu)
-{
-    if (fmt == WQ_FMT_LUT3) return workspace_for(cached_plan(wq::KIND_MFMA_LUT, N, K, cu));
-    return std::max(workspace_for(cached_plan(wq::KIND_MFMA_FP8, N, K, cu)),
-                    workspace_for(cached_plan(wq::KIND_GEMV_FP8, N, K, cu)));
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -194,10 +173,12 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
     if (!shape_ok(fmt, N, K)) return WQ_ERR_SHAPE;
     if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_ERR_PATH;
     if (M == 0) return WQ_OK;
-    if (!packed || !x || !y || !workspace) return WQ_ERR_NULL;
+    if (!packed || !x || !y) return WQ_ERR_NULL;
     if (ldx < K || ldy < N) return WQ_ERR_LD;
     if (!aligned16(packed) || !aligned16(x) || ldx % 8) return WQ_ERR_ALIGN;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 15) || (reinterpret_cast<uintptr_t>(y) & 1)) return WQ_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(y) & 1) return WQ_ERR_ALIGN;
+    (void)workspace;          // the split-K schedule needs no workspace (0 bytes)
+    (void)workspace_bytes;
 
     const Options& o = options();
     int kind;
@@ -219,7 +200,6 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
     wq_status st = current_device(&dev);
     if (st != WQ_OK) return st;
     const Plan p = cached_plan(kind, N, K, dev.cu);
-    if (workspace_bytes < workspace_max(fmt, N, K, dev.cu)) return WQ_ERR_WORKSPACE;
 
     GemmArgs a{};
     const uint8_t* base = static_cast<const uint8_t*>(packed);
@@ -235,10 +215,6 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
     a.KB = p.KB;
     a.n_tiles = p.n_tiles;
     a.n_cg = p.n_cg;
-    a.G = p.G;
-    a.U = p.U;
-    a.counters = static_cast<uint32_t*>(workspace);
-    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(p.n_tiles));
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // rows 0..15, then (for M > 16) rows 16..M-1 as a second pass
@@ -249,7 +225,7 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
         a.y = y + r0 * ldy;
         a.ldy = ldy;
         a.rows = rows;
-        hipError_t e = wq::launch_gemm(kind, p.nt, kind == wq::KIND_GEMV_FP8 ? rows : 0, a, p.lds, s);
+        hipError_t e = wq::launch_gemm(kind, p.nt, kind == wq::KIND_GEMV_FP8 ? rows : 0, a, p.split, s);
         if (e != hipSuccess) return WQ_ERR_HIP;
     }
     return WQ_OK;
@@ -351,11 +327,13 @@ wq_status wq_gemm_lut3(const void* packed, int64_t N, int64_t K, const uint16_t*
 
 size_t wq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K)
 {
+    // Every output tile is reduced inside one work-group (LDS), so no device
+    // workspace is needed for any format, shape or M.
+    (void)fmt;
     (void)M;
-    if (!shape_ok(fmt, N, K)) return 0;
-    DevInfo dev;
-    if (current_device(&dev) != WQ_OK) return 0;
-    return workspace_max(fmt, N, K, dev.cu);
+    (void)N;
+    (void)K;
+    return 0;
 }
 
 wq_status wq_unpack_fp8_block(const void* packed, int64_t N, int64_t K, uint16_t* w_bf16, void* hip_stream)

@@ -141,4 +141,14 @@ __device__ __forceinline__ uint4 load16(const void* p)
     return *reinterpret_cast<const uint4*>(p);
 }
 
+// 16-byte load of data that is read-only for the kernel's lifetime, through
+// the constant address space: a wave-uniform address becomes a scalar load
+// into SGPRs.
+__device__ __forceinline__ uint4 load_uniform16(const void* p)
+{
+    typedef const __attribute__((address_space(4))) u32x4_t* cptr;
+    const u32x4_t v = *(cptr)(p);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 }  // namespace wq

@@ -8,8 +8,10 @@
 
 namespace wq {
 
-constexpr int kWavesPerWG = 4;            // work-group = 4 wave64 = 256 lanes
-constexpr int kThreadsPerWG = kWavesPerWG * 64;
+// Prefetch depth (K blocks in flight per wave beyond the one being computed).
+constexpr int kDepthMfmaFp8 = 2;
+constexpr int kDepthMfmaLut = 2;
+constexpr int kDepthGemv = 2;
 
 enum Kind : int {
     KIND_MFMA_FP8 = 0,   // 16-row BF16 MFMA tile, FP8 block-scaled weights
@@ -17,13 +19,18 @@ enum Kind : int {
     KIND_GEMV_FP8 = 2,   // strict-K-order FP32 GEMV, M <= 4, FP8 weights
 };
 
-// Everything a GEMM launch needs.  A "unit" is one column group (NT tiles of
-// 16 output columns) times one 128-wide K block; the U = n_cg * KB units are
-// split into G contiguous, near-equal ranges, one per persistent work-group.
+// Largest split (waves per work-group) a kernel may use.  A work-group runs
+// on one CU, so its S waves must fit the register file: the launch bound
+// 64*S caps a wave at 512/ceil(S/4) VGPRs.  The 4-tile kernels (MFMA and
+// GEMV) need up to 256 (S <= 8); the narrow MFMA kernels fit in 128 (S <= 16).
+constexpr int max_split(int kind, int nt) { return (kind == KIND_GEMV_FP8 || nt >= 4) ? 8 : 16; }
+
+// Everything a GEMM launch needs.  The grid has one work-group per column
+// group (NT tiles of 16 output columns); its S waves split the K blocks.
 struct GemmArgs {
     const uint8_t* codes;     // packed code units
     const void* scales;       // FP8: float [N/128][KB]; LUT: half [n_tiles][KB][16]
-    const uint16_t* qmap;     // LUT: 8 FP16 map entries (16-byte aligned)
+    const uint16_t* qmap;     // LUT: 8 FP16 map entries (4-byte aligned)
     const uint16_t* x;        // activations [rows][ldx]
     int64_t ldx;
     uint16_t* y;              // outputs [rows][ldy]
@@ -32,15 +39,10 @@ struct GemmArgs {
     int N;                    // output columns
     int KB;                   // K / 128
     int n_tiles;              // N / 16
-    int n_cg;                 // column groups = ceil(n_tiles / NT)
-    int G;                    // work-groups in the grid
-    int64_t U;                // units = n_cg * KB
-    float* partials;          // workspace: [G][2][16 * 16 * NT] FP32 partial tiles
-    uint32_t* counters;       // workspace: [n_cg] arrival counters (kept at zero)
+    int n_cg;                 // column groups = ceil(n_tiles / NT) = grid size
 };
 
-hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, size_t lds_bytes,
-                       hipStream_t stream);
+hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream);
 
 hipError_t launch_pack_fp8(const uint8_t* w, int64_t ldw, const float* scales, int64_t N,
                            int64_t K, uint8_t* packed, hipStream_t stream);

@@ -16,40 +16,31 @@
 //         high nibble.  Group scales follow as FP16 [tile][kb][16 rows], then
 //         the 8 map entries (FP16), then a 16-byte pack-status word.
 //
-// GEMM schedule.  U = n_cg * KB units (a column group = NT tiles) are split
-// into G contiguous ranges, one per persistent work-group, and each range into
-// 4 contiguous per-wave ranges (stream-K; the FLUTE PR credits "striped
-// Stream-K" for a tail-free grid, and the atlas "Module m16_tc" docs, section
-// "WHY THE FFN ARM LOSES", show what a partial last wave costs).  A wave walks
-// its units with the next unit's loads in flight, folds each 128-K block onto
-// FP32 accumulators, and on leaving a column group parks its partial tile in
-// LDS.  The work-group then sums its waves' partials in wave order; a column
-// group shared with neighbouring work-groups goes through the workspace and
-// the last work-group to arrive sums all contributions in work-group order.
-// Every sum therefore has a fixed order: results are deterministic.
+// GEMM schedule.  One work-group owns one column group (NT tiles of 16 output
+// columns) over the whole of K.  Its S waves split the K blocks into S
+// contiguous, near-equal ranges (split-K), so a low-N projection still puts
+// enough waves on the chip; S is chosen per shape by the host.  Each wave walks
+// its range with the next D units' loads in flight (a register ring), folds
+// every 128-K block onto FP32 accumulators, and parks its partial tile in LDS;
+// the work-group then sums the S partials in wave order and writes y.  No two
+// work-groups share an output, so there is no cross-work-group traffic, no
+// workspace and no fence, and every sum has a fixed order: results are
+// deterministic and do not depend on M.
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
 namespace wq {
 
-// 4 KiB of zeros: the source of loads that have nothing to fetch (the
-// prefetch past the end of a wave's range, tiles past N, batch rows >= M).
-// Loading from here keeps every load unconditional.
+// 4 KiB of zeros: the source of loads that have nothing to fetch (prefetch
+// past the end of a wave's range, tiles past N, batch rows >= M).  Loading
+// from here keeps every load unconditional, so the compiler can count loads
+// in flight statically.
 __device__ __attribute__((aligned(256))) uint8_t g_zero_page[4096];
 
-__device__ __forceinline__ int64_t range_begin(int64_t U, int G, int g)
-{
-    return (U * g) / G;
-}
-
-// The work-group whose range holds unit u.
-__device__ __forceinline__ int wg_of(int64_t U, int G, int64_t u)
-{
-    return (int)(((u + 1) * G - 1) / U);
-}
-
 // ======================================================================
-// Policies: per-unit loads and compute for each kernel kind.
+// Policies: per-unit loads and compute for each kernel kind.  A policy is
+// bound to one column group; load(r, kb, valid) fetches K block kb into the
+// register set r (from the zero page when !valid), compute(r) consumes it.
 // ======================================================================
 
 // ---- FP8 weights, 16-row BF16 MFMA tile ------------------------------------
@@ -57,53 +48,51 @@ __device__ __forceinline__ int wg_of(int64_t U, int G, int64_t u)
 // (lane: batch row m = l%16).  Output D[n][m] -> lane holds n = 4(l/16)+v.
 template <int NT>
 struct MfmaFp8 {
+    static constexpr int KIND = KIND_MFMA_FP8;
     static constexpr int CGW = NT * 16;
     struct Unit {
         uint4 w[NT][2];
         uint4 x[4];
         float s;
-        int valid;
     };
     const GemmArgs& a;
     int lane;
-    const uint16_t* xrow;   // this lane's batch row, or nullptr if >= rows
+    int ntiles;               // valid tiles in this column group
+    const uint8_t* wbase;     // this lane's bytes of tile 0, K block 0
+    const uint16_t* xrow;     // this lane's batch row (+ K-group offset), or nullptr
+    const float* srow;        // block-scale row of this column group
     f32x4_t outer[NT];
 
-    __device__ MfmaFp8(const GemmArgs& args, int l) : a(args), lane(l)
+    __device__ MfmaFp8(const GemmArgs& args, int l, int cg) : a(args), lane(l)
     {
-        int m = l & 15;
-        xrow = (m < a.rows) ? a.x + (int64_t)m * a.ldx : nullptr;
+        const int m = l & 15;
+        ntiles = min(NT, a.n_tiles - cg * NT);
+        wbase = a.codes + (((int64_t)cg * NT * a.KB) << 11) + l * 16;
+        xrow = (m < a.rows) ? a.x + (int64_t)m * a.ldx + (l >> 4) * 16 : nullptr;
+        srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(cg * CGW / 128) * a.KB;
 #pragma unroll
         for (int t = 0; t < NT; ++t) outer[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    __device__ __forceinline__ void load(Unit& r, int64_t u, bool valid) const
+    __device__ __forceinline__ void load(Unit& r, int kb, bool valid) const
     {
-        const int64_t cg = valid ? u / a.KB : 0;
-        const int kb = valid ? (int)(u - cg * a.KB) : 0;
-        const int g4 = lane >> 4;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int64_t tile = cg * NT + t;
-            const uint8_t* p = (valid && tile < a.n_tiles)
-                                   ? a.codes + ((tile * a.KB + kb) << 11) + lane * 16
-                                   : g_zero_page + lane * 16;
+            const bool ok = valid && t < ntiles;
+            const uint8_t* p = ok ? wbase + (((int64_t)t * a.KB + kb) << 11) : g_zero_page + lane * 16;
             r.w[t][0] = load_stream16(p);
-            r.w[t][1] = load_stream16(p + ((valid && tile < a.n_tiles) ? 1024 : 0));
+            r.w[t][1] = load_stream16(p + (ok ? 1024 : 0));
         }
-        const uint16_t* xb = (valid && xrow) ? xrow + kb * 128 + g4 * 16 : nullptr;
 #pragma unroll
         for (int f = 0; f < 4; ++f) {  // f = 2j + h -> k offset 64j + 8h
-            const void* p = xb ? (const void*)(xb + (f >> 1) * 64 + (f & 1) * 8)
-                               : (const void*)(g_zero_page + 1024 + f * 16);
+            const void* p = (valid && xrow) ? (const void*)(xrow + kb * 128 + (f >> 1) * 64 + (f & 1) * 8)
+                                            : (const void*)(g_zero_page + 1024 + f * 16);
             r.x[f] = load16(p);
         }
-        const float* sc = reinterpret_cast<const float*>(a.scales);
-        r.s = valid ? sc[(cg * CGW / 128) * a.KB + kb] : 0.f;
-        r.valid = valid;
+        r.s = valid ? srow[kb] : 0.f;
     }
 
-    __device__ __forceinline__ void compute(const Unit& r)
+    __device__ __forceinline__ void compute(const Unit& r, int)
     {
         f32x4_t blk[NT];
 #pragma unroll
@@ -127,37 +116,41 @@ struct MfmaFp8 {
     }
 
     // slot: [16 rows][CGW] FP32 partial tile of this wave
-    __device__ __forceinline__ void flush(float* slot)
+    __device__ __forceinline__ void store_partial(float* slot) const
     {
         const int m = lane & 15, n4 = (lane >> 4) * 4;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            *reinterpret_cast<f32x4_t*>(slot + m * CGW + t * 16 + n4) = outer[t];
-            outer[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(slot + m * CGW + t * 16 + n4) = outer[t];
     }
 };
 
 // ---- 3-bit LUT weights, 16-row FP16 MFMA tile -------------------------------
 template <int NT>
 struct MfmaLut {
+    static constexpr int KIND = KIND_MFMA_LUT;
     static constexpr int CGW = NT * 16;
     struct Unit {
         uint4 w[NT];
         uint4 x[4];
         uint32_t g[NT];      // FP16 group-scale bits, zero-extended
-        int valid;
     };
     const GemmArgs& a;
     int lane;
+    int ntiles;
+    const uint8_t* wbase;
+    const uint16_t* gbase;   // this lane's group scale of tile 0, K block 0
     const uint16_t* xrow;
-    uint32_t q[4];          // map entries as FP16 pairs
+    uint32_t q[4];           // map entries as FP16 pairs
     f32x4_t acc[NT];
 
-    __device__ MfmaLut(const GemmArgs& args, int l) : a(args), lane(l)
+    __device__ MfmaLut(const GemmArgs& args, int l, int cg) : a(args), lane(l)
     {
-        int m = l & 15;
-        xrow = (m < a.rows) ? a.x + (int64_t)m * a.ldx : nullptr;
+        const int m = l & 15;
+        ntiles = min(NT, a.n_tiles - cg * NT);
+        const int64_t unit0 = (int64_t)cg * NT * a.KB;
+        wbase = a.codes + (unit0 << 10) + l * 16;
+        gbase = reinterpret_cast<const uint16_t*>(a.scales) + unit0 * 16 + (l & 15);
+        xrow = (m < a.rows) ? a.x + (int64_t)m * a.ldx + (l >> 4) * 32 : nullptr;
         const uint32_t* qm = reinterpret_cast<const uint32_t*>(a.qmap);
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = qm[i];
@@ -165,31 +158,24 @@ struct MfmaLut {
         for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    __device__ __forceinline__ void load(Unit& r, int64_t u, bool valid) const
+    __device__ __forceinline__ void load(Unit& r, int kb, bool valid) const
     {
-        const int64_t cg = valid ? u / a.KB : 0;
-        const int kb = valid ? (int)(u - cg * a.KB) : 0;
-        const int g4 = lane >> 4;
-        const uint16_t* sc = reinterpret_cast<const uint16_t*>(a.scales);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int64_t tile = cg * NT + t;
-            const bool ok = valid && tile < a.n_tiles;
-            const int64_t unit = tile * a.KB + kb;
-            const uint8_t* p = ok ? a.codes + (unit << 10) + lane * 16 : g_zero_page + lane * 16;
-            r.w[t] = load_stream16(p);
-            r.g[t] = ok ? (uint32_t)sc[unit * 16 + (lane & 15)] : 0u;
+            const bool ok = valid && t < ntiles;
+            const int64_t u = (int64_t)t * a.KB + kb;
+            r.w[t] = load_stream16(ok ? wbase + (u << 10) : g_zero_page + lane * 16);
+            r.g[t] = ok ? (uint32_t)gbase[u * 16] : 0u;
         }
-        const uint16_t* xb = (valid && xrow) ? xrow + kb * 128 + g4 * 32 : nullptr;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const void* p = xb ? (const void*)(xb + s * 8) : (const void*)(g_zero_page + 1024 + s * 16);
+            const void* p = (valid && xrow) ? (const void*)(xrow + kb * 128 + s * 8)
+                                            : (const void*)(g_zero_page + 1024 + s * 16);
             r.x[s] = load16(p);
         }
-        r.valid = valid;
     }
 
-    __device__ __forceinline__ void compute(const Unit& r)
+    __device__ __forceinline__ void compute(const Unit& r, int)
     {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -201,98 +187,72 @@ struct MfmaLut {
         }
     }
 
-    __device__ __forceinline__ void flush(float* slot)
+    __device__ __forceinline__ void store_partial(float* slot) const
     {
         const int m = lane & 15, n4 = (lane >> 4) * 4;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            *reinterpret_cast<f32x4_t*>(slot + m * CGW + t * 16 + n4) = acc[t];
-            acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(slot + m * CGW + t * 16 + n4) = acc[t];
     }
 };
 
 // ---- FP8 weights, strict-K-order GEMV (MR <= 4 rows) ------------------------
-// Lane l owns output column n = l%16 of each tile and the K slice
-// 16(l/16) .. +15 of each 64-wide chunk.  One FP32 accumulator per (tile, row)
-// and lane takes its products in increasing k; each 128-K block is then folded
-// onto the outer accumulator times the block scale.  At a column-group end
-// the four K-slice lanes of a column are summed in a fixed butterfly.
-template <int NT, int MR>
+// The wave covers 4 tiles (64 columns): lane l owns column l%16 of tile l/16.
+// For each 64-wide chunk it loads the chunk's four K groups g = 0..3 of its
+// column (the same 16-byte pieces the MFMA path loads, just gathered per K
+// group across four tiles), so every lane needs the same 16 activations at a
+// time: x is wave-uniform and read with scalar loads.  Each (row, column)
+// keeps one FP32 accumulator that takes its products in strictly increasing
+// k over the wave's K range; each 128-K block is folded onto the outer
+// accumulator times the block scale.  The K split across waves is summed in
+// wave order afterwards.
+template <int MR>
 struct GemvFp8 {
-    static constexpr int CGW = NT * 16;
+    static constexpr int KIND = KIND_GEMV_FP8;
+    static constexpr int CGW = 64;
     struct Unit {
-        uint4 w[NT][2];
-        uint4 x[MR][2][2];   // [row][chunk j][half]
+        uint4 w[2][4];       // [chunk j][K group g]
         float s;
-        int valid;
     };
     const GemmArgs& a;
     int lane;
-    float outer[NT][MR];
+    bool tile_ok;
+    const uint8_t* wbase;    // this lane's column in tile l/16, K group 0, K block 0
+    const uint16_t* xg;      // x (wave-uniform)
+    const float* srow;
+    float outer[MR];
 
-    __device__ GemvFp8(const GemmArgs& args, int l) : a(args), lane(l)
+    __device__ GemvFp8(const GemmArgs& args, int l, int cg) : a(args), lane(l)
     {
+        const int64_t tile = (int64_t)cg * 4 + (l >> 4);
+        tile_ok = tile < a.n_tiles;
+        wbase = a.codes + ((tile * a.KB) << 11) + (l & 15) * 16;
+        xg = a.x;
+        srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(cg * CGW / 128) * a.KB;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int m = 0; m < MR; ++m) outer[t][m] = 0.f;
+        for (int m = 0; m < MR; ++m) outer[m] = 0.f;
     }
 
-    __device__ __forceinline__ void load(Unit& r, int64_t u, bool valid) const
+    __device__ __forceinline__ void load(Unit& r, int kb, bool valid) const
     {
-        const int64_t cg = valid ? u / a.KB : 0;
-        const int kb = valid ? (int)(u - cg * a.KB) : 0;
-        const int g4 = lane >> 4;
+        const bool ok = valid && tile_ok;
+        const uint8_t* p = ok ? wbase + ((int64_t)kb << 11) : g_zero_page + (lane & 15) * 16;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int64_t tile = cg * NT + t;
-            const bool ok = valid && tile < a.n_tiles;
-            const uint8_t* p = ok ? a.codes + ((tile * a.KB + kb) << 11) + lane * 16
-                                  : g_zero_page + lane * 16;
-            r.w[t][0] = load_stream16(p);
-            r.w[t][1] = load_stream16(p + (ok ? 1024 : 0));
-        }
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int m = 0; m < MR; ++m)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const void* p = valid ? (const void*)(a.x + (int64_t)m * a.ldx + kb * 128 + j * 64 + g4 * 16 + hh * 8)
-                                          : (const void*)(g_zero_page + 1024 + (m * 4 + j * 2 + hh) * 16);
-                    r.x[m][j][hh] = load16(p);
-                }
-        const float* sc = reinterpret_cast<const float*>(a.scales);
-        r.s = valid ? sc[(cg * CGW / 128) * a.KB + kb] : 0.f;
-        r.valid = valid;
+            for (int g = 0; g < 4; ++g) r.w[j][g] = load_stream16(p + (ok ? j * 1024 + g * 256 : 0));
+        r.s = valid ? srow[kb] : 0.f;
     }
 
-    __device__ __forceinline__ void compute(const Unit& r)
+    __device__ __forceinline__ void compute(const Unit& r, int kb)
     {
-        float blk[NT][MR];
+        float blk[MR];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int m = 0; m < MR; ++m) blk[m] = 0.f;
 #pragma unroll
-            for (int m = 0; m < MR; ++m) blk[t][m] = 0.f;
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            float xf[MR][16];
-#pragma unroll
-            for (int m = 0; m < MR; ++m)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const uint4 v = r.x[m][j][hh];
-                    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        xf[m][hh * 8 + 2 * i] = bf16_bits_to_f32(d[i] & 0xFFFFu);
-                        xf[m][hh * 8 + 2 * i + 1] = bf16_bits_to_f32(d[i] >> 16);
-                    }
-                }
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const uint4 w = r.w[t][j];
+            for (int g = 0; g < 4; ++g) {
+                const uint4 w = r.w[j][g];
                 const uint32_t d[4] = {w.x, w.y, w.z, w.w};
                 float wf[16];
 #pragma unroll
@@ -304,143 +264,72 @@ struct GemvFp8 {
                     wf[4 * i + 2] = hi[0];
                     wf[4 * i + 3] = hi[1];
                 }
+                const int k0 = kb * 128 + j * 64 + g * 16;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
+                for (int m = 0; m < MR; ++m) {
+                    const uint16_t* xp = xg + (int64_t)m * a.ldx + k0;
+                    const uint4 xa = load_uniform16(xp), xb = load_uniform16(xp + 8);
+                    const uint32_t xd[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-                    for (int m = 0; m < MR; ++m) blk[t][m] = __builtin_fmaf(xf[m][i], wf[i], blk[t][m]);
+                    for (int i = 0; i < 8; ++i) {
+                        blk[m] = __builtin_fmaf(bf16_bits_to_f32(xd[i] & 0xFFFFu), wf[2 * i], blk[m]);
+                        blk[m] = __builtin_fmaf(bf16_bits_to_f32(xd[i] >> 16), wf[2 * i + 1], blk[m]);
+                    }
+                }
             }
-        }
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int m = 0; m < MR; ++m) outer[t][m] = __builtin_fmaf(r.s, blk[t][m], outer[t][m]);
+        for (int m = 0; m < MR; ++m) outer[m] = __builtin_fmaf(r.s, blk[m], outer[m]);
     }
 
-    __device__ __forceinline__ void flush(float* slot)
+    __device__ __forceinline__ void store_partial(float* slot) const
     {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int m = 0; m < MR; ++m) {
-                float v = outer[t][m];
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                if (lane < 16) slot[m * CGW + t * 16 + lane] = v;
-                outer[t][m] = 0.f;
-            }
+        for (int m = 0; m < MR; ++m) slot[m * CGW + lane] = outer[m];
     }
 };
 
 // ======================================================================
-// The persistent stream-K GEMM kernel.
+// The split-K GEMM kernel: grid = column groups, block = S waves.
 // ======================================================================
-template <class Pol, bool F16_OUT>
-__global__ void __launch_bounds__(kThreadsPerWG)
+template <class Pol, int D, bool F16_OUT>
+__global__ void __launch_bounds__(64 * max_split(Pol::KIND, Pol::CGW / 16))
 gemm_kernel(GemmArgs a)
 {
     constexpr int CGW = Pol::CGW;
     constexpr int SLOT = 16 * CGW;            // floats in one partial tile
-    extern __shared__ float lds[];            // [slots][kWavesPerWG][SLOT]
-    __shared__ uint32_t s_arrival;
+    extern __shared__ float lds[];            // [S][SLOT]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = blockIdx.x;
-    const int64_t ub = range_begin(a.U, a.G, g), ue = range_begin(a.U, a.G, g + 1);
-    const int64_t len = ue - ub;
-    const int64_t cg_first = ub / a.KB;
-    const int64_t cg_last = (ue - 1) / a.KB;
+    const int S = blockDim.x >> 6;
+    const int cg = blockIdx.x;
+    const int kb0 = (a.KB * wave) / S, kb1 = (a.KB * (wave + 1)) / S;
 
-    // ---------------- per-wave stream over its unit range ----------------
+    Pol pol(a, lane, cg);
     {
-        const int64_t wb = ub + (len * wave) / kWavesPerWG;
-        const int64_t we = ub + (len * (wave + 1)) / kWavesPerWG;
-        Pol pol(a, lane);
-        if (wb < we) {
-            typename Pol::Unit r0, r1;
-            pol.load(r0, wb, true);
-            int64_t u = wb;
-            while (true) {
-                pol.load(r1, u + 1, u + 1 < we);
-                pol.compute(r0);
-                if (u + 1 == we || (u + 1) % a.KB == 0)
-                    pol.flush(lds + ((u / a.KB - cg_first) * kWavesPerWG + wave) * SLOT);
-                if (++u >= we) break;
-                pol.load(r0, u + 1, u + 1 < we);
-                pol.compute(r1);
-                if (u + 1 == we || (u + 1) % a.KB == 0)
-                    pol.flush(lds + ((u / a.KB - cg_first) * kWavesPerWG + wave) * SLOT);
-                if (++u >= we) break;
+        typename Pol::Unit r[D + 1];
+#pragma unroll
+        for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, kb0 + i < kb1);
+        for (int kb = kb0; kb < kb1; kb += D + 1) {
+#pragma unroll
+            for (int j = 0; j <= D; ++j) {
+                const int nxt = kb + j + D;
+                pol.load(r[(j + D) % (D + 1)], nxt, nxt < kb1);
+                if (kb + j < kb1) pol.compute(r[j], kb + j);
             }
         }
     }
+    pol.store_partial(lds + wave * SLOT);
     __syncthreads();
 
-    // ---------------- work-group reduction and epilogue ------------------
-    for (int64_t c = cg_first; c <= cg_last; ++c) {
-        const int64_t c0 = c * a.KB, c1 = c0 + a.KB;
-        const bool covered = (c0 >= ub) && (c1 <= ue);
-        uint32_t wmask = 0;
-#pragma unroll
-        for (int w = 0; w < kWavesPerWG; ++w) {
-            const int64_t b = ub + (len * w) / kWavesPerWG, e = ub + (len * (w + 1)) / kWavesPerWG;
-            if (b < e && b < c1 && e > c0) wmask |= 1u << w;
-        }
-        const float* slots = lds + (c - cg_first) * kWavesPerWG * SLOT;
-        const int nout = a.rows * CGW;
-        float* part = a.partials + ((int64_t)g * 2 + (c == cg_first ? 0 : 1)) * SLOT;
-        for (int e = tid; e < nout; e += kThreadsPerWG) {
-            float v = 0.f;
-            bool first = true;
-#pragma unroll
-            for (int w = 0; w < kWavesPerWG; ++w)
-                if (wmask & (1u << w)) {
-                    const float p = slots[w * SLOT + e];
-                    v = first ? p : v + p;
-                    first = false;
-                }
-            if (covered) {
-                const int m = e / CGW;
-                const int64_t n = c * CGW + (e - m * CGW);
-                if (n < a.N)
-                    a.y[m * a.ldy + n] = F16_OUT ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
-            } else {
-                part[e] = v;
-            }
-        }
-        if (covered) continue;
-
-        // publish this work-group's partial; the last of the column group's
-        // work-groups to arrive sums every contribution in work-group order
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (tid == 0) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            s_arrival = __hip_atomic_fetch_add(a.counters + c, 1u, __ATOMIC_ACQ_REL,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        const int gf = wg_of(a.U, a.G, c0), gl = wg_of(a.U, a.G, c1 - 1);
-        if (s_arrival == (uint32_t)(gl - gf)) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            for (int e = tid; e < nout; e += kThreadsPerWG) {
-                float v = 0.f;
-                for (int gg = gf; gg <= gl; ++gg) {
-                    const int64_t first_cg = range_begin(a.U, a.G, gg) / a.KB;
-                    const float p = __builtin_nontemporal_load(
-                        a.partials + ((int64_t)gg * 2 + (c == first_cg ? 0 : 1)) * SLOT + e);
-                    v = (gg == gf) ? p : v + p;
-                }
-                const int m = e / CGW;
-                const int64_t n = c * CGW + (e - m * CGW);
-                if (n < a.N)
-                    a.y[m * a.ldy + n] = F16_OUT ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
-            }
-            if (tid == 0)
-                __hip_atomic_store(a.counters + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();   // s_arrival is reused by the next column group
+    const int nout = a.rows * CGW;
+    for (int e = tid; e < nout; e += blockDim.x) {
+        float v = lds[e];
+        for (int w = 1; w < S; ++w) v += lds[w * SLOT + e];
+        const int m = e / CGW;
+        const int64_t n = (int64_t)cg * CGW + (e - m * CGW);
+        if (n < a.N) a.y[m * a.ldy + n] = F16_OUT ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
     }
 }
 
@@ -572,43 +461,47 @@ __global__ void unpack_lut3_kernel(const uint8_t* __restrict__ packed, int64_t N
 // Launchers
 // ======================================================================
 
-template <class Pol, bool F16>
-static hipError_t launch_one(const GemmArgs& a, size_t lds, hipStream_t s)
+template <class Pol, int D, bool F16>
+static hipError_t launch_one(const GemmArgs& a, int split, hipStream_t s)
 {
-    auto fn = gemm_kernel<Pol, F16>;
+    auto fn = gemm_kernel<Pol, D, F16>;
+    const size_t lds = (size_t)split * 16 * Pol::CGW * sizeof(float);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fn, dim3(a.G), dim3(kThreadsPerWG), lds, s, a);
+    hipLaunchKernelGGL(fn, dim3(a.n_cg), dim3(split * 64), lds, s, a);
     return hipGetLastError();
 }
 
 template <int NT>
-static hipError_t launch_nt(int kind, int rows, const GemmArgs& a, size_t lds, hipStream_t s)
+static hipError_t launch_nt(int kind, int rows, const GemmArgs& a, int split, hipStream_t s)
 {
     switch (kind) {
-    case KIND_MFMA_FP8: return launch_one<MfmaFp8<NT>, false>(a, lds, s);
-    case KIND_MFMA_LUT: return launch_one<MfmaLut<NT>, true>(a, lds, s);
-    case KIND_GEMV_FP8:
-        switch (rows) {
-        case 1: return launch_one<GemvFp8<NT, 1>, false>(a, lds, s);
-        case 2: return launch_one<GemvFp8<NT, 2>, false>(a, lds, s);
-        case 3: return launch_one<GemvFp8<NT, 3>, false>(a, lds, s);
-        case 4: return launch_one<GemvFp8<NT, 4>, false>(a, lds, s);
-        default: return hipErrorInvalidValue;
-        }
+    case KIND_MFMA_FP8: return launch_one<MfmaFp8<NT>, kDepthMfmaFp8, false>(a, split, s);
+    case KIND_MFMA_LUT: return launch_one<MfmaLut<NT>, kDepthMfmaLut, true>(a, split, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, size_t lds_bytes, hipStream_t stream)
+hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream)
 {
+    if (split < 1 || split > max_split(kind, nt)) return hipErrorInvalidValue;
+    if (kind == KIND_GEMV_FP8) {
+        if (nt != 4) return hipErrorInvalidValue;
+        switch (gemv_rows) {
+        case 1: return launch_one<GemvFp8<1>, kDepthGemv, false>(a, split, stream);
+        case 2: return launch_one<GemvFp8<2>, kDepthGemv, false>(a, split, stream);
+        case 3: return launch_one<GemvFp8<3>, kDepthGemv, false>(a, split, stream);
+        case 4: return launch_one<GemvFp8<4>, kDepthGemv, false>(a, split, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (nt) {
-    case 2: return launch_nt<2>(kind, gemv_rows, a, lds_bytes, stream);
-    case 4: return launch_nt<4>(kind, gemv_rows, a, lds_bytes, stream);
-    case 8: return launch_nt<8>(kind, gemv_rows, a, lds_bytes, stream);
+    case 1: return launch_nt<1>(kind, gemv_rows, a, split, stream);
+    case 2: return launch_nt<2>(kind, gemv_rows, a, split, stream);
+    case 4: return launch_nt<4>(kind, gemv_rows, a, split, stream);
     default: return hipErrorInvalidValue;
     }
 }

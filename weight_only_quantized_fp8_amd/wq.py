@@ -21,6 +21,12 @@ __all__ = [
     "workspace", "pack_fp8", "pack_lut3", "gemm_fp8", "gemm_lut3",
 ]
 
+# torch ships its own HIP runtime under the same soname as the system one
+# (libamdhip64.so.7).  Loading torch first makes libwq bind to that already
+# loaded runtime, so torch's device pointers and streams are valid in libwq's
+# calls; loading libwq first would bring in a second, separate runtime.
+import torch  # noqa: E402,F401  (must precede the CDLL below)
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwq.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError("libwq.so is not built (%s); run __graft_entry__.build() or "
@@ -69,7 +75,7 @@ def _ptr(t) -> int | None:
         return None
     if isinstance(t, int):
         return t
-    return t.data_ptr()
+    return t.data_ptr() or None
 
 
 def _stream(stream) -> int | None:
@@ -79,6 +85,10 @@ def _stream(stream) -> int | None:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _ld(t) -> int:
@@ -114,15 +124,16 @@ def wq_pack_fp8_block(w_e4m3, scales, N: int, K: int, packed, stream=None) -> No
            "wq_pack_fp8_block")
 
 
-def wq_gemm_fp8_block(packed, N: int, K: int, x, y, M: int, workspace, stream=None) -> None:
+def wq_gemm_fp8_block(packed, N: int, K: int, x, y, M: int, workspace=None, stream=None) -> None:
     _check(lib.wq_gemm_fp8_block(_ptr(packed), N, K, _ptr(x), _ld(x), _ptr(y), _ld(y), M, _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+                                 _nbytes(workspace), _stream(stream)),
            "wq_gemm_fp8_block")
 
 
-def wq_gemm_fp8_block_path(packed, N: int, K: int, x, y, M: int, workspace, path: int, stream=None) -> None:
+def wq_gemm_fp8_block_path(packed, N: int, K: int, x, y, M: int, workspace=None, path: int = WQ_PATH_AUTO,
+                           stream=None) -> None:
     _check(lib.wq_gemm_fp8_block_path(_ptr(packed), N, K, _ptr(x), _ld(x), _ptr(y), _ld(y), M, _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(), path, _stream(stream)),
+                                      _nbytes(workspace), path, _stream(stream)),
            "wq_gemm_fp8_block_path")
 
 
@@ -131,9 +142,9 @@ def wq_pack_lut3(codes, qmap, scales, N: int, K: int, packed, stream=None) -> No
                             _stream(stream)), "wq_pack_lut3")
 
 
-def wq_gemm_lut3(packed, N: int, K: int, x, y, M: int, workspace, stream=None) -> None:
+def wq_gemm_lut3(packed, N: int, K: int, x, y, M: int, workspace=None, stream=None) -> None:
     _check(lib.wq_gemm_lut3(_ptr(packed), N, K, _ptr(x), _ld(x), _ptr(y), _ld(y), M, _ptr(workspace),
-                            workspace.numel() * workspace.element_size(), _stream(stream)), "wq_gemm_lut3")
+                            _nbytes(workspace), _stream(stream)), "wq_gemm_lut3")
 
 
 def wq_unpack_fp8_block(packed, N: int, K: int, w_bf16, stream=None) -> None:
@@ -152,11 +163,9 @@ def wq_unpack_lut3(packed, N: int, K: int, w_f16, stream=None) -> None:
 # -------------------------------------------------------- torch helpers
 
 def workspace(fmt: int, N: int, K: int, device="cuda"):
-    """Zero-filled workspace for GEMMs of this format and shape (any M, any path)."""
+    """Workspace for GEMMs of this format and shape (any M, any path); it may be empty."""
     import torch
     nbytes = wq_gemm_workspace_bytes(fmt, 1, N, K)
-    if nbytes == 0:
-        raise WqError(2, "wq_gemm_workspace_bytes")
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
@@ -178,7 +187,7 @@ def pack_lut3(codes, qmap, scales, stream=None):
     return packed
 
 
-def gemm_fp8(packed, N: int, K: int, x, ws, path: int = WQ_PATH_AUTO, stream=None):
+def gemm_fp8(packed, N: int, K: int, x, ws=None, path: int = WQ_PATH_AUTO, stream=None):
     """y [M, N] (bfloat16) = x [M, K] (bfloat16) . dequant(W)^T."""
     import torch
     M = x.shape[0]
@@ -187,7 +196,7 @@ def gemm_fp8(packed, N: int, K: int, x, ws, path: int = WQ_PATH_AUTO, stream=Non
     return y
 
 
-def gemm_lut3(packed, N: int, K: int, x, ws, stream=None):
+def gemm_lut3(packed, N: int, K: int, x, ws=None, stream=None):
     """y [M, N] (float16) = x [M, K] (float16) . dequant(W)^T."""
     import torch
     M = x.shape[0]
