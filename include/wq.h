@@ -42,7 +42,8 @@
  * sweeps without a rebuild; the defaults are the per-shape plan):
  *   WQ_FORCE_PATH   = auto | gemv | mfma  path for wq_gemm_fp8_block (default auto)
  *   WQ_NT           = 1 | 2 | 4           16-column MFMA tiles per wave
- *   WQ_SPLIT        = 1 .. 16             waves splitting K inside a work-group
+ *   WQ_SN           = 1 | 2 | 4           column-waves sharing each K block's activations
+ *   WQ_SPLIT        = 1 .. 16             waves per work-group (SN x K-groups)
  *   WQ_WAVES_PER_CU = 1 .. 32             resident waves per CU the plan aims for (4)
  */
 #ifndef WQ_H_
@@ -84,6 +85,17 @@ const char* wq_status_str(wq_status s);
 /* Version of the packed layouts written by wq_pack_*; a packed buffer is a
  * deterministic, byte-for-byte function of the pack inputs and this number. */
 int wq_packed_format_version(void);
+
+/* Tuning and test hook: override the per-shape plan of later calls.  nt =
+ * 16-column tiles per wave (1, 2, 4), sn = column-waves sharing activations
+ * (1, 2, 4), split = waves per work-group (1..16, rounded to the kernel's
+ * limit and to a multiple of sn), waves_per_cu = the resident-wave target of
+ * the automatic plan; 0 selects the automatic choice for each.  Replaces the
+ * WQ_NT / WQ_SN / WQ_SPLIT / WQ_WAVES_PER_CU environment values.  The FP8
+ * GEMV path ignores nt and sn.  Results stay within the documented tolerance
+ * for every setting, but bit patterns may differ between settings.  Not meant
+ * to be called while GEMMs are being queued from other threads. */
+wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu);
 
 /* ------------------------------------------------------------ FP8 block */
 

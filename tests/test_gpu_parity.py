@@ -252,3 +252,40 @@ def test_zero_rows_and_zero_matrix():
     for path in (MFMA, GEMV):
         y, _ = U.run_fp8(U.pack_fp8(codes, scales), N, K, xbits[: (8 if path == MFMA else 4)], path=path)
         assert not (y & 0x7FFF).any()
+
+
+# ------------------------------------------------------ every kernel variant
+
+TUNINGS = [(1, 1, 1), (1, 1, 16), (1, 2, 4), (1, 4, 16), (2, 1, 3), (2, 1, 8), (2, 2, 6), (2, 4, 4),
+           (2, 4, 16), (4, 1, 5), (4, 2, 8), (4, 4, 4), (4, 4, 8)]
+
+
+@pytest.fixture
+def tuning_reset():
+    yield
+    U.wqmod().wq_set_tuning(0, 0, 0, 0)
+
+
+@pytest.mark.parametrize("nt,sn,split", TUNINGS, ids=["nt%d-sn%d-s%d" % t for t in TUNINGS])
+def test_every_tiling_matches_oracle(nt, sn, split, tuning_reset):
+    """Ragged column groups (tiles past N inside a group), K ranges of unequal
+    length, and M on both sides of 8 and 16, for each tiling."""
+    wq = U.wqmod()
+    wq.wq_set_tuning(nt, sn, split, 0)
+    U.note("tiling nt=%d sn=%d split=%d" % (nt, sn, split))
+    for N, K in ((384, 1152), (640, 640)):
+        codes, scales = synth.fp8_weights(N, K, 500 + N)
+        packed = U.pack_fp8(codes, scales)
+        for M in (1, 5, 16, 20):
+            xbits = synth.x_bf16(M, K, 600 + M)
+            y, _ = U.run_fp8(packed, N, K, xbits, path=MFMA)
+            r = U.grade_fp8(y, xbits, codes, scales, K)
+            assert r.ok, "fp8 N=%d K=%d M=%d: %s" % (N, K, M, r)
+    for N, K in ((48, 384), (272, 1152)):
+        c, q, g = synth.lut3_weights(N, K, 700 + N)
+        packed = U.pack_lut3(c, q, g)
+        for M in (1, 7, 16, 24):
+            xh = synth.x_f16(M, K, 800 + M)
+            y, _ = U.run_lut3(packed, N, K, xh)
+            r = U.grade_lut3(y, xh, c, q, g, K)
+            assert r.ok, "lut3 N=%d K=%d M=%d: %s" % (N, K, M, r)

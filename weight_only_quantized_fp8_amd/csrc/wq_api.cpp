@@ -23,13 +23,17 @@ constexpr int kMaxDevices = 64;
 struct Options {
     int force_path = WQ_PATH_AUTO;
     int nt = 0;              // 0 = per-shape choice
+    int sn = 0;              // 0 = per-shape choice
     int split = 0;           // 0 = per-shape choice
     int waves_per_cu = 4;    // target resident waves per compute unit
 };
 
+Options g_opts;
+std::mutex g_opts_mu;
+
 const Options& options()
 {
-    static Options o;
+    static Options& o = g_opts;
     static std::once_flag once;
     std::call_once(once, [] {
         if (const char* p = std::getenv("WQ_FORCE_PATH")) {
@@ -39,6 +43,10 @@ const Options& options()
         if (const char* p = std::getenv("WQ_NT")) {
             int v = std::atoi(p);
             if (v == 1 || v == 2 || v == 4) o.nt = v;
+        }
+        if (const char* p = std::getenv("WQ_SN")) {
+            int v = std::atoi(p);
+            if (v == 1 || v == 2 || v == 4) o.sn = v;
         }
         if (const char* p = std::getenv("WQ_SPLIT")) {
             int v = std::atoi(p);
@@ -88,14 +96,16 @@ wq_status current_device(DevInfo* info, int* dev_out = nullptr)
 }
 
 // --------------------------------------------------------------------- plan
-// One work-group per column group of NT 16-column tiles; its S waves split
-// the K blocks.  NT and S are chosen so that about `waves_per_cu` waves per
-// compute unit are resident: wide tiles (NT = 4, each activation fragment
-// feeds four MFMAs) where N allows, narrower tiles and a deeper K split for
-// the low-N projections.
+// A work-group covers SN*NT tiles of 16 output columns over all of K: SN
+// column-waves (NT tiles each) share the activations of each K block, and SK
+// K-groups split the K blocks (split = SN*SK waves).  NT, SN and SK are chosen
+// so that about `waves_per_cu` waves per compute unit are resident: shared
+// activations where N leaves enough column groups, narrower groups and a
+// deeper K split for the low-N projections.
 struct Plan {
     int kind = 0;
-    int nt = 4;
+    int nt = 2;
+    int sn = 1;
     int split = 1;
     int n_tiles = 0, n_cg = 0, KB = 0;
 };
@@ -107,19 +117,28 @@ Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
     p.n_tiles = (int)(N / 16);
     p.KB = (int)(K / 128);
     const int target = std::max(1, cu * o.waves_per_cu);
-    // The GEMV always covers 4 tiles per wave (one column per lane); its plan
-    // must not depend on M (batch invariance), and it does not.
-    int nt = 4;
-    if (kind != wq::KIND_GEMV_FP8) {
-        if (o.nt) nt = o.nt;
-        else
-            while (nt > 1 && (int64_t)((p.n_tiles + nt - 1) / nt) * wq::max_split(kind, nt) < target) nt /= 2;
+    if (kind == wq::KIND_GEMV_FP8) {
+        // the GEMV covers 4 tiles per wave (one column per lane) and stages no
+        // activations; its plan must not depend on M (batch invariance)
+        p.nt = 4;
+        p.sn = 1;
+    } else {
+        p.nt = o.nt ? o.nt : (p.n_tiles >= 2 * cu ? 2 : 1);
+        if (o.sn) p.sn = o.sn;
+        else {
+            // share activations across 4 column-waves while that still leaves
+            // at least one work-group per compute unit
+            p.sn = (p.n_tiles / (p.nt * 4) >= cu) ? 4 : 1;
+        }
     }
-    p.nt = nt;
-    p.n_cg = (p.n_tiles + nt - 1) / nt;
-    int s = o.split ? o.split : (int)std::lround((double)target / p.n_cg);
-    s = std::max(1, std::min(s, std::min(wq::max_split(kind, nt), p.KB)));
-    p.split = s;
+    const int group = p.nt * p.sn;
+    p.n_cg = (p.n_tiles + group - 1) / group;
+    const int maxs = wq::max_split(kind, p.nt, p.sn);
+    int sk;
+    if (o.split) sk = std::max(1, o.split / p.sn);
+    else sk = (int)std::lround((double)target / ((double)p.n_cg * p.sn));
+    sk = std::max(1, std::min(sk, std::min(maxs / p.sn, p.KB)));   // every K group gets >= 1 block
+    p.split = sk * p.sn;
     return p;
 }
 
@@ -141,10 +160,11 @@ int g_plan_count = 0, g_plan_next = 0;
 Plan cached_plan(int kind, int64_t N, int64_t K, int cu)
 {
     const PlanKey key{kind, N, K, cu};
+    options();   // read the environment once, before the first plan
     std::lock_guard<std::mutex> lk(g_plan_mu);
     for (int i = 0; i < g_plan_count; ++i)
         if (g_plan_keys[i] == key) return g_plans[i];
-    Plan p = make_plan(kind, N, K, cu, options());
+    Plan p = make_plan(kind, N, K, cu, g_opts);
     g_plan_keys[g_plan_next] = key;
     g_plans[g_plan_next] = p;
     g_plan_next = (g_plan_next + 1) % kPlanCache;
@@ -225,7 +245,7 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
         a.y = y + r0 * ldy;
         a.ldy = ldy;
         a.rows = rows;
-        hipError_t e = wq::launch_gemm(kind, p.nt, kind == wq::KIND_GEMV_FP8 ? rows : 0, a, p.split, s);
+        hipError_t e = wq::launch_gemm(kind, p.nt, p.sn, kind == wq::KIND_GEMV_FP8 ? rows : 0, a, p.split, s);
         if (e != hipSuccess) return WQ_ERR_HIP;
     }
     return WQ_OK;
@@ -253,6 +273,22 @@ const char* wq_status_str(wq_status s)
 }
 
 int wq_packed_format_version(void) { return kPackedFormatVersion; }
+
+wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu)
+{
+    if (nt != 0 && nt != 1 && nt != 2 && nt != 4) return WQ_ERR_SHAPE;
+    if (sn != 0 && sn != 1 && sn != 2 && sn != 4) return WQ_ERR_SHAPE;
+    if (split < 0 || split > 16 || waves_per_cu < 0 || waves_per_cu > 32) return WQ_ERR_SHAPE;
+    options();
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    g_opts.nt = nt;
+    g_opts.sn = sn;
+    g_opts.split = split;
+    g_opts.waves_per_cu = waves_per_cu ? waves_per_cu : 4;
+    g_plan_count = 0;
+    g_plan_next = 0;
+    return WQ_OK;
+}
 
 size_t wq_fp8_block_packed_bytes(int64_t N, int64_t K)
 {

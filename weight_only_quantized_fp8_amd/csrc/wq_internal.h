@@ -21,9 +21,13 @@ enum Kind : int {
 
 // Largest split (waves per work-group) a kernel may use.  A work-group runs
 // on one CU, so its S waves must fit the register file: the launch bound
-// 64*S caps a wave at 512/ceil(S/4) VGPRs.  The 4-tile kernels (MFMA and
-// GEMV) need up to 256 (S <= 8); the narrow MFMA kernels fit in 128 (S <= 16).
-constexpr int max_split(int kind, int nt) { return (kind == KIND_GEMV_FP8 || nt >= 4) ? 8 : 16; }
+// 64*S caps a wave at 512/ceil(S/4) VGPRs.  The GEMV and the 4-tile MFMA
+// kernels, and the 2-tile ones that stage their own activations, need more
+// than 128 (S <= 8); the others fit in 128 (S <= 16).
+constexpr int max_split(int kind, int nt, int sn)
+{
+    return (kind == KIND_GEMV_FP8 || nt >= 4 || (nt == 2 && sn == 1)) ? 8 : 16;
+}
 
 // Everything a GEMM launch needs.  The grid has one work-group per column
 // group (NT tiles of 16 output columns); its S waves split the K blocks.
@@ -39,10 +43,12 @@ struct GemmArgs {
     int N;                    // output columns
     int KB;                   // K / 128
     int n_tiles;              // N / 16
-    int n_cg;                 // column groups = ceil(n_tiles / NT) = grid size
+    int n_cg;                 // column groups = grid size
 };
 
-hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream);
+// nt: tiles per wave; sn: column-waves sharing activations (split % sn == 0);
+// split: waves per work-group; the grid has a.n_cg = ceil(n_tiles/(nt*sn)) groups.
+hipError_t launch_gemm(int kind, int nt, int sn, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream);
 
 hipError_t launch_pack_fp8(const uint8_t* w, int64_t ldw, const float* scales, int64_t N,
                            int64_t K, uint8_t* packed, hipStream_t stream);

@@ -43,33 +43,96 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_page[4096];
 // register set r (from the zero page when !valid), compute(r) consumes it.
 // ======================================================================
 
+// ---- activation staging for the MFMA tiles ---------------------------------
+// The MFMA operand layout gives consecutive lanes consecutive batch rows, so
+// loading fragments straight from x would make every 16-byte lane piece its
+// own L1 access.  Instead x for one K block (16 rows x 128 k, 4 KiB) is loaded
+// coalesced, as four 1 KiB pieces f: 8 consecutive lanes read one row's
+// 128-byte segment (rows (l>>3) + 8(f&1), k = 64(f>>1) + 8(l&7) .. +7).  The
+// pieces go to an LDS buffer whose rows are padded by 16 bytes, and the
+// fragments are read back with 16-byte LDS reads: with the pad, the 16 rows
+// read by a 16-lane group start 4 banks apart and cover all 64 banks once
+// (the same stride arithmetic as the shared-memory pad in the arc PR "FP8
+// bank conflict + the dispatch threshold's provenance", "What landed").
+// When SN column-waves share a K range, each loads 4/SN of the pieces and
+// all of them read the shared buffer.
+constexpr int kXRowBytes = 128 * 2 + 16;          // padded LDS row
+constexpr int kXStageBytes = 16 * kXRowBytes;     // one K block of x
+
+template <int XP>   // pieces this wave loads
+struct XStage {
+    const uint16_t* xl;       // x at this lane's k offset (8 * (l & 7))
+    int64_t ldx;
+    int rows;
+    int lane;
+    int f0;                   // first piece of this wave
+
+    __device__ void init(const GemmArgs& a, int l, int first_piece)
+    {
+        lane = l;
+        f0 = first_piece;
+        xl = a.x + (l & 7) * 8;
+        ldx = a.ldx;
+        rows = a.rows;
+    }
+
+    __device__ __forceinline__ void load(uint4 (&xr)[XP], int kb, bool valid) const
+    {
+#pragma unroll
+        for (int i = 0; i < XP; ++i) {
+            const int f = f0 + i;
+            const int r = (lane >> 3) + 8 * (f & 1);
+            const void* p = (valid && r < rows) ? (const void*)(xl + r * ldx + kb * 128 + (f >> 1) * 64)
+                                                : (const void*)(g_zero_page + 1024 + (lane & 7) * 16);
+            xr[i] = load16(p);
+        }
+    }
+
+    __device__ __forceinline__ void stage(uint8_t* buf, const uint4 (&xr)[XP]) const
+    {
+#pragma unroll
+        for (int i = 0; i < XP; ++i) {
+            const int f = f0 + i;
+            const int r = (lane >> 3) + 8 * (f & 1);
+            const int k = (f >> 1) * 64 + (lane & 7) * 8;
+            *reinterpret_cast<uint4*>(buf + r * kXRowBytes + k * 2) = xr[i];
+        }
+    }
+
+    // 8 consecutive activations of batch row (l % 16) starting at k
+    __device__ __forceinline__ uint4 frag(const uint8_t* buf, int k) const
+    {
+        return *reinterpret_cast<const uint4*>(buf + (lane & 15) * kXRowBytes + k * 2);
+    }
+};
+
 // ---- FP8 weights, 16-row BF16 MFMA tile ------------------------------------
 // A operand = dequantised weights (lane: row n = l%16), B operand = x
 // (lane: batch row m = l%16).  Output D[n][m] -> lane holds n = 4(l/16)+v.
-template <int NT>
+template <int NT, int SN>
 struct MfmaFp8 {
     static constexpr int KIND = KIND_MFMA_FP8;
-    static constexpr int CGW = NT * 16;
+    static constexpr int NTILES = NT;
+    static constexpr int XP = 4 / SN;
     struct Unit {
         uint4 w[NT][2];
-        uint4 x[4];
+        uint4 x[XP];
         float s;
     };
     const GemmArgs& a;
     int lane;
-    int ntiles;               // valid tiles in this column group
-    const uint8_t* wbase;     // this lane's bytes of tile 0, K block 0
-    const uint16_t* xrow;     // this lane's batch row (+ K-group offset), or nullptr
-    const float* srow;        // block-scale row of this column group
+    int ntiles;               // valid tiles of this wave
+    const uint8_t* wbase;     // this lane's bytes of the wave's tile 0, K block 0
+    const float* srow;        // block-scale row of this wave's tiles
+    XStage<XP> xs;
     f32x4_t outer[NT];
 
-    __device__ MfmaFp8(const GemmArgs& args, int l, int cg) : a(args), lane(l)
+    __device__ MfmaFp8(const GemmArgs& args, int l, int tile0, int piece0) : a(args), lane(l)
     {
-        const int m = l & 15;
-        ntiles = min(NT, a.n_tiles - cg * NT);
-        wbase = a.codes + (((int64_t)cg * NT * a.KB) << 11) + l * 16;
-        xrow = (m < a.rows) ? a.x + (int64_t)m * a.ldx + (l >> 4) * 16 : nullptr;
-        srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(cg * CGW / 128) * a.KB;
+        ntiles = min(NT, a.n_tiles - tile0);
+        wbase = a.codes + (((int64_t)tile0 * a.KB) << 11) + l * 16;
+        srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(tile0 * 16 / 128) * a.KB;
+        xs.init(a, l, piece0);
 #pragma unroll
         for (int t = 0; t < NT; ++t) outer[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -83,24 +146,21 @@ struct MfmaFp8 {
             r.w[t][0] = load_stream16(p);
             r.w[t][1] = load_stream16(p + (ok ? 1024 : 0));
         }
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {  // f = 2j + h -> k offset 64j + 8h
-            const void* p = (valid && xrow) ? (const void*)(xrow + kb * 128 + (f >> 1) * 64 + (f & 1) * 8)
-                                            : (const void*)(g_zero_page + 1024 + f * 16);
-            r.x[f] = load16(p);
-        }
-        r.s = valid ? srow[kb] : 0.f;
+        xs.load(r.x, kb, valid);
+        r.s = (valid && ntiles > 0) ? srow[kb] : 0.f;   // a wave past N reads no scale
     }
 
-    __device__ __forceinline__ void compute(const Unit& r, int)
+    __device__ __forceinline__ void stage(uint8_t* buf, const Unit& r) const { xs.stage(buf, r.x); }
+
+    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* buf)
     {
         f32x4_t blk[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) blk[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, r.x[f]);
+        for (int f = 0; f < 4; ++f) {  // f = 2j + h -> k offset 64j + 16(l/16) + 8h
             const int j = f >> 1, h = f & 1;
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xs.frag(buf, j * 64 + (lane >> 4) * 16 + h * 8));
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const uint4 w = r.w[t][j];
@@ -115,42 +175,42 @@ struct MfmaFp8 {
             for (int v = 0; v < 4; ++v) outer[t][v] = __builtin_fmaf(r.s, blk[t][v], outer[t][v]);
     }
 
-    // slot: [16 rows][CGW] FP32 partial tile of this wave
+    // slot: [16 rows][NT*16] FP32 partial tile of this wave
     __device__ __forceinline__ void store_partial(float* slot) const
     {
         const int m = lane & 15, n4 = (lane >> 4) * 4;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(slot + m * CGW + t * 16 + n4) = outer[t];
+        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(slot + m * NT * 16 + t * 16 + n4) = outer[t];
     }
 };
 
 // ---- 3-bit LUT weights, 16-row FP16 MFMA tile -------------------------------
-template <int NT>
+template <int NT, int SN>
 struct MfmaLut {
     static constexpr int KIND = KIND_MFMA_LUT;
-    static constexpr int CGW = NT * 16;
+    static constexpr int NTILES = NT;
+    static constexpr int XP = 4 / SN;
     struct Unit {
         uint4 w[NT];
-        uint4 x[4];
+        uint4 x[XP];
         uint32_t g[NT];      // FP16 group-scale bits, zero-extended
     };
     const GemmArgs& a;
     int lane;
     int ntiles;
     const uint8_t* wbase;
-    const uint16_t* gbase;   // this lane's group scale of tile 0, K block 0
-    const uint16_t* xrow;
+    const uint16_t* gbase;   // this lane's group scale of the wave's tile 0, K block 0
+    XStage<XP> xs;
     uint32_t q[4];           // map entries as FP16 pairs
     f32x4_t acc[NT];
 
-    __device__ MfmaLut(const GemmArgs& args, int l, int cg) : a(args), lane(l)
+    __device__ MfmaLut(const GemmArgs& args, int l, int tile0, int piece0) : a(args), lane(l)
     {
-        const int m = l & 15;
-        ntiles = min(NT, a.n_tiles - cg * NT);
-        const int64_t unit0 = (int64_t)cg * NT * a.KB;
+        ntiles = min(NT, a.n_tiles - tile0);
+        const int64_t unit0 = (int64_t)tile0 * a.KB;
         wbase = a.codes + (unit0 << 10) + l * 16;
         gbase = reinterpret_cast<const uint16_t*>(a.scales) + unit0 * 16 + (l & 15);
-        xrow = (m < a.rows) ? a.x + (int64_t)m * a.ldx + (l >> 4) * 32 : nullptr;
+        xs.init(a, l, piece0);
         const uint32_t* qm = reinterpret_cast<const uint32_t*>(a.qmap);
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = qm[i];
@@ -167,23 +227,23 @@ struct MfmaLut {
             r.w[t] = load_stream16(ok ? wbase + (u << 10) : g_zero_page + lane * 16);
             r.g[t] = ok ? (uint32_t)gbase[u * 16] : 0u;
         }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const void* p = (valid && xrow) ? (const void*)(xrow + kb * 128 + s * 8)
-                                            : (const void*)(g_zero_page + 1024 + s * 16);
-            r.x[s] = load16(p);
-        }
+        xs.load(r.x, kb, valid);
     }
 
-    __device__ __forceinline__ void compute(const Unit& r, int)
+    __device__ __forceinline__ void stage(uint8_t* buf, const Unit& r) const { xs.stage(buf, r.x); }
+
+    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* buf)
     {
+        f16x8_t b[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)   // K group (l/16) holds k = 32(l/16) + 8s + e
+            b[s] = __builtin_bit_cast(f16x8_t, xs.frag(buf, (lane >> 4) * 32 + s * 8));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, (uint16_t)r.g[t]));
             const uint32_t wd[4] = {r.w[t].x, r.w[t].y, r.w[t].z, r.w[t].w};
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                acc[t] = mfma_f16(lut_decode8(wd[s], pl), __builtin_bit_cast(f16x8_t, r.x[s]), acc[t]);
+            for (int s = 0; s < 4; ++s) acc[t] = mfma_f16(lut_decode8(wd[s], pl), b[s], acc[t]);
         }
     }
 
@@ -191,7 +251,7 @@ struct MfmaLut {
     {
         const int m = lane & 15, n4 = (lane >> 4) * 4;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(slot + m * CGW + t * 16 + n4) = acc[t];
+        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(slot + m * NT * 16 + t * 16 + n4) = acc[t];
     }
 };
 
@@ -208,6 +268,7 @@ struct MfmaLut {
 template <int MR>
 struct GemvFp8 {
     static constexpr int KIND = KIND_GEMV_FP8;
+    static constexpr int NTILES = 4;
     static constexpr int CGW = 64;
     struct Unit {
         uint4 w[2][4];       // [chunk j][K group g]
@@ -221,13 +282,13 @@ struct GemvFp8 {
     const float* srow;
     float outer[MR];
 
-    __device__ GemvFp8(const GemmArgs& args, int l, int cg) : a(args), lane(l)
+    __device__ GemvFp8(const GemmArgs& args, int l, int tile0, int) : a(args), lane(l)
     {
-        const int64_t tile = (int64_t)cg * 4 + (l >> 4);
+        const int64_t tile = (int64_t)tile0 + (l >> 4);
         tile_ok = tile < a.n_tiles;
         wbase = a.codes + ((tile * a.KB) << 11) + (l & 15) * 16;
         xg = a.x;
-        srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(cg * CGW / 128) * a.KB;
+        srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(tile0 * 16 / 128) * a.KB;
 #pragma unroll
         for (int m = 0; m < MR; ++m) outer[m] = 0.f;
     }
@@ -242,6 +303,8 @@ struct GemvFp8 {
             for (int g = 0; g < 4; ++g) r.w[j][g] = load_stream16(p + (ok ? j * 1024 + g * 256 : 0));
         r.s = valid ? srow[kb] : 0.f;
     }
+
+    __device__ __forceinline__ void stage(uint8_t*, const Unit&) const {}
 
     __device__ __forceinline__ void compute(const Unit& r, int kb)
     {
@@ -291,46 +354,85 @@ struct GemvFp8 {
 // ======================================================================
 // The split-K GEMM kernel: grid = column groups, block = S waves.
 // ======================================================================
-template <class Pol, int D, bool F16_OUT>
-__global__ void __launch_bounds__(64 * max_split(Pol::KIND, Pol::CGW / 16))
+// ======================================================================
+// The GEMM kernel.  Grid: one work-group per column group of SN*NT tiles.
+// Block: S = SN*SK waves; wave w is column-wave cw = w % SN (tiles
+// cw*NT .. +NT of the group) in K group kg = w / SN (K blocks
+// KB*kg/SK .. KB*(kg+1)/SK).  The SN waves of a K group share each K block's
+// activations through an LDS buffer (double-buffered, one barrier per K
+// block); with SN = 1 each wave stages its own activations and no barrier is
+// needed.  After the K loop every wave parks its partial tile in LDS and the
+// work-group sums the SK partials of each column in K-group order.
+// ======================================================================
+template <int SN>
+constexpr int x_buffers() { return SN > 1 ? 2 : 1; }
+
+template <class Pol, int D, int SN, bool F16_OUT>
+__global__ void __launch_bounds__(64 * max_split(Pol::KIND, Pol::NTILES, SN))
 gemm_kernel(GemmArgs a)
 {
-    constexpr int CGW = Pol::CGW;
-    constexpr int SLOT = 16 * CGW;            // floats in one partial tile
-    extern __shared__ float lds[];            // [S][SLOT]
+    constexpr int NT = Pol::NTILES;
+    constexpr int TW = NT * 16;                       // columns of one wave
+    constexpr int XB = x_buffers<SN>();
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int S = blockDim.x >> 6;
-    const int cg = blockIdx.x;
-    const int kb0 = (a.KB * wave) / S, kb1 = (a.KB * (wave + 1)) / S;
+    const int SK = S / SN;
+    const int cw = wave % SN, kg = wave / SN;
+    const int kb0 = (a.KB * kg) / SK, kb1 = (a.KB * (kg + 1)) / SK;
+    const int len = kb1 - kb0;
+    const int steps = (a.KB + SK - 1) / SK;           // the longest K range; every wave runs it
+    uint8_t* xbuf = lds + (SN > 1 ? kg : wave) * XB * kXStageBytes;
+    const int tile0 = (blockIdx.x * SN + cw) * NT;
 
-    Pol pol(a, lane, cg);
+    Pol pol(a, lane, tile0, cw * (4 / SN));
     {
         typename Pol::Unit r[D + 1];
 #pragma unroll
-        for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, kb0 + i < kb1);
-        for (int kb = kb0; kb < kb1; kb += D + 1) {
+        for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len);
+        pol.stage(xbuf, r[0]);
+        for (int i = 0; i < steps; i += D + 1) {
 #pragma unroll
             for (int j = 0; j <= D; ++j) {
-                const int nxt = kb + j + D;
-                pol.load(r[(j + D) % (D + 1)], nxt, nxt < kb1);
-                if (kb + j < kb1) pol.compute(r[j], kb + j);
+                const int step = i + j;
+                pol.load(r[(j + D) % (D + 1)], kb0 + step + D, step + D < len);
+                if (SN > 1) __syncthreads();
+                uint8_t* cur = xbuf + (step & (XB - 1)) * kXStageBytes;
+                if (step < len) {
+                    if constexpr (Pol::KIND == KIND_GEMV_FP8) pol.compute(r[j], kb0 + step);
+                    else pol.compute(r[j], cur);
+                }
+                pol.stage(xbuf + ((step + 1) & (XB - 1)) * kXStageBytes, r[(j + 1) % (D + 1)]);
             }
         }
     }
-    pol.store_partial(lds + wave * SLOT);
+    __syncthreads();   // every wave is done with the staging buffers
+    float* part = reinterpret_cast<float*>(lds);           // [S][16][TW]
+    pol.store_partial(part + wave * 16 * TW);
     __syncthreads();
 
-    const int nout = a.rows * CGW;
+    const int cols = SN * TW;
+    const int nout = a.rows * cols;
     for (int e = tid; e < nout; e += blockDim.x) {
-        float v = lds[e];
-        for (int w = 1; w < S; ++w) v += lds[w * SLOT + e];
-        const int m = e / CGW;
-        const int64_t n = (int64_t)cg * CGW + (e - m * CGW);
+        const int m = e / cols, c = e - m * cols;
+        const int w0 = c / TW, cc = c - w0 * TW;
+        const float* p = part + (w0 * 16 + m) * TW + cc;    // wave w0 (K group 0)
+        float v = p[0];
+        for (int k = 1; k < SK; ++k) v += p[(int64_t)k * SN * 16 * TW];
+        const int64_t n = (int64_t)blockIdx.x * cols + c;
         if (n < a.N) a.y[m * a.ldy + n] = F16_OUT ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
     }
+}
+
+template <class Pol, int SN>
+constexpr int gemm_lds_bytes(int split)
+{
+    const int stage = (SN > 1 ? split / SN : split) * x_buffers<SN>() * kXStageBytes;
+    const int parts = split * 16 * Pol::NTILES * 16 * 4;
+    return stage > parts ? stage : parts;
 }
 
 // ======================================================================
@@ -461,11 +563,11 @@ __global__ void unpack_lut3_kernel(const uint8_t* __restrict__ packed, int64_t N
 // Launchers
 // ======================================================================
 
-template <class Pol, int D, bool F16>
+template <class Pol, int D, int SN, bool F16>
 static hipError_t launch_one(const GemmArgs& a, int split, hipStream_t s)
 {
-    auto fn = gemm_kernel<Pol, D, F16>;
-    const size_t lds = (size_t)split * 16 * Pol::CGW * sizeof(float);
+    auto fn = gemm_kernel<Pol, D, SN, F16>;
+    const size_t lds = (size_t)gemm_lds_bytes<Pol, SN>(split);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -475,33 +577,42 @@ static hipError_t launch_one(const GemmArgs& a, int split, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int NT>
-static hipError_t launch_nt(int kind, int rows, const GemmArgs& a, int split, hipStream_t s)
+template <int NT, int SN>
+static hipError_t launch_mfma(int kind, const GemmArgs& a, int split, hipStream_t s)
 {
-    switch (kind) {
-    case KIND_MFMA_FP8: return launch_one<MfmaFp8<NT>, kDepthMfmaFp8, false>(a, split, s);
-    case KIND_MFMA_LUT: return launch_one<MfmaLut<NT>, kDepthMfmaLut, true>(a, split, s);
+    if (kind == KIND_MFMA_FP8) return launch_one<MfmaFp8<NT, SN>, kDepthMfmaFp8, SN, false>(a, split, s);
+    return launch_one<MfmaLut<NT, SN>, kDepthMfmaLut, SN, true>(a, split, s);
+}
+
+template <int NT>
+static hipError_t launch_nt(int kind, int sn, const GemmArgs& a, int split, hipStream_t s)
+{
+    switch (sn) {
+    case 1: return launch_mfma<NT, 1>(kind, a, split, s);
+    case 2: return launch_mfma<NT, 2>(kind, a, split, s);
+    case 4: return launch_mfma<NT, 4>(kind, a, split, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream)
+hipError_t launch_gemm(int kind, int nt, int sn, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream)
 {
-    if (split < 1 || split > max_split(kind, nt)) return hipErrorInvalidValue;
+    if (split < 1 || split > max_split(kind, nt, sn) || split % sn) return hipErrorInvalidValue;
     if (kind == KIND_GEMV_FP8) {
-        if (nt != 4) return hipErrorInvalidValue;
+        if (nt != 4 || sn != 1) return hipErrorInvalidValue;
         switch (gemv_rows) {
-        case 1: return launch_one<GemvFp8<1>, kDepthGemv, false>(a, split, stream);
-        case 2: return launch_one<GemvFp8<2>, kDepthGemv, false>(a, split, stream);
-        case 3: return launch_one<GemvFp8<3>, kDepthGemv, false>(a, split, stream);
-        case 4: return launch_one<GemvFp8<4>, kDepthGemv, false>(a, split, stream);
+        case 1: return launch_one<GemvFp8<1>, kDepthGemv, 1, false>(a, split, stream);
+        case 2: return launch_one<GemvFp8<2>, kDepthGemv, 1, false>(a, split, stream);
+        case 3: return launch_one<GemvFp8<3>, kDepthGemv, 1, false>(a, split, stream);
+        case 4: return launch_one<GemvFp8<4>, kDepthGemv, 1, false>(a, split, stream);
         default: return hipErrorInvalidValue;
         }
     }
+    if (kind != KIND_MFMA_FP8 && kind != KIND_MFMA_LUT) return hipErrorInvalidValue;
     switch (nt) {
-    case 1: return launch_nt<1>(kind, gemv_rows, a, split, stream);
-    case 2: return launch_nt<2>(kind, gemv_rows, a, split, stream);
-    case 4: return launch_nt<4>(kind, gemv_rows, a, split, stream);
+    case 1: return launch_nt<1>(kind, sn, a, split, stream);
+    case 2: return launch_nt<2>(kind, sn, a, split, stream);
+    case 4: return launch_nt<4>(kind, sn, a, split, stream);
     default: return hipErrorInvalidValue;
     }
 }

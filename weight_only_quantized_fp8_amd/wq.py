@@ -14,7 +14,7 @@ import os
 __all__ = [
     "WqError", "LIB_PATH", "lib",
     "WQ_OK", "WQ_FMT_FP8_BLOCK", "WQ_FMT_LUT3", "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA",
-    "wq_status_str", "wq_packed_format_version",
+    "wq_status_str", "wq_packed_format_version", "wq_set_tuning",
     "wq_fp8_block_packed_bytes", "wq_pack_fp8_block", "wq_gemm_fp8_block", "wq_gemm_fp8_block_path",
     "wq_lut3_packed_bytes", "wq_pack_lut3", "wq_gemm_lut3",
     "wq_gemm_workspace_bytes", "wq_unpack_fp8_block", "wq_unpack_fp8_block_f32", "wq_unpack_lut3",
@@ -41,6 +41,7 @@ _P, _I64, _SZ, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c
 _SIGS = {
     "wq_status_str": (ctypes.c_char_p, [_INT]),
     "wq_packed_format_version": (_INT, []),
+    "wq_set_tuning": (_INT, [_INT, _INT, _INT, _INT]),
     "wq_fp8_block_packed_bytes": (_SZ, [_I64, _I64]),
     "wq_pack_fp8_block": (_INT, [_P, _I64, _P, _I64, _I64, _P, _P]),
     "wq_gemm_fp8_block": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
@@ -105,6 +106,10 @@ def wq_status_str(status: int) -> str:
 
 def wq_packed_format_version() -> int:
     return lib.wq_packed_format_version()
+
+
+def wq_set_tuning(nt: int = 0, sn: int = 0, split: int = 0, waves_per_cu: int = 0) -> None:
+    _check(lib.wq_set_tuning(nt, sn, split, waves_per_cu), "wq_set_tuning")
 
 
 def wq_fp8_block_packed_bytes(N: int, K: int) -> int:
