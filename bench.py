@@ -2,7 +2,7 @@
 """Benchmark of the decode-phase weight-only-quantized GEMM on one MI355X.
 
 A step is one call of the hot path (dispatch, weight stream, activation staging,
-dequant, matrix-core inner product, stream-K scheduling, epilogue) on one batch:
+dequant, matrix-core inner product, split-K scheduling, epilogue) on one batch:
 by default the FP8 block-scaled FFN gate/up projection, N=17408, K=5120, M=16,
 BF16 activations.  Inputs are synthetic and seeded (synth/), already resident in
 HBM before timing starts.  Each step reads a different copy of the packed
@@ -116,41 +116,66 @@ class Workload:
         return 1 if self.M <= 16 else 2
 
 
-def time_workload(w: Workload, steps: int, warmup: int):
+def time_workload(w: Workload, steps: int, warmup: int, use_graph: bool = True):
+    """Time `steps` back-to-back steps between two HIP events on the stream the
+    library launches on.  With use_graph the steps are captured once into a HIP
+    graph and replayed, so the host's per-call launch cost (Python, ctypes,
+    hipLaunchKernel) does not sit between the kernels; the graph's output is
+    checked bit for bit against an eager call first."""
     import torch
-    stream = torch.cuda.current_stream()
     for _ in range(warmup):
         w.step()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        w.i = 0
+        w.step()                                   # eager reference on copy 0
+        torch.cuda.synchronize()
+        ref = w.y.clone()
+        w.y.zero_()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            graph = torch.cuda.CUDAGraph()
+            w.i = 0
+            with torch.cuda.graph(graph, stream=s):
+                for _ in range(steps):
+                    w.step()
+        torch.cuda.current_stream().wait_stream(s)
+        for rep in range(2):                       # replays agree with the eager result
+            w.y.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            # the last captured step used copy (steps-1) % copies, identical bytes to copy 0
+            if not torch.equal(w.y.view(torch.int16), ref.view(torch.int16)):
+                raise RuntimeError("graph replay %d differs from the eager result" % rep)
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     h0 = time.perf_counter()
-    t_begin.record(stream)
-    for i in range(steps):
-        starts[i].record(stream)
-        w.step()
-        ends[i].record(stream)
-    t_end.record(stream)
+    t0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(steps):
+            w.step()
+    t1.record(stream)
     torch.cuda.synchronize()
     host_s = time.perf_counter() - h0
-    total_ms = t_begin.elapsed_time(t_end)
-    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    mean_step_ms = sum(per) / len(per)
+    total_ms = t0.elapsed_time(t1)
     return {
         "ms_per_step": total_ms / steps,
         "host_ms_per_step": host_s * 1e3 / steps,
-        "launch_ms_mean": mean_step_ms / w.launches_per_step(),
-        "step_ms_p10": per[int(0.1 * (len(per) - 1))],
-        "step_ms_p50": per[int(0.5 * (len(per) - 1))],
-        "step_ms_p90": per[int(0.9 * (len(per) - 1))],
+        "launch_ms_mean": total_ms / steps / w.launches_per_step(),
+        "graph": graph is not None,
     }
 
 
-def cpu_baseline(name: str, M: int):
-    """The oracle as it stands, on the host cores, over the whole workload."""
-    import numpy as np
+def cpu_baseline(name: str, M: int, min_seconds: float = 3.0, max_reps: int = 20):
+    """The oracle as it stands, on the host cores, over the whole workload (all
+    outputs), repeated until min_seconds of wall time; the median pass counts."""
     import oracle
     import synth
     fmt, N, K, _ = synth.CONFIGS[name]
@@ -159,17 +184,21 @@ def cpu_baseline(name: str, M: int):
     if fmt == "fp8":
         codes, scales = synth.fp8_weights(N, K, seed)
         x = synth.x_bf16(M, K, seed + 100)
-        t0 = time.perf_counter()
-        oracle.gemm_fp8(x, codes, scales, nthreads=threads)
+        run = lambda: oracle.gemm_fp8(x, codes, scales, nthreads=threads)
     else:
         codes, qmap, g = synth.lut3_weights(N, K, seed)
         x = synth.x_f16(M, K, seed + 100)
+        run = lambda: oracle.gemm_lut3(x, codes, qmap, g, nthreads=threads)
+    times = []
+    start = time.perf_counter()
+    while len(times) < max_reps and (time.perf_counter() - start < min_seconds or len(times) < 3):
         t0 = time.perf_counter()
-        oracle.gemm_lut3(x, codes, qmap, g, nthreads=threads)
-    dt = time.perf_counter() - t0
-    del np
+        run()
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     return {"value": weight_bytes(fmt, N, K) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "whole %s workload N=%d K=%d M=%d, all outputs, one pass (%.2f s wall)" % (name, N, K, M, dt),
+            "sample": "whole %s workload N=%d K=%d M=%d, all %d outputs; median of %d passes, %.3f s each"
+                      % (name, N, K, M, M * N, len(times), dt),
             "seconds": dt}
 
 
@@ -182,6 +211,7 @@ def main(argv=None) -> int:
     ap.add_argument("--M", type=int, default=16)
     ap.add_argument("--all", action="store_true", help="also time every other workload and M")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true", help="launch each step from Python instead of a HIP graph")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -198,7 +228,7 @@ def main(argv=None) -> int:
     import synth
     print("bench: preparing %s M=%d" % (args.config, args.M), file=sys.stderr, flush=True)
     w = Workload(args.config, args.M)
-    r = time_workload(w, args.steps, args.warmup)
+    r = time_workload(w, args.steps, args.warmup, use_graph=not args.eager)
     value = w.wbytes / (r["ms_per_step"] * 1e-3) / 1e9
     achieved = w.abytes / (r["launch_ms_mean"] * 1e-3) / 1e9
     key = "%s_M%d" % (args.config, args.M)
@@ -224,9 +254,11 @@ def main(argv=None) -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": w.abytes,
                      "launch_us_mean": round(r["launch_ms_mean"] * 1e3, 3)},
-        "timing": {k: round(v * 1e3, 3) for k, v in r.items()},
+        "timing": {"us_per_step": round(r["ms_per_step"] * 1e3, 3),
+                   "host_us_per_step": round(r["host_ms_per_step"] * 1e3, 3),
+                   "hip_graph": r["graph"],
+                   "method": "HIP events around %d back-to-back steps on the library's stream" % args.steps},
     }
-    out["timing"] = {"us_" + k.replace("_ms", ""): v for k, v in out["timing"].items()}
     del w
     torch.cuda.empty_cache()
 
@@ -240,11 +272,12 @@ def main(argv=None) -> int:
                     continue
                 print("bench: %s M=%d" % (name, M), file=sys.stderr, flush=True)
                 wk = Workload(name, M)
-                rk = time_workload(wk, max(20, args.steps // 4), max(5, args.warmup // 4))
+                rk = time_workload(wk, max(20, args.steps // 4), max(5, args.warmup // 4),
+                                   use_graph=not args.eager)
                 gbs = wk.wbytes * wk.launches_per_step() / (rk["ms_per_step"] * 1e-3) / 1e9
                 extra["%s_M%d" % (name, M)] = {
                     "us_per_call": round(rk["ms_per_step"] * 1e3, 2),
-                    "us_launch_mean": round(rk["launch_ms_mean"] * 1e3, 2),
+                    "us_per_launch": round(rk["launch_ms_mean"] * 1e3, 2),
                     "stream_GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                     "passes": wk.launches_per_step()}
                 del wk

@@ -289,3 +289,41 @@ def test_every_tiling_matches_oracle(nt, sn, split, tuning_reset):
             y, _ = U.run_lut3(packed, N, K, xh)
             r = U.grade_lut3(y, xh, c, q, g, K)
             assert r.ok, "lut3 N=%d K=%d M=%d: %s" % (N, K, M, r)
+
+
+def test_hip_graph_replays_match_eager():
+    """The GEMM captured in a HIP graph (no memset nodes: the library queues
+    kernels only) replays to the eager result every time, with eager work and
+    synchronisations between the replays."""
+    wq = U.wqmod()
+    U.note("hip graph replay")
+    N, K, M = 640, 1280, 16
+    codes, scales = synth.fp8_weights(N, K, 90)
+    packed = U.pack_fp8(codes, scales)
+    x = U.t_u16(synth.x_bf16(M, K, 91), torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=U.DEV)
+    c, q, g = synth.lut3_weights(N, K, 92)
+    pl = U.pack_lut3(c, q, g)
+    xh = U.t_u16(synth.x_f16(M, K, 93), torch.float16)
+    yl = torch.empty((M, N), dtype=torch.float16, device=U.DEV)
+    wq.wq_gemm_fp8_block(packed, N, K, x, y, M)
+    wq.wq_gemm_lut3(pl, N, K, xh, yl, M)
+    torch.cuda.synchronize()
+    ref, refl = y.clone(), yl.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            wq.wq_gemm_fp8_block(packed, N, K, x, y, M)
+            wq.wq_gemm_lut3(pl, N, K, xh, yl, M)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        y.fill_(7.0)
+        yl.fill_(7.0)
+        wq.wq_gemm_fp8_block_path(packed, N, K, x[:3], y[:3], 3, None, GEMV)   # eager work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), rep
+        assert torch.equal(yl.view(torch.int16), refl.view(torch.int16)), rep

@@ -110,25 +110,54 @@ struct Plan {
     int n_tiles = 0, n_cg = 0, KB = 0;
 };
 
+// Tilings measured fastest on MI355X (256 CUs) for the decode shapes of the
+// FFN and attention projections (per-shape dispatch, as in the FLUTE PR's
+// "data-driven per-shape dispatch"); other shapes use the rule below.
+struct TableEntry {
+    int kind;
+    int64_t N, K;
+    int nt, sn, split;
+};
+constexpr TableEntry kTable[] = {
+    {wq::KIND_MFMA_FP8, 17408, 5120, 2, 1, 1},    // FFN gate/up
+    {wq::KIND_MFMA_FP8, 5120, 17408, 2, 1, 4},    // FFN down
+    {wq::KIND_MFMA_FP8, 6144, 5120, 2, 1, 4},     // attention Q
+    {wq::KIND_MFMA_FP8, 1024, 5120, 1, 1, 16},    // attention K, V
+    {wq::KIND_MFMA_FP8, 5120, 6144, 2, 1, 4},     // attention output
+    {wq::KIND_MFMA_LUT, 28672, 8192, 1, 4, 8},    // 3-bit LUT 28672x8192
+};
+
 Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
 {
     Plan p;
     p.kind = kind;
     p.n_tiles = (int)(N / 16);
     p.KB = (int)(K / 128);
-    const int target = std::max(1, cu * o.waves_per_cu);
+    const TableEntry* te = nullptr;
+    if (cu == 256)
+        for (const TableEntry& e : kTable)
+            if (e.kind == kind && e.N == N && e.K == K) te = &e;
     if (kind == wq::KIND_GEMV_FP8) {
         // the GEMV covers 4 tiles per wave (one column per lane) and stages no
         // activations; its plan must not depend on M (batch invariance)
         p.nt = 4;
         p.sn = 1;
+    } else if (o.nt || o.sn) {
+        p.nt = o.nt ? o.nt : 2;
+        p.sn = o.sn ? o.sn : 1;
+    } else if (te) {
+        p.nt = te->nt;
+        p.sn = te->sn;
     } else {
-        p.nt = o.nt ? o.nt : (p.n_tiles >= 2 * cu ? 2 : 1);
-        if (o.sn) p.sn = o.sn;
-        else {
-            // share activations across 4 column-waves while that still leaves
-            // at least one work-group per compute unit
-            p.sn = (p.n_tiles / (p.nt * 4) >= cu) ? 4 : 1;
+        // Two tiles per wave where N allows (each activation fragment feeds two
+        // MFMAs), one for the low-N projections; the LUT format, whose weight
+        // units are half the bytes, shares activations across 4 column-waves
+        // when that still leaves a work-group per compute unit.
+        p.nt = p.n_tiles >= cu ? 2 : 1;
+        p.sn = 1;
+        if (kind == wq::KIND_MFMA_LUT && p.n_tiles / 4 >= cu) {
+            p.nt = 1;
+            p.sn = 4;
         }
     }
     const int group = p.nt * p.sn;
@@ -136,7 +165,13 @@ Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
     const int maxs = wq::max_split(kind, p.nt, p.sn);
     int sk;
     if (o.split) sk = std::max(1, o.split / p.sn);
-    else sk = (int)std::lround((double)target / ((double)p.n_cg * p.sn));
+    else if (te && !o.nt && !o.sn && kind != wq::KIND_GEMV_FP8) sk = te->split / te->sn;
+    else {
+        // aim at `waves_per_cu` resident waves (more for 1-tile waves, which
+        // carry half the bytes each)
+        const double target = (double)cu * o.waves_per_cu * (p.nt == 1 ? 1.6 : 1.0) * 0.625;
+        sk = (int)std::lround(target / ((double)p.n_cg * p.sn));
+    }
     sk = std::max(1, std::min(sk, std::min(maxs / p.sn, p.KB)));   // every K group gets >= 1 block
     p.split = sk * p.sn;
     return p;
