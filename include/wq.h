@@ -41,9 +41,9 @@
  * Environment options, read once at the first call that needs them (for
  * sweeps without a rebuild; the defaults are the per-shape plan):
  *   WQ_FORCE_PATH   = auto | gemv | mfma  path for wq_gemm_fp8_block (default auto)
- *   WQ_NT           = 1 | 2 | 4           16-column MFMA tiles per wave
- *   WQ_SN           = 1 | 2 | 4           column-waves sharing each K block's activations
- *   WQ_SPLIT        = 1 .. 16             waves per work-group (SN x K-groups)
+ *   WQ_NT           = 1 | 2               16-column MFMA tiles per wave
+ *   WQ_SN           = 1 .. 8              column-waves sharing staged activations
+ *   WQ_SPLIT        = 1 .. 8              waves per work-group (SN x K-groups)
  *   WQ_WAVES_PER_CU = 1 .. 32             resident waves per CU the plan aims for (4)
  */
 #ifndef WQ_H_
@@ -87,10 +87,10 @@ const char* wq_status_str(wq_status s);
 int wq_packed_format_version(void);
 
 /* Tuning and test hook: override the per-shape plan of later calls.  nt =
- * 16-column tiles per wave (1, 2, 4), sn = column-waves sharing activations
- * (1, 2, 4), split = waves per work-group (1..16, rounded to the kernel's
- * limit and to a multiple of sn), waves_per_cu = the resident-wave target of
- * the automatic plan; 0 selects the automatic choice for each.  Replaces the
+ * 16-column tiles per wave (1, 2), sn = column-waves sharing activations
+ * (1..8), split = waves per work-group (1..8, rounded down to a multiple of
+ * sn; at most 4 K groups), waves_per_cu = the resident-wave target of the
+ * automatic plan; 0 selects the automatic choice for each.  Replaces the
  * WQ_NT / WQ_SN / WQ_SPLIT / WQ_WAVES_PER_CU environment values.  The FP8
  * GEMV path ignores nt and sn.  Results stay within the documented tolerance
  * for every setting, but bit patterns may differ between settings.  Not meant

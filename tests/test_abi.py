@@ -51,7 +51,7 @@ def test_workspace_is_empty():
 
 
 def test_sizes_are_host_arithmetic():
-    assert wq.wq_packed_format_version() == 1
+    assert wq.wq_packed_format_version() == 2
     assert wq.wq_fp8_block_packed_bytes(17408, 5120) == 17408 * 5120 + 4 * 136 * 40
     assert wq.wq_lut3_packed_bytes(28672, 8192) == 28672 * 8192 // 2 + 2 * 28672 * 64 + 32
     assert wq.wq_fp8_block_packed_bytes(100, 128) == 0      # N not a multiple of 128

@@ -256,8 +256,10 @@ def test_zero_rows_and_zero_matrix():
 
 # ------------------------------------------------------ every kernel variant
 
-TUNINGS = [(1, 1, 1), (1, 1, 16), (1, 2, 4), (1, 4, 16), (2, 1, 3), (2, 1, 8), (2, 2, 6), (2, 4, 4),
-           (2, 4, 16), (4, 1, 5), (4, 2, 8), (4, 4, 4), (4, 4, 8)]
+# (nt, sn, split): every activation-piece count per lane the kernels are built
+# for (sn = 1, 2, 3, 4/5, 6/7, 8), one to four K groups, 1- and 2-tile waves
+TUNINGS = [(1, 1, 1), (1, 1, 4), (2, 1, 3), (1, 2, 4), (2, 2, 8), (1, 3, 6), (2, 3, 6), (1, 4, 4),
+           (1, 4, 8), (2, 4, 8), (1, 5, 5), (1, 6, 6), (1, 7, 7), (2, 7, 7), (1, 8, 8), (2, 8, 8)]
 
 
 @pytest.fixture

@@ -16,7 +16,7 @@ namespace {
 
 using wq::GemmArgs;
 
-constexpr int kPackedFormatVersion = 1;
+constexpr int kPackedFormatVersion = 2;
 constexpr int kMaxDevices = 64;
 
 // ----------------------------------------------------------------- options
@@ -29,7 +29,6 @@ struct Options {
 };
 
 Options g_opts;
-std::mutex g_opts_mu;
 
 const Options& options()
 {
@@ -42,15 +41,15 @@ const Options& options()
         }
         if (const char* p = std::getenv("WQ_NT")) {
             int v = std::atoi(p);
-            if (v == 1 || v == 2 || v == 4) o.nt = v;
+            if (v == 1 || v == 2) o.nt = v;
         }
         if (const char* p = std::getenv("WQ_SN")) {
             int v = std::atoi(p);
-            if (v == 1 || v == 2 || v == 4) o.sn = v;
+            if (v >= 1 && v <= 8) o.sn = v;
         }
         if (const char* p = std::getenv("WQ_SPLIT")) {
             int v = std::atoi(p);
-            if (v >= 1 && v <= 16) o.split = v;
+            if (v >= 1 && v <= 8) o.split = v;
         }
         if (const char* p = std::getenv("WQ_WAVES_PER_CU")) {
             int v = std::atoi(p);
@@ -97,14 +96,14 @@ wq_status current_device(DevInfo* info, int* dev_out = nullptr)
 
 // --------------------------------------------------------------------- plan
 // A work-group covers SN*NT tiles of 16 output columns over all of K: SN
-// column-waves (NT tiles each) share the activations of each K block, and SK
-// K-groups split the K blocks (split = SN*SK waves).  NT, SN and SK are chosen
-// so that about `waves_per_cu` waves per compute unit are resident: shared
-// activations where N leaves enough column groups, narrower groups and a
-// deeper K split for the low-N projections.
+// column-waves (NT tiles each) share staged activation chunks, and SK K-groups
+// split the K blocks (split = SN*SK waves).  Sharing cuts the activation
+// reads (every work-group reads x once), so a plan takes as many tiles per
+// work-group as still leaves about one work-group per compute unit, and adds
+// K groups where that leaves too few waves.
 struct Plan {
     int kind = 0;
-    int nt = 2;
+    int nt = 1;
     int sn = 1;
     int split = 1;
     int n_tiles = 0, n_cg = 0, KB = 0;
@@ -119,12 +118,12 @@ struct TableEntry {
     int nt, sn, split;
 };
 constexpr TableEntry kTable[] = {
-    {wq::KIND_MFMA_FP8, 17408, 5120, 2, 1, 1},    // FFN gate/up
-    {wq::KIND_MFMA_FP8, 5120, 17408, 2, 1, 4},    // FFN down
-    {wq::KIND_MFMA_FP8, 6144, 5120, 2, 1, 4},     // attention Q
-    {wq::KIND_MFMA_FP8, 1024, 5120, 1, 1, 16},    // attention K, V
-    {wq::KIND_MFMA_FP8, 5120, 6144, 2, 1, 4},     // attention output
-    {wq::KIND_MFMA_LUT, 28672, 8192, 1, 4, 8},    // 3-bit LUT 28672x8192
+    {wq::KIND_MFMA_FP8, 17408, 5120, 1, 6, 6},    // FFN gate/up
+    {wq::KIND_MFMA_FP8, 5120, 17408, 1, 2, 8},    // FFN down
+    {wq::KIND_MFMA_FP8, 6144, 5120, 1, 2, 4},     // attention Q
+    {wq::KIND_MFMA_FP8, 1024, 5120, 1, 1, 4},     // attention K, V
+    {wq::KIND_MFMA_FP8, 5120, 6144, 1, 2, 8},     // attention output
+    {wq::KIND_MFMA_LUT, 28672, 8192, 1, 4, 4},    // 3-bit LUT 28672x8192
 };
 
 Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
@@ -143,36 +142,30 @@ Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
         p.nt = 4;
         p.sn = 1;
     } else if (o.nt || o.sn) {
-        p.nt = o.nt ? o.nt : 2;
-        p.sn = o.sn ? o.sn : 1;
+        p.nt = o.nt ? o.nt : 1;
+        p.sn = o.sn ? std::min(o.sn, wq::kMaxSplit) : 1;
     } else if (te) {
         p.nt = te->nt;
         p.sn = te->sn;
     } else {
-        // Two tiles per wave where N allows (each activation fragment feeds two
-        // MFMAs), one for the low-N projections; the LUT format, whose weight
-        // units are half the bytes, shares activations across 4 column-waves
-        // when that still leaves a work-group per compute unit.
-        p.nt = p.n_tiles >= cu ? 2 : 1;
-        p.sn = 1;
-        if (kind == wq::KIND_MFMA_LUT && p.n_tiles / 4 >= cu) {
-            p.nt = 1;
-            p.sn = 4;
-        }
+        // one tile per wave; as many column-waves per work-group as leaves at
+        // least one work-group per compute unit (at most 8)
+        p.nt = 1;
+        p.sn = std::max(1, std::min(8, p.n_tiles / std::max(1, cu)));
     }
     const int group = p.nt * p.sn;
     p.n_cg = (p.n_tiles + group - 1) / group;
-    const int maxs = wq::max_split(kind, p.nt, p.sn);
+    int max_sk = std::min(wq::kMaxSplit / p.sn, p.KB);   // every K group gets >= 1 block
+    if (kind != wq::KIND_GEMV_FP8) max_sk = std::min(max_sk, wq::kMaxKGroups);
     int sk;
     if (o.split) sk = std::max(1, o.split / p.sn);
     else if (te && !o.nt && !o.sn && kind != wq::KIND_GEMV_FP8) sk = te->split / te->sn;
     else {
-        // aim at `waves_per_cu` resident waves (more for 1-tile waves, which
-        // carry half the bytes each)
-        const double target = (double)cu * o.waves_per_cu * (p.nt == 1 ? 1.6 : 1.0) * 0.625;
+        // aim at `waves_per_cu` resident waves per compute unit
+        const double target = (double)cu * o.waves_per_cu;
         sk = (int)std::lround(target / ((double)p.n_cg * p.sn));
     }
-    sk = std::max(1, std::min(sk, std::min(maxs / p.sn, p.KB)));   // every K group gets >= 1 block
+    sk = std::max(1, std::min(sk, max_sk));
     p.split = sk * p.sn;
     return p;
 }
@@ -270,6 +263,7 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
     a.KB = p.KB;
     a.n_tiles = p.n_tiles;
     a.n_cg = p.n_cg;
+    a.sn = p.sn;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // rows 0..15, then (for M > 16) rows 16..M-1 as a second pass
@@ -280,7 +274,7 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
         a.y = y + r0 * ldy;
         a.ldy = ldy;
         a.rows = rows;
-        hipError_t e = wq::launch_gemm(kind, p.nt, p.sn, kind == wq::KIND_GEMV_FP8 ? rows : 0, a, p.split, s);
+        hipError_t e = wq::launch_gemm(kind, p.nt, kind == wq::KIND_GEMV_FP8 ? rows : 0, a, p.split, s);
         if (e != hipSuccess) return WQ_ERR_HIP;
     }
     return WQ_OK;
@@ -311,9 +305,8 @@ int wq_packed_format_version(void) { return kPackedFormatVersion; }
 
 wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu)
 {
-    if (nt != 0 && nt != 1 && nt != 2 && nt != 4) return WQ_ERR_SHAPE;
-    if (sn != 0 && sn != 1 && sn != 2 && sn != 4) return WQ_ERR_SHAPE;
-    if (split < 0 || split > 16 || waves_per_cu < 0 || waves_per_cu > 32) return WQ_ERR_SHAPE;
+    if (nt < 0 || nt > 2 || sn < 0 || sn > 8) return WQ_ERR_SHAPE;
+    if (split < 0 || split > 8 || waves_per_cu < 0 || waves_per_cu > 32) return WQ_ERR_SHAPE;
     options();
     std::lock_guard<std::mutex> lk(g_plan_mu);
     g_opts.nt = nt;

@@ -144,6 +144,45 @@ __device__ __forceinline__ uint4 load16(const void* p)
 // 16-byte load of data that is read-only for the kernel's lifetime, through
 // the constant address space: a wave-uniform address becomes a scalar load
 // into SGPRs.
+// ------------------------------------------------------------ buffer loads
+// A buffer resource covers [base, base + bytes); a load whose per-lane offset
+// (VGPR offset + instruction offset) lies at or past `bytes` returns zeros
+// instead of touching memory.  The per-unit offset of a wave-uniform stream
+// goes in the SGPR offset, so advancing a stream costs no VALU; selecting a
+// resource with zero bytes turns a whole load into zeros.
+typedef __amdgpu_buffer_rsrc_t buf_t;
+constexpr uint32_t kBufOutOfRange = 0x80000000u;   // a VGPR offset past every resource used here
+
+__device__ __forceinline__ buf_t make_buf(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// streaming (non-temporal) 16-byte load
+__device__ __forceinline__ uint4 buf_load_stream16(buf_t r, uint32_t voff, uint32_t soff)
+{
+    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint4 buf_load16(buf_t r, uint32_t voff, uint32_t soff)
+{
+    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint32_t buf_load_u16(buf_t r, uint32_t voff, uint32_t soff)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// wave-uniform 4-byte load through the scalar (constant) cache
+__device__ __forceinline__ float load_uniform_f32(const void* p)
+{
+    typedef const __attribute__((address_space(4))) float* cptr;
+    return *(cptr)(p);
+}
+
 __device__ __forceinline__ uint4 load_uniform16(const void* p)
 {
     typedef const __attribute__((address_space(4))) u32x4_t* cptr;

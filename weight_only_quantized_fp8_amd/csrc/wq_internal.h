@@ -8,9 +8,11 @@
 
 namespace wq {
 
-// Prefetch depth (K blocks in flight per wave beyond the one being computed).
-constexpr int kDepthMfmaFp8 = 2;
-constexpr int kDepthMfmaLut = 2;
+// Prefetch depth: weight units in flight per wave beyond the one being
+// computed (the register ring has depth + 1 slots).  A LUT unit is half the
+// bytes of an FP8 unit and costs more VALU to decode, so its ring is deeper.
+constexpr int kDepthMfmaFp8 = 3;
+constexpr int kDepthMfmaLut = 7;
 constexpr int kDepthGemv = 2;
 
 enum Kind : int {
@@ -19,14 +21,31 @@ enum Kind : int {
     KIND_GEMV_FP8 = 2,   // strict-K-order FP32 GEMV, M <= 4, FP8 weights
 };
 
-// Largest split (waves per work-group) a kernel may use.  A work-group runs
-// on one CU, so its S waves must fit the register file: the launch bound
-// 64*S caps a wave at 512/ceil(S/4) VGPRs.  The GEMV and the 4-tile MFMA
-// kernels, and the 2-tile ones that stage their own activations, need more
-// than 128 (S <= 8); the others fit in 128 (S <= 16).
-constexpr int max_split(int kind, int nt, int sn)
+// K blocks of activations staged per chunk (the K group synchronises once
+// per chunk).
+constexpr int kChunkBlocks = 4;
+
+// Each K group of an MFMA work-group double-buffers one activation chunk in
+// LDS (2 x 4 K blocks x 16 rows x 272 bytes = 34816 bytes); the 160 KiB of LDS
+// of a compute unit bound the K groups of one work-group at 4.
+constexpr int kMaxKGroups = 4;
+
+// 16-byte activation pieces each lane loads per chunk when SN column-waves
+// share it: ceil(chunk pieces / (64 * SN)), chunk pieces = 4 * 16 rows * 16.
+constexpr int x_pieces_per_lane(int sn) { return (kChunkBlocks * 256 + 64 * sn - 1) / (64 * sn); }
+
+// Largest split (waves per work-group).  The kernels are built for work-groups
+// of at most 8 waves, which lets a wave hold up to 256 VGPRs (2 waves per
+// SIMD): the register ring, the activation pieces in flight and the
+// unrolled MFMA steps of a chunk need more than 128.
+constexpr int kMaxSplit = 8;
+
+// Whether (nt, sn, split) is a launchable tiling for this kernel kind.
+constexpr bool split_ok(int kind, int nt, int sn, int split)
 {
-    return (kind == KIND_GEMV_FP8 || nt >= 4 || (nt == 2 && sn == 1)) ? 8 : 16;
+    if (sn < 1 || split < 1 || split % sn || split > kMaxSplit) return false;
+    if (kind == KIND_GEMV_FP8) return nt == 4 && sn == 1;
+    return (nt == 1 || nt == 2) && split / sn <= kMaxKGroups;
 }
 
 // Everything a GEMM launch needs.  The grid has one work-group per column
@@ -44,11 +63,12 @@ struct GemmArgs {
     int KB;                   // K / 128
     int n_tiles;              // N / 16
     int n_cg;                 // column groups = grid size
+    int sn;                   // column-waves per work-group sharing activations
 };
 
-// nt: tiles per wave; sn: column-waves sharing activations (split % sn == 0);
+// nt: tiles per wave; a.sn: column-waves sharing activations (split % sn == 0);
 // split: waves per work-group; the grid has a.n_cg = ceil(n_tiles/(nt*sn)) groups.
-hipError_t launch_gemm(int kind, int nt, int sn, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream);
+hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream);
 
 hipError_t launch_pack_fp8(const uint8_t* w, int64_t ldw, const float* scales, int64_t N,
                            int64_t K, uint8_t* packed, hipStream_t stream);

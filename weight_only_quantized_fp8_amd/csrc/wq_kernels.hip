@@ -1,20 +1,24 @@
 // gfx950 kernels of libwq: the decode GEMM (MFMA tile and strict-order GEMV)
 // for FP8 block-scaled and 3-bit LUT weights, and the pack / unpack kernels.
 //
-// Packed layouts (version 1).  A "unit" is 16 rows of W (one MFMA tile along
+// Packed layouts (version 2).  A "unit" is 16 rows of W (one MFMA tile along
 // N) by one 128-wide K block, stored contiguously, units ordered (tile, kb)
 // with kb fastest.  Inside a unit every 16-byte piece is what one lane loads
 // (the FLUTE PR "Add optimized_w3", "Core contributions" item 2: one
-// coalesced 16-byte load lands directly in the lane's matrix-core operand):
+// coalesced 16-byte load lands directly in the lane's matrix-core operand).
+// Both formats order K the same way: MFMA step s of a K block covers
+// k = 32s .. 32s+31, and lane group g = l/16 holds k = 32s + 8g .. +7, so the
+// four groups' activations of one batch row are one contiguous 64-byte run.
 //
 //   FP8   unit = 2048 B = two 1 KiB chunks j = 0, 1.  Lane l of chunk j holds
-//         the 16 codes W[16t + l%16][128kb + 64j + 16(l/16) + i], i = 0..15.
-//         Block scales follow the codes as FP32 [N/128][K/128].
-//   LUT3  unit = 1024 B.  Lane l holds 32 codes of row n = 16t + l%16 at
-//         k = 128kb + 32(l/16) + 8s + e (s, e = 0..7 blocks of the 4 dwords):
-//         dword s, byte b carries e = b in its low nibble, e = b + 4 in its
-//         high nibble.  Group scales follow as FP16 [tile][kb][16 rows], then
-//         the 8 map entries (FP16), then a 16-byte pack-status word.
+//         16 codes of row 16t + l%16: byte i is k = 128kb + 32(2j + i/8) +
+//         8(l/16) + i%8 (steps 2j and 2j+1).  Block scales follow the codes as
+//         FP32 [N/128][K/128].
+//   LUT3  unit = 1024 B.  Lane l holds 32 codes of row 16t + l%16 in 4 dwords
+//         s: byte b carries k = 128kb + 32s + 8(l/16) + e with e = b in its low
+//         nibble and e = b + 4 in its high nibble.  Group scales follow as FP16
+//         [tile][kb][16 rows], then the 8 map entries (FP16), then a 16-byte
+//         pack-status word.
 //
 // GEMM schedule.  One work-group owns one column group (NT tiles of 16 output
 // columns) over the whole of K.  Its S waves split the K blocks into S
@@ -44,95 +48,95 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_page[4096];
 // ======================================================================
 
 // ---- activation staging for the MFMA tiles ---------------------------------
-// The MFMA operand layout gives consecutive lanes consecutive batch rows, so
-// loading fragments straight from x would make every 16-byte lane piece its
-// own L1 access.  Instead x for one K block (16 rows x 128 k, 4 KiB) is loaded
-// coalesced, as four 1 KiB pieces f: 8 consecutive lanes read one row's
-// 128-byte segment (rows (l>>3) + 8(f&1), k = 64(f>>1) + 8(l&7) .. +7).  The
-// pieces go to an LDS buffer whose rows are padded by 16 bytes, and the
-// fragments are read back with 16-byte LDS reads: with the pad, the 16 rows
-// read by a 16-lane group start 4 banks apart and cover all 64 banks once
-// (the same stride arithmetic as the shared-memory pad in the arc PR "FP8
-// bank conflict + the dispatch threshold's provenance", "What landed").
-// When SN column-waves share a K range, each loads 4/SN of the pieces and
-// all of them read the shared buffer.
-constexpr int kXRowBytes = 128 * 2 + 16;          // padded LDS row
-constexpr int kXStageBytes = 16 * kXRowBytes;     // one K block of x
+// x is staged through LDS in chunks of kChunkBlocks K blocks.  The SN
+// column-waves of a K group share every chunk: its 16-byte pieces are dealt
+// round-robin over the group's SN*64 lanes, consecutive lanes taking
+// consecutive pieces of one row, so each load instruction reads whole
+// 256-byte row runs.  A chunk is loaded one chunk ahead of its use -- before
+// the weight loads issued in between -- so the wait that precedes staging it
+// never waits for weights still in flight, and the K group synchronises once
+// per chunk (double buffer, one barrier) rather than once per K block.
+// LDS rows are padded by 16 bytes: the 16 rows a 16-lane group reads for one
+// MFMA operand then start 4 banks apart and cover all 64 banks once (the
+// stride arithmetic of the shared-memory pad in the arc PR "FP8 bank conflict
+// + the dispatch threshold's provenance", "What landed").
+constexpr int kXRowBytes = 128 * 2 + 16;                    // padded LDS row of one K block
+constexpr int kXBlockBytes = 16 * kXRowBytes;               // one K block of x (16 rows)
+constexpr int kXChunkBytes = kChunkBlocks * kXBlockBytes;
+constexpr int kXChunkPieces = kChunkBlocks * 16 * 16;       // 16-byte pieces per chunk
 
-template <int XP>   // pieces this wave loads
-struct XStage {
-    const uint16_t* xl;       // x at this lane's k offset (8 * (l & 7))
-    int64_t ldx;
-    int rows;
-    int lane;
-    int f0;                   // first piece of this wave
+template <int XPL>   // pieces per lane: >= kXChunkPieces / (64 * SN)
+struct XChunk {
+    buf_t rx;                 // x rows 0 .. M-1
+    uint32_t vo[XPL];         // byte offset of piece i in the chunk at K block 0, or out of range
+    int blk[XPL];             // K block of piece i inside the chunk (large: no piece)
+    int dst[XPL];             // LDS offset of piece i inside a chunk buffer (-1: no piece)
+    uint4 r[XPL];
 
-    __device__ void init(const GemmArgs& a, int l, int first_piece)
+    __device__ void init(const GemmArgs& a, int lane, int cw, int sn)
     {
-        lane = l;
-        f0 = first_piece;
-        xl = a.x + (l & 7) * 8;
-        ldx = a.ldx;
-        rows = a.rows;
-    }
-
-    __device__ __forceinline__ void load(uint4 (&xr)[XP], int kb, bool valid) const
-    {
+        rx = make_buf(a.x, (uint32_t)(((int64_t)(a.rows - 1) * a.ldx + (int64_t)a.KB * 128) * 2));
 #pragma unroll
-        for (int i = 0; i < XP; ++i) {
-            const int f = f0 + i;
-            const int r = (lane >> 3) + 8 * (f & 1);
-            const void* p = (valid && r < rows) ? (const void*)(xl + r * ldx + kb * 128 + (f >> 1) * 64)
-                                                : (const void*)(g_zero_page + 1024 + (lane & 7) * 16);
-            xr[i] = load16(p);
+        for (int i = 0; i < XPL; ++i) {
+            const int q = cw * 64 + lane + i * sn * 64;
+            const int b = q >> 8, row = (q >> 4) & 15, seg = q & 15;
+            const bool ok = q < kXChunkPieces && row < a.rows;
+            blk[i] = ok ? b : (1 << 29);
+            vo[i] = ok ? (uint32_t)(row * a.ldx * 2 + b * 256 + seg * 16) : kBufOutOfRange;
+            dst[i] = q < kXChunkPieces ? b * kXBlockBytes + row * kXRowBytes + seg * 16 : -1;
         }
     }
 
-    __device__ __forceinline__ void stage(uint8_t* buf, const uint4 (&xr)[XP]) const
+    // Issue the loads of the chunk that starts at K block kb; blocks >= kb_end,
+    // rows >= M and pieces past the chunk read zeros.
+    __device__ __forceinline__ void load(int kb, int kb_end)
     {
 #pragma unroll
-        for (int i = 0; i < XP; ++i) {
-            const int f = f0 + i;
-            const int r = (lane >> 3) + 8 * (f & 1);
-            const int k = (f >> 1) * 64 + (lane & 7) * 8;
-            *reinterpret_cast<uint4*>(buf + r * kXRowBytes + k * 2) = xr[i];
-        }
+        for (int i = 0; i < XPL; ++i)
+            r[i] = buf_load16(rx, kb + blk[i] < kb_end ? vo[i] : kBufOutOfRange, (uint32_t)kb * 256u);
     }
 
-    // 8 consecutive activations of batch row (l % 16) starting at k
-    __device__ __forceinline__ uint4 frag(const uint8_t* buf, int k) const
+    __device__ __forceinline__ void stage(uint8_t* buf) const
     {
-        return *reinterpret_cast<const uint4*>(buf + (lane & 15) * kXRowBytes + k * 2);
+#pragma unroll
+        for (int i = 0; i < XPL; ++i)
+            if (dst[i] >= 0) *reinterpret_cast<uint4*>(buf + dst[i]) = r[i];
     }
 };
+
+// 8 consecutive activations of batch row (lane % 16), from k on, of one staged K block
+__device__ __forceinline__ uint4 x_frag(const uint8_t* blk, int lane, int k)
+{
+    return *reinterpret_cast<const uint4*>(blk + (lane & 15) * kXRowBytes + k * 2);
+}
 
 // ---- FP8 weights, 16-row BF16 MFMA tile ------------------------------------
 // A operand = dequantised weights (lane: row n = l%16), B operand = x
 // (lane: batch row m = l%16).  Output D[n][m] -> lane holds n = 4(l/16)+v.
-template <int NT, int SN>
+template <int NT>
 struct MfmaFp8 {
     static constexpr int KIND = KIND_MFMA_FP8;
     static constexpr int NTILES = NT;
-    static constexpr int XP = 4 / SN;
+    static constexpr bool STAGED = true;
     struct Unit {
         uint4 w[NT][2];
-        uint4 x[XP];
         float s;
     };
-    const GemmArgs& a;
     int lane;
+    int KB;
     int ntiles;               // valid tiles of this wave
-    const uint8_t* wbase;     // this lane's bytes of the wave's tile 0, K block 0
+    buf_t rw;                 // code units of the wave's tiles (zero bytes past N)
+    buf_t rnull;              // zero bytes: loads return zeros
     const float* srow;        // block-scale row of this wave's tiles
-    XStage<XP> xs;
     f32x4_t outer[NT];
 
-    __device__ MfmaFp8(const GemmArgs& args, int l, int tile0, int piece0) : a(args), lane(l)
+    __device__ MfmaFp8(const GemmArgs& a, int l, int tile0) : lane(l), KB(a.KB)
     {
-        ntiles = min(NT, a.n_tiles - tile0);
-        wbase = a.codes + (((int64_t)tile0 * a.KB) << 11) + l * 16;
-        srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(tile0 * 16 / 128) * a.KB;
-        xs.init(a, l, piece0);
+        ntiles = max(0, min(NT, a.n_tiles - tile0));
+        const uint8_t* base = a.codes + (((int64_t)min(tile0, a.n_tiles) * a.KB) << 11);
+        rw = make_buf(base, (uint32_t)(ntiles * a.KB) << 11);
+        rnull = make_buf(base, 0);
+        srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(min(tile0, a.n_tiles - 1) * 16 / 128) * a.KB;
 #pragma unroll
         for (int t = 0; t < NT; ++t) outer[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -141,31 +145,32 @@ struct MfmaFp8 {
     {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const bool ok = valid && t < ntiles;
-            const uint8_t* p = ok ? wbase + (((int64_t)t * a.KB + kb) << 11) : g_zero_page + lane * 16;
-            r.w[t][0] = load_stream16(p);
-            r.w[t][1] = load_stream16(p + (ok ? 1024 : 0));
+            const buf_t rs = (valid && t < ntiles) ? rw : rnull;
+            const uint32_t so = (uint32_t)(t * KB + kb) << 11;
+            r.w[t][0] = buf_load_stream16(rs, lane * 16, so);
+            r.w[t][1] = buf_load_stream16(rs, lane * 16 + 1024, so);
         }
-        xs.load(r.x, kb, valid);
-        r.s = (valid && ntiles > 0) ? srow[kb] : 0.f;   // a wave past N reads no scale
+        // a unit with nothing to fetch (and a wave past N) reads a zero scale
+        r.s = load_uniform_f32((valid && ntiles > 0) ? (const void*)(srow + kb) : (const void*)g_zero_page);
     }
 
-    __device__ __forceinline__ void stage(uint8_t* buf, const Unit& r) const { xs.stage(buf, r.x); }
-
-    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* buf)
+    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk)
     {
+        bf16x8_t b[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f)    // MFMA step f = 2j + h: lane group g holds k = 32f + 8g .. +7
+            b[f] = __builtin_bit_cast(bf16x8_t, x_frag(xblk, lane, f * 32 + (lane >> 4) * 8));
         f32x4_t blk[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) blk[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {  // f = 2j + h -> k offset 64j + 16(l/16) + 8h
+        for (int f = 0; f < 4; ++f) {
             const int j = f >> 1, h = f & 1;
-            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xs.frag(buf, j * 64 + (lane >> 4) * 16 + h * 8));
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const uint4 w = r.w[t][j];
                 const bf16x8_t av = h ? e4m3x8_to_bf16x8(w.z, w.w) : e4m3x8_to_bf16x8(w.x, w.y);
-                blk[t] = mfma_bf16(av, b, blk[t]);
+                blk[t] = mfma_bf16(av, b[f], blk[t]);
             }
         }
         // two-level fold: one FP32 FMA per 128-K block and output
@@ -185,32 +190,31 @@ struct MfmaFp8 {
 };
 
 // ---- 3-bit LUT weights, 16-row FP16 MFMA tile -------------------------------
-template <int NT, int SN>
+template <int NT>
 struct MfmaLut {
     static constexpr int KIND = KIND_MFMA_LUT;
     static constexpr int NTILES = NT;
-    static constexpr int XP = 4 / SN;
+    static constexpr bool STAGED = true;
     struct Unit {
         uint4 w[NT];
-        uint4 x[XP];
         uint32_t g[NT];      // FP16 group-scale bits, zero-extended
     };
-    const GemmArgs& a;
     int lane;
+    int KB;
     int ntiles;
-    const uint8_t* wbase;
-    const uint16_t* gbase;   // this lane's group scale of the wave's tile 0, K block 0
-    XStage<XP> xs;
+    buf_t rw;                // code units of the wave's tiles (zero bytes past N)
+    buf_t rg;                // group scales of the wave's tiles
+    buf_t rnull;             // zero bytes: loads return zeros
     uint32_t q[4];           // map entries as FP16 pairs
     f32x4_t acc[NT];
 
-    __device__ MfmaLut(const GemmArgs& args, int l, int tile0, int piece0) : a(args), lane(l)
+    __device__ MfmaLut(const GemmArgs& a, int l, int tile0) : lane(l), KB(a.KB)
     {
-        ntiles = min(NT, a.n_tiles - tile0);
-        const int64_t unit0 = (int64_t)tile0 * a.KB;
-        wbase = a.codes + (unit0 << 10) + l * 16;
-        gbase = reinterpret_cast<const uint16_t*>(a.scales) + unit0 * 16 + (l & 15);
-        xs.init(a, l, piece0);
+        ntiles = max(0, min(NT, a.n_tiles - tile0));
+        const int64_t unit0 = (int64_t)min(tile0, a.n_tiles) * a.KB;
+        rw = make_buf(a.codes + (unit0 << 10), (uint32_t)(ntiles * a.KB) << 10);
+        rg = make_buf(reinterpret_cast<const uint8_t*>(a.scales) + unit0 * 32, (uint32_t)(ntiles * a.KB) * 32u);
+        rnull = make_buf(a.codes, 0);
         const uint32_t* qm = reinterpret_cast<const uint32_t*>(a.qmap);
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = qm[i];
@@ -223,21 +227,18 @@ struct MfmaLut {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const bool ok = valid && t < ntiles;
-            const int64_t u = (int64_t)t * a.KB + kb;
-            r.w[t] = load_stream16(ok ? wbase + (u << 10) : g_zero_page + lane * 16);
-            r.g[t] = ok ? (uint32_t)gbase[u * 16] : 0u;
+            const uint32_t u = (uint32_t)(t * KB + kb);
+            r.w[t] = buf_load_stream16(ok ? rw : rnull, lane * 16, u << 10);
+            r.g[t] = buf_load_u16(ok ? rg : rnull, (lane & 15) * 2, u * 32);
         }
-        xs.load(r.x, kb, valid);
     }
 
-    __device__ __forceinline__ void stage(uint8_t* buf, const Unit& r) const { xs.stage(buf, r.x); }
-
-    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* buf)
+    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk)
     {
         f16x8_t b[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)   // K group (l/16) holds k = 32(l/16) + 8s + e
-            b[s] = __builtin_bit_cast(f16x8_t, xs.frag(buf, (lane >> 4) * 32 + s * 8));
+        for (int s = 0; s < 4; ++s)   // MFMA step s: lane group g holds k = 32s + 8g + e
+            b[s] = __builtin_bit_cast(f16x8_t, x_frag(xblk, lane, s * 32 + (lane >> 4) * 8));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, (uint16_t)r.g[t]));
@@ -257,10 +258,12 @@ struct MfmaLut {
 
 // ---- FP8 weights, strict-K-order GEMV (MR <= 4 rows) ------------------------
 // The wave covers 4 tiles (64 columns): lane l owns column l%16 of tile l/16.
-// For each 64-wide chunk it loads the chunk's four K groups g = 0..3 of its
-// column (the same 16-byte pieces the MFMA path loads, just gathered per K
-// group across four tiles), so every lane needs the same 16 activations at a
-// time: x is wave-uniform and read with scalar loads.  Each (row, column)
+// For each K block it loads the eight 16-byte pieces (chunk j, lane group g)
+// of its column -- the same pieces the MFMA path loads, gathered per lane
+// group across four tiles -- so every lane needs the same activations at a
+// time: x is wave-uniform and read with scalar loads.  Piece (j, g) holds the
+// 8-wide runs k = 64j + 8g and 64j + 32 + 8g, so visiting (j, half, g) in
+// that nesting walks the block's runs in increasing k.  Each (row, column)
 // keeps one FP32 accumulator that takes its products in strictly increasing
 // k over the wave's K range; each 128-K block is folded onto the outer
 // accumulator times the block scale.  The K split across waves is summed in
@@ -270,19 +273,20 @@ struct GemvFp8 {
     static constexpr int KIND = KIND_GEMV_FP8;
     static constexpr int NTILES = 4;
     static constexpr int CGW = 64;
+    static constexpr bool STAGED = false;
     struct Unit {
-        uint4 w[2][4];       // [chunk j][K group g]
+        uint4 w[2][4];       // [chunk j][lane group g]
         float s;
     };
     const GemmArgs& a;
     int lane;
     bool tile_ok;
-    const uint8_t* wbase;    // this lane's column in tile l/16, K group 0, K block 0
+    const uint8_t* wbase;    // this lane's column in tile l/16, lane group 0, K block 0
     const uint16_t* xg;      // x (wave-uniform)
     const float* srow;
     float outer[MR];
 
-    __device__ GemvFp8(const GemmArgs& args, int l, int tile0, int) : a(args), lane(l)
+    __device__ GemvFp8(const GemmArgs& args, int l, int tile0) : a(args), lane(l)
     {
         const int64_t tile = (int64_t)tile0 + (l >> 4);
         tile_ok = tile < a.n_tiles;
@@ -304,8 +308,6 @@ struct GemvFp8 {
         r.s = valid ? srow[kb] : 0.f;
     }
 
-    __device__ __forceinline__ void stage(uint8_t*, const Unit&) const {}
-
     __device__ __forceinline__ void compute(const Unit& r, int kb)
     {
         float blk[MR];
@@ -314,32 +316,26 @@ struct GemvFp8 {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint4 w = r.w[j][g];
-                const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-                float wf[16];
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x2_t lo = e4m3x2_to_f32x2<false>(d[i]);
-                    const f32x2_t hi = e4m3x2_to_f32x2<true>(d[i]);
-                    wf[4 * i + 0] = lo[0];
-                    wf[4 * i + 1] = lo[1];
-                    wf[4 * i + 2] = hi[0];
-                    wf[4 * i + 3] = hi[1];
-                }
-                const int k0 = kb * 128 + j * 64 + g * 16;
+                for (int g = 0; g < 4; ++g) {
+                    const uint4 w = r.w[j][g];
+                    const uint32_t d0 = h ? w.z : w.x, d1 = h ? w.w : w.y;
+                    const f32x2_t w0 = e4m3x2_to_f32x2<false>(d0), w1 = e4m3x2_to_f32x2<true>(d0);
+                    const f32x2_t w2 = e4m3x2_to_f32x2<false>(d1), w3 = e4m3x2_to_f32x2<true>(d1);
+                    const float wf[8] = {w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+                    const int k0 = kb * 128 + j * 64 + h * 32 + g * 8;
 #pragma unroll
-                for (int m = 0; m < MR; ++m) {
-                    const uint16_t* xp = xg + (int64_t)m * a.ldx + k0;
-                    const uint4 xa = load_uniform16(xp), xb = load_uniform16(xp + 8);
-                    const uint32_t xd[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+                    for (int m = 0; m < MR; ++m) {
+                        const uint4 xa = load_uniform16(xg + (int64_t)m * a.ldx + k0);
+                        const uint32_t xd[4] = {xa.x, xa.y, xa.z, xa.w};
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        blk[m] = __builtin_fmaf(bf16_bits_to_f32(xd[i] & 0xFFFFu), wf[2 * i], blk[m]);
-                        blk[m] = __builtin_fmaf(bf16_bits_to_f32(xd[i] >> 16), wf[2 * i + 1], blk[m]);
+                        for (int i = 0; i < 4; ++i) {
+                            blk[m] = __builtin_fmaf(bf16_bits_to_f32(xd[i] & 0xFFFFu), wf[2 * i], blk[m]);
+                            blk[m] = __builtin_fmaf(bf16_bits_to_f32(xd[i] >> 16), wf[2 * i + 1], blk[m]);
+                        }
                     }
                 }
-            }
 #pragma unroll
         for (int m = 0; m < MR; ++m) outer[m] = __builtin_fmaf(r.s, blk[m], outer[m]);
     }
@@ -352,60 +348,83 @@ struct GemvFp8 {
 };
 
 // ======================================================================
-// The split-K GEMM kernel: grid = column groups, block = S waves.
-// ======================================================================
-// ======================================================================
 // The GEMM kernel.  Grid: one work-group per column group of SN*NT tiles.
 // Block: S = SN*SK waves; wave w is column-wave cw = w % SN (tiles
 // cw*NT .. +NT of the group) in K group kg = w / SN (K blocks
-// KB*kg/SK .. KB*(kg+1)/SK).  The SN waves of a K group share each K block's
-// activations through an LDS buffer (double-buffered, one barrier per K
-// block); with SN = 1 each wave stages its own activations and no barrier is
-// needed.  After the K loop every wave parks its partial tile in LDS and the
-// work-group sums the SK partials of each column in K-group order.
+// KB*kg/SK .. KB*(kg+1)/SK).  Each wave streams its units through a ring of
+// D+1 register slots with D units in flight.  The SN waves of a K group share
+// staged activation chunks (see XChunk).  After the K loop every wave parks
+// its partial tile in LDS and the work-group sums the SK partials of each
+// column in K-group order.
 // ======================================================================
-template <int SN>
-constexpr int x_buffers() { return SN > 1 ? 2 : 1; }
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 
-template <class Pol, int D, int SN, bool F16_OUT>
-__global__ void __launch_bounds__(64 * max_split(Pol::KIND, Pol::NTILES, SN))
+template <class Pol, int D, int XPL, bool F16_OUT>
+__global__ void __launch_bounds__(64 * kMaxSplit)
 gemm_kernel(GemmArgs a)
 {
     constexpr int NT = Pol::NTILES;
     constexpr int TW = NT * 16;                       // columns of one wave
-    constexpr int XB = x_buffers<SN>();
+    constexpr int R = D + 1;                          // ring slots
+    constexpr int CH = kChunkBlocks;
+    // steps per unrolled body: whole ring turns and an even number of chunks,
+    // so ring slots and chunk buffers are compile-time in the body
+    constexpr int L = Pol::STAGED ? lcm_c(R, 2 * CH) : R;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int S = blockDim.x >> 6;
+    const int SN = a.sn;
     const int SK = S / SN;
     const int cw = wave % SN, kg = wave / SN;
     const int kb0 = (a.KB * kg) / SK, kb1 = (a.KB * (kg + 1)) / SK;
     const int len = kb1 - kb0;
     const int steps = (a.KB + SK - 1) / SK;           // the longest K range; every wave runs it
-    uint8_t* xbuf = lds + (SN > 1 ? kg : wave) * XB * kXStageBytes;
     const int tile0 = (blockIdx.x * SN + cw) * NT;
 
-    Pol pol(a, lane, tile0, cw * (4 / SN));
+    Pol pol(a, lane, tile0);
     {
-        typename Pol::Unit r[D + 1];
+        typename Pol::Unit r[R];
+        if constexpr (Pol::STAGED) {
+            uint8_t* xb = lds + kg * 2 * kXChunkBytes;   // this K group's two chunk buffers
+            XChunk<XPL> xc;
+            xc.init(a, lane, cw, SN);
+            xc.load(kb0, kb1);
 #pragma unroll
-        for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len);
-        pol.stage(xbuf, r[0]);
-        for (int i = 0; i < steps; i += D + 1) {
+            for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len);
+            xc.stage(xb);
+            xc.load(kb0 + CH, kb1);
+            if (SN > 1) __syncthreads();
+            for (int i = 0; i < steps; i += L) {
 #pragma unroll
-            for (int j = 0; j <= D; ++j) {
-                const int step = i + j;
-                pol.load(r[(j + D) % (D + 1)], kb0 + step + D, step + D < len);
-                if (SN > 1) __syncthreads();
-                uint8_t* cur = xbuf + (step & (XB - 1)) * kXStageBytes;
-                if (step < len) {
-                    if constexpr (Pol::KIND == KIND_GEMV_FP8) pol.compute(r[j], kb0 + step);
-                    else pol.compute(r[j], cur);
+                for (int j = 0; j < L; ++j) {
+                    const int step = i + j;
+                    const int par = (j / CH) & 1;         // buffer of the current chunk
+                    pol.load(r[(j + D) % R], kb0 + step + D, step + D < len);
+                    // past the K range the slot holds zero weights and a zero
+                    // scale and the chunk zero activations: the update adds +0
+                    pol.compute(r[j % R], xb + par * kXChunkBytes + (j % CH) * kXBlockBytes);
+                    if ((j + 1) % CH == 0) {
+                        xc.stage(xb + (par ^ 1) * kXChunkBytes);
+                        xc.load(kb0 + step + 1 + CH, kb1);
+                        if (SN > 1) __syncthreads();
+                        if (step + 1 >= steps) break;     // uniform: every wave leaves here
+                    }
                 }
-                pol.stage(xbuf + ((step + 1) & (XB - 1)) * kXStageBytes, r[(j + 1) % (D + 1)]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len);
+            for (int i = 0; i < steps; i += R) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int step = i + j;
+                    pol.load(r[(j + D) % R], kb0 + step + D, step + D < len);
+                    if (step < len) pol.compute(r[j], kb0 + step);
+                }
             }
         }
     }
@@ -427,10 +446,10 @@ gemm_kernel(GemmArgs a)
     }
 }
 
-template <class Pol, int SN>
-constexpr int gemm_lds_bytes(int split)
+template <class Pol>
+int gemm_lds_bytes(int split, int sn)
 {
-    const int stage = (SN > 1 ? split / SN : split) * x_buffers<SN>() * kXStageBytes;
+    const int stage = Pol::STAGED ? (split / sn) * 2 * kXChunkBytes : 0;
     const int parts = split * 16 * Pol::NTILES * 16 * 4;
     return stage > parts ? stage : parts;
 }
@@ -450,6 +469,18 @@ __device__ __forceinline__ uint4 gather16(const uint8_t* src)
     return make_uint4(d[0], d[1], d[2], d[3]);
 }
 
+// the 8 codes of (row n, MFMA step s, lane group g) start at k = 128kb + 32s + 8g
+__device__ __forceinline__ uint2 gather8(const uint8_t* src)
+{
+    if ((reinterpret_cast<uintptr_t>(src) & 7) == 0) return *reinterpret_cast<const uint2*>(src);
+    uint32_t d[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        d[i] = (uint32_t)src[4 * i] | ((uint32_t)src[4 * i + 1] << 8) | ((uint32_t)src[4 * i + 2] << 16) |
+               ((uint32_t)src[4 * i + 3] << 24);
+    return make_uint2(d[0], d[1]);
+}
+
 __global__ void pack_fp8_kernel(const uint8_t* __restrict__ w, int64_t ldw, const float* __restrict__ scales,
                                 int64_t N, int64_t K, uint8_t* __restrict__ packed)
 {
@@ -460,8 +491,9 @@ __global__ void pack_fp8_kernel(const uint8_t* __restrict__ w, int64_t ldw, cons
         const int64_t unit = idx >> 7;
         const int64_t t = unit / KB, kb = unit - t * KB;
         const int64_t n = t * 16 + (l & 15);
-        const int64_t k0 = kb * 128 + j * 64 + (l >> 4) * 16;
-        reinterpret_cast<uint4*>(packed)[idx] = gather16(w + n * ldw + k0);
+        const uint8_t* row = w + n * ldw + kb * 128 + (l >> 4) * 8;
+        const uint2 a = gather8(row + 64 * j), b = gather8(row + 64 * j + 32);
+        reinterpret_cast<uint4*>(packed)[idx] = make_uint4(a.x, a.y, b.x, b.y);
     }
     if (idx < (N / 128) * KB) reinterpret_cast<float*>(packed + N * K)[idx] = scales[idx];
 }
@@ -480,7 +512,7 @@ __global__ void pack_lut3_kernel(const uint8_t* __restrict__ codes, int64_t ldc,
         const int64_t unit = idx >> 6;
         const int64_t t = unit / KB, kb = unit - t * KB;
         const int64_t n = t * 16 + (l & 15);
-        const uint8_t* src = codes + n * ldc + kb * 128 + (l >> 4) * 32;
+        const uint8_t* src = codes + n * ldc + kb * 128 + (l >> 4) * 8;
         uint32_t d[4];
         uint32_t bad = 0;
 #pragma unroll
@@ -488,7 +520,7 @@ __global__ void pack_lut3_kernel(const uint8_t* __restrict__ codes, int64_t ldc,
             uint32_t word = 0;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const uint32_t lo = src[8 * s + b], hi = src[8 * s + b + 4];
+                const uint32_t lo = src[32 * s + b], hi = src[32 * s + b + 4];
                 bad |= (lo | hi) & ~7u;
                 word |= ((lo & 15u) | ((hi & 15u) << 4)) << (8 * b);
             }
@@ -515,7 +547,7 @@ __global__ void unpack_fp8_kernel(const uint8_t* __restrict__ packed, int64_t N,
     const int64_t unit = idx >> 7;
     const int64_t t = unit / KB, kb = unit - t * KB;
     const int64_t n = t * 16 + (l & 15);
-    const int64_t k0 = kb * 128 + j * 64 + (l >> 4) * 16;
+    const int64_t k0 = kb * 128 + 64 * j + (l >> 4) * 8;   // bytes 0..7 at k0, bytes 8..15 at k0 + 32
     const uint4 w = reinterpret_cast<const uint4*>(packed)[idx];
     if (f32_out) {
         const uint32_t d[4] = {w.x, w.y, w.z, w.w};
@@ -524,16 +556,17 @@ __global__ void unpack_fp8_kernel(const uint8_t* __restrict__ packed, int64_t N,
         for (int i = 0; i < 4; ++i) {
             const f32x2_t lo = e4m3x2_to_f32x2<false>(d[i]);
             const f32x2_t hi = e4m3x2_to_f32x2<true>(d[i]);
-            o[4 * i + 0] = lo[0];
-            o[4 * i + 1] = lo[1];
-            o[4 * i + 2] = hi[0];
-            o[4 * i + 3] = hi[1];
+            float* q = o + (i >> 1) * 32 + (i & 1) * 4;
+            q[0] = lo[0];
+            q[1] = lo[1];
+            q[2] = hi[0];
+            q[3] = hi[1];
         }
     } else {
         uint16_t* o = reinterpret_cast<uint16_t*>(out) + n * K + k0;
         const bf16x8_t a = e4m3x8_to_bf16x8(w.x, w.y), b = e4m3x8_to_bf16x8(w.z, w.w);
         *reinterpret_cast<uint4*>(o) = __builtin_bit_cast(uint4, a);
-        *reinterpret_cast<uint4*>(o + 8) = __builtin_bit_cast(uint4, b);
+        *reinterpret_cast<uint4*>(o + 32) = __builtin_bit_cast(uint4, b);
     }
 }
 
@@ -553,21 +586,21 @@ __global__ void unpack_lut3_kernel(const uint8_t* __restrict__ packed, int64_t N
     const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, sc[unit * 16 + (l & 15)]));
     const uint4 w = reinterpret_cast<const uint4*>(packed)[idx];
     const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-    uint16_t* o = out + n * K + kb * 128 + (l >> 4) * 32;
+    uint16_t* o = out + n * K + kb * 128 + (l >> 4) * 8;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        *reinterpret_cast<uint4*>(o + 8 * s) = __builtin_bit_cast(uint4, lut_decode8(d[s], pl));
+        *reinterpret_cast<uint4*>(o + 32 * s) = __builtin_bit_cast(uint4, lut_decode8(d[s], pl));
 }
 
 // ======================================================================
 // Launchers
 // ======================================================================
 
-template <class Pol, int D, int SN, bool F16>
+template <class Pol, int D, int XPL, bool F16>
 static hipError_t launch_one(const GemmArgs& a, int split, hipStream_t s)
 {
-    auto fn = gemm_kernel<Pol, D, SN, F16>;
-    const size_t lds = (size_t)gemm_lds_bytes<Pol, SN>(split);
+    auto fn = gemm_kernel<Pol, D, XPL, F16>;
+    const size_t lds = (size_t)gemm_lds_bytes<Pol>(split, a.sn);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -577,29 +610,32 @@ static hipError_t launch_one(const GemmArgs& a, int split, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int NT, int SN>
+template <int NT, int XPL>
 static hipError_t launch_mfma(int kind, const GemmArgs& a, int split, hipStream_t s)
 {
-    if (kind == KIND_MFMA_FP8) return launch_one<MfmaFp8<NT, SN>, kDepthMfmaFp8, SN, false>(a, split, s);
-    return launch_one<MfmaLut<NT, SN>, kDepthMfmaLut, SN, true>(a, split, s);
+    if (kind == KIND_MFMA_FP8) return launch_one<MfmaFp8<NT>, kDepthMfmaFp8, XPL, false>(a, split, s);
+    return launch_one<MfmaLut<NT>, kDepthMfmaLut, XPL, true>(a, split, s);
 }
 
 template <int NT>
-static hipError_t launch_nt(int kind, int sn, const GemmArgs& a, int split, hipStream_t s)
+static hipError_t launch_nt(int kind, const GemmArgs& a, int split, hipStream_t s)
 {
-    switch (sn) {
-    case 1: return launch_mfma<NT, 1>(kind, a, split, s);
-    case 2: return launch_mfma<NT, 2>(kind, a, split, s);
+    switch (x_pieces_per_lane(a.sn)) {
+    case 16: return launch_mfma<NT, 16>(kind, a, split, s);
+    case 8: return launch_mfma<NT, 8>(kind, a, split, s);
+    case 6: return launch_mfma<NT, 6>(kind, a, split, s);
     case 4: return launch_mfma<NT, 4>(kind, a, split, s);
+    case 3: return launch_mfma<NT, 3>(kind, a, split, s);
+    case 2: return launch_mfma<NT, 2>(kind, a, split, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemm(int kind, int nt, int sn, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream)
+hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream)
 {
-    if (split < 1 || split > max_split(kind, nt, sn) || split % sn) return hipErrorInvalidValue;
+    if (!split_ok(kind, nt, a.sn, split)) return hipErrorInvalidValue;
     if (kind == KIND_GEMV_FP8) {
-        if (nt != 4 || sn != 1) return hipErrorInvalidValue;
+        if (nt != 4 || a.sn != 1) return hipErrorInvalidValue;
         switch (gemv_rows) {
         case 1: return launch_one<GemvFp8<1>, kDepthGemv, 1, false>(a, split, stream);
         case 2: return launch_one<GemvFp8<2>, kDepthGemv, 1, false>(a, split, stream);
@@ -610,9 +646,8 @@ hipError_t launch_gemm(int kind, int nt, int sn, int gemv_rows, const GemmArgs& 
     }
     if (kind != KIND_MFMA_FP8 && kind != KIND_MFMA_LUT) return hipErrorInvalidValue;
     switch (nt) {
-    case 1: return launch_nt<1>(kind, sn, a, split, stream);
-    case 2: return launch_nt<2>(kind, sn, a, split, stream);
-    case 4: return launch_nt<4>(kind, sn, a, split, stream);
+    case 1: return launch_nt<1>(kind, a, split, stream);
+    case 2: return launch_nt<2>(kind, a, split, stream);
     default: return hipErrorInvalidValue;
     }
 }
