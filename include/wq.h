@@ -142,9 +142,10 @@ wq_status wq_gemm_fp8_block_path(const void* packed, int64_t N, int64_t K,
 
 /* ----------------------------------------------------------------- LUT3 */
 
-/* Bytes of the packed LUT matrix: N*K/2 nibble bytes + 2*N*(K/128) scale
- * bytes + 32 bytes (map and pack status).  Returns 0 for an unsupported
- * shape (N not a positive multiple of 16 or K not of 128). */
+/* Bytes of the packed LUT matrix: N*K/2 nibble bytes + 16*N*ceil(K/1024)
+ * scale bytes (K blocks padded to a multiple of 8) + 32 bytes (map and pack
+ * status).  Returns 0 for an unsupported shape (N not a positive multiple of
+ * 16 or K not of 128). */
 size_t wq_lut3_packed_bytes(int64_t N, int64_t K);
 
 /* Pack a 3-bit LUT weight matrix.

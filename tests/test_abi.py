@@ -57,7 +57,7 @@ def test_sizes_are_host_arithmetic():
     assert wq.wq_fp8_block_packed_bytes(100, 128) == 0      # N not a multiple of 128
     assert wq.wq_fp8_block_packed_bytes(128, 100) == 0
     assert wq.wq_lut3_packed_bytes(24, 128) == 0           # N not a multiple of 16
-    assert wq.wq_lut3_packed_bytes(48, 256) == 48 * 128 + 2 * 48 * 2 + 32
+    assert wq.wq_lut3_packed_bytes(48, 256) == 48 * 128 + 3 * 256 + 32   # K blocks padded to 8
 
 
 L = wq.lib

@@ -209,6 +209,10 @@ bool shape_ok(int fmt, int64_t N, int64_t K)
     return false;
 }
 
+// Group scales of the packed LUT matrix: per tile and run of 8 K blocks, 16
+// rows x 8 FP16 (256 bytes); K block counts are padded to a multiple of 8.
+size_t lut3_scale_bytes(int64_t N, int64_t K) { return (size_t)(N / 16) * (size_t)((K / 128 + 7) / 8) * 256; }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Shared front end of the two GEMMs.
@@ -257,7 +261,7 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
         a.qmap = nullptr;
     } else {
         a.scales = base + N * K / 2;
-        a.qmap = reinterpret_cast<const uint16_t*>(base + N * K / 2 + 2 * N * (K / 128));
+        a.qmap = reinterpret_cast<const uint16_t*>(base + N * K / 2 + lut3_scale_bytes(N, K));
     }
     a.N = (int)N;
     a.KB = p.KB;
@@ -327,7 +331,7 @@ size_t wq_fp8_block_packed_bytes(int64_t N, int64_t K)
 size_t wq_lut3_packed_bytes(int64_t N, int64_t K)
 {
     if (!shape_ok(WQ_FMT_LUT3, N, K)) return 0;
-    return (size_t)(N * K / 2) + 2 * (size_t)N * (size_t)(K / 128) + 32;
+    return (size_t)(N * K / 2) + lut3_scale_bytes(N, K) + 32;
 }
 
 wq_status wq_pack_fp8_block(const uint8_t* w_e4m3, int64_t ldw, const float* scales, int64_t N, int64_t K,
@@ -373,7 +377,7 @@ wq_status wq_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* qmap, 
     if (st != WQ_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     uint8_t* pk = static_cast<uint8_t*>(packed);
-    uint32_t* status = reinterpret_cast<uint32_t*>(pk + N * K / 2 + 2 * N * (K / 128) + 16);
+    uint32_t* status = reinterpret_cast<uint32_t*>(pk + N * K / 2 + lut3_scale_bytes(N, K) + 16);
     if (wq::launch_pack_lut3(codes, ldc, qmap, scales, N, K, pk, status, s) != hipSuccess) return WQ_ERR_HIP;
     uint32_t host_status = 0;
     if (hipMemcpyAsync(&host_status, status, sizeof(host_status), hipMemcpyDeviceToHost, s) != hipSuccess)

@@ -17,8 +17,10 @@
 //   LUT3  unit = 1024 B.  Lane l holds 32 codes of row 16t + l%16 in 4 dwords
 //         s: byte b carries k = 128kb + 32s + 8(l/16) + e with e = b in its low
 //         nibble and e = b + 4 in its high nibble.  Group scales follow as FP16
-//         [tile][kb][16 rows], then the 8 map entries (FP16), then a 16-byte
-//         pack-status word.
+//         [tile][kb / 8][16 rows][kb % 8] (K blocks padded to a multiple of 8
+//         with zeros), so one 16-byte load brings a row's scales for 8 K
+//         blocks; then the 8 map entries (FP16), then a 16-byte pack-status
+//         word.
 //
 // GEMM schedule.  One work-group owns one column group (NT tiles of 16 output
 // columns) over the whole of K.  Its S waves split the K blocks into S
@@ -118,6 +120,7 @@ struct MfmaFp8 {
     static constexpr int KIND = KIND_MFMA_FP8;
     static constexpr int NTILES = NT;
     static constexpr bool STAGED = true;
+    static constexpr int KALIGN = 1;      // K-group ranges start at any K block
     struct Unit {
         uint4 w[NT][2];
         float s;
@@ -141,7 +144,7 @@ struct MfmaFp8 {
         for (int t = 0; t < NT; ++t) outer[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    __device__ __forceinline__ void load(Unit& r, int kb, bool valid) const
+    __device__ __forceinline__ void load(Unit& r, int kb, bool valid, int) const
     {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -154,7 +157,7 @@ struct MfmaFp8 {
         r.s = load_uniform_f32((valid && ntiles > 0) ? (const void*)(srow + kb) : (const void*)g_zero_page);
     }
 
-    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk)
+    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk, int)
     {
         bf16x8_t b[4];
 #pragma unroll
@@ -190,58 +193,77 @@ struct MfmaFp8 {
 };
 
 // ---- 3-bit LUT weights, 16-row FP16 MFMA tile -------------------------------
+// Group scales come as one 16-byte load per row and run of 8 K blocks, issued
+// with the weights of the run's first unit; K-group ranges start at multiples
+// of 8 blocks, so a unit's place in its run is its (compile-time) position in
+// the unrolled loop.
 template <int NT>
 struct MfmaLut {
     static constexpr int KIND = KIND_MFMA_LUT;
     static constexpr int NTILES = NT;
     static constexpr bool STAGED = true;
+    static constexpr int KALIGN = 8;      // K blocks per group-scale load
     struct Unit {
         uint4 w[NT];
-        uint32_t g[NT];      // FP16 group-scale bits, zero-extended
+        uint4 gv[NT];        // FP16 group scales of 8 K blocks (loaded by a run's first unit only)
     };
     int lane;
     int KB;
+    int KB8;
     int ntiles;
     buf_t rw;                // code units of the wave's tiles (zero bytes past N)
     buf_t rg;                // group scales of the wave's tiles
     buf_t rnull;             // zero bytes: loads return zeros
     uint32_t q[4];           // map entries as FP16 pairs
+    uint4 gcur[NT];          // group scales of the current run
     f32x4_t acc[NT];
 
-    __device__ MfmaLut(const GemmArgs& a, int l, int tile0) : lane(l), KB(a.KB)
+    __device__ MfmaLut(const GemmArgs& a, int l, int tile0) : lane(l), KB(a.KB), KB8((a.KB + 7) / 8)
     {
         ntiles = max(0, min(NT, a.n_tiles - tile0));
-        const int64_t unit0 = (int64_t)min(tile0, a.n_tiles) * a.KB;
-        rw = make_buf(a.codes + (unit0 << 10), (uint32_t)(ntiles * a.KB) << 10);
-        rg = make_buf(reinterpret_cast<const uint8_t*>(a.scales) + unit0 * 32, (uint32_t)(ntiles * a.KB) * 32u);
+        const int t0 = min(tile0, a.n_tiles);
+        rw = make_buf(a.codes + (((int64_t)t0 * a.KB) << 10), (uint32_t)(ntiles * a.KB) << 10);
+        rg = make_buf(reinterpret_cast<const uint8_t*>(a.scales) + (int64_t)t0 * KB8 * 256,
+                      (uint32_t)(ntiles * KB8) * 256u);
         rnull = make_buf(a.codes, 0);
         const uint32_t* qm = reinterpret_cast<const uint32_t*>(a.qmap);
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = qm[i];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; ++t) {
+            acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            gcur[t] = make_uint4(0, 0, 0, 0);
+        }
     }
 
-    __device__ __forceinline__ void load(Unit& r, int kb, bool valid) const
+    // pos: the unit's position in the unrolled loop, == kb (mod 8)
+    __device__ __forceinline__ void load(Unit& r, int kb, bool valid, int pos) const
     {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const bool ok = valid && t < ntiles;
-            const uint32_t u = (uint32_t)(t * KB + kb);
-            r.w[t] = buf_load_stream16(ok ? rw : rnull, lane * 16, u << 10);
-            r.g[t] = buf_load_u16(ok ? rg : rnull, (lane & 15) * 2, u * 32);
+            r.w[t] = buf_load_stream16(ok ? rw : rnull, lane * 16, (uint32_t)(t * KB + kb) << 10);
+            if ((pos & 7) == 0)
+                r.gv[t] = buf_load16(ok ? rg : rnull, (lane & 15) * 16, (uint32_t)(t * KB8 + (kb >> 3)) * 256u);
         }
     }
 
-    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk)
+    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk, int pos)
     {
+        const int e = pos & 7;
+        if (e == 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) gcur[t] = r.gv[t];
+        }
         f16x8_t b[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s)   // MFMA step s: lane group g holds k = 32s + 8g + e
             b[s] = __builtin_bit_cast(f16x8_t, x_frag(xblk, lane, s * 32 + (lane >> 4) * 8));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, (uint16_t)r.g[t]));
+            const uint32_t gd = e < 2 ? gcur[t].x : e < 4 ? gcur[t].y : e < 6 ? gcur[t].z : gcur[t].w;
+            const uint16_t gbits = (uint16_t)((e & 1) ? gd >> 16 : gd & 0xFFFFu);
+            const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, gbits));
             const uint32_t wd[4] = {r.w[t].x, r.w[t].y, r.w[t].z, r.w[t].w};
 #pragma unroll
             for (int s = 0; s < 4; ++s) acc[t] = mfma_f16(lut_decode8(wd[s], pl), b[s], acc[t]);
@@ -274,6 +296,7 @@ struct GemvFp8 {
     static constexpr int NTILES = 4;
     static constexpr int CGW = 64;
     static constexpr bool STAGED = false;
+    static constexpr int KALIGN = 1;
     struct Unit {
         uint4 w[2][4];       // [chunk j][lane group g]
         float s;
@@ -297,7 +320,7 @@ struct GemvFp8 {
         for (int m = 0; m < MR; ++m) outer[m] = 0.f;
     }
 
-    __device__ __forceinline__ void load(Unit& r, int kb, bool valid) const
+    __device__ __forceinline__ void load(Unit& r, int kb, bool valid, int) const
     {
         const bool ok = valid && tile_ok;
         const uint8_t* p = ok ? wbase + ((int64_t)kb << 11) : g_zero_page + (lane & 15) * 16;
@@ -371,6 +394,7 @@ gemm_kernel(GemmArgs a)
     // steps per unrolled body: whole ring turns and an even number of chunks,
     // so ring slots and chunk buffers are compile-time in the body
     constexpr int L = Pol::STAGED ? lcm_c(R, 2 * CH) : R;
+    static_assert(L % Pol::KALIGN == 0, "a unit's place in its scale run must be its loop position");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -380,9 +404,12 @@ gemm_kernel(GemmArgs a)
     const int SN = a.sn;
     const int SK = S / SN;
     const int cw = wave % SN, kg = wave / SN;
-    const int kb0 = (a.KB * kg) / SK, kb1 = (a.KB * (kg + 1)) / SK;
+    // K group kg covers K blocks [kb0, kb1); ranges start at multiples of KALIGN
+    constexpr int KA = Pol::KALIGN;
+    const int KBA = (a.KB + KA - 1) / KA;
+    const int kb0 = KA * ((KBA * kg) / SK), kb1 = min(a.KB, KA * ((KBA * (kg + 1)) / SK));
     const int len = kb1 - kb0;
-    const int steps = (a.KB + SK - 1) / SK;           // the longest K range; every wave runs it
+    const int steps = KA * ((KBA + SK - 1) / SK);      // the longest K range; every wave runs it
     const int tile0 = (blockIdx.x * SN + cw) * NT;
 
     Pol pol(a, lane, tile0);
@@ -394,7 +421,7 @@ gemm_kernel(GemmArgs a)
             xc.init(a, lane, cw, SN);
             xc.load(kb0, kb1);
 #pragma unroll
-            for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len);
+            for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len, i);
             xc.stage(xb);
             xc.load(kb0 + CH, kb1);
             if (SN > 1) __syncthreads();
@@ -403,10 +430,10 @@ gemm_kernel(GemmArgs a)
                 for (int j = 0; j < L; ++j) {
                     const int step = i + j;
                     const int par = (j / CH) & 1;         // buffer of the current chunk
-                    pol.load(r[(j + D) % R], kb0 + step + D, step + D < len);
+                    pol.load(r[(j + D) % R], kb0 + step + D, step + D < len, j + D);
                     // past the K range the slot holds zero weights and a zero
                     // scale and the chunk zero activations: the update adds +0
-                    pol.compute(r[j % R], xb + par * kXChunkBytes + (j % CH) * kXBlockBytes);
+                    pol.compute(r[j % R], xb + par * kXChunkBytes + (j % CH) * kXBlockBytes, j);
                     if ((j + 1) % CH == 0) {
                         xc.stage(xb + (par ^ 1) * kXChunkBytes);
                         xc.load(kb0 + step + 1 + CH, kb1);
@@ -417,12 +444,12 @@ gemm_kernel(GemmArgs a)
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len);
+            for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len, i);
             for (int i = 0; i < steps; i += R) {
 #pragma unroll
                 for (int j = 0; j < R; ++j) {
                     const int step = i + j;
-                    pol.load(r[(j + D) % R], kb0 + step + D, step + D < len);
+                    pol.load(r[(j + D) % R], kb0 + step + D, step + D < len, j + D);
                     if (step < len) pol.compute(r[j], kb0 + step);
                 }
             }
@@ -530,12 +557,13 @@ __global__ void pack_lut3_kernel(const uint8_t* __restrict__ codes, int64_t ldc,
         if (bad) atomicOr(status, 1u);
     }
     uint16_t* sc_out = reinterpret_cast<uint16_t*>(packed + N * K / 2);
-    if (idx < n_tiles * KB * 16) {
-        const int64_t r = idx & 15, unit = idx >> 4;
-        const int64_t t = unit / KB, kb = unit - t * KB;
-        sc_out[idx] = scales[(t * 16 + r) * KB + kb];
+    const int64_t KB8 = (KB + 7) / 8;
+    if (idx < n_tiles * KB8 * 128) {
+        const int64_t e = idx & 7, r = (idx >> 3) & 15, grp = idx >> 7;
+        const int64_t t = grp / KB8, kb = (grp - t * KB8) * 8 + e;
+        sc_out[idx] = kb < KB ? scales[(t * 16 + r) * KB + kb] : (uint16_t)0;
     }
-    if (idx < 8) sc_out[n_tiles * KB * 16 + idx] = qmap[idx];
+    if (idx < 8) sc_out[n_tiles * KB8 * 128 + idx] = qmap[idx];
 }
 
 __global__ void unpack_fp8_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K, void* out, int f32_out)
@@ -580,10 +608,12 @@ __global__ void unpack_lut3_kernel(const uint8_t* __restrict__ packed, int64_t N
     const int64_t unit = idx >> 6;
     const int64_t t = unit / KB, kb = unit - t * KB;
     const int64_t n = t * 16 + (l & 15);
+    const int64_t KB8 = (KB + 7) / 8;
     const uint16_t* sc = reinterpret_cast<const uint16_t*>(packed + N * K / 2);
-    const uint32_t* qm = reinterpret_cast<const uint32_t*>(sc + n_tiles * KB * 16);
+    const uint32_t* qm = reinterpret_cast<const uint32_t*>(sc + n_tiles * KB8 * 128);
     const uint32_t q[4] = {qm[0], qm[1], qm[2], qm[3]};
-    const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, sc[unit * 16 + (l & 15)]));
+    const uint16_t g = sc[((t * KB8 + kb / 8) * 16 + (l & 15)) * 8 + kb % 8];
+    const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, g));
     const uint4 w = reinterpret_cast<const uint4*>(packed)[idx];
     const uint32_t d[4] = {w.x, w.y, w.z, w.w};
     uint16_t* o = out + n * K + kb * 128 + (l >> 4) * 8;
@@ -668,7 +698,8 @@ hipError_t launch_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* q
     hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(4), 0, stream, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n = N * K / 32 > N * (K / 128) ? N * K / 32 : N * (K / 128);
+    const int64_t n_scales = (N / 16) * ((K / 128 + 7) / 8) * 128;
+    const int64_t n = N * K / 32 > n_scales ? N * K / 32 : n_scales;
     hipLaunchKernelGGL(pack_lut3_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, codes, ldc, qmap, scales, N, K,
                        packed, status);
     return hipGetLastError();
