@@ -123,7 +123,7 @@ constexpr TableEntry kTable[] = {
     {wq::KIND_MFMA_FP8, 6144, 5120, 1, 2, 4},     // attention Q
     {wq::KIND_MFMA_FP8, 1024, 5120, 1, 1, 4},     // attention K, V
     {wq::KIND_MFMA_FP8, 5120, 6144, 1, 2, 8},     // attention output
-    {wq::KIND_MFMA_LUT, 28672, 8192, 1, 4, 4},    // 3-bit LUT 28672x8192
+    {wq::KIND_MFMA_LUT, 28672, 8192, 1, 8, 8},    // 3-bit LUT 28672x8192
 };
 
 Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)

@@ -183,6 +183,8 @@ struct MfmaFp8 {
             for (int v = 0; v < 4; ++v) outer[t][v] = __builtin_fmaf(r.s, blk[t][v], outer[t][v]);
     }
 
+    __device__ __forceinline__ f32x4_t result(int t) const { return outer[t]; }
+
     // slot: [16 rows][NT*16] FP32 partial tile of this wave
     __device__ __forceinline__ void store_partial(float* slot) const
     {
@@ -269,6 +271,8 @@ struct MfmaLut {
             for (int s = 0; s < 4; ++s) acc[t] = mfma_f16(lut_decode8(wd[s], pl), b[s], acc[t]);
         }
     }
+
+    __device__ __forceinline__ f32x4_t result(int t) const { return acc[t]; }
 
     __device__ __forceinline__ void store_partial(float* slot) const
     {
@@ -453,6 +457,25 @@ gemm_kernel(GemmArgs a)
                     if (step < len) pol.compute(r[j], kb0 + step);
                 }
             }
+        }
+    }
+    if constexpr (Pol::STAGED) {
+        if (SK == 1) {
+            // no K split: each wave rounds and stores its own tiles (lane l
+            // holds rows n = 4(l/16) .. +3 of batch row m = l % 16)
+            const int m = lane & 15;
+            if (m < a.rows) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    if (t < pol.ntiles) {
+                        const f32x4_t v = pol.result(t);
+                        uint16_t* yp = a.y + (int64_t)m * a.ldy + (tile0 + t) * 16 + (lane >> 4) * 4;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) yp[i] = F16_OUT ? f32_to_f16_rne(v[i]) : f32_to_bf16_rne(v[i]);
+                    }
+                }
+            }
+            return;
         }
     }
     __syncthreads();   // every wave is done with the staging buffers
