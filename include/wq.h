@@ -43,7 +43,7 @@
  *   WQ_FORCE_PATH   = auto | gemv | mfma  path for wq_gemm_fp8_block (default auto)
  *   WQ_NT           = 1 | 2               16-column MFMA tiles per wave
  *   WQ_SN           = 1 .. 8              column-waves sharing staged activations
- *   WQ_SPLIT        = 1 .. 8              waves per work-group (SN x K-groups)
+ *   WQ_SPLIT        = 1 .. 16             waves per work-group (SN x K-groups)
  *   WQ_WAVES_PER_CU = 1 .. 32             resident waves per CU the plan aims for (4)
  */
 #ifndef WQ_H_
@@ -88,9 +88,11 @@ int wq_packed_format_version(void);
 
 /* Tuning and test hook: override the per-shape plan of later calls.  nt =
  * 16-column tiles per wave (1, 2), sn = column-waves sharing activations
- * (1..8), split = waves per work-group (1..8, rounded down to a multiple of
- * sn; at most 4 K groups), waves_per_cu = the resident-wave target of the
- * automatic plan; 0 selects the automatic choice for each.  Replaces the
+ * (1..8), split = waves per work-group (1..16, rounded down to a multiple of
+ * sn and clamped to the kernel's limits: at most 4 K groups, and at most 8
+ * waves except for one-tile LUT work-groups with sn >= 4), waves_per_cu = the
+ * resident-wave target of the automatic plan; 0 selects the automatic choice
+ * for each.  Replaces the
  * WQ_NT / WQ_SN / WQ_SPLIT / WQ_WAVES_PER_CU environment values.  The FP8
  * GEMV path ignores nt and sn.  Results stay within the documented tolerance
  * for every setting, but bit patterns may differ between settings.  Not meant

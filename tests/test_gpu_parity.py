@@ -257,9 +257,11 @@ def test_zero_rows_and_zero_matrix():
 # ------------------------------------------------------ every kernel variant
 
 # (nt, sn, split): every activation-piece count per lane the kernels are built
-# for (sn = 1, 2, 3, 4/5, 6/7, 8), one to four K groups, 1- and 2-tile waves
+# for (sn = 1, 2, 3, 4/5, 6/7, 8), one to four K groups, 1- and 2-tile waves,
+# and the 16-wave work-groups of the one-tile LUT kernels (FP8 clamps to 8)
 TUNINGS = [(1, 1, 1), (1, 1, 4), (2, 1, 3), (1, 2, 4), (2, 2, 8), (1, 3, 6), (2, 3, 6), (1, 4, 4),
-           (1, 4, 8), (2, 4, 8), (1, 5, 5), (1, 6, 6), (1, 7, 7), (2, 7, 7), (1, 8, 8), (2, 8, 8)]
+           (1, 4, 8), (2, 4, 8), (1, 5, 5), (1, 6, 6), (1, 7, 7), (2, 7, 7), (1, 8, 8), (2, 8, 8),
+           (1, 4, 16), (1, 7, 14)]
 
 
 @pytest.fixture

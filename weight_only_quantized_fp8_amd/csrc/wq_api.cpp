@@ -49,7 +49,7 @@ const Options& options()
         }
         if (const char* p = std::getenv("WQ_SPLIT")) {
             int v = std::atoi(p);
-            if (v >= 1 && v <= 8) o.split = v;
+            if (v >= 1 && v <= 16) o.split = v;
         }
         if (const char* p = std::getenv("WQ_WAVES_PER_CU")) {
             int v = std::atoi(p);
@@ -118,12 +118,12 @@ struct TableEntry {
     int nt, sn, split;
 };
 constexpr TableEntry kTable[] = {
-    {wq::KIND_MFMA_FP8, 17408, 5120, 1, 6, 6},    // FFN gate/up
+    {wq::KIND_MFMA_FP8, 17408, 5120, 1, 5, 5},    // FFN gate/up
     {wq::KIND_MFMA_FP8, 5120, 17408, 1, 2, 8},    // FFN down
     {wq::KIND_MFMA_FP8, 6144, 5120, 1, 2, 4},     // attention Q
     {wq::KIND_MFMA_FP8, 1024, 5120, 1, 1, 4},     // attention K, V
     {wq::KIND_MFMA_FP8, 5120, 6144, 1, 2, 8},     // attention output
-    {wq::KIND_MFMA_LUT, 28672, 8192, 1, 8, 8},    // 3-bit LUT 28672x8192
+    {wq::KIND_MFMA_LUT, 28672, 8192, 1, 7, 14},   // 3-bit LUT 28672x8192
 };
 
 Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
@@ -143,7 +143,7 @@ Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
         p.sn = 1;
     } else if (o.nt || o.sn) {
         p.nt = o.nt ? o.nt : 1;
-        p.sn = o.sn ? std::min(o.sn, wq::kMaxSplit) : 1;
+        p.sn = o.sn ? std::min(o.sn, 8) : 1;
     } else if (te) {
         p.nt = te->nt;
         p.sn = te->sn;
@@ -155,7 +155,7 @@ Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
     }
     const int group = p.nt * p.sn;
     p.n_cg = (p.n_tiles + group - 1) / group;
-    int max_sk = std::min(wq::kMaxSplit / p.sn, p.KB);   // every K group gets >= 1 block
+    int max_sk = std::min(wq::max_split(kind, p.nt, p.sn) / p.sn, p.KB);   // every K group gets >= 1 block
     if (kind != wq::KIND_GEMV_FP8) max_sk = std::min(max_sk, wq::kMaxKGroups);
     int sk;
     if (o.split) sk = std::max(1, o.split / p.sn);
@@ -310,7 +310,7 @@ int wq_packed_format_version(void) { return kPackedFormatVersion; }
 wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu)
 {
     if (nt < 0 || nt > 2 || sn < 0 || sn > 8) return WQ_ERR_SHAPE;
-    if (split < 0 || split > 8 || waves_per_cu < 0 || waves_per_cu > 32) return WQ_ERR_SHAPE;
+    if (split < 0 || split > 16 || waves_per_cu < 0 || waves_per_cu > 32) return WQ_ERR_SHAPE;
     options();
     std::lock_guard<std::mutex> lk(g_plan_mu);
     g_opts.nt = nt;

@@ -34,17 +34,26 @@ constexpr int kMaxKGroups = 4;
 // share it: ceil(chunk pieces / (64 * SN)), chunk pieces = 4 * 16 rows * 16.
 constexpr int x_pieces_per_lane(int sn) { return (kChunkBlocks * 256 + 64 * sn - 1) / (64 * sn); }
 
-// Largest split (waves per work-group).  The kernels are built for work-groups
-// of at most 8 waves, which lets a wave hold up to 256 VGPRs (2 waves per
-// SIMD): the register ring, the activation pieces in flight and the
-// unrolled MFMA steps of a chunk need more than 128.
-constexpr int kMaxSplit = 8;
+// Largest split (waves per work-group).  A work-group runs on one CU, and a
+// launch bound of 64*S waves caps a wave at 512/ceil(S/4) VGPRs.  Most
+// kernels are built for work-groups of at most 8 waves, which lets a wave
+// hold up to 256 VGPRs: the register ring, the activation pieces in flight
+// and the unrolled MFMA steps of a chunk need more than 128.  One-tile LUT
+// waves with at most 4 activation pieces per lane fit in 128 and are built
+// for up to 16 waves, so a work-group can split K across more waves than it
+// has SIMDs.
+constexpr int max_split_xpl(int kind, int nt, int xpl)
+{
+    return (kind == KIND_MFMA_LUT && nt == 1 && xpl <= 4) ? 16 : 8;
+}
+constexpr int max_split(int kind, int nt, int sn) { return max_split_xpl(kind, nt, x_pieces_per_lane(sn)); }
 
 // Whether (nt, sn, split) is a launchable tiling for this kernel kind.
 constexpr bool split_ok(int kind, int nt, int sn, int split)
 {
-    if (sn < 1 || split < 1 || split % sn || split > kMaxSplit) return false;
+    if (sn < 1 || split < 1 || split % sn || split > max_split(kind, nt, sn)) return false;
     if (kind == KIND_GEMV_FP8) return nt == 4 && sn == 1;
+    if (sn > 8) return false;                 // activation pieces per lane >= 2
     return (nt == 1 || nt == 2) && split / sn <= kMaxKGroups;
 }
 

@@ -388,7 +388,7 @@ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 
 template <class Pol, int D, int XPL, bool F16_OUT>
-__global__ void __launch_bounds__(64 * kMaxSplit)
+__global__ void __launch_bounds__(64 * max_split_xpl(Pol::KIND, Pol::NTILES, XPL))
 gemm_kernel(GemmArgs a)
 {
     constexpr int NT = Pol::NTILES;
