@@ -72,11 +72,13 @@ typedef enum {
 typedef enum { WQ_FMT_FP8_BLOCK = 0, WQ_FMT_LUT3 = 1 } wq_format;
 
 /* Kernel path for the GEMM.  AUTO follows the batch ladder of the atlas
- * "Module m16_tc" docs (section ARM ORDER): FP8 uses the strict-K-order GEMV
- * for M <= 4 and the 16-row MFMA tile for M = 5..16; the LUT format uses the
- * MFMA tile for every M = 1..16 (one mainloop across the decode band, as in
- * the FLUTE PR's "Results").  M = 17..32 always runs the MFMA tile twice, on
- * rows 0..15 and 16..M-1 ("ARM ORDER": two contiguous row halves). */
+ * "Module m16_tc" docs (section ARM ORDER) with the crossover measured on
+ * MI355X (arc PR, "The threshold"): FP8 uses the strict-K-order GEMV for
+ * M = 1 and the 16-row MFMA tile for M = 2..16 (the GEMV serves M <= 4 when
+ * asked for explicitly); the LUT format uses the MFMA tile for every M = 1..16
+ * (one mainloop across the decode band, as in the FLUTE PR's "Results").
+ * M = 17..32 always runs the MFMA tile twice, on rows 0..15 and 16..M-1
+ * ("ARM ORDER": two contiguous row halves). */
 typedef enum { WQ_PATH_AUTO = 0, WQ_PATH_GEMV = 1, WQ_PATH_MFMA = 2 } wq_path;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -94,7 +96,7 @@ int wq_packed_format_version(void);
  * resident-wave target of the automatic plan; 0 selects the automatic choice
  * for each.  Replaces the
  * WQ_NT / WQ_SN / WQ_SPLIT / WQ_WAVES_PER_CU environment values.  The FP8
- * GEMV path ignores nt and sn.  Results stay within the documented tolerance
+ * GEMV path always runs one tile per wave (it ignores nt).  Results stay within the documented tolerance
  * for every setting, but bit patterns may differ between settings.  Not meant
  * to be called while GEMMs are being queued from other threads. */
 wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu);

@@ -285,6 +285,11 @@ def test_every_tiling_matches_oracle(nt, sn, split, tuning_reset):
             y, _ = U.run_fp8(packed, N, K, xbits, path=MFMA)
             r = U.grade_fp8(y, xbits, codes, scales, K)
             assert r.ok, "fp8 N=%d K=%d M=%d: %s" % (N, K, M, r)
+        for M in (1, 3):   # the GEMV takes the same (sn, split); it always runs one tile per wave
+            xbits = synth.x_bf16(M, K, 650 + M)
+            y, _ = U.run_fp8(packed, N, K, xbits, path=GEMV)
+            r = U.grade_fp8(y, xbits, codes, scales, K)
+            assert r.ok, "fp8 gemv N=%d K=%d M=%d: %s" % (N, K, M, r)
     for N, K in ((48, 384), (272, 1152)):
         c, q, g = synth.lut3_weights(N, K, 700 + N)
         packed = U.pack_lut3(c, q, g)

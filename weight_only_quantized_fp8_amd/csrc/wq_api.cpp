@@ -109,6 +109,14 @@ struct Plan {
     int n_tiles = 0, n_cg = 0, KB = 0;
 };
 
+// Largest M the automatic ladder sends to the FP8 GEMV.  Measured on MI355X
+// over the FFN and attention shapes: the strict-order FP32 GEMV is faster
+// than the MFMA tile at M = 1 (by 5-15%), about even at M = 2 and slower
+// from M = 3 on, where its FP32 FMAs (M per weight) outweigh the stream; the
+// MFMA tile's time does not change with M.  (The arc PR, "The threshold":
+// the crossover is a measured lever, not a constant of the method.)
+constexpr int64_t kGemvAutoMaxM = 1;
+
 // Tilings measured fastest on MI355X (256 CUs) for the decode shapes of the
 // FFN and attention projections (per-shape dispatch, as in the FLUTE PR's
 // "data-driven per-shape dispatch"); other shapes use the rule below.
@@ -124,6 +132,8 @@ constexpr TableEntry kTable[] = {
     {wq::KIND_MFMA_FP8, 1024, 5120, 1, 1, 4},     // attention K, V
     {wq::KIND_MFMA_FP8, 5120, 6144, 1, 2, 8},     // attention output
     {wq::KIND_MFMA_LUT, 28672, 8192, 1, 7, 14},   // 3-bit LUT 28672x8192
+    {wq::KIND_GEMV_FP8, 6144, 5120, 1, 2, 8},     // attention Q (other GEMV shapes: the FP8 rows)
+    {wq::KIND_GEMV_FP8, 1024, 5120, 1, 2, 8},     // attention K, V
 };
 
 Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
@@ -133,19 +143,19 @@ Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
     p.n_tiles = (int)(N / 16);
     p.KB = (int)(K / 128);
     const TableEntry* te = nullptr;
-    if (cu == 256)
+    if (cu == 256) {
         for (const TableEntry& e : kTable)
             if (e.kind == kind && e.N == N && e.K == K) te = &e;
-    if (kind == wq::KIND_GEMV_FP8) {
-        // the GEMV covers 4 tiles per wave (one column per lane) and stages no
-        // activations; its plan must not depend on M (batch invariance)
-        p.nt = 4;
-        p.sn = 1;
-    } else if (o.nt || o.sn) {
-        p.nt = o.nt ? o.nt : 1;
+        // the GEMV streams the same one-tile units as the FP8 MFMA tile
+        if (!te && kind == wq::KIND_GEMV_FP8)
+            for (const TableEntry& e : kTable)
+                if (e.kind == wq::KIND_MFMA_FP8 && e.N == N && e.K == K) te = &e;
+    }
+    if (o.nt || o.sn) {
+        p.nt = kind == wq::KIND_GEMV_FP8 ? 1 : (o.nt ? o.nt : 1);
         p.sn = o.sn ? std::min(o.sn, 8) : 1;
     } else if (te) {
-        p.nt = te->nt;
+        p.nt = kind == wq::KIND_GEMV_FP8 ? 1 : te->nt;
         p.sn = te->sn;
     } else {
         // one tile per wave; as many column-waves per work-group as leaves at
@@ -156,10 +166,10 @@ Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o)
     const int group = p.nt * p.sn;
     p.n_cg = (p.n_tiles + group - 1) / group;
     int max_sk = std::min(wq::max_split(kind, p.nt, p.sn) / p.sn, p.KB);   // every K group gets >= 1 block
-    if (kind != wq::KIND_GEMV_FP8) max_sk = std::min(max_sk, wq::kMaxKGroups);
+    max_sk = std::min(max_sk, wq::kMaxKGroups);
     int sk;
     if (o.split) sk = std::max(1, o.split / p.sn);
-    else if (te && !o.nt && !o.sn && kind != wq::KIND_GEMV_FP8) sk = te->split / te->sn;
+    else if (te && !o.nt && !o.sn) sk = te->split / te->sn;
     else {
         // aim at `waves_per_cu` resident waves per compute unit
         const double target = (double)cu * o.waves_per_cu;
@@ -239,7 +249,7 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
         kind = wq::KIND_MFMA_LUT;
     } else {
         int eff = path == WQ_PATH_AUTO ? o.force_path : path;
-        if (eff == WQ_PATH_AUTO) eff = M <= 4 ? WQ_PATH_GEMV : WQ_PATH_MFMA;
+        if (eff == WQ_PATH_AUTO) eff = M <= kGemvAutoMaxM ? WQ_PATH_GEMV : WQ_PATH_MFMA;
         if (eff == WQ_PATH_GEMV && M > 4) {
             if (path == WQ_PATH_GEMV) return WQ_ERR_PATH;
             eff = WQ_PATH_MFMA;   // a forced GEMV lever only applies where it can run

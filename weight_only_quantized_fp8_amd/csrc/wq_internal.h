@@ -13,12 +13,12 @@ namespace wq {
 // bytes of an FP8 unit and costs more VALU to decode, so its ring is deeper.
 constexpr int kDepthMfmaFp8 = 3;
 constexpr int kDepthMfmaLut = 7;
-constexpr int kDepthGemv = 2;
+constexpr int kDepthGemv = 3;
 
 enum Kind : int {
     KIND_MFMA_FP8 = 0,   // 16-row BF16 MFMA tile, FP8 block-scaled weights
     KIND_MFMA_LUT = 1,   // 16-row FP16 MFMA tile, 3-bit LUT weights
-    KIND_GEMV_FP8 = 2,   // strict-K-order FP32 GEMV, M <= 4, FP8 weights
+    KIND_GEMV_FP8 = 2,   // strict-K-order FP32 GEMV, M <= 4, FP8 weights, one tile per wave
 };
 
 // K blocks of activations staged per chunk (the K group synchronises once
@@ -31,8 +31,13 @@ constexpr int kChunkBlocks = 4;
 constexpr int kMaxKGroups = 4;
 
 // 16-byte activation pieces each lane loads per chunk when SN column-waves
-// share it: ceil(chunk pieces / (64 * SN)), chunk pieces = 4 * 16 rows * 16.
-constexpr int x_pieces_per_lane(int sn) { return (kChunkBlocks * 256 + 64 * sn - 1) / (64 * sn); }
+// share it: ceil(chunk pieces / (64 * SN)); a chunk is 4 K blocks x 16 rows x
+// 16 pieces for the MFMA tiles, 4 K blocks x 4 rows x 16 pieces for the GEMV.
+constexpr int x_pieces_per_lane(int kind, int sn)
+{
+    const int pieces = kChunkBlocks * (kind == KIND_GEMV_FP8 ? 4 : 16) * 16;
+    return (pieces + 64 * sn - 1) / (64 * sn);
+}
 
 // Largest split (waves per work-group).  A work-group runs on one CU, and a
 // launch bound of 64*S waves caps a wave at 512/ceil(S/4) VGPRs.  Most
@@ -44,17 +49,17 @@ constexpr int x_pieces_per_lane(int sn) { return (kChunkBlocks * 256 + 64 * sn -
 // has SIMDs.
 constexpr int max_split_xpl(int kind, int nt, int xpl)
 {
-    return (kind == KIND_MFMA_LUT && nt == 1 && xpl <= 4) ? 16 : 8;
+    return ((kind == KIND_MFMA_LUT && nt == 1 && xpl <= 4) || kind == KIND_GEMV_FP8) ? 16 : 8;
 }
-constexpr int max_split(int kind, int nt, int sn) { return max_split_xpl(kind, nt, x_pieces_per_lane(sn)); }
+constexpr int max_split(int kind, int nt, int sn) { return max_split_xpl(kind, nt, x_pieces_per_lane(kind, sn)); }
 
 // Whether (nt, sn, split) is a launchable tiling for this kernel kind.
 constexpr bool split_ok(int kind, int nt, int sn, int split)
 {
     if (sn < 1 || split < 1 || split % sn || split > max_split(kind, nt, sn)) return false;
-    if (kind == KIND_GEMV_FP8) return nt == 4 && sn == 1;
-    if (sn > 8) return false;                 // activation pieces per lane >= 2
-    return (nt == 1 || nt == 2) && split / sn <= kMaxKGroups;
+    if (sn > 8 || split / sn > kMaxKGroups) return false;
+    if (kind == KIND_GEMV_FP8) return nt == 1;
+    return nt == 1 || nt == 2;
 }
 
 // Everything a GEMM launch needs.  The grid has one work-group per column

@@ -69,6 +69,8 @@ constexpr int kXChunkPieces = kChunkBlocks * 16 * 16;       // 16-byte pieces pe
 
 template <int XPL>   // pieces per lane: >= kXChunkPieces / (64 * SN)
 struct XChunk {
+    static constexpr int kChunkBytes = kXChunkBytes;
+    static constexpr int kBlockBytes = kXBlockBytes;
     buf_t rx;                 // x rows 0 .. M-1
     uint32_t vo[XPL];         // byte offset of piece i in the chunk at K block 0, or out of range
     int blk[XPL];             // K block of piece i inside the chunk (large: no piece)
@@ -112,15 +114,70 @@ __device__ __forceinline__ uint4 x_frag(const uint8_t* blk, int lane, int k)
     return *reinterpret_cast<const uint4*>(blk + (lane & 15) * kXRowBytes + k * 2);
 }
 
-// ---- FP8 weights, 16-row BF16 MFMA tile ------------------------------------
-// A operand = dequantised weights (lane: row n = l%16), B operand = x
-// (lane: batch row m = l%16).  Output D[n][m] -> lane holds n = 4(l/16)+v.
+// ---- activation staging for the GEMV ----------------------------------------
+// The GEMV needs rows 0..3 only, as FP32: a chunk is staged as FP32
+// [block][4 rows][128] (each activation converted once per work-group, not
+// once per use), loaded as 4 rows x 256-byte runs per instruction.
+constexpr int kGemvRows = 4;
+constexpr int kGemvBlockBytes = kGemvRows * 128 * 4;
+constexpr int kGemvChunkPieces = kChunkBlocks * kGemvRows * 16;   // 16-byte BF16 pieces per chunk
+
+template <int XPL>   // pieces per lane: >= kGemvChunkPieces / (64 * SN)
+struct XChunkF32 {
+    static constexpr int kChunkBytes = kChunkBlocks * kGemvBlockBytes;
+    static constexpr int kBlockBytes = kGemvBlockBytes;
+    buf_t rx;
+    uint32_t vo[XPL];
+    int blk[XPL];
+    int dst[XPL];
+    uint4 r[XPL];
+
+    __device__ void init(const GemmArgs& a, int lane, int cw, int sn)
+    {
+        rx = make_buf(a.x, (uint32_t)(((int64_t)(a.rows - 1) * a.ldx + (int64_t)a.KB * 128) * 2));
+#pragma unroll
+        for (int i = 0; i < XPL; ++i) {
+            const int q = cw * 64 + lane + i * sn * 64;
+            const int b = q >> 6, row = (q >> 4) & 3, seg = q & 15;
+            const bool ok = q < kGemvChunkPieces && row < a.rows;
+            blk[i] = ok ? b : (1 << 29);
+            vo[i] = ok ? (uint32_t)(row * a.ldx * 2 + b * 256 + seg * 16) : kBufOutOfRange;
+            dst[i] = q < kGemvChunkPieces ? b * kGemvBlockBytes + row * 512 + seg * 32 : -1;
+        }
+    }
+
+    __device__ __forceinline__ void load(int kb, int kb_end)
+    {
+#pragma unroll
+        for (int i = 0; i < XPL; ++i)
+            r[i] = buf_load16(rx, kb + blk[i] < kb_end ? vo[i] : kBufOutOfRange, (uint32_t)kb * 256u);
+    }
+
+    // BF16 -> FP32 is exact: the BF16 bits become the top half of the FP32 word
+    __device__ __forceinline__ void stage(uint8_t* buf) const
+    {
+#pragma unroll
+        for (int i = 0; i < XPL; ++i)
+            if (dst[i] >= 0) {
+                const uint32_t d[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+                uint32_t f[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    f[2 * e] = d[e] << 16;
+                    f[2 * e + 1] = d[e] & 0xFFFF0000u;
+                }
+                uint4* o = reinterpret_cast<uint4*>(buf + dst[i]);
+                o[0] = make_uint4(f[0], f[1], f[2], f[3]);
+                o[1] = make_uint4(f[4], f[5], f[6], f[7]);
+            }
+    }
+};
+
+// ---- FP8 weight stream (shared by the MFMA tile and the GEMV) ---------------
+// A unit is one tile's 2 KiB of codes for one K block: lane l loads 16 codes
+// of row l%16 from each 1 KiB chunk, plus the block scale (scalar load).
 template <int NT>
-struct MfmaFp8 {
-    static constexpr int KIND = KIND_MFMA_FP8;
-    static constexpr int NTILES = NT;
-    static constexpr bool STAGED = true;
-    static constexpr int KALIGN = 1;      // K-group ranges start at any K block
+struct Fp8Stream {
     struct Unit {
         uint4 w[NT][2];
         float s;
@@ -131,17 +188,14 @@ struct MfmaFp8 {
     buf_t rw;                 // code units of the wave's tiles (zero bytes past N)
     buf_t rnull;              // zero bytes: loads return zeros
     const float* srow;        // block-scale row of this wave's tiles
-    f32x4_t outer[NT];
 
-    __device__ MfmaFp8(const GemmArgs& a, int l, int tile0) : lane(l), KB(a.KB)
+    __device__ Fp8Stream(const GemmArgs& a, int l, int tile0) : lane(l), KB(a.KB)
     {
         ntiles = max(0, min(NT, a.n_tiles - tile0));
         const uint8_t* base = a.codes + (((int64_t)min(tile0, a.n_tiles) * a.KB) << 11);
         rw = make_buf(base, (uint32_t)(ntiles * a.KB) << 11);
         rnull = make_buf(base, 0);
         srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(min(tile0, a.n_tiles - 1) * 16 / 128) * a.KB;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) outer[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
     __device__ __forceinline__ void load(Unit& r, int kb, bool valid, int) const
@@ -155,6 +209,27 @@ struct MfmaFp8 {
         }
         // a unit with nothing to fetch (and a wave past N) reads a zero scale
         r.s = load_uniform_f32((valid && ntiles > 0) ? (const void*)(srow + kb) : (const void*)g_zero_page);
+    }
+};
+
+// ---- FP8 weights, 16-row BF16 MFMA tile ------------------------------------
+// A operand = dequantised weights (lane: row n = l%16), B operand = x
+// (lane: batch row m = l%16).  Output D[n][m] -> lane holds n = 4(l/16)+v.
+template <int NT>
+struct MfmaFp8 : Fp8Stream<NT> {
+    static constexpr int KIND = KIND_MFMA_FP8;
+    static constexpr int NTILES = NT;
+    static constexpr int KALIGN = 1;      // K-group ranges start at any K block
+    template <int XPL> using Stage = XChunk<XPL>;
+    using typename Fp8Stream<NT>::Unit;
+    using Fp8Stream<NT>::lane;
+    using Fp8Stream<NT>::ntiles;
+    f32x4_t outer[NT];
+
+    __device__ MfmaFp8(const GemmArgs& a, int l, int tile0) : Fp8Stream<NT>(a, l, tile0)
+    {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) outer[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
     __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk, int)
@@ -183,7 +258,22 @@ struct MfmaFp8 {
             for (int v = 0; v < 4; ++v) outer[t][v] = __builtin_fmaf(r.s, blk[t][v], outer[t][v]);
     }
 
-    __device__ __forceinline__ f32x4_t result(int t) const { return outer[t]; }
+    // no K split: round and store this wave's tiles (lane l holds rows
+    // n = 4(l/16) .. +3 of batch row m = l % 16)
+    template <bool F16_OUT>
+    __device__ __forceinline__ void store_direct(const GemmArgs& a, int tile0) const
+    {
+        const int m = lane & 15;
+        if (m >= a.rows) return;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < ntiles) {
+                uint16_t* yp = a.y + (int64_t)m * a.ldy + (tile0 + t) * 16 + (lane >> 4) * 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) yp[i] = F16_OUT ? f32_to_f16_rne(outer[t][i]) : f32_to_bf16_rne(outer[t][i]);
+            }
+        }
+    }
 
     // slot: [16 rows][NT*16] FP32 partial tile of this wave
     __device__ __forceinline__ void store_partial(float* slot) const
@@ -203,8 +293,8 @@ template <int NT>
 struct MfmaLut {
     static constexpr int KIND = KIND_MFMA_LUT;
     static constexpr int NTILES = NT;
-    static constexpr bool STAGED = true;
     static constexpr int KALIGN = 8;      // K blocks per group-scale load
+    template <int XPL> using Stage = XChunk<XPL>;
     struct Unit {
         uint4 w[NT];
         uint4 gv[NT];        // FP16 group scales of 8 K blocks (loaded by a run's first unit only)
@@ -272,7 +362,20 @@ struct MfmaLut {
         }
     }
 
-    __device__ __forceinline__ f32x4_t result(int t) const { return acc[t]; }
+    template <bool F16_OUT>
+    __device__ __forceinline__ void store_direct(const GemmArgs& a, int tile0) const
+    {
+        const int m = lane & 15;
+        if (m >= a.rows) return;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < ntiles) {
+                uint16_t* yp = a.y + (int64_t)m * a.ldy + (tile0 + t) * 16 + (lane >> 4) * 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) yp[i] = F16_OUT ? f32_to_f16_rne(acc[t][i]) : f32_to_bf16_rne(acc[t][i]);
+            }
+        }
+    }
 
     __device__ __forceinline__ void store_partial(float* slot) const
     {
@@ -283,94 +386,93 @@ struct MfmaLut {
 };
 
 // ---- FP8 weights, strict-K-order GEMV (MR <= 4 rows) ------------------------
-// The wave covers 4 tiles (64 columns): lane l owns column l%16 of tile l/16.
-// For each K block it loads the eight 16-byte pieces (chunk j, lane group g)
-// of its column -- the same pieces the MFMA path loads, gathered per lane
-// group across four tiles -- so every lane needs the same activations at a
-// time: x is wave-uniform and read with scalar loads.  Piece (j, g) holds the
-// 8-wide runs k = 64j + 8g and 64j + 32 + 8g, so visiting (j, half, g) in
-// that nesting walks the block's runs in increasing k.  Each (row, column)
-// keeps one FP32 accumulator that takes its products in strictly increasing
-// k over the wave's K range; each 128-K block is folded onto the outer
-// accumulator times the block scale.  The K split across waves is summed in
-// wave order afterwards.
+// One tile per wave, loaded exactly as the MFMA tile loads it: lane l holds
+// column c = l%16 and, within each 32-wide MFMA step s of a K block, the
+// 8-wide run k = 32s + 8g .. +7 of lane group g = l/16.  Each (lane, row)
+// keeps one FP32 accumulator that takes its products x*w in strictly
+// increasing k over the lane's runs; each 128-K block is folded onto the
+// outer accumulator times the block scale.  The four lane groups of a column
+// are then summed by a fixed butterfly ((g0+g1) + (g2+g3)), and a K split
+// across waves in K-group order.  The arithmetic of a row never depends on
+// M, so row r of an M-row call equals the same row of a 1-row call bit for
+// bit.
 template <int MR>
-struct GemvFp8 {
+struct GemvFp8 : Fp8Stream<1> {
     static constexpr int KIND = KIND_GEMV_FP8;
-    static constexpr int NTILES = 4;
-    static constexpr int CGW = 64;
-    static constexpr bool STAGED = false;
+    static constexpr int NTILES = 1;
     static constexpr int KALIGN = 1;
-    struct Unit {
-        uint4 w[2][4];       // [chunk j][lane group g]
-        float s;
-    };
-    const GemmArgs& a;
-    int lane;
-    bool tile_ok;
-    const uint8_t* wbase;    // this lane's column in tile l/16, lane group 0, K block 0
-    const uint16_t* xg;      // x (wave-uniform)
-    const float* srow;
+    template <int XPL> using Stage = XChunkF32<XPL>;
     float outer[MR];
 
-    __device__ GemvFp8(const GemmArgs& args, int l, int tile0) : a(args), lane(l)
+    __device__ GemvFp8(const GemmArgs& a, int l, int tile0) : Fp8Stream<1>(a, l, tile0)
     {
-        const int64_t tile = (int64_t)tile0 + (l >> 4);
-        tile_ok = tile < a.n_tiles;
-        wbase = a.codes + ((tile * a.KB) << 11) + (l & 15) * 16;
-        xg = a.x;
-        srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(tile0 * 16 / 128) * a.KB;
 #pragma unroll
         for (int m = 0; m < MR; ++m) outer[m] = 0.f;
     }
 
-    __device__ __forceinline__ void load(Unit& r, int kb, bool valid, int) const
+    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk, int)
     {
-        const bool ok = valid && tile_ok;
-        const uint8_t* p = ok ? wbase + ((int64_t)kb << 11) : g_zero_page + (lane & 15) * 16;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) r.w[j][g] = load_stream16(p + (ok ? j * 1024 + g * 256 : 0));
-        r.s = valid ? srow[kb] : 0.f;
-    }
-
-    __device__ __forceinline__ void compute(const Unit& r, int kb)
-    {
+        const int g = lane >> 4;
         float blk[MR];
 #pragma unroll
         for (int m = 0; m < MR; ++m) blk[m] = 0.f;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int s = 0; s < 4; ++s) {   // increasing k: step s covers k = 32s + 8g .. +7
+            const uint4 w = r.w[0][s >> 1];
+            const uint32_t d0 = (s & 1) ? w.z : w.x, d1 = (s & 1) ? w.w : w.y;
+            const f32x2_t w0 = e4m3x2_to_f32x2<false>(d0), w1 = e4m3x2_to_f32x2<true>(d0);
+            const f32x2_t w2 = e4m3x2_to_f32x2<false>(d1), w3 = e4m3x2_to_f32x2<true>(d1);
+            const float wf[8] = {w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int m = 0; m < MR; ++m) {
+                const float* xp = reinterpret_cast<const float*>(xblk + m * 512 + (32 * s + 8 * g) * 4);
+                const f32x4_t xa = *reinterpret_cast<const f32x4_t*>(xp);
+                const f32x4_t xc = *reinterpret_cast<const f32x4_t*>(xp + 4);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint4 w = r.w[j][g];
-                    const uint32_t d0 = h ? w.z : w.x, d1 = h ? w.w : w.y;
-                    const f32x2_t w0 = e4m3x2_to_f32x2<false>(d0), w1 = e4m3x2_to_f32x2<true>(d0);
-                    const f32x2_t w2 = e4m3x2_to_f32x2<false>(d1), w3 = e4m3x2_to_f32x2<true>(d1);
-                    const float wf[8] = {w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
-                    const int k0 = kb * 128 + j * 64 + h * 32 + g * 8;
+                for (int i = 0; i < 4; ++i) blk[m] = __builtin_fmaf(xa[i], wf[i], blk[m]);
 #pragma unroll
-                    for (int m = 0; m < MR; ++m) {
-                        const uint4 xa = load_uniform16(xg + (int64_t)m * a.ldx + k0);
-                        const uint32_t xd[4] = {xa.x, xa.y, xa.z, xa.w};
+                for (int i = 0; i < 4; ++i) blk[m] = __builtin_fmaf(xc[i], wf[4 + i], blk[m]);
+            }
+            // keep each step's activation reads next to their use: hoisting
+            // them across steps and units would hold MR*32 floats per unit
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            blk[m] = __builtin_fmaf(bf16_bits_to_f32(xd[i] & 0xFFFFu), wf[2 * i], blk[m]);
-                            blk[m] = __builtin_fmaf(bf16_bits_to_f32(xd[i] >> 16), wf[2 * i + 1], blk[m]);
-                        }
-                    }
-                }
+            for (int m = 0; m < MR; ++m) asm volatile("" : "+v"(blk[m])::"memory");
+        }
 #pragma unroll
         for (int m = 0; m < MR; ++m) outer[m] = __builtin_fmaf(r.s, blk[m], outer[m]);
     }
 
+    // the column's total over the four lane groups (identical in all four)
+    __device__ __forceinline__ float column_sum(int m) const
+    {
+        float v = outer[m];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        return v;
+    }
+
+    template <bool F16_OUT>
+    __device__ __forceinline__ void store_direct(const GemmArgs& a, int tile0) const
+    {
+        float v[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) v[m] = column_sum(m);
+        if (lane >= 16 || ntiles < 1) return;
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            if (m < a.rows) a.y[(int64_t)m * a.ldy + tile0 * 16 + lane] = f32_to_bf16_rne(v[m]);
+    }
+
+    // slot: [16 rows][16] FP32 partial tile of this wave (rows < MR written)
     __device__ __forceinline__ void store_partial(float* slot) const
     {
+        float v[MR];
 #pragma unroll
-        for (int m = 0; m < MR; ++m) slot[m * CGW + lane] = outer[m];
+        for (int m = 0; m < MR; ++m) v[m] = column_sum(m);
+        if (lane < 16) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) slot[m * 16 + lane] = v[m];
+        }
     }
 };
 
@@ -391,13 +493,14 @@ template <class Pol, int D, int XPL, bool F16_OUT>
 __global__ void __launch_bounds__(64 * max_split_xpl(Pol::KIND, Pol::NTILES, XPL))
 gemm_kernel(GemmArgs a)
 {
+    using XS = typename Pol::template Stage<XPL>;
     constexpr int NT = Pol::NTILES;
     constexpr int TW = NT * 16;                       // columns of one wave
     constexpr int R = D + 1;                          // ring slots
     constexpr int CH = kChunkBlocks;
     // steps per unrolled body: whole ring turns and an even number of chunks,
     // so ring slots and chunk buffers are compile-time in the body
-    constexpr int L = Pol::STAGED ? lcm_c(R, 2 * CH) : R;
+    constexpr int L = lcm_c(R, 2 * CH);
     static_assert(L % Pol::KALIGN == 0, "a unit's place in its scale run must be its loop position");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -419,64 +522,36 @@ gemm_kernel(GemmArgs a)
     Pol pol(a, lane, tile0);
     {
         typename Pol::Unit r[R];
-        if constexpr (Pol::STAGED) {
-            uint8_t* xb = lds + kg * 2 * kXChunkBytes;   // this K group's two chunk buffers
-            XChunk<XPL> xc;
-            xc.init(a, lane, cw, SN);
-            xc.load(kb0, kb1);
+        uint8_t* xb = lds + kg * 2 * XS::kChunkBytes;   // this K group's two chunk buffers
+        XS xc;
+        xc.init(a, lane, cw, SN);
+        xc.load(kb0, kb1);
 #pragma unroll
-            for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len, i);
-            xc.stage(xb);
-            xc.load(kb0 + CH, kb1);
-            if (SN > 1) __syncthreads();
-            for (int i = 0; i < steps; i += L) {
+        for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len, i);
+        xc.stage(xb);
+        xc.load(kb0 + CH, kb1);
+        if (SN > 1) __syncthreads();
+        for (int i = 0; i < steps; i += L) {
 #pragma unroll
-                for (int j = 0; j < L; ++j) {
-                    const int step = i + j;
-                    const int par = (j / CH) & 1;         // buffer of the current chunk
-                    pol.load(r[(j + D) % R], kb0 + step + D, step + D < len, j + D);
-                    // past the K range the slot holds zero weights and a zero
-                    // scale and the chunk zero activations: the update adds +0
-                    pol.compute(r[j % R], xb + par * kXChunkBytes + (j % CH) * kXBlockBytes, j);
-                    if ((j + 1) % CH == 0) {
-                        xc.stage(xb + (par ^ 1) * kXChunkBytes);
-                        xc.load(kb0 + step + 1 + CH, kb1);
-                        if (SN > 1) __syncthreads();
-                        if (step + 1 >= steps) break;     // uniform: every wave leaves here
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len, i);
-            for (int i = 0; i < steps; i += R) {
-#pragma unroll
-                for (int j = 0; j < R; ++j) {
-                    const int step = i + j;
-                    pol.load(r[(j + D) % R], kb0 + step + D, step + D < len, j + D);
-                    if (step < len) pol.compute(r[j], kb0 + step);
+            for (int j = 0; j < L; ++j) {
+                const int step = i + j;
+                const int par = (j / CH) & 1;         // buffer of the current chunk
+                pol.load(r[(j + D) % R], kb0 + step + D, step + D < len, j + D);
+                // past the K range the slot holds zero weights and a zero
+                // scale and the chunk zero activations: the update adds +0
+                pol.compute(r[j % R], xb + par * XS::kChunkBytes + (j % CH) * XS::kBlockBytes, j);
+                if ((j + 1) % CH == 0) {
+                    xc.stage(xb + (par ^ 1) * XS::kChunkBytes);
+                    xc.load(kb0 + step + 1 + CH, kb1);
+                    if (SN > 1) __syncthreads();
+                    if (step + 1 >= steps) break;     // uniform: every wave leaves here
                 }
             }
         }
     }
-    if constexpr (Pol::STAGED) {
-        if (SK == 1) {
-            // no K split: each wave rounds and stores its own tiles (lane l
-            // holds rows n = 4(l/16) .. +3 of batch row m = l % 16)
-            const int m = lane & 15;
-            if (m < a.rows) {
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    if (t < pol.ntiles) {
-                        const f32x4_t v = pol.result(t);
-                        uint16_t* yp = a.y + (int64_t)m * a.ldy + (tile0 + t) * 16 + (lane >> 4) * 4;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) yp[i] = F16_OUT ? f32_to_f16_rne(v[i]) : f32_to_bf16_rne(v[i]);
-                    }
-                }
-            }
-            return;
-        }
+    if (SK == 1) {
+        pol.template store_direct<F16_OUT>(a, tile0);
+        return;
     }
     __syncthreads();   // every wave is done with the staging buffers
     float* part = reinterpret_cast<float*>(lds);           // [S][16][TW]
@@ -496,10 +571,10 @@ gemm_kernel(GemmArgs a)
     }
 }
 
-template <class Pol>
+template <class Pol, int XPL>
 int gemm_lds_bytes(int split, int sn)
 {
-    const int stage = Pol::STAGED ? (split / sn) * 2 * kXChunkBytes : 0;
+    const int stage = (split / sn) * 2 * Pol::template Stage<XPL>::kChunkBytes;
     const int parts = split * 16 * Pol::NTILES * 16 * 4;
     return stage > parts ? stage : parts;
 }
@@ -653,7 +728,7 @@ template <class Pol, int D, int XPL, bool F16>
 static hipError_t launch_one(const GemmArgs& a, int split, hipStream_t s)
 {
     auto fn = gemm_kernel<Pol, D, XPL, F16>;
-    const size_t lds = (size_t)gemm_lds_bytes<Pol>(split, a.sn);
+    const size_t lds = (size_t)gemm_lds_bytes<Pol, XPL>(split, a.sn);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -673,7 +748,7 @@ static hipError_t launch_mfma(int kind, const GemmArgs& a, int split, hipStream_
 template <int NT>
 static hipError_t launch_nt(int kind, const GemmArgs& a, int split, hipStream_t s)
 {
-    switch (x_pieces_per_lane(a.sn)) {
+    switch (x_pieces_per_lane(kind, a.sn)) {
     case 16: return launch_mfma<NT, 16>(kind, a, split, s);
     case 8: return launch_mfma<NT, 8>(kind, a, split, s);
     case 6: return launch_mfma<NT, 6>(kind, a, split, s);
@@ -684,16 +759,26 @@ static hipError_t launch_nt(int kind, const GemmArgs& a, int split, hipStream_t 
     }
 }
 
+template <int MR>
+static hipError_t launch_gemv(const GemmArgs& a, int split, hipStream_t s)
+{
+    switch (x_pieces_per_lane(KIND_GEMV_FP8, a.sn)) {
+    case 4: return launch_one<GemvFp8<MR>, kDepthGemv, 4, false>(a, split, s);
+    case 2: return launch_one<GemvFp8<MR>, kDepthGemv, 2, false>(a, split, s);
+    case 1: return launch_one<GemvFp8<MR>, kDepthGemv, 1, false>(a, split, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream)
 {
     if (!split_ok(kind, nt, a.sn, split)) return hipErrorInvalidValue;
     if (kind == KIND_GEMV_FP8) {
-        if (nt != 4 || a.sn != 1) return hipErrorInvalidValue;
         switch (gemv_rows) {
-        case 1: return launch_one<GemvFp8<1>, kDepthGemv, 1, false>(a, split, stream);
-        case 2: return launch_one<GemvFp8<2>, kDepthGemv, 1, false>(a, split, stream);
-        case 3: return launch_one<GemvFp8<3>, kDepthGemv, 1, false>(a, split, stream);
-        case 4: return launch_one<GemvFp8<4>, kDepthGemv, 1, false>(a, split, stream);
+        case 1: return launch_gemv<1>(a, split, stream);
+        case 2: return launch_gemv<2>(a, split, stream);
+        case 3: return launch_gemv<3>(a, split, stream);
+        case 4: return launch_gemv<4>(a, split, stream);
         default: return hipErrorInvalidValue;
         }
     }
