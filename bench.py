@@ -36,9 +36,10 @@ ROTATE_TARGET_BYTES = 1 << 30
 
 
 def weight_bytes(fmt: str, N: int, K: int) -> int:
+    """Packed bytes a call streams: codes + scales (+ the LUT map)."""
     if fmt == "fp8":
         return N * K + 4 * (N // 128) * (K // 128)
-    return N * K // 2 + 2 * N * (K // 128) + 16
+    return N * K // 2 + 16 * N * ((K // 128 + 7) // 8) + 16
 
 
 def algorithmic_bytes(fmt: str, N: int, K: int, M: int) -> int:
