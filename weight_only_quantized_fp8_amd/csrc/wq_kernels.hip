@@ -22,31 +22,33 @@
 //         blocks; then the 8 map entries (FP16), then a 16-byte pack-status
 //         word.
 //
-// GEMM schedule.  One work-group owns one column group (NT tiles of 16 output
-// columns) over the whole of K.  Its S waves split the K blocks into S
-// contiguous, near-equal ranges (split-K), so a low-N projection still puts
-// enough waves on the chip; S is chosen per shape by the host.  Each wave walks
-// its range with the next D units' loads in flight (a register ring), folds
-// every 128-K block onto FP32 accumulators, and parks its partial tile in LDS;
-// the work-group then sums the S partials in wave order and writes y.  No two
-// work-groups share an output, so there is no cross-work-group traffic, no
-// workspace and no fence, and every sum has a fixed order: results are
-// deterministic and do not depend on M.
+// GEMM schedule.  One work-group owns one column group (SN column-waves of
+// NT tiles of 16 output columns) over the whole of K.  Its waves form SK
+// K groups that split the K blocks into contiguous ranges (split-K), so a
+// low-N projection still puts enough waves on the chip; SN and SK are chosen
+// per shape by the host.  Each wave walks its range with the next D units'
+// loads in flight (a register ring) while the column-waves of a K group
+// share activation chunks staged in LDS.  Every 128-K block is folded onto
+// FP32 accumulators.  With one K group each wave stores its own outputs;
+// otherwise the work-group sums the K groups' partial tiles in LDS in a fixed
+// order.  No two work-groups share an output, so there is no cross-work-group
+// traffic, no workspace and no fence, and every sum has a fixed order:
+// results are deterministic and do not depend on M.
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
 namespace wq {
 
-// 4 KiB of zeros: the source of loads that have nothing to fetch (prefetch
-// past the end of a wave's range, tiles past N, batch rows >= M).  Loading
-// from here keeps every load unconditional, so the compiler can count loads
-// in flight statically.
+// 4 KiB of zeros: the source of the block-scale load of a unit with nothing
+// to fetch (vector loads use a zero-byte buffer resource instead).
 __device__ __attribute__((aligned(256))) uint8_t g_zero_page[4096];
 
 // ======================================================================
 // Policies: per-unit loads and compute for each kernel kind.  A policy is
-// bound to one column group; load(r, kb, valid) fetches K block kb into the
-// register set r (from the zero page when !valid), compute(r) consumes it.
+// bound to one wave's tiles; load(r, kb, valid, pos) issues the loads of K
+// block kb into the register set r (zeros when !valid), compute(r, xblk, pos)
+// consumes it with the staged activations of that block; pos is the unit's
+// compile-time position in the unrolled loop.
 // ======================================================================
 
 // ---- activation staging for the MFMA tiles ---------------------------------
