@@ -77,8 +77,11 @@ typedef enum { WQ_FMT_FP8_BLOCK = 0, WQ_FMT_LUT3 = 1 } wq_format;
  * M = 1 and the 16-row MFMA tile for M = 2..16 (the GEMV serves M <= 4 when
  * asked for explicitly); the LUT format uses the MFMA tile for every M = 1..16
  * (one mainloop across the decode band, as in the FLUTE PR's "Results").
- * M = 17..32 always runs the MFMA tile twice, on rows 0..15 and 16..M-1
- * ("ARM ORDER": two contiguous row halves). */
+ * M = 17..32 runs the MFMA tile on the two contiguous row halves 0..15 and
+ * 16..M-1 ("ARM ORDER"): in one pass, each dequantised weight operand feeding
+ * both halves, when the plan has one tile per wave (every built-in plan), and
+ * as two passes otherwise.  Either way each row gets the arithmetic of a
+ * 16-row call. */
 typedef enum { WQ_PATH_AUTO = 0, WQ_PATH_GEMV = 1, WQ_PATH_MFMA = 2 } wq_path;
 
 /* Human-readable name of a status code (static storage, never NULL). */

@@ -280,9 +280,13 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
     a.sn = p.sn;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    // rows 0..15, then (for M > 16) rows 16..M-1 as a second pass
-    for (int64_t r0 = 0; r0 < M; r0 += 16) {
-        const int rows = (int)std::min<int64_t>(16, M - r0);
+    // One-tile MFMA waves serve M = 17..32 in one pass (each dequantised
+    // operand feeds both 16-row halves); two-tile waves run the rows 0..15
+    // and 16..M-1 as two passes.  Either way every row sees the same
+    // arithmetic as in a call of at most 16 rows.
+    const int64_t rows_per_launch = (kind != wq::KIND_GEMV_FP8 && p.nt == 1) ? 32 : 16;
+    for (int64_t r0 = 0; r0 < M; r0 += rows_per_launch) {
+        const int rows = (int)std::min<int64_t>(rows_per_launch, M - r0);
         a.x = x + r0 * ldx;
         a.ldx = ldx;
         a.y = y + r0 * ldy;

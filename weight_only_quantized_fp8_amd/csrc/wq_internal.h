@@ -72,7 +72,7 @@ struct GemmArgs {
     int64_t ldx;
     uint16_t* y;              // outputs [rows][ldy]
     int64_t ldy;
-    int rows;                 // 1..16 rows in this launch
+    int rows;                 // rows in this launch: 1..16, or 17..32 (one-tile MFMA waves)
     int N;                    // output columns
     int KB;                   // K / 128
     int n_tiles;              // N / 16

@@ -64,15 +64,19 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_page[4096];
 // MFMA operand then start 4 banks apart and cover all 64 banks once (the
 // stride arithmetic of the shared-memory pad in the arc PR "FP8 bank conflict
 // + the dispatch threshold's provenance", "What landed").
+// With MT = 2 (single-pass M = 17..32) a staged block holds 32 rows and a
+// chunk holds half as many K blocks, so the chunk's bytes and pieces stay the
+// same.
 constexpr int kXRowBytes = 128 * 2 + 16;                    // padded LDS row of one K block
-constexpr int kXBlockBytes = 16 * kXRowBytes;               // one K block of x (16 rows)
-constexpr int kXChunkBytes = kChunkBlocks * kXBlockBytes;
 constexpr int kXChunkPieces = kChunkBlocks * 16 * 16;       // 16-byte pieces per chunk
 
-template <int XPL>   // pieces per lane: >= kXChunkPieces / (64 * SN)
+template <int XPL, int MT>   // pieces per lane: >= kXChunkPieces / (64 * SN); row tiles
 struct XChunk {
-    static constexpr int kChunkBytes = kXChunkBytes;
-    static constexpr int kBlockBytes = kXBlockBytes;
+    static constexpr int kRows = 16 * MT;
+    static constexpr int kBlocks = kChunkBlocks / MT;       // K blocks per chunk
+    static constexpr int kBlockBytes = kRows * kXRowBytes;
+    static constexpr int kChunkBytes = kBlocks * kBlockBytes;
+    static_assert(kBlocks * kRows * 16 == kXChunkPieces, "a chunk has the same pieces for every MT");
     buf_t rx;                 // x rows 0 .. M-1
     uint32_t vo[XPL];         // byte offset of piece i in the chunk at K block 0, or out of range
     int blk[XPL];             // K block of piece i inside the chunk (large: no piece)
@@ -85,11 +89,11 @@ struct XChunk {
 #pragma unroll
         for (int i = 0; i < XPL; ++i) {
             const int q = cw * 64 + lane + i * sn * 64;
-            const int b = q >> 8, row = (q >> 4) & 15, seg = q & 15;
+            const int b = q / (kRows * 16), row = (q >> 4) % kRows, seg = q & 15;
             const bool ok = q < kXChunkPieces && row < a.rows;
             blk[i] = ok ? b : (1 << 29);
             vo[i] = ok ? (uint32_t)(row * a.ldx * 2 + b * 256 + seg * 16) : kBufOutOfRange;
-            dst[i] = q < kXChunkPieces ? b * kXBlockBytes + row * kXRowBytes + seg * 16 : -1;
+            dst[i] = q < kXChunkPieces ? b * kBlockBytes + row * kXRowBytes + seg * 16 : -1;
         }
     }
 
@@ -110,10 +114,10 @@ struct XChunk {
     }
 };
 
-// 8 consecutive activations of batch row (lane % 16), from k on, of one staged K block
-__device__ __forceinline__ uint4 x_frag(const uint8_t* blk, int lane, int k)
+// 8 consecutive activations of batch row 16*mt + lane % 16, from k on, of one staged K block
+__device__ __forceinline__ uint4 x_frag(const uint8_t* blk, int lane, int k, int mt = 0)
 {
-    return *reinterpret_cast<const uint4*>(blk + (lane & 15) * kXRowBytes + k * 2);
+    return *reinterpret_cast<const uint4*>(blk + (mt * 16 + (lane & 15)) * kXRowBytes + k * 2);
 }
 
 // ---- activation staging for the GEMV ----------------------------------------
@@ -126,6 +130,7 @@ constexpr int kGemvChunkPieces = kChunkBlocks * kGemvRows * 16;   // 16-byte BF1
 
 template <int XPL>   // pieces per lane: >= kGemvChunkPieces / (64 * SN)
 struct XChunkF32 {
+    static constexpr int kBlocks = kChunkBlocks;
     static constexpr int kChunkBytes = kChunkBlocks * kGemvBlockBytes;
     static constexpr int kBlockBytes = kGemvBlockBytes;
     buf_t rx;
@@ -217,72 +222,94 @@ struct Fp8Stream {
 // ---- FP8 weights, 16-row BF16 MFMA tile ------------------------------------
 // A operand = dequantised weights (lane: row n = l%16), B operand = x
 // (lane: batch row m = l%16).  Output D[n][m] -> lane holds n = 4(l/16)+v.
-template <int NT>
+// MT = 2 serves M = 17..32 in one pass: each dequantised A operand feeds two
+// MFMAs, one per 16-row half of the batch, with the same per-row arithmetic
+// as the 16-row tile.
+template <int NT, int MT>
 struct MfmaFp8 : Fp8Stream<NT> {
     static constexpr int KIND = KIND_MFMA_FP8;
     static constexpr int NTILES = NT;
+    static constexpr int ROWS = 16 * MT;
     static constexpr int KALIGN = 1;      // K-group ranges start at any K block
-    template <int XPL> using Stage = XChunk<XPL>;
+    template <int XPL> using Stage = XChunk<XPL, MT>;
     using typename Fp8Stream<NT>::Unit;
     using Fp8Stream<NT>::lane;
     using Fp8Stream<NT>::ntiles;
-    f32x4_t outer[NT];
+    f32x4_t outer[NT][MT];
 
     __device__ MfmaFp8(const GemmArgs& a, int l, int tile0) : Fp8Stream<NT>(a, l, tile0)
     {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) outer[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int h = 0; h < MT; ++h) outer[t][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
     __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk, int)
     {
-        bf16x8_t b[4];
+        bf16x8_t b[MT][4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f)    // MFMA step f = 2j + h: lane group g holds k = 32f + 8g .. +7
-            b[f] = __builtin_bit_cast(bf16x8_t, x_frag(xblk, lane, f * 32 + (lane >> 4) * 8));
-        f32x4_t blk[NT];
+        for (int h = 0; h < MT; ++h)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) blk[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int f = 0; f < 4; ++f)    // MFMA step f = 2j + h: lane group g holds k = 32f + 8g .. +7
+                b[h][f] = __builtin_bit_cast(bf16x8_t, x_frag(xblk, lane, f * 32 + (lane >> 4) * 8, h));
+        f32x4_t blk[NT][MT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int h = 0; h < MT; ++h) blk[t][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-            const int j = f >> 1, h = f & 1;
+            const int j = f >> 1, hi = f & 1;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const uint4 w = r.w[t][j];
-                const bf16x8_t av = h ? e4m3x8_to_bf16x8(w.z, w.w) : e4m3x8_to_bf16x8(w.x, w.y);
-                blk[t] = mfma_bf16(av, b[f], blk[t]);
+                const bf16x8_t av = hi ? e4m3x8_to_bf16x8(w.z, w.w) : e4m3x8_to_bf16x8(w.x, w.y);
+#pragma unroll
+                for (int h = 0; h < MT; ++h) blk[t][h] = mfma_bf16(av, b[h][f], blk[t][h]);
             }
         }
         // two-level fold: one FP32 FMA per 128-K block and output
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) outer[t][v] = __builtin_fmaf(r.s, blk[t][v], outer[t][v]);
+            for (int h = 0; h < MT; ++h)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) outer[t][h][v] = __builtin_fmaf(r.s, blk[t][h][v], outer[t][h][v]);
     }
 
     // no K split: round and store this wave's tiles (lane l holds rows
-    // n = 4(l/16) .. +3 of batch row m = l % 16)
+    // n = 4(l/16) .. +3 of batch row m = 16h + l % 16)
     template <bool F16_OUT>
     __device__ __forceinline__ void store_direct(const GemmArgs& a, int tile0) const
     {
-        const int m = lane & 15;
-        if (m >= a.rows) return;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < ntiles) {
-                uint16_t* yp = a.y + (int64_t)m * a.ldy + (tile0 + t) * 16 + (lane >> 4) * 4;
+        for (int h = 0; h < MT; ++h) {
+            const int m = 16 * h + (lane & 15);
+            if (m >= a.rows) continue;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) yp[i] = F16_OUT ? f32_to_f16_rne(outer[t][i]) : f32_to_bf16_rne(outer[t][i]);
+            for (int t = 0; t < NT; ++t) {
+                if (t < ntiles) {
+                    uint16_t* yp = a.y + (int64_t)m * a.ldy + (tile0 + t) * 16 + (lane >> 4) * 4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        yp[i] = F16_OUT ? f32_to_f16_rne(outer[t][h][i]) : f32_to_bf16_rne(outer[t][h][i]);
+                }
             }
         }
     }
 
-    // slot: [16 rows][NT*16] FP32 partial tile of this wave
+    // slot: [ROWS][NT*16] FP32 partial tile of this wave
     __device__ __forceinline__ void store_partial(float* slot) const
     {
-        const int m = lane & 15, n4 = (lane >> 4) * 4;
+        const int n4 = (lane >> 4) * 4;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(slot + m * NT * 16 + t * 16 + n4) = outer[t];
+        for (int h = 0; h < MT; ++h) {
+            const int m = 16 * h + (lane & 15);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<f32x4_t*>(slot + m * NT * 16 + t * 16 + n4) = outer[t][h];
+        }
     }
 };
 
@@ -291,12 +318,13 @@ struct MfmaFp8 : Fp8Stream<NT> {
 // with the weights of the run's first unit; K-group ranges start at multiples
 // of 8 blocks, so a unit's place in its run is its (compile-time) position in
 // the unrolled loop.
-template <int NT>
+template <int NT, int MT>
 struct MfmaLut {
     static constexpr int KIND = KIND_MFMA_LUT;
     static constexpr int NTILES = NT;
+    static constexpr int ROWS = 16 * MT;
     static constexpr int KALIGN = 8;      // K blocks per group-scale load
-    template <int XPL> using Stage = XChunk<XPL>;
+    template <int XPL> using Stage = XChunk<XPL, MT>;
     struct Unit {
         uint4 w[NT];
         uint4 gv[NT];        // FP16 group scales of 8 K blocks (loaded by a run's first unit only)
@@ -310,7 +338,7 @@ struct MfmaLut {
     buf_t rnull;             // zero bytes: loads return zeros
     uint32_t q[4];           // map entries as FP16 pairs
     uint4 gcur[NT];          // group scales of the current run
-    f32x4_t acc[NT];
+    f32x4_t acc[NT][MT];
 
     __device__ MfmaLut(const GemmArgs& a, int l, int tile0) : lane(l), KB(a.KB), KB8((a.KB + 7) / 8)
     {
@@ -325,7 +353,8 @@ struct MfmaLut {
         for (int i = 0; i < 4; ++i) q[i] = qm[i];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int h = 0; h < MT; ++h) acc[t][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             gcur[t] = make_uint4(0, 0, 0, 0);
         }
     }
@@ -349,10 +378,12 @@ struct MfmaLut {
 #pragma unroll
             for (int t = 0; t < NT; ++t) gcur[t] = r.gv[t];
         }
-        f16x8_t b[4];
+        f16x8_t b[MT][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)   // MFMA step s: lane group g holds k = 32s + 8g + e
-            b[s] = __builtin_bit_cast(f16x8_t, x_frag(xblk, lane, s * 32 + (lane >> 4) * 8));
+        for (int h = 0; h < MT; ++h)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)   // MFMA step s: lane group g holds k = 32s + 8g + e
+                b[h][s] = __builtin_bit_cast(f16x8_t, x_frag(xblk, lane, s * 32 + (lane >> 4) * 8, h));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint32_t gd = e < 2 ? gcur[t].x : e < 4 ? gcur[t].y : e < 6 ? gcur[t].z : gcur[t].w;
@@ -360,30 +391,43 @@ struct MfmaLut {
             const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, gbits));
             const uint32_t wd[4] = {r.w[t].x, r.w[t].y, r.w[t].z, r.w[t].w};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc[t] = mfma_f16(lut_decode8(wd[s], pl), b[s], acc[t]);
+            for (int s = 0; s < 4; ++s) {
+                const f16x8_t av = lut_decode8(wd[s], pl);
+#pragma unroll
+                for (int h = 0; h < MT; ++h) acc[t][h] = mfma_f16(av, b[h][s], acc[t][h]);
+            }
         }
     }
 
     template <bool F16_OUT>
     __device__ __forceinline__ void store_direct(const GemmArgs& a, int tile0) const
     {
-        const int m = lane & 15;
-        if (m >= a.rows) return;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < ntiles) {
-                uint16_t* yp = a.y + (int64_t)m * a.ldy + (tile0 + t) * 16 + (lane >> 4) * 4;
+        for (int h = 0; h < MT; ++h) {
+            const int m = 16 * h + (lane & 15);
+            if (m >= a.rows) continue;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) yp[i] = F16_OUT ? f32_to_f16_rne(acc[t][i]) : f32_to_bf16_rne(acc[t][i]);
+            for (int t = 0; t < NT; ++t) {
+                if (t < ntiles) {
+                    uint16_t* yp = a.y + (int64_t)m * a.ldy + (tile0 + t) * 16 + (lane >> 4) * 4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        yp[i] = F16_OUT ? f32_to_f16_rne(acc[t][h][i]) : f32_to_bf16_rne(acc[t][h][i]);
+                }
             }
         }
     }
 
     __device__ __forceinline__ void store_partial(float* slot) const
     {
-        const int m = lane & 15, n4 = (lane >> 4) * 4;
+        const int n4 = (lane >> 4) * 4;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(slot + m * NT * 16 + t * 16 + n4) = acc[t];
+        for (int h = 0; h < MT; ++h) {
+            const int m = 16 * h + (lane & 15);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<f32x4_t*>(slot + m * NT * 16 + t * 16 + n4) = acc[t][h];
+        }
     }
 };
 
@@ -402,6 +446,7 @@ template <int MR>
 struct GemvFp8 : Fp8Stream<1> {
     static constexpr int KIND = KIND_GEMV_FP8;
     static constexpr int NTILES = 1;
+    static constexpr int ROWS = 16;       // rows of the partial-tile slot (MR used)
     static constexpr int KALIGN = 1;
     template <int XPL> using Stage = XChunkF32<XPL>;
     float outer[MR];
@@ -499,7 +544,8 @@ gemm_kernel(GemmArgs a)
     constexpr int NT = Pol::NTILES;
     constexpr int TW = NT * 16;                       // columns of one wave
     constexpr int R = D + 1;                          // ring slots
-    constexpr int CH = kChunkBlocks;
+    constexpr int CH = XS::kBlocks;                   // K blocks per activation chunk
+    constexpr int PR = Pol::ROWS;                     // rows of a partial tile
     // steps per unrolled body: whole ring turns and an even number of chunks,
     // so ring slots and chunk buffers are compile-time in the body
     constexpr int L = lcm_c(R, 2 * CH);
@@ -556,8 +602,8 @@ gemm_kernel(GemmArgs a)
         return;
     }
     __syncthreads();   // every wave is done with the staging buffers
-    float* part = reinterpret_cast<float*>(lds);           // [S][16][TW]
-    pol.store_partial(part + wave * 16 * TW);
+    float* part = reinterpret_cast<float*>(lds);           // [S][PR][TW]
+    pol.store_partial(part + wave * PR * TW);
     __syncthreads();
 
     const int cols = SN * TW;
@@ -565,9 +611,9 @@ gemm_kernel(GemmArgs a)
     for (int e = tid; e < nout; e += blockDim.x) {
         const int m = e / cols, c = e - m * cols;
         const int w0 = c / TW, cc = c - w0 * TW;
-        const float* p = part + (w0 * 16 + m) * TW + cc;    // wave w0 (K group 0)
+        const float* p = part + (w0 * PR + m) * TW + cc;    // wave w0 (K group 0)
         float v = p[0];
-        for (int k = 1; k < SK; ++k) v += p[(int64_t)k * SN * 16 * TW];
+        for (int k = 1; k < SK; ++k) v += p[(int64_t)k * SN * PR * TW];
         const int64_t n = (int64_t)blockIdx.x * cols + c;
         if (n < a.N) a.y[m * a.ldy + n] = F16_OUT ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
     }
@@ -577,7 +623,7 @@ template <class Pol, int XPL>
 int gemm_lds_bytes(int split, int sn)
 {
     const int stage = (split / sn) * 2 * Pol::template Stage<XPL>::kChunkBytes;
-    const int parts = split * 16 * Pol::NTILES * 16 * 4;
+    const int parts = split * Pol::ROWS * Pol::NTILES * 16 * 4;
     return stage > parts ? stage : parts;
 }
 
@@ -740,23 +786,23 @@ static hipError_t launch_one(const GemmArgs& a, int split, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int NT, int XPL>
+template <int NT, int MT, int XPL>
 static hipError_t launch_mfma(int kind, const GemmArgs& a, int split, hipStream_t s)
 {
-    if (kind == KIND_MFMA_FP8) return launch_one<MfmaFp8<NT>, kDepthMfmaFp8, XPL, false>(a, split, s);
-    return launch_one<MfmaLut<NT>, kDepthMfmaLut, XPL, true>(a, split, s);
+    if (kind == KIND_MFMA_FP8) return launch_one<MfmaFp8<NT, MT>, kDepthMfmaFp8, XPL, false>(a, split, s);
+    return launch_one<MfmaLut<NT, MT>, kDepthMfmaLut, XPL, true>(a, split, s);
 }
 
-template <int NT>
+template <int NT, int MT>
 static hipError_t launch_nt(int kind, const GemmArgs& a, int split, hipStream_t s)
 {
     switch (x_pieces_per_lane(kind, a.sn)) {
-    case 16: return launch_mfma<NT, 16>(kind, a, split, s);
-    case 8: return launch_mfma<NT, 8>(kind, a, split, s);
-    case 6: return launch_mfma<NT, 6>(kind, a, split, s);
-    case 4: return launch_mfma<NT, 4>(kind, a, split, s);
-    case 3: return launch_mfma<NT, 3>(kind, a, split, s);
-    case 2: return launch_mfma<NT, 2>(kind, a, split, s);
+    case 16: return launch_mfma<NT, MT, 16>(kind, a, split, s);
+    case 8: return launch_mfma<NT, MT, 8>(kind, a, split, s);
+    case 6: return launch_mfma<NT, MT, 6>(kind, a, split, s);
+    case 4: return launch_mfma<NT, MT, 4>(kind, a, split, s);
+    case 3: return launch_mfma<NT, MT, 3>(kind, a, split, s);
+    case 2: return launch_mfma<NT, MT, 2>(kind, a, split, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -785,9 +831,13 @@ hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int s
         }
     }
     if (kind != KIND_MFMA_FP8 && kind != KIND_MFMA_LUT) return hipErrorInvalidValue;
+    if (a.rows > 16) {
+        if (nt != 1 || a.rows > 32) return hipErrorInvalidValue;
+        return launch_nt<1, 2>(kind, a, split, stream);
+    }
     switch (nt) {
-    case 1: return launch_nt<1>(kind, a, split, stream);
-    case 2: return launch_nt<2>(kind, a, split, stream);
+    case 1: return launch_nt<1, 1>(kind, a, split, stream);
+    case 2: return launch_nt<2, 1>(kind, a, split, stream);
     default: return hipErrorInvalidValue;
     }
 }
