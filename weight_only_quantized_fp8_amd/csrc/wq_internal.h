@@ -9,10 +9,11 @@
 namespace wq {
 
 // Prefetch depth: weight units in flight per wave beyond the one being
-// computed (the register ring has depth + 1 slots).  A LUT unit is half the
-// bytes of an FP8 unit and costs more VALU to decode, so its ring is deeper.
+// computed (the register ring has depth + 1 slots).  Depths 3 to 7 measured
+// within noise of each other for both formats; 3 keeps the most registers
+// free.
 constexpr int kDepthMfmaFp8 = 3;
-constexpr int kDepthMfmaLut = 7;
+constexpr int kDepthMfmaLut = 3;
 constexpr int kDepthGemv = 3;
 
 enum Kind : int {

@@ -546,10 +546,10 @@ gemm_kernel(GemmArgs a)
     constexpr int R = D + 1;                          // ring slots
     constexpr int CH = XS::kBlocks;                   // K blocks per activation chunk
     constexpr int PR = Pol::ROWS;                     // rows of a partial tile
-    // steps per unrolled body: whole ring turns and an even number of chunks,
-    // so ring slots and chunk buffers are compile-time in the body
-    constexpr int L = lcm_c(R, 2 * CH);
-    static_assert(L % Pol::KALIGN == 0, "a unit's place in its scale run must be its loop position");
+    // steps per unrolled body: whole ring turns, an even number of chunks and
+    // whole scale runs, so ring slots, chunk buffers and a unit's place in its
+    // scale run are compile-time in the body
+    constexpr int L = lcm_c(lcm_c(R, 2 * CH), Pol::KALIGN);
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x;
