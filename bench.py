@@ -39,7 +39,8 @@ def weight_bytes(fmt: str, N: int, K: int) -> int:
     """Packed bytes a call streams: codes + scales (+ the LUT map)."""
     if fmt == "fp8":
         return N * K + 4 * (N // 128) * (K // 128)
-    return N * K // 2 + 16 * N * ((K // 128 + 7) // 8) + 16
+    code_bytes = N * K * 3 // 8 if fmt == "lut3d" else N * K // 2     # 3 bits or one nibble a code
+    return code_bytes + 16 * N * ((K // 128 + 7) // 8) + 16
 
 
 def algorithmic_bytes(fmt: str, N: int, K: int, M: int) -> int:
@@ -97,14 +98,18 @@ class Workload:
             self.ws = wq.workspace(wq.WQ_FMT_FP8_BLOCK, N, K, dev)
             self._call = lambda p: wq.wq_gemm_fp8_block(p, N, K, self.x, self.y, M, self.ws)
         else:
+            dense = self.fmt == "lut3d"
             codes, qmap, g = synth.lut3_weights(N, K, seed)
             t16 = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16)
-            p0 = wq.pack_lut3(torch.from_numpy(codes).to(dev), t16(qmap), t16(g))
+            pack = wq.pack_lut3_dense if dense else wq.pack_lut3
+            p0 = pack(torch.from_numpy(codes).to(dev), t16(qmap), t16(g))
+            del codes
             x = synth.x_f16(M, K, seed + 100)
             self.x = t16(x)
             self.y = torch.empty((M, N), dtype=torch.float16, device=dev)
-            self.ws = wq.workspace(wq.WQ_FMT_LUT3, N, K, dev)
-            self._call = lambda p: wq.wq_gemm_lut3(p, N, K, self.x, self.y, M, self.ws)
+            self.ws = wq.workspace(wq.WQ_FMT_LUT3_DENSE if dense else wq.WQ_FMT_LUT3, N, K, dev)
+            gemm = wq.wq_gemm_lut3_dense if dense else wq.wq_gemm_lut3
+            self._call = lambda p: gemm(p, N, K, self.x, self.y, M, self.ws)
         self.packed = [p0] + [p0.clone() for _ in range(copies - 1)]
         torch.cuda.synchronize()
         self.i = 0
@@ -250,7 +255,8 @@ def main(argv=None) -> int:
         "dtype": "bf16" if w.fmt == "fp8" else "f16",
         "data": "synthetic",
         "config": {"workload": "%s %s N=%d K=%d M=%d" % (args.config, w.fmt, w.N, w.K, args.M),
-                   "format": "fp8_e4m3_block128x128" if w.fmt == "fp8" else "lut3_group128",
+                   "format": {"fp8": "fp8_e4m3_block128x128", "lut3": "lut3_group128",
+                              "lut3d": "lut3_dense_group128"}[w.fmt],
                    "N": w.N, "K": w.K, "M": args.M, "weight_bytes_per_step": w.wbytes,
                    "weight_copies_rotated": w.copies, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

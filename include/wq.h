@@ -18,7 +18,13 @@
  *     FP16 scale per (row, 128-wide K group); each dequantised weight is
  *     rounded to FP16 before it is accumulated (FLUTE PR "Add optimized_w3:
  *     3-bit LUT GEMM on a new mainloop", "Core contributions" item 1 and
- *     "Results").  Activations and outputs are FP16.
+ *     "Results").  Activations and outputs are FP16.  Stored either with one
+ *     code per 4-bit nibble (the FLUTE PR's "Core contributions" item 2: the
+ *     loaded word is already the byte-permute selector) or densely at 3 bits
+ *     a code (25% fewer bytes to stream, for 5 more ALU operations per 32
+ *     codes to gather the selectors; the FLUTE PR's "Why this exists" names
+ *     this trade in FLUTE's own bit-sliced 3-bit storage).  Both layouts give
+ *     bit-identical GEMM results.
  *
  * Work flow (FLUTE PR, "Core contributions" item 2: pack once, offline):
  *   1. wq_pack_* reorders canonical row-major [N, K] codes (plus scales and
@@ -62,14 +68,14 @@ typedef enum {
     WQ_ERR_SHAPE = 2,      /* M, N or K outside what the format/path supports         */
     WQ_ERR_LD = 3,         /* a leading dimension is smaller than the row length      */
     WQ_ERR_WORKSPACE = 4,  /* workspace smaller than wq_gemm_workspace_bytes() (unused) */
-    WQ_ERR_CODE = 5,       /* wq_pack_lut3 found a code > 7 (packed buffer not valid) */
+    WQ_ERR_CODE = 5,       /* a LUT packer found a code > 7 (packed buffer not valid) */
     WQ_ERR_DEVICE = 6,     /* current device is not gfx950                            */
     WQ_ERR_HIP = 7,        /* a HIP runtime call failed (includes: no device)         */
     WQ_ERR_ALIGN = 8,      /* pointer or leading dimension breaks a 16-byte alignment */
     WQ_ERR_PATH = 9        /* requested path cannot serve this format / M             */
 } wq_status;
 
-typedef enum { WQ_FMT_FP8_BLOCK = 0, WQ_FMT_LUT3 = 1 } wq_format;
+typedef enum { WQ_FMT_FP8_BLOCK = 0, WQ_FMT_LUT3 = 1, WQ_FMT_LUT3_DENSE = 2 } wq_format;
 
 /* Kernel path for the GEMM.  AUTO follows the batch ladder of the atlas
  * "Module m16_tc" docs (section ARM ORDER) with the crossover measured on
@@ -176,6 +182,25 @@ wq_status wq_gemm_lut3(const void* packed, int64_t N, int64_t K,
                        uint16_t* y, int64_t ldy, int64_t M,
                        void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Dense form of the LUT format: the same codes, map and scales, with the
+ * codes stored at 3 bits each.  Packed bytes: N*K*3/8 code bytes + 16*N*
+ * ceil(K/1024) scale bytes + 32; 0 for an unsupported shape (as
+ * wq_lut3_packed_bytes).  Arguments, limits, errors and synchronisation of
+ * the three calls are those of wq_pack_lut3 / wq_gemm_lut3 / wq_unpack_lut3;
+ * a GEMM on a dense matrix returns the same bits as on the nibble-packed
+ * matrix of the same inputs (the layouts differ only in how the codes are
+ * stored, the arithmetic is the same). */
+size_t wq_lut3_dense_packed_bytes(int64_t N, int64_t K);
+
+wq_status wq_pack_lut3_dense(const uint8_t* codes, int64_t ldc, const uint16_t* qmap,
+                             const uint16_t* scales, int64_t N, int64_t K,
+                             void* packed, void* hip_stream);
+
+wq_status wq_gemm_lut3_dense(const void* packed, int64_t N, int64_t K,
+                             const uint16_t* x, int64_t ldx,
+                             uint16_t* y, int64_t ldy, int64_t M,
+                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------ workspace */
 
 /* Workspace bytes a GEMM of this format and shape needs (the same for every M
@@ -197,6 +222,10 @@ wq_status wq_unpack_fp8_block_f32(const void* packed, int64_t N, int64_t K,
 /* out[n][k] = fp16_rne(qmap[code] * scale[n][k/128]) */
 wq_status wq_unpack_lut3(const void* packed, int64_t N, int64_t K,
                          uint16_t* w_f16, void* hip_stream);
+
+/* The same for a matrix packed by wq_pack_lut3_dense. */
+wq_status wq_unpack_lut3_dense(const void* packed, int64_t N, int64_t K,
+                               uint16_t* w_f16, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -41,9 +41,11 @@ __all__ = [
 SEEDS = {
     "tiny": 1000, "gate_up": 1001, "down": 1002, "lut3": 1003,
     "attn_q": 1004, "attn_k": 1005, "attn_v": 1006, "attn_o": 1007,
+    "lut3d": 1003,     # the "lut3" matrix and activations, stored densely (3 bits a code)
 }
 
-# name -> (format, N, K, M sweep)
+# name -> (format, N, K, M sweep); format "lut3d" is the LUT format with the
+# codes stored at 3 bits each instead of one per nibble
 CONFIGS = {
     "tiny":    ("fp8", 256, 512, (1,)),
     "gate_up": ("fp8", 17408, 5120, (1, 4, 8, 16)),
@@ -53,6 +55,7 @@ CONFIGS = {
     "attn_k":  ("fp8", 1024, 5120, (16,)),
     "attn_v":  ("fp8", 1024, 5120, (16,)),
     "attn_o":  ("fp8", 5120, 6144, (16,)),
+    "lut3d":   ("lut3d", 28672, 8192, (1, 2, 4, 8, 16)),
 }
 
 _BLOCK = 128

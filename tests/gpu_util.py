@@ -96,15 +96,18 @@ def grade_fp8(ybits, xbits, codes, scales, K, cols=None, floor=None):
 
 # ------------------------------------------------------------------ LUT3
 
-def pack_lut3(codes, qmap, scales):
+def pack_lut3(codes, qmap, scales, dense=False):
+    """dense: the 3-bit-per-code layout (wq_pack_lut3_dense) instead of nibbles."""
     wq = wqmod()
     N, K = codes.shape
-    packed = torch.empty(wq.wq_lut3_packed_bytes(N, K), dtype=torch.uint8, device=DEV)
-    wq.wq_pack_lut3(t_u8(codes), t_u16(qmap, torch.float16), t_u16(scales, torch.float16), N, K, packed)
+    nbytes = (wq.wq_lut3_dense_packed_bytes if dense else wq.wq_lut3_packed_bytes)(N, K)
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    (wq.wq_pack_lut3_dense if dense else wq.wq_pack_lut3)(
+        t_u8(codes), t_u16(qmap, torch.float16), t_u16(scales, torch.float16), N, K, packed)
     return packed
 
 
-def run_lut3(packed, N, K, xbits, M=None, ws=None, ldy=None, y_init=None):
+def run_lut3(packed, N, K, xbits, M=None, ws=None, ldy=None, y_init=None, dense=False):
     wq = wqmod()
     M = xbits.shape[0] if M is None else M
     x = t_u16(xbits, torch.float16)
@@ -112,8 +115,9 @@ def run_lut3(packed, N, K, xbits, M=None, ws=None, ldy=None, y_init=None):
     y = torch.empty((max(M, 1), ldy), dtype=torch.float16, device=DEV)
     if y_init is not None:
         y.copy_(t_u16(y_init, torch.float16))
-    ws = wq.workspace(wq.WQ_FMT_LUT3, N, K, DEV) if ws is None else ws
-    wq.wq_gemm_lut3(packed, N, K, x, y, M, ws)
+    fmt = wq.WQ_FMT_LUT3_DENSE if dense else wq.WQ_FMT_LUT3
+    ws = wq.workspace(fmt, N, K, DEV) if ws is None else ws
+    (wq.wq_gemm_lut3_dense if dense else wq.wq_gemm_lut3)(packed, N, K, x, y, M, ws)
     torch.cuda.synchronize()
     full = bits_of(y)
     return full[:M, :N], full

@@ -46,18 +46,23 @@ def test_status_strings():
 
 
 def test_workspace_is_empty():
-    for fmt, N, K in ((0, 17408, 5120), (0, 256, 512), (1, 28672, 8192), (1, 48, 256)):
+    for fmt, N, K in ((0, 17408, 5120), (0, 256, 512), (1, 28672, 8192), (1, 48, 256), (2, 28672, 8192)):
         assert wq.wq_gemm_workspace_bytes(fmt, 16, N, K) == 0
 
 
 def test_sizes_are_host_arithmetic():
-    assert wq.wq_packed_format_version() == 2
+    assert wq.wq_packed_format_version() == 3
     assert wq.wq_fp8_block_packed_bytes(17408, 5120) == 17408 * 5120 + 4 * 136 * 40
     assert wq.wq_lut3_packed_bytes(28672, 8192) == 28672 * 8192 // 2 + 2 * 28672 * 64 + 32
     assert wq.wq_fp8_block_packed_bytes(100, 128) == 0      # N not a multiple of 128
     assert wq.wq_fp8_block_packed_bytes(128, 100) == 0
     assert wq.wq_lut3_packed_bytes(24, 128) == 0           # N not a multiple of 16
     assert wq.wq_lut3_packed_bytes(48, 256) == 48 * 128 + 3 * 256 + 32   # K blocks padded to 8
+    # dense: 3 bits a code, the same scales, map and status word
+    assert wq.wq_lut3_dense_packed_bytes(28672, 8192) == 28672 * 8192 * 3 // 8 + 2 * 28672 * 64 + 32
+    assert wq.wq_lut3_dense_packed_bytes(48, 256) == 48 * 96 + 3 * 256 + 32
+    assert wq.wq_lut3_dense_packed_bytes(24, 128) == 0
+    assert wq.wq_lut3_dense_packed_bytes(32, 100) == 0
 
 
 L = wq.lib
@@ -90,6 +95,7 @@ def test_m_zero_is_a_no_op():
     # M == 0 queues nothing and returns WQ_OK before looking at the pointers
     assert L.wq_gemm_fp8_block(None, 256, 512, None, 512, None, 256, 0, None, 0, None) == 0
     assert L.wq_gemm_lut3(None, 48, 512, None, 512, None, 48, 0, None, 0, None) == 0
+    assert L.wq_gemm_lut3_dense(None, 48, 512, None, 512, None, 48, 0, None, 0, None) == 0
 
 
 @pytest.mark.parametrize("path,expect", [(3, 9), (-1, 9)])
@@ -105,6 +111,7 @@ def test_bad_path(path, expect):
 ])
 def test_lut_gemm_validation(args, expect):
     assert L.wq_gemm_lut3(*args, None) == expect
+    assert L.wq_gemm_lut3_dense(*args, None) == expect
 
 
 def test_lut_has_no_gemv_path():
@@ -125,6 +132,12 @@ def test_lut_has_no_gemv_path():
     (lambda: L.wq_unpack_fp8_block(P, 256, 500, P, None), 2),
     (lambda: L.wq_unpack_fp8_block_f32(P, 256, 512, P + 4, None), 8),
     (lambda: L.wq_unpack_lut3(P, 8, 512, P, None), 2),
+    (lambda: L.wq_pack_lut3_dense(P, 512, None, P, 48, 512, P, None), 1),
+    (lambda: L.wq_pack_lut3_dense(P, 100, P, P, 48, 512, P, None), 3),
+    (lambda: L.wq_pack_lut3_dense(P, 512, P, P, 50, 512, P, None), 2),
+    (lambda: L.wq_pack_lut3_dense(P, 512, P, P, 48, 512, P + 8, None), 8),
+    (lambda: L.wq_unpack_lut3_dense(P, 8, 512, P, None), 2),
+    (lambda: L.wq_unpack_lut3_dense(None, 16, 512, P, None), 1),
 ])
 def test_pack_unpack_validation(call, expect):
     assert call() == expect
@@ -143,4 +156,5 @@ def test_valid_call_without_device_reports_hip_error():
     # arguments pass every host check; with no GPU the device query fails cleanly
     assert L.wq_gemm_fp8_block(P, 256, 512, P, 512, P, 256, 1, P, BIG, None) == 7
     assert L.wq_gemm_lut3(P, 48, 512, P, 512, P, 48, 4, P, BIG, None) == 7
+    assert L.wq_gemm_lut3_dense(P, 48, 512, P, 512, P, 48, 4, P, BIG, None) == 7
     assert L.wq_pack_fp8_block(P, 512, P, 256, 512, P, None) == 7

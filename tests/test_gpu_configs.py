@@ -27,8 +27,9 @@ def test_config_parity(name, M):
     else:
         codes, qmap, g = data
         xbits = synth.x_f16(M, K, synth.SEEDS[name] + 100)
-        packed = _packed(name, lambda: U.pack_lut3(codes, qmap, g))
-        y, _ = U.run_lut3(packed, N, K, xbits)
+        dense = fmt == "lut3d"
+        packed = _packed(name, lambda: U.pack_lut3(codes, qmap, g, dense=dense))
+        y, _ = U.run_lut3(packed, N, K, xbits, dense=dense)
         r = U.grade_lut3(y, xbits, codes, qmap, g, K, cols=cols)
     U.note("  %s" % r)
     assert r.ok, str(r)

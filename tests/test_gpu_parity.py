@@ -8,7 +8,9 @@
 * integer-exact inputs: the GPU result equals the exact integer rounded to BF16;
 * invariants: power-of-two scale linearity, M=32 = two M=16 halves, GEMV rows =
   M=1 calls, MFMA rows = the M=16 call, determinism over repeats, strides and
-  canaries, workspace left zeroed, pack determinism.
+  canaries, workspace left zeroed, pack determinism;
+* the dense 3-bit LUT layout passes every LUT test and gives the nibble
+  layout's GEMM bits exactly.
 """
 import numpy as np
 import pytest
@@ -48,10 +50,11 @@ def test_unpack_fp8_every_code_bit_exact():
     assert np.array_equal(g32[~nan], ref[~nan]) and np.array_equal(np.signbit(g32[~nan]), np.signbit(ref[~nan]))
 
 
-def test_unpack_lut3_bit_exact_including_subnormal_products():
+@pytest.mark.parametrize("dense", [False, True], ids=["nibble", "dense"])
+def test_unpack_lut3_bit_exact_including_subnormal_products(dense):
     wq = U.wqmod()
     N, K = 48, 512                       # 3 tiles: a ragged column group for 4-tile groups
-    U.note("unpack lut3 %dx%d" % (N, K))
+    U.note("unpack lut3 %dx%d dense=%d" % (N, K, dense))
     rng = np.random.Generator(np.random.PCG64(5))
     codes = rng.integers(0, 8, size=(N, K), dtype=np.uint8)
     codes[0, :8] = np.arange(8)
@@ -59,9 +62,9 @@ def test_unpack_lut3_bit_exact_including_subnormal_products():
     qmap[2] = np.float16(0.0)
     g = (rng.uniform(0.5, 1.0, size=(N, K // 128)) * np.ldexp(1.0, rng.integers(-20, 3, size=(N, K // 128))))
     g = g.astype(np.float16)
-    packed = U.pack_lut3(codes, qmap.view(np.uint16), g.view(np.uint16))
+    packed = U.pack_lut3(codes, qmap.view(np.uint16), g.view(np.uint16), dense=dense)
     out = torch.empty((N, K), dtype=torch.float16, device=U.DEV)
-    wq.wq_unpack_lut3(packed, N, K, out)
+    (wq.wq_unpack_lut3_dense if dense else wq.wq_unpack_lut3)(packed, N, K, out)
     torch.cuda.synchronize()
     ref = oracle.f16_rne(oracle.dequant_lut3(codes, qmap.view(np.uint16), g.view(np.uint16)))
     got = U.bits_of(out)
@@ -81,16 +84,26 @@ def test_pack_is_deterministic_and_stride_free():
     p1 = U.pack_lut3(c, q, g).cpu().numpy()
     p2 = U.pack_lut3(c, q, g).cpu().numpy()
     assert np.array_equal(p1, p2)
+    d1 = U.pack_lut3(c, q, g, dense=True).cpu().numpy()
+    d2 = U.pack_lut3(c, q, g, dense=True).cpu().numpy()
+    assert np.array_equal(d1, d2)
+    # the two layouts share everything after the codes: scales, map, status
+    assert d1.size == p1.size - 80 * 384 // 8
+    assert np.array_equal(d1[80 * 384 * 3 // 8:], p1[80 * 384 // 2:])
 
 
-def test_pack_lut3_rejects_code_above_7():
+@pytest.mark.parametrize("dense", [False, True], ids=["nibble", "dense"])
+def test_pack_lut3_rejects_code_above_7(dense):
     wq = U.wqmod()
-    U.note("pack lut3 bad code")
+    U.note("pack lut3 bad code dense=%d" % dense)
     c, q, g = synth.lut3_weights(32, 256, 43)
-    c[17, 200] = 9
-    with pytest.raises(wq.WqError) as e:
-        U.pack_lut3(c, q, g)
-    assert e.value.status == 5
+    for bad in (8, 9, 255):               # 8: the 3-bit field itself is 0 -- still rejected
+        c2 = c.copy()
+        c2[17, 200] = bad
+        with pytest.raises(wq.WqError) as e:
+            U.pack_lut3(c2, q, g, dense=dense)
+        assert e.value.status == 5
+    U.pack_lut3(c, q, g, dense=dense)      # a valid matrix after a rejected one packs cleanly
 
 
 # ------------------------------------------------------------------- GEMM
@@ -118,15 +131,30 @@ LUT_SHAPES = [(48, 256), (272, 1024), (1024, 384), (528, 2048)]
 
 @pytest.mark.parametrize("N,K", LUT_SHAPES)
 @pytest.mark.parametrize("M", [1, 2, 4, 7, 16, 20, 32])
-def test_gemm_lut3_parity(N, K, M):
-    U.note("lut3 parity N=%d K=%d M=%d" % (N, K, M))
+@pytest.mark.parametrize("dense", [False, True], ids=["nibble", "dense"])
+def test_gemm_lut3_parity(N, K, M, dense):
+    U.note("lut3 parity N=%d K=%d M=%d dense=%d" % (N, K, M, dense))
     c, q, g = synth.lut3_weights(N, K, 300 + N + K)
     xbits = synth.x_f16(M, K, 400 + M)
-    packed = U.pack_lut3(c, q, g)
-    y, _ = U.run_lut3(packed, N, K, xbits)
+    packed = U.pack_lut3(c, q, g, dense=dense)
+    y, _ = U.run_lut3(packed, N, K, xbits, dense=dense)
     r = U.grade_lut3(y, xbits, c, q, g, K)
     assert r.ok, str(r)
     assert r.rel_rms < 4e-3, r
+
+
+@pytest.mark.parametrize("N,K", [(48, 256), (528, 2048), (1024, 1152)])
+def test_dense_lut3_gives_the_nibble_bits(N, K):
+    """The two storage layouts feed the same decode and the same arithmetic, so
+    the GEMM outputs agree bit for bit for every M (both 16-row halves too)."""
+    U.note("lut3 dense == nibble N=%d K=%d" % (N, K))
+    c, q, g = synth.lut3_weights(N, K, 900 + N)
+    pn, pd = U.pack_lut3(c, q, g), U.pack_lut3(c, q, g, dense=True)
+    x32 = synth.x_f16(32, K, 901)
+    for M in (1, 3, 8, 16, 17, 32):
+        yn, _ = U.run_lut3(pn, N, K, x32[:M])
+        yd, _ = U.run_lut3(pd, N, K, x32[:M], dense=True)
+        assert np.array_equal(yn, yd), M
 
 
 def test_integer_exact_results_are_exact():
@@ -149,8 +177,9 @@ def test_integer_exact_results_are_exact():
     g = np.ones((N, K // 128), dtype=np.float16).view(np.uint16)
     xh = xi.astype(np.float16).view(np.uint16)
     exact_l = oracle.f16_rne((xi @ (ci.astype(np.int64) - 4).T).astype(np.float64))
-    yl, _ = U.run_lut3(U.pack_lut3(ci, qmap, g), N, K, xh)
-    assert np.array_equal(yl, exact_l)
+    for dense in (False, True):
+        yl, _ = U.run_lut3(U.pack_lut3(ci, qmap, g, dense=dense), N, K, xh, dense=dense)
+        assert np.array_equal(yl, exact_l), dense
 
 
 def test_invariants_fp8():
@@ -188,8 +217,9 @@ def test_invariants_fp8():
         assert np.array_equal(yr, ya if path == MFMA else np.vstack(ones[:4])), i
 
 
-def test_invariants_lut3():
-    U.note("invariants lut3")
+@pytest.mark.parametrize("dense", [False, True], ids=["nibble", "dense"])
+def test_invariants_lut3(dense):
+    U.note("invariants lut3 dense=%d" % dense)
     N, K = 528, 1024
     c, q, g = synth.lut3_weights(N, K, 47)
     # doubling the group scales doubles every dequantised weight exactly only
@@ -199,10 +229,10 @@ def test_invariants_lut3():
     assert (np.abs(q.view(np.float16).astype(np.float64)).min() * g.view(np.float16).astype(np.float64).min()
             >= 2.0 ** -14)
     x32 = synth.x_f16(32, K, 48)
-    packed = U.pack_lut3(c, q, g)
+    packed = U.pack_lut3(c, q, g, dense=dense)
     g2 = (g.view(np.float16).astype(np.float32) * 2).astype(np.float16).view(np.uint16)
-    y32, _ = U.run_lut3(packed, N, K, x32)
-    y32b, _ = U.run_lut3(U.pack_lut3(c, q, g2), N, K, x32)
+    y32, _ = U.run_lut3(packed, N, K, x32, dense=dense)
+    y32b, _ = U.run_lut3(U.pack_lut3(c, q, g2, dense=dense), N, K, x32, dense=dense)
     v1, v2 = oracle.f16_value(y32), oracle.f16_value(y32b)
     # exact where the FP16 output is normal; an output that cancelled into the
     # FP16 subnormal range is rounded on a fixed 2^-24 grid, so there doubling
@@ -210,16 +240,16 @@ def test_invariants_lut3():
     normal = np.abs(v1) >= 2.0 ** -14
     assert np.array_equal(v2[normal], 2 * v1[normal])
     assert np.all(np.abs(v2[~normal] - 2 * v1[~normal]) <= 2.0 ** -24)
-    ya, _ = U.run_lut3(packed, N, K, x32[:16])
-    yb, _ = U.run_lut3(packed, N, K, x32[16:])
+    ya, _ = U.run_lut3(packed, N, K, x32[:16], dense=dense)
+    yb, _ = U.run_lut3(packed, N, K, x32[16:], dense=dense)
     assert np.array_equal(np.vstack([ya, yb]), y32)
     for M in (1, 2, 7, 15):
-        yM, _ = U.run_lut3(packed, N, K, x32[:M])
+        yM, _ = U.run_lut3(packed, N, K, x32[:M], dense=dense)
         assert np.array_equal(yM, ya[:M]), M
     wq = U.wqmod()
-    ws = wq.workspace(wq.WQ_FMT_LUT3, N, K, U.DEV)
+    ws = wq.workspace(wq.WQ_FMT_LUT3_DENSE if dense else wq.WQ_FMT_LUT3, N, K, U.DEV)
     for i in range(20):
-        yr, _ = U.run_lut3(packed, N, K, x32[:16], ws=ws)
+        yr, _ = U.run_lut3(packed, N, K, x32[:16], ws=ws, dense=dense)
         assert np.array_equal(yr, ya), i
 
 
@@ -239,8 +269,9 @@ def test_strides_and_canaries():
     assert U.grade_fp8(y4, xs[:4], codes, scales, K).ok and np.all(full4[:, N:] == 0x7FAB)
     c, q, g = synth.lut3_weights(N, K, 51)
     xh = synth.x_f16(M, K, 52, ld=K + 8)
-    yl, fl = U.run_lut3(U.pack_lut3(c, q, g), N, K, xh, ldy=ldy, y_init=canary)
-    assert U.grade_lut3(yl, xh, c, q, g, K).ok and np.all(fl[:, N:] == 0x7FAB)
+    for dense in (False, True):
+        yl, fl = U.run_lut3(U.pack_lut3(c, q, g, dense=dense), N, K, xh, ldy=ldy, y_init=canary, dense=dense)
+        assert U.grade_lut3(yl, xh, c, q, g, K).ok and np.all(fl[:, N:] == 0x7FAB), dense
 
 
 def test_zero_rows_and_zero_matrix():
@@ -293,11 +324,14 @@ def test_every_tiling_matches_oracle(nt, sn, split, tuning_reset):
     for N, K in ((48, 384), (272, 1152)):
         c, q, g = synth.lut3_weights(N, K, 700 + N)
         packed = U.pack_lut3(c, q, g)
+        packed_d = U.pack_lut3(c, q, g, dense=True)
         for M in (1, 7, 16, 24):
             xh = synth.x_f16(M, K, 800 + M)
             y, _ = U.run_lut3(packed, N, K, xh)
             r = U.grade_lut3(y, xh, c, q, g, K)
             assert r.ok, "lut3 N=%d K=%d M=%d: %s" % (N, K, M, r)
+            yd, _ = U.run_lut3(packed_d, N, K, xh, dense=True)
+            assert np.array_equal(yd, y), "lut3 dense N=%d K=%d M=%d" % (N, K, M)
 
 
 def test_hip_graph_replays_match_eager():
@@ -313,12 +347,15 @@ def test_hip_graph_replays_match_eager():
     y = torch.empty((M, N), dtype=torch.bfloat16, device=U.DEV)
     c, q, g = synth.lut3_weights(N, K, 92)
     pl = U.pack_lut3(c, q, g)
+    pd = U.pack_lut3(c, q, g, dense=True)
     xh = U.t_u16(synth.x_f16(M, K, 93), torch.float16)
     yl = torch.empty((M, N), dtype=torch.float16, device=U.DEV)
+    yd = torch.empty((M, N), dtype=torch.float16, device=U.DEV)
     wq.wq_gemm_fp8_block(packed, N, K, x, y, M)
     wq.wq_gemm_lut3(pl, N, K, xh, yl, M)
+    wq.wq_gemm_lut3_dense(pd, N, K, xh, yd, M)
     torch.cuda.synchronize()
-    ref, refl = y.clone(), yl.clone()
+    ref, refl, refd = y.clone(), yl.clone(), yd.clone()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
@@ -326,13 +363,16 @@ def test_hip_graph_replays_match_eager():
         with torch.cuda.graph(graph, stream=s):
             wq.wq_gemm_fp8_block(packed, N, K, x, y, M)
             wq.wq_gemm_lut3(pl, N, K, xh, yl, M)
+            wq.wq_gemm_lut3_dense(pd, N, K, xh, yd, M)
     torch.cuda.current_stream().wait_stream(s)
     for rep in range(4):
         y.fill_(7.0)
         yl.fill_(7.0)
+        yd.fill_(7.0)
         wq.wq_gemm_fp8_block_path(packed, N, K, x[:3], y[:3], 3, None, GEMV)   # eager work in between
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), rep
         assert torch.equal(yl.view(torch.int16), refl.view(torch.int16)), rep
+        assert torch.equal(yd.view(torch.int16), refd.view(torch.int16)), rep

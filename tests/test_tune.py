@@ -4,14 +4,14 @@ import pytest
 
 def test_candidates_respect_the_kernel_limits():
     from weight_only_quantized_fp8_amd import tune
-    for fmt in ("fp8", "lut3"):
+    for fmt in ("fp8", "lut3", "lut3d"):
         for gemv in ((False, True) if fmt == "fp8" else (False,)):
             c = tune.candidates(fmt, gemv)
             assert c and len(set(c)) == len(c)
             for nt, sn, split in c:
                 assert 1 <= sn <= 8 and split % sn == 0 and split // sn <= 4
                 assert nt in ((1,) if gemv else (1, 2))
-                assert split <= 8 or gemv or (fmt == "lut3" and nt == 1 and sn >= 4)
+                assert split <= 8 or gemv or (fmt != "fp8" and nt == 1 and sn >= 4)
 
 
 @pytest.mark.gpu
@@ -19,7 +19,8 @@ def test_candidates_respect_the_kernel_limits():
     ["--fmt", "fp8", "--N", "384", "--K", "1152", "--M", "16", "--top", "3"],
     ["--fmt", "fp8", "--N", "384", "--K", "1152", "--M", "2", "--path", "gemv", "--top", "3"],
     ["--fmt", "lut3", "--N", "272", "--K", "1152", "--M", "24", "--top", "3"],
-], ids=["fp8-mfma", "fp8-gemv", "lut3-m24"])
+    ["--fmt", "lut3d", "--N", "272", "--K", "1152", "--M", "7", "--top", "3"],
+], ids=["fp8-mfma", "fp8-gemv", "lut3-m24", "lut3d-m7"])
 def test_every_candidate_passes_the_exactness_gate(args, capsys):
     from weight_only_quantized_fp8_amd import tune
     assert tune.main(args) == 0

@@ -16,7 +16,7 @@ namespace {
 
 using wq::GemmArgs;
 
-constexpr int kPackedFormatVersion = 2;
+constexpr int kPackedFormatVersion = 3;
 constexpr int kMaxDevices = 64;
 
 // ----------------------------------------------------------------- options
@@ -132,6 +132,7 @@ constexpr TableEntry kTable[] = {
     {wq::KIND_MFMA_FP8, 1024, 5120, 1, 1, 4},     // attention K, V
     {wq::KIND_MFMA_FP8, 5120, 6144, 1, 2, 8},     // attention output
     {wq::KIND_MFMA_LUT, 28672, 8192, 1, 7, 7},    // 3-bit LUT 28672x8192
+    {wq::KIND_MFMA_LUT3D, 28672, 8192, 1, 7, 7},  // 3-bit LUT 28672x8192, dense codes
     {wq::KIND_GEMV_FP8, 6144, 5120, 1, 2, 8},     // attention Q (other GEMV shapes: the FP8 rows)
     {wq::KIND_GEMV_FP8, 1024, 5120, 1, 2, 8},     // attention K, V
 };
@@ -215,8 +216,14 @@ bool shape_ok(int fmt, int64_t N, int64_t K)
     if (N <= 0 || K <= 0 || K % 128) return false;
     if (N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return false;
     if (fmt == WQ_FMT_FP8_BLOCK) return N % 128 == 0;
-    if (fmt == WQ_FMT_LUT3) return N % 16 == 0;
+    if (fmt == WQ_FMT_LUT3 || fmt == WQ_FMT_LUT3_DENSE) return N % 16 == 0;
     return false;
+}
+
+// Code bytes of a packed LUT matrix: 4 bits a code (nibbles) or 3 (dense).
+size_t lut3_code_bytes(int fmt, int64_t N, int64_t K)
+{
+    return fmt == WQ_FMT_LUT3_DENSE ? (size_t)(N * K / 8 * 3) : (size_t)(N * K / 2);
 }
 
 // Group scales of the packed LUT matrix: per tile and run of 8 K blocks, 16
@@ -225,7 +232,7 @@ size_t lut3_scale_bytes(int64_t N, int64_t K) { return (size_t)(N / 16) * (size_
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Shared front end of the two GEMMs.
+// Shared front end of the GEMMs.
 wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                       uint16_t* y, int64_t ldy, int64_t M, void* workspace, size_t workspace_bytes, int path,
                       void* stream)
@@ -244,9 +251,9 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
 
     const Options& o = options();
     int kind;
-    if (fmt == WQ_FMT_LUT3) {
+    if (fmt != WQ_FMT_FP8_BLOCK) {
         if (path == WQ_PATH_GEMV) return WQ_ERR_PATH;
-        kind = wq::KIND_MFMA_LUT;
+        kind = fmt == WQ_FMT_LUT3_DENSE ? wq::KIND_MFMA_LUT3D : wq::KIND_MFMA_LUT;
     } else {
         int eff = path == WQ_PATH_AUTO ? o.force_path : path;
         if (eff == WQ_PATH_AUTO) eff = M <= kGemvAutoMaxM ? WQ_PATH_GEMV : WQ_PATH_MFMA;
@@ -270,8 +277,9 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
         a.scales = base + N * K;
         a.qmap = nullptr;
     } else {
-        a.scales = base + N * K / 2;
-        a.qmap = reinterpret_cast<const uint16_t*>(base + N * K / 2 + lut3_scale_bytes(N, K));
+        const size_t cb = lut3_code_bytes(fmt, N, K);
+        a.scales = base + cb;
+        a.qmap = reinterpret_cast<const uint16_t*>(base + cb + lut3_scale_bytes(N, K));
     }
     a.N = (int)N;
     a.KB = p.KB;
@@ -296,6 +304,44 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
         if (e != hipSuccess) return WQ_ERR_HIP;
     }
     return WQ_OK;
+}
+
+// Shared body of the two LUT packers (nibble and dense code layouts).
+wq_status pack_lut3_common(int fmt, const uint8_t* codes, int64_t ldc, const uint16_t* qmap, const uint16_t* scales,
+                           int64_t N, int64_t K, void* packed, void* hip_stream)
+{
+    if (!shape_ok(fmt, N, K)) return WQ_ERR_SHAPE;
+    if (!codes || !qmap || !scales || !packed) return WQ_ERR_NULL;
+    if (ldc < K) return WQ_ERR_LD;
+    if (!aligned16(packed) || (reinterpret_cast<uintptr_t>(scales) & 1) || (reinterpret_cast<uintptr_t>(qmap) & 1))
+        return WQ_ERR_ALIGN;
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    uint8_t* pk = static_cast<uint8_t*>(packed);
+    uint32_t* status = reinterpret_cast<uint32_t*>(pk + lut3_code_bytes(fmt, N, K) + lut3_scale_bytes(N, K) + 16);
+    if (wq::launch_pack_lut3(codes, ldc, qmap, scales, N, K, pk, status, fmt == WQ_FMT_LUT3_DENSE, s) != hipSuccess)
+        return WQ_ERR_HIP;
+    uint32_t host_status = 0;
+    if (hipMemcpyAsync(&host_status, status, sizeof(host_status), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return WQ_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return WQ_ERR_HIP;
+    return host_status ? WQ_ERR_CODE : WQ_OK;
+}
+
+wq_status unpack_lut3_common(int fmt, const void* packed, int64_t N, int64_t K, uint16_t* w_f16, void* hip_stream)
+{
+    if (!shape_ok(fmt, N, K)) return WQ_ERR_SHAPE;
+    if (!packed || !w_f16) return WQ_ERR_NULL;
+    if (!aligned16(packed) || !aligned16(w_f16)) return WQ_ERR_ALIGN;
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    return wq::launch_unpack_lut3(static_cast<const uint8_t*>(packed), N, K, w_f16, fmt == WQ_FMT_LUT3_DENSE,
+                                  static_cast<hipStream_t>(hip_stream)) == hipSuccess
+               ? WQ_OK
+               : WQ_ERR_HIP;
 }
 
 }  // namespace
@@ -345,7 +391,13 @@ size_t wq_fp8_block_packed_bytes(int64_t N, int64_t K)
 size_t wq_lut3_packed_bytes(int64_t N, int64_t K)
 {
     if (!shape_ok(WQ_FMT_LUT3, N, K)) return 0;
-    return (size_t)(N * K / 2) + lut3_scale_bytes(N, K) + 32;
+    return lut3_code_bytes(WQ_FMT_LUT3, N, K) + lut3_scale_bytes(N, K) + 32;
+}
+
+size_t wq_lut3_dense_packed_bytes(int64_t N, int64_t K)
+{
+    if (!shape_ok(WQ_FMT_LUT3_DENSE, N, K)) return 0;
+    return lut3_code_bytes(WQ_FMT_LUT3_DENSE, N, K) + lut3_scale_bytes(N, K) + 32;
 }
 
 wq_status wq_pack_fp8_block(const uint8_t* w_e4m3, int64_t ldw, const float* scales, int64_t N, int64_t K,
@@ -381,23 +433,13 @@ wq_status wq_gemm_fp8_block_path(const void* packed, int64_t N, int64_t K, const
 wq_status wq_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* qmap, const uint16_t* scales, int64_t N,
                        int64_t K, void* packed, void* hip_stream)
 {
-    if (!shape_ok(WQ_FMT_LUT3, N, K)) return WQ_ERR_SHAPE;
-    if (!codes || !qmap || !scales || !packed) return WQ_ERR_NULL;
-    if (ldc < K) return WQ_ERR_LD;
-    if (!aligned16(packed) || (reinterpret_cast<uintptr_t>(scales) & 1) || (reinterpret_cast<uintptr_t>(qmap) & 1))
-        return WQ_ERR_ALIGN;
-    DevInfo dev;
-    wq_status st = current_device(&dev);
-    if (st != WQ_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    uint8_t* pk = static_cast<uint8_t*>(packed);
-    uint32_t* status = reinterpret_cast<uint32_t*>(pk + N * K / 2 + lut3_scale_bytes(N, K) + 16);
-    if (wq::launch_pack_lut3(codes, ldc, qmap, scales, N, K, pk, status, s) != hipSuccess) return WQ_ERR_HIP;
-    uint32_t host_status = 0;
-    if (hipMemcpyAsync(&host_status, status, sizeof(host_status), hipMemcpyDeviceToHost, s) != hipSuccess)
-        return WQ_ERR_HIP;
-    if (hipStreamSynchronize(s) != hipSuccess) return WQ_ERR_HIP;
-    return host_status ? WQ_ERR_CODE : WQ_OK;
+    return pack_lut3_common(WQ_FMT_LUT3, codes, ldc, qmap, scales, N, K, packed, hip_stream);
+}
+
+wq_status wq_pack_lut3_dense(const uint8_t* codes, int64_t ldc, const uint16_t* qmap, const uint16_t* scales,
+                             int64_t N, int64_t K, void* packed, void* hip_stream)
+{
+    return pack_lut3_common(WQ_FMT_LUT3_DENSE, codes, ldc, qmap, scales, N, K, packed, hip_stream);
 }
 
 wq_status wq_gemm_lut3(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, uint16_t* y,
@@ -405,6 +447,13 @@ wq_status wq_gemm_lut3(const void* packed, int64_t N, int64_t K, const uint16_t*
 {
     return gemm_common(WQ_FMT_LUT3, packed, N, K, x, ldx, y, ldy, M, workspace, workspace_bytes, WQ_PATH_AUTO,
                        hip_stream);
+}
+
+wq_status wq_gemm_lut3_dense(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, uint16_t* y,
+                             int64_t ldy, int64_t M, void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    return gemm_common(WQ_FMT_LUT3_DENSE, packed, N, K, x, ldx, y, ldy, M, workspace, workspace_bytes,
+                       WQ_PATH_AUTO, hip_stream);
 }
 
 size_t wq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K)
@@ -448,16 +497,12 @@ wq_status wq_unpack_fp8_block_f32(const void* packed, int64_t N, int64_t K, floa
 
 wq_status wq_unpack_lut3(const void* packed, int64_t N, int64_t K, uint16_t* w_f16, void* hip_stream)
 {
-    if (!shape_ok(WQ_FMT_LUT3, N, K)) return WQ_ERR_SHAPE;
-    if (!packed || !w_f16) return WQ_ERR_NULL;
-    if (!aligned16(packed) || !aligned16(w_f16)) return WQ_ERR_ALIGN;
-    DevInfo dev;
-    wq_status st = current_device(&dev);
-    if (st != WQ_OK) return st;
-    return wq::launch_unpack_lut3(static_cast<const uint8_t*>(packed), N, K, w_f16,
-                                  static_cast<hipStream_t>(hip_stream)) == hipSuccess
-               ? WQ_OK
-               : WQ_ERR_HIP;
+    return unpack_lut3_common(WQ_FMT_LUT3, packed, N, K, w_f16, hip_stream);
+}
+
+wq_status wq_unpack_lut3_dense(const void* packed, int64_t N, int64_t K, uint16_t* w_f16, void* hip_stream)
+{
+    return unpack_lut3_common(WQ_FMT_LUT3_DENSE, packed, N, K, w_f16, hip_stream);
 }
 
 }  // extern "C"

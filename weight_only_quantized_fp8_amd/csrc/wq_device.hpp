@@ -104,6 +104,20 @@ __device__ __forceinline__ f16x8_t lut_decode8(uint32_t word, const LutPlanes& p
     return __builtin_bit_cast(f16x8_t, r);
 }
 
+// Dense 3-bit layout: a lane's 32 codes of one K block sit in three dwords.
+// Dwords 0..2 carry MFMA steps 0..2 in the nibble positions above (bits 0-2
+// and 4-6 of each byte); the codes of step 3 are spread over the spare bits:
+// bit i of code e=b sits at bit 3 of byte b of dword i, and bit i of code
+// e=b+4 at bit 7.  This gathers them into one word in the nibble layout (bits
+// 3 and 7 of the result are junk; lut_decode8 ignores them): 3 shifts and 2
+// bit-field inserts.
+__device__ __forceinline__ uint32_t lut3d_step3_word(uint32_t d0, uint32_t d1, uint32_t d2)
+{
+    const uint32_t a = d0 >> 3, b = d1 >> 2, c = d2 >> 1;
+    const uint32_t ab = (a & 0x11111111u) | (b & ~0x11111111u);     // bits 0, 4 from d0; 1, 5 from d1
+    return (ab & 0x33333333u) | (c & ~0x33333333u);                 // bits 2, 6 from d2
+}
+
 // ------------------------------------------------------------------ MFMA
 // D(16x16) += A(16x32) * B(32x16).  Lane l supplies A row (l % 16) and B
 // column (l % 16), eight K values each at K group (l / 16); lane l receives
@@ -163,6 +177,15 @@ __device__ __forceinline__ uint4 buf_load_stream16(buf_t r, uint32_t voff, uint3
 {
     const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
     return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// 12 bytes (three dwords), non-temporal like buf_load_stream16; the fourth
+// component of the result is zero.
+__device__ __forceinline__ uint4 buf_load_stream12(buf_t r, uint32_t voff, uint32_t soff)
+{
+    typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+    const u32x3_t v = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 2));
+    return make_uint4(v[0], v[1], v[2], 0u);
 }
 
 __device__ __forceinline__ uint4 buf_load16(buf_t r, uint32_t voff, uint32_t soff)

@@ -20,7 +20,10 @@ enum Kind : int {
     KIND_MFMA_FP8 = 0,   // 16-row BF16 MFMA tile, FP8 block-scaled weights
     KIND_MFMA_LUT = 1,   // 16-row FP16 MFMA tile, 3-bit LUT weights
     KIND_GEMV_FP8 = 2,   // strict-K-order FP32 GEMV, M <= 4, FP8 weights, one tile per wave
+    KIND_MFMA_LUT3D = 3, // 16-row FP16 MFMA tile, 3-bit LUT weights stored densely (3 bits a code)
 };
+
+constexpr bool is_lut_kind(int kind) { return kind == KIND_MFMA_LUT || kind == KIND_MFMA_LUT3D; }
 
 // K blocks of activations staged per chunk (the K group synchronises once
 // per chunk).
@@ -50,7 +53,7 @@ constexpr int x_pieces_per_lane(int kind, int sn)
 // has SIMDs.
 constexpr int max_split_xpl(int kind, int nt, int xpl)
 {
-    return ((kind == KIND_MFMA_LUT && nt == 1 && xpl <= 4) || kind == KIND_GEMV_FP8) ? 16 : 8;
+    return ((is_lut_kind(kind) && nt == 1 && xpl <= 4) || kind == KIND_GEMV_FP8) ? 16 : 8;
 }
 constexpr int max_split(int kind, int nt, int sn) { return max_split_xpl(kind, nt, x_pieces_per_lane(kind, sn)); }
 
@@ -67,7 +70,7 @@ constexpr bool split_ok(int kind, int nt, int sn, int split)
 // group (NT tiles of 16 output columns); its S waves split the K blocks.
 struct GemmArgs {
     const uint8_t* codes;     // packed code units
-    const void* scales;       // FP8: float [N/128][KB]; LUT: half [n_tiles][KB][16]
+    const void* scales;       // FP8: float [N/128][KB]; LUT: half [n_tiles][KB/8][16][8]
     const uint16_t* qmap;     // LUT: 8 FP16 map entries (4-byte aligned)
     const uint16_t* x;        // activations [rows][ldx]
     int64_t ldx;
@@ -87,12 +90,13 @@ hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int s
 
 hipError_t launch_pack_fp8(const uint8_t* w, int64_t ldw, const float* scales, int64_t N,
                            int64_t K, uint8_t* packed, hipStream_t stream);
+// dense: the 3-bit-per-code layout (N*K*3/8 code bytes) instead of nibbles
 hipError_t launch_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* qmap,
                             const uint16_t* scales, int64_t N, int64_t K, uint8_t* packed,
-                            uint32_t* status, hipStream_t stream);
+                            uint32_t* status, bool dense, hipStream_t stream);
 hipError_t launch_unpack_fp8(const uint8_t* packed, int64_t N, int64_t K, void* out,
                              bool f32_out, hipStream_t stream);
 hipError_t launch_unpack_lut3(const uint8_t* packed, int64_t N, int64_t K, uint16_t* out,
-                              hipStream_t stream);
+                              bool dense, hipStream_t stream);
 
 }  // namespace wq

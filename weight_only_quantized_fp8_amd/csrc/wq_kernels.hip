@@ -1,7 +1,7 @@
 // gfx950 kernels of libwq: the decode GEMM (MFMA tile and strict-order GEMV)
 // for FP8 block-scaled and 3-bit LUT weights, and the pack / unpack kernels.
 //
-// Packed layouts (version 2).  A "unit" is 16 rows of W (one MFMA tile along
+// Packed layouts (version 3).  A "unit" is 16 rows of W (one MFMA tile along
 // N) by one 128-wide K block, stored contiguously, units ordered (tile, kb)
 // with kb fastest.  Inside a unit every 16-byte piece is what one lane loads
 // (the FLUTE PR "Add optimized_w3", "Core contributions" item 2: one
@@ -21,6 +21,14 @@
 //         with zeros), so one 16-byte load brings a row's scales for 8 K
 //         blocks; then the 8 map entries (FP16), then a 16-byte pack-status
 //         word.
+//   LUT3D the dense 3-bit form of LUT3: unit = 768 B, lane l holds the same 32
+//         codes in 3 dwords (12 bytes at 12l).  Dwords s = 0..2 carry step s
+//         exactly as LUT3 does; the 8 codes of step 3 fill the spare bits 3
+//         and 7 of every byte: bit i of code e = b at bit 3 of byte b of dword
+//         i, and of code e = b + 4 at bit 7 (the byte-plane idea of FLUTE's own
+//         3-bit storage, named in the FLUTE PR's "Why this exists", traded for
+//         5 more ALU operations per 32 codes).  Scales, map and status word
+//         follow as in LUT3.
 //
 // GEMM schedule.  One work-group owns one column group (SN column-waves of
 // NT tiles of 16 output columns) over the whole of K.  Its waves form SK
@@ -317,10 +325,11 @@ struct MfmaFp8 : Fp8Stream<NT> {
 // Group scales come as one 16-byte load per row and run of 8 K blocks, issued
 // with the weights of the run's first unit; K-group ranges start at multiples
 // of 8 blocks, so a unit's place in its run is its (compile-time) position in
-// the unrolled loop.
-template <int NT, int MT>
+// the unrolled loop.  DENSE selects the 3-bit-per-code unit layout.
+template <int NT, int MT, bool DENSE>
 struct MfmaLut {
-    static constexpr int KIND = KIND_MFMA_LUT;
+    static constexpr int KIND = DENSE ? KIND_MFMA_LUT3D : KIND_MFMA_LUT;
+    static constexpr uint32_t kUnitBytes = DENSE ? 768u : 1024u;
     static constexpr int NTILES = NT;
     static constexpr int ROWS = 16 * MT;
     static constexpr int KALIGN = 8;      // K blocks per group-scale load
@@ -344,7 +353,7 @@ struct MfmaLut {
     {
         ntiles = max(0, min(NT, a.n_tiles - tile0));
         const int t0 = min(tile0, a.n_tiles);
-        rw = make_buf(a.codes + (((int64_t)t0 * a.KB) << 10), (uint32_t)(ntiles * a.KB) << 10);
+        rw = make_buf(a.codes + (int64_t)t0 * a.KB * kUnitBytes, (uint32_t)(ntiles * a.KB) * kUnitBytes);
         rg = make_buf(reinterpret_cast<const uint8_t*>(a.scales) + (int64_t)t0 * KB8 * 256,
                       (uint32_t)(ntiles * KB8) * 256u);
         rnull = make_buf(a.codes, 0);
@@ -365,7 +374,9 @@ struct MfmaLut {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const bool ok = valid && t < ntiles;
-            r.w[t] = buf_load_stream16(ok ? rw : rnull, lane * 16, (uint32_t)(t * KB + kb) << 10);
+            const uint32_t soff = (uint32_t)(t * KB + kb) * kUnitBytes;
+            r.w[t] = DENSE ? buf_load_stream12(ok ? rw : rnull, lane * 12, soff)
+                           : buf_load_stream16(ok ? rw : rnull, lane * 16, soff);
             if ((pos & 7) == 0)
                 r.gv[t] = buf_load16(ok ? rg : rnull, (lane & 15) * 16, (uint32_t)(t * KB8 + (kb >> 3)) * 256u);
         }
@@ -389,7 +400,8 @@ struct MfmaLut {
             const uint32_t gd = e < 2 ? gcur[t].x : e < 4 ? gcur[t].y : e < 6 ? gcur[t].z : gcur[t].w;
             const uint16_t gbits = (uint16_t)((e & 1) ? gd >> 16 : gd & 0xFFFFu);
             const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, gbits));
-            const uint32_t wd[4] = {r.w[t].x, r.w[t].y, r.w[t].z, r.w[t].w};
+            const uint32_t w3 = DENSE ? lut3d_step3_word(r.w[t].x, r.w[t].y, r.w[t].z) : r.w[t].w;
+            const uint32_t wd[4] = {r.w[t].x, r.w[t].y, r.w[t].z, w3};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const f16x8_t av = lut_decode8(wd[s], pl);
@@ -675,7 +687,7 @@ __global__ void clear_status_kernel(uint32_t* status) { status[threadIdx.x] = 0u
 
 __global__ void pack_lut3_kernel(const uint8_t* __restrict__ codes, int64_t ldc, const uint16_t* __restrict__ qmap,
                                  const uint16_t* __restrict__ scales, int64_t N, int64_t K,
-                                 uint8_t* __restrict__ packed, uint32_t* status)
+                                 uint8_t* __restrict__ packed, uint32_t* status, int dense)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t KB = K / 128;
@@ -699,10 +711,21 @@ __global__ void pack_lut3_kernel(const uint8_t* __restrict__ codes, int64_t ldc,
             }
             d[s] = word;
         }
-        reinterpret_cast<uint4*>(packed)[idx] = make_uint4(d[0], d[1], d[2], d[3]);
+        if (dense) {
+            // step 3's code bit i goes to bits 3 and 7 of dword i
+            uint32_t o[3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) o[i] = (d[i] & 0x77777777u) | (((d[3] >> i) & 0x11111111u) << 3);
+            uint32_t* dst = reinterpret_cast<uint32_t*>(packed) + idx * 3;
+            dst[0] = o[0];
+            dst[1] = o[1];
+            dst[2] = o[2];
+        } else {
+            reinterpret_cast<uint4*>(packed)[idx] = make_uint4(d[0], d[1], d[2], d[3]);
+        }
         if (bad) atomicOr(status, 1u);
     }
-    uint16_t* sc_out = reinterpret_cast<uint16_t*>(packed + N * K / 2);
+    uint16_t* sc_out = reinterpret_cast<uint16_t*>(packed + (dense ? N * K / 8 * 3 : N * K / 2));
     const int64_t KB8 = (KB + 7) / 8;
     if (idx < n_tiles * KB8 * 128) {
         const int64_t e = idx & 7, r = (idx >> 3) & 15, grp = idx >> 7;
@@ -744,7 +767,7 @@ __global__ void unpack_fp8_kernel(const uint8_t* __restrict__ packed, int64_t N,
     }
 }
 
-__global__ void unpack_lut3_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K, uint16_t* out)
+__global__ void unpack_lut3_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K, uint16_t* out, int dense)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= N * K / 32) return;
@@ -755,13 +778,25 @@ __global__ void unpack_lut3_kernel(const uint8_t* __restrict__ packed, int64_t N
     const int64_t t = unit / KB, kb = unit - t * KB;
     const int64_t n = t * 16 + (l & 15);
     const int64_t KB8 = (KB + 7) / 8;
-    const uint16_t* sc = reinterpret_cast<const uint16_t*>(packed + N * K / 2);
+    const uint16_t* sc = reinterpret_cast<const uint16_t*>(packed + (dense ? N * K / 8 * 3 : N * K / 2));
     const uint32_t* qm = reinterpret_cast<const uint32_t*>(sc + n_tiles * KB8 * 128);
     const uint32_t q[4] = {qm[0], qm[1], qm[2], qm[3]};
     const uint16_t g = sc[((t * KB8 + kb / 8) * 16 + (l & 15)) * 8 + kb % 8];
     const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, g));
-    const uint4 w = reinterpret_cast<const uint4*>(packed)[idx];
-    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+    uint32_t d[4];
+    if (dense) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(packed) + idx * 3;
+        d[0] = src[0];
+        d[1] = src[1];
+        d[2] = src[2];
+        d[3] = lut3d_step3_word(d[0], d[1], d[2]);
+    } else {
+        const uint4 w = reinterpret_cast<const uint4*>(packed)[idx];
+        d[0] = w.x;
+        d[1] = w.y;
+        d[2] = w.z;
+        d[3] = w.w;
+    }
     uint16_t* o = out + n * K + kb * 128 + (l >> 4) * 8;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -790,7 +825,8 @@ template <int NT, int MT, int XPL>
 static hipError_t launch_mfma(int kind, const GemmArgs& a, int split, hipStream_t s)
 {
     if (kind == KIND_MFMA_FP8) return launch_one<MfmaFp8<NT, MT>, kDepthMfmaFp8, XPL, false>(a, split, s);
-    return launch_one<MfmaLut<NT, MT>, kDepthMfmaLut, XPL, true>(a, split, s);
+    if (kind == KIND_MFMA_LUT3D) return launch_one<MfmaLut<NT, MT, true>, kDepthMfmaLut, XPL, true>(a, split, s);
+    return launch_one<MfmaLut<NT, MT, false>, kDepthMfmaLut, XPL, true>(a, split, s);
 }
 
 template <int NT, int MT>
@@ -830,7 +866,7 @@ hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int s
         default: return hipErrorInvalidValue;
         }
     }
-    if (kind != KIND_MFMA_FP8 && kind != KIND_MFMA_LUT) return hipErrorInvalidValue;
+    if (kind != KIND_MFMA_FP8 && !is_lut_kind(kind)) return hipErrorInvalidValue;
     if (a.rows > 16) {
         if (nt != 1 || a.rows > 32) return hipErrorInvalidValue;
         return launch_nt<1, 2>(kind, a, split, stream);
@@ -853,7 +889,7 @@ hipError_t launch_pack_fp8(const uint8_t* w, int64_t ldw, const float* scales, i
 }
 
 hipError_t launch_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* qmap, const uint16_t* scales,
-                            int64_t N, int64_t K, uint8_t* packed, uint32_t* status, hipStream_t stream)
+                            int64_t N, int64_t K, uint8_t* packed, uint32_t* status, bool dense, hipStream_t stream)
 {
     hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(4), 0, stream, status);
     hipError_t e = hipGetLastError();
@@ -861,7 +897,7 @@ hipError_t launch_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* q
     const int64_t n_scales = (N / 16) * ((K / 128 + 7) / 8) * 128;
     const int64_t n = N * K / 32 > n_scales ? N * K / 32 : n_scales;
     hipLaunchKernelGGL(pack_lut3_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, codes, ldc, qmap, scales, N, K,
-                       packed, status);
+                       packed, status, (int)dense);
     return hipGetLastError();
 }
 
@@ -872,9 +908,11 @@ hipError_t launch_unpack_fp8(const uint8_t* packed, int64_t N, int64_t K, void* 
     return hipGetLastError();
 }
 
-hipError_t launch_unpack_lut3(const uint8_t* packed, int64_t N, int64_t K, uint16_t* out, hipStream_t stream)
+hipError_t launch_unpack_lut3(const uint8_t* packed, int64_t N, int64_t K, uint16_t* out, bool dense,
+                              hipStream_t stream)
 {
-    hipLaunchKernelGGL(unpack_lut3_kernel, dim3(blocks_for(N * K / 32)), dim3(256), 0, stream, packed, N, K, out);
+    hipLaunchKernelGGL(unpack_lut3_kernel, dim3(blocks_for(N * K / 32)), dim3(256), 0, stream, packed, N, K, out,
+                       (int)dense);
     return hipGetLastError();
 }
 

@@ -57,12 +57,14 @@ def _inputs(fmt: str, N: int, K: int, M: int, dev: str, seed: int, path: int):
         codes = torch.randint(0, 8, (N, K), generator=g, dtype=torch.uint8)
         qmap = torch.sort(torch.randn(8, generator=g)).values.to(torch.float16)
         gs = (torch.rand(N, K // 128, generator=g) * 0.015 + 0.005).to(torch.float16)
-        packed = wq.pack_lut3(codes.to(dev), qmap.to(dev), gs.to(dev))
+        dense = fmt == "lut3d"
+        packed = (wq.pack_lut3_dense if dense else wq.pack_lut3)(codes.to(dev), qmap.to(dev), gs.to(dev))
         x = torch.randn(M, K, generator=g).to(torch.float16).to(dev)
         wh = torch.empty(N, K, dtype=torch.float16, device=dev)
-        wq.wq_unpack_lut3(packed, N, K, wh)
+        (wq.wq_unpack_lut3_dense if dense else wq.wq_unpack_lut3)(packed, N, K, wh)
         wd = wh.float()
-        call = lambda p, y: wq.wq_gemm_lut3(p, N, K, x, y, M)
+        gemm = wq.wq_gemm_lut3_dense if dense else wq.wq_gemm_lut3
+        call = lambda p, y: gemm(p, N, K, x, y, M)
         y = torch.empty(M, N, dtype=torch.float16, device=dev)
     ref = x.float() @ wd.t()
     floor = FLOOR_COEF * math.sqrt(K) * x.float().abs().max().item() * wd.abs().max().item()
@@ -103,7 +105,7 @@ def candidates(fmt: str, gemv: bool = False):
     for nt in ((1,) if gemv else (1, 2)):
         for sn in range(1, 9):
             pieces = math.ceil(16 / sn)
-            max_split = 16 if (gemv or (fmt == "lut3" and nt == 1 and pieces <= 4)) else 8
+            max_split = 16 if (gemv or (fmt in ("lut3", "lut3d") and nt == 1 and pieces <= 4)) else 8
             for sk in (1, 2, 3, 4):
                 if sn * sk <= max_split:
                     out.append((nt, sn, sn * sk))
@@ -112,7 +114,8 @@ def candidates(fmt: str, gemv: bool = False):
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--fmt", choices=("fp8", "lut3"), default="fp8")
+    ap.add_argument("--fmt", choices=("fp8", "lut3", "lut3d"), default="fp8",
+                    help="lut3d: the LUT format with codes stored at 3 bits each")
     ap.add_argument("--N", type=int, required=True)
     ap.add_argument("--K", type=int, required=True)
     ap.add_argument("--M", type=int, default=16)
@@ -153,7 +156,7 @@ def main(argv=None) -> int:
     if results:
         nt, sn, split = results[0][1]
         kind = ("wq::KIND_GEMV_FP8" if args.path == "gemv" else "wq::KIND_MFMA_FP8") if args.fmt == "fp8" \
-            else "wq::KIND_MFMA_LUT"
+            else ("wq::KIND_MFMA_LUT3D" if args.fmt == "lut3d" else "wq::KIND_MFMA_LUT")
         print("table row: {%s, %d, %d, %d, %d, %d}," % (kind, args.N, args.K, nt, sn, split))
     return 0 if results else 1
 

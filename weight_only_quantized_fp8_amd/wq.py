@@ -17,6 +17,8 @@ __all__ = [
     "wq_status_str", "wq_packed_format_version", "wq_set_tuning",
     "wq_fp8_block_packed_bytes", "wq_pack_fp8_block", "wq_gemm_fp8_block", "wq_gemm_fp8_block_path",
     "wq_lut3_packed_bytes", "wq_pack_lut3", "wq_gemm_lut3",
+    "WQ_FMT_LUT3_DENSE", "wq_lut3_dense_packed_bytes", "wq_pack_lut3_dense", "wq_gemm_lut3_dense",
+    "wq_unpack_lut3_dense", "pack_lut3_dense", "gemm_lut3_dense",
     "wq_gemm_workspace_bytes", "wq_unpack_fp8_block", "wq_unpack_fp8_block_f32", "wq_unpack_lut3",
     "workspace", "pack_fp8", "pack_lut3", "gemm_fp8", "gemm_lut3",
 ]
@@ -34,7 +36,7 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 WQ_OK = 0
-WQ_FMT_FP8_BLOCK, WQ_FMT_LUT3 = 0, 1
+WQ_FMT_FP8_BLOCK, WQ_FMT_LUT3, WQ_FMT_LUT3_DENSE = 0, 1, 2
 WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 
 _P, _I64, _SZ, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
@@ -49,6 +51,10 @@ _SIGS = {
     "wq_lut3_packed_bytes": (_SZ, [_I64, _I64]),
     "wq_pack_lut3": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _P]),
     "wq_gemm_lut3": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
+    "wq_lut3_dense_packed_bytes": (_SZ, [_I64, _I64]),
+    "wq_pack_lut3_dense": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _P]),
+    "wq_gemm_lut3_dense": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
+    "wq_unpack_lut3_dense": (_INT, [_P, _I64, _I64, _P, _P]),
     "wq_gemm_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
     "wq_unpack_fp8_block": (_INT, [_P, _I64, _I64, _P, _P]),
     "wq_unpack_fp8_block_f32": (_INT, [_P, _I64, _I64, _P, _P]),
@@ -120,6 +126,10 @@ def wq_lut3_packed_bytes(N: int, K: int) -> int:
     return lib.wq_lut3_packed_bytes(N, K)
 
 
+def wq_lut3_dense_packed_bytes(N: int, K: int) -> int:
+    return lib.wq_lut3_dense_packed_bytes(N, K)
+
+
 def wq_gemm_workspace_bytes(fmt: int, M: int, N: int, K: int) -> int:
     return lib.wq_gemm_workspace_bytes(fmt, M, N, K)
 
@@ -152,6 +162,16 @@ def wq_gemm_lut3(packed, N: int, K: int, x, y, M: int, workspace=None, stream=No
                             _nbytes(workspace), _stream(stream)), "wq_gemm_lut3")
 
 
+def wq_pack_lut3_dense(codes, qmap, scales, N: int, K: int, packed, stream=None) -> None:
+    _check(lib.wq_pack_lut3_dense(_ptr(codes), _ld(codes), _ptr(qmap), _ptr(scales), N, K, _ptr(packed),
+                                  _stream(stream)), "wq_pack_lut3_dense")
+
+
+def wq_gemm_lut3_dense(packed, N: int, K: int, x, y, M: int, workspace=None, stream=None) -> None:
+    _check(lib.wq_gemm_lut3_dense(_ptr(packed), N, K, _ptr(x), _ld(x), _ptr(y), _ld(y), M, _ptr(workspace),
+                                  _nbytes(workspace), _stream(stream)), "wq_gemm_lut3_dense")
+
+
 def wq_unpack_fp8_block(packed, N: int, K: int, w_bf16, stream=None) -> None:
     _check(lib.wq_unpack_fp8_block(_ptr(packed), N, K, _ptr(w_bf16), _stream(stream)), "wq_unpack_fp8_block")
 
@@ -163,6 +183,10 @@ def wq_unpack_fp8_block_f32(packed, N: int, K: int, w_f32, stream=None) -> None:
 
 def wq_unpack_lut3(packed, N: int, K: int, w_f16, stream=None) -> None:
     _check(lib.wq_unpack_lut3(_ptr(packed), N, K, _ptr(w_f16), _stream(stream)), "wq_unpack_lut3")
+
+
+def wq_unpack_lut3_dense(packed, N: int, K: int, w_f16, stream=None) -> None:
+    _check(lib.wq_unpack_lut3_dense(_ptr(packed), N, K, _ptr(w_f16), _stream(stream)), "wq_unpack_lut3_dense")
 
 
 # -------------------------------------------------------- torch helpers
@@ -207,4 +231,22 @@ def gemm_lut3(packed, N: int, K: int, x, ws=None, stream=None):
     M = x.shape[0]
     y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     wq_gemm_lut3(packed, N, K, x, y, M, ws, stream)
+    return y
+
+
+def pack_lut3_dense(codes, qmap, scales, stream=None):
+    """Pack 3-bit codes [N, K] (uint8), FP16 map [8] and FP16 group scales densely (3 bits a code)."""
+    import torch
+    N, K = codes.shape[0], codes.shape[1]
+    packed = torch.empty(wq_lut3_dense_packed_bytes(N, K), dtype=torch.uint8, device=codes.device)
+    wq_pack_lut3_dense(codes, qmap, scales, N, K, packed, stream)
+    return packed
+
+
+def gemm_lut3_dense(packed, N: int, K: int, x, ws=None, stream=None):
+    """y [M, N] (float16) = x [M, K] (float16) . dequant(W)^T for a densely packed matrix."""
+    import torch
+    M = x.shape[0]
+    y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    wq_gemm_lut3_dense(packed, N, K, x, y, M, ws, stream)
     return y
