@@ -100,6 +100,12 @@ def _declare(lib):
     lib.wqo_gemm_fp8.argtypes = [P, I64, P, I64, P, I64, I64, I64, P, I64, P, ctypes.c_int]
     lib.wqo_gemm_lut3.restype = ctypes.c_int
     lib.wqo_gemm_lut3.argtypes = [P, I64, P, I64, P, P, I64, I64, I64, P, I64, P, ctypes.c_int]
+    lib.wqo_e4m3_rne.restype = ctypes.c_uint8
+    lib.wqo_e4m3_rne.argtypes = [ctypes.c_float]
+    lib.wqo_quantize_x_fp8.restype = ctypes.c_int
+    lib.wqo_quantize_x_fp8.argtypes = [P, I64, I64, I64, P, P]
+    lib.wqo_gemm_w8a8.restype = ctypes.c_int
+    lib.wqo_gemm_w8a8.argtypes = [P, I64, P, P, I64, P, I64, I64, I64, P, I64, P, ctypes.c_int]
 
 
 def _ptr(a: np.ndarray):
@@ -222,4 +228,48 @@ def gemm_lut3(x_bits: np.ndarray, codes: np.ndarray, qmap: np.ndarray, scales: n
                                _ptr(y), nthreads or default_threads())
     if rc:
         raise ValueError("wqo_gemm_lut3 failed: %d" % rc)
+    return y
+
+
+# ------------------------------------------------------------------- W8A8
+
+def e4m3_rne(v) -> np.ndarray:
+    """Nearest E4M3FN code (ties to even) of each binary32 value, |v| <= 448."""
+    a = np.ascontiguousarray(v, dtype=np.float32).ravel()
+    lib = _load()
+    return np.array([lib.wqo_e4m3_rne(float(t)) for t in a], dtype=np.uint8).reshape(np.shape(v))
+
+
+def quantize_x_fp8(x_bits: np.ndarray, K: int | None = None):
+    """(codes uint8 [M, K], scales float32 [M, K/128]) of BF16 x bits [M, ldx]:
+    per (row, 128-K group) s = amax/448, codes = e4m3_rne(clamp(x/s, +-448))."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    M, ldx = x.shape
+    K = ldx if K is None else K
+    codes = np.empty((M, K), dtype=np.uint8)
+    scales = np.empty((M, K // 128), dtype=np.float32)
+    rc = _load().wqo_quantize_x_fp8(_ptr(x), ldx, M, K, _ptr(codes), _ptr(scales))
+    if rc:
+        raise ValueError("wqo_quantize_x_fp8 failed: %d" % rc)
+    return codes, scales
+
+
+def gemm_w8a8(x_codes: np.ndarray, x_scales: np.ndarray, codes: np.ndarray, scales: np.ndarray,
+              K: int | None = None, cols=None, nthreads: int | None = None) -> np.ndarray:
+    """y64 [M, N] (or [M, len(cols)]) for FP8 activations (codes [M, ldxq], scales
+    [M, K/128]) and FP8 block-scaled weights (codes [N, ldq], scales [N/128, K/128])."""
+    xq = np.ascontiguousarray(x_codes, dtype=np.uint8)
+    sx = np.ascontiguousarray(x_scales, dtype=np.float32)
+    q = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.float32)
+    M, ldxq = xq.shape
+    N, ldq = q.shape
+    K = ldq if K is None else K
+    c, cp = _cols_arg(cols)
+    nc = N if c is None else c.size
+    y = np.empty((M, nc), dtype=np.float64)
+    rc = _load().wqo_gemm_w8a8(_ptr(xq), ldxq, _ptr(sx), _ptr(q), ldq, _ptr(s), M, N, K, cp, nc, _ptr(y),
+                               nthreads or default_threads())
+    if rc:
+        raise ValueError("wqo_gemm_w8a8 failed: %d" % rc)
     return y

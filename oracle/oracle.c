@@ -26,6 +26,16 @@
  *     accumulate).
  *   - E4M3 is read as OCP E4M3FN (bias 7, no infinities, S.1111.111 is NaN),
  *     the pages being silent on the flavour.
+ *   - W8A8 (both operands FP8): the arc PR's "Worth a separate change" section
+ *     notes that block-scaled FP8 GEMMs need the activations in FP8 too, i.e.
+ *     an activation quantiser, which it does not specify; the atlas ladder
+ *     ("ARM ORDER", rung 6) puts a W8A8 block-scaled tier above the decode
+ *     band.  Reading used here: one FP32 scale per (row, 128-wide K group),
+ *     s = amax / 448 in binary32 (s = 1 for an all-zero group), code =
+ *     E4M3 nearest-even of clamp(x / s, -448, 448) with the division in
+ *     binary32 -- the same rule as the weights' 128x128 block quantiser.  The
+ *     product is then y[m,n] = sum_k (e4m3(xq[m,k]) sx[m][k/128]) *
+ *     (e4m3(q[n,k]) s[n/128][k/128]).
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC -pthread.
  */
@@ -266,6 +276,61 @@ static int run_gemm(job_t proto, int nthreads)
     return err;
 }
 
+/* ------------------------------------------------ activation quantiser (W8A8) */
+
+/* Nearest OCP E4M3FN code to a finite binary32 value v with |v| <= 448, ties
+ * to the even code.  The E4M3 grid: m * 2^-9 below 2^-6 (m = 0..7, and m = 8
+ * is the smallest normal, code 0x08), (1 + m/8) * 2^(e-7) above.  Everything
+ * is exact in binary64; nearbyint() rounds half to even. */
+static uint8_t e4m3_rne_code(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a < ldexp(1.0, -6)) {
+        double m = nearbyint(ldexp(a, 9));         /* 0 .. 8 */
+        return (uint8_t)(sign | (uint8_t)m);
+    }
+    int e2;
+    (void)frexp(a, &e2);                           /* a = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;                                /* a in [2^E, 2^(E+1)) */
+    double q = nearbyint(ldexp(a, 3 - E));         /* 8 .. 16 */
+    if (q == 16.0) {
+        q = 8.0;
+        E += 1;
+    }
+    return (uint8_t)(sign | (uint8_t)((E + 7) << 3) | (uint8_t)(q - 8.0));
+}
+
+uint8_t wqo_e4m3_rne(float v) { return e4m3_rne_code(v); }
+
+/* codes [M][K] and scales [M][K/128] of BF16 x [M][ldx]:
+ * s = amax/448 (binary32; 1 for an all-zero group), code = e4m3_rne(clamp(x/s)). */
+int wqo_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int64_t K,
+                       uint8_t* codes, float* scales)
+{
+    if (K % WQO_BLOCK || ldx < K) return -2;
+    int64_t kb_n = K / WQO_BLOCK;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t kb = 0; kb < kb_n; ++kb) {
+            const uint16_t* xr = x_bf16 + m * ldx + kb * WQO_BLOCK;
+            float amax = 0.0f;
+            for (int i = 0; i < WQO_BLOCK; ++i) {
+                float a = fabsf((float)wqo_bf16_value(xr[i]));
+                if (a > amax) amax = a;
+            }
+            float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+            scales[m * kb_n + kb] = s;
+            for (int i = 0; i < WQO_BLOCK; ++i) {
+                float q = (float)wqo_bf16_value(xr[i]) / s;
+                if (q > 448.0f) q = 448.0f;
+                if (q < -448.0f) q = -448.0f;
+                codes[m * K + kb * WQO_BLOCK + i] = e4m3_rne_code(q);
+            }
+        }
+    }
+    return 0;
+}
+
 /* x_bits: [M][ldx] BF16 (x_is_f16 == 0) or FP16 (x_is_f16 == 1). */
 static double* decode_x(const uint16_t* x_bits, int64_t ldx, int64_t M, int64_t K, int is_f16)
 {
@@ -302,6 +367,26 @@ int wqo_gemm_lut3(const uint16_t* x_f16, int64_t ldx, const uint8_t* c, int64_t 
     double* x = decode_x(x_f16, ldx, M, K, 1);
     if (!x) return -3;
     job_t j = {1, x, c, ldc, NULL, qmap, g, M, N, K, cols, cols ? ncols : N, y, 1, 0, 0};
+    int err = run_gemm(j, nthreads);
+    free(x);
+    return err;
+}
+
+/* y64[m][ci] = sum_k e4m3(xq[m,k]) * sx[m][k/128] * e4m3(q[n,k]) * s[n/128][k/128]:
+ * both operands are decoded exactly into binary64 and summed as in
+ * wqo_gemm_fp8 (one accumulator, k increasing). */
+int wqo_gemm_w8a8(const uint8_t* xq, int64_t ldxq, const float* sx, const uint8_t* q, int64_t ldq,
+                  const float* s, int64_t M, int64_t N, int64_t K,
+                  const int64_t* cols, int64_t ncols, double* y, int nthreads)
+{
+    if (N % WQO_BLOCK || K % WQO_BLOCK || ldxq < K || ldq < K) return -2;
+    int64_t kb_n = K / WQO_BLOCK;
+    double* x = (double*)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    if (!x) return -3;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            x[m * K + k] = wqo_e4m3_value(xq[m * ldxq + k]) * (double)sx[m * kb_n + k / WQO_BLOCK];
+    job_t j = {0, x, q, ldq, s, NULL, NULL, M, N, K, cols, cols ? ncols : N, y, 1, 0, 0};
     int err = run_gemm(j, nthreads);
     free(x);
     return err;

@@ -412,9 +412,150 @@ def pin_strides_rows_cols_threads():
     assert np.array_equal(oracle.gemm_lut3(xhs, c, q, g, K=K, nthreads=3), yl), "LUT x stride / threads"
 
 
+# -------------------------------------------------------------------- W8A8
+
+def _e4m3_table():
+    """The 254 finite E4M3FN values (library decode), their codes, sorted by value."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = _torch_e4m3(codes)
+    keep = np.isfinite(vals)
+    return vals[keep], codes[keep]
+
+
+def _brute_e4m3(v: float, vals, codes) -> int:
+    """Nearest finite E4M3 value by exhaustive search in exact rationals, ties to the even code;
+    a negative value keeps its sign (rounds to -0 when it rounds to zero)."""
+    fv = Fraction(v)
+    best = None
+    for val, code in zip(vals, codes):
+        if val == 0 and (int(code) & 0x80) != (0x80 if math.copysign(1.0, v) < 0 else 0):
+            continue
+        d = abs(fv - Fraction(float(val)))
+        key = (d, int(code) & 1)
+        if best is None or key < best[0]:
+            best = (key, int(code))
+    return best[1]
+
+
+def _e4m3_inputs(seed: int) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    vals, _ = _e4m3_table()
+    pos = np.unique(vals[vals >= 0])
+    v = list(pos) + list(-pos)
+    for a, b in zip(pos[:-1], pos[1:]):            # ties and their float32 neighbours
+        mid = np.float32((a + b) / 2)
+        v += [mid, np.nextafter(mid, np.float32(np.inf)), np.nextafter(mid, np.float32(0))]
+    v += list(_rand_doubles(rng, 400, -12, 9).clip(-448, 448))
+    v += [0.0, -0.0, 448.0, -448.0, 2.0 ** -10, -(2.0 ** -10), 2.0 ** -11]
+    return np.array(v, dtype=np.float32)
+
+
+def pin_e4m3_encode():
+    v = _e4m3_inputs(40)
+    got = oracle.e4m3_rne(v)
+    # (1) torch's float32 -> float8_e4m3fn cast (round to nearest even)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want), "e4m3_rne != torch cast at %r" % v[np.argmax(got != want)]
+    # (2) exhaustive nearest-value search in exact rationals
+    vals, codes = _e4m3_table()
+    for x, g in list(zip(v, got))[::3]:
+        assert _brute_e4m3(float(x), vals, codes) == int(g), (float(x), hex(int(g)))
+
+
+def _quant_fixture(seed: int, ld_pad: int = 0):
+    """BF16 activations [5, 512 (+pad)]: random groups, an all-zero group, a group whose
+    largest magnitude is negative, one with amax 448 (scale 1), tiny and huge groups."""
+    M, K = 5, 512
+    x = synth.normal_matrix(M, K, seed)
+    x[1, 128:256] = 0.0
+    x[2, 0:128] = np.abs(x[2, 0:128])
+    x[2, 7] = -9.5
+    x[3, 256:384] = np.clip(x[3, 256:384] * 40, -447, 447)
+    x[3, 300] = 448.0
+    x[4, 0:128] *= 1e-6
+    x[4, 384:512] *= 3e4
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if ld_pad:
+        wide = np.full((M, K + ld_pad), 0x7FC1, dtype=np.uint16)
+        wide[:, :K] = bits
+        return wide, K
+    return bits, K
+
+
+def pin_quantize_x():
+    xb, K = _quant_fixture(41)
+    codes, sc = oracle.quantize_x_fp8(xb)
+    xv = _torch_bf16(xb).astype(np.float32)            # BF16 -> binary32 is exact
+    for m in range(xb.shape[0]):
+        for kb in range(K // 128):
+            blk = xv[m, kb * 128:(kb + 1) * 128]
+            amax = np.float32(np.abs(blk).max())
+            s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+            assert sc[m, kb] == s, (m, kb, sc[m, kb], s)
+            q = np.clip(blk / s, np.float32(-448), np.float32(448)).astype(np.float32)   # numpy binary32 division
+            want = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(codes[m, kb * 128:(kb + 1) * 128], want), (m, kb)
+            if amax > 0:   # the largest magnitude lands on +-448 exactly
+                i = int(np.argmax(np.abs(blk)))
+                assert codes[m, kb * 128 + i] in (0x7E, 0xFE), (m, kb, hex(codes[m, kb * 128 + i]))
+    assert sc[1, 1] == 1.0 and not codes[1, 128:256].any(), "all-zero group"
+    assert sc[3, 2] == 1.0, "amax 448 gives scale 1"
+    assert codes[2, 7] == 0xFE, "negative extreme"
+    # the padding of a strided x is never read
+    xs, _ = _quant_fixture(41, ld_pad=40)
+    c2, s2 = oracle.quantize_x_fp8(xs, K=K)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, sc), "x stride"
+
+
+def pin_gemm_w8a8_exact():
+    rng = np.random.Generator(np.random.PCG64(42))
+    M, N, K = 2, 256, 256
+    xb = synth.x_bf16(M, K, 43)
+    xq, sx = oracle.quantize_x_fp8(xb)
+    q = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x31
+    sw = rng.uniform(0.05, 3.0, size=(N // 128, K // 128)).astype(np.float32)
+    cols = [0, 1, 100, 127, 128, 200, 255]
+    wide = np.full((M, K + 64), 0x7F, dtype=np.uint8)            # NaN codes in the padding
+    wide[:, :K] = xq
+    y64 = oracle.gemm_w8a8(wide, sx, q, sw, K=K, cols=cols)
+    xv, wv = _torch_e4m3(xq), _torch_e4m3(q)
+    exact, absdot = [], []
+    for m in range(M):
+        row, ad = [], []
+        for n in cols:
+            acc, tot = Fraction(0), 0.0
+            for k in range(K):
+                a = Fraction(float(xv[m, k])) * Fraction(float(sx[m, k // 128]))
+                b = Fraction(float(wv[n, k])) * Fraction(float(sw[n // 128, k // 128]))
+                acc += a * b
+                tot += abs(float(a * b))
+            row.append(acc)
+            ad.append(Fraction(tot) * Fraction(101, 100))
+        exact.append(row)
+        absdot.append(ad)
+    _check_against_exact(y64, exact, absdot, K)
+
+
+def pin_w8a8_integer_exact():
+    """Groups holding 448 quantise with scale 1, so small integers pass through exactly."""
+    rng = np.random.Generator(np.random.PCG64(44))
+    M, N, K = 3, 128, 384
+    xi = rng.integers(-6, 7, size=(M, K)).astype(np.int64)
+    xi[:, ::128] = 448
+    wi = rng.integers(-8, 9, size=(N, K))
+    xb = torch.from_numpy(xi.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xq, sx = oracle.quantize_x_fp8(xb)
+    assert np.all(sx == 1.0)
+    q = torch.from_numpy(wi.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    y64 = oracle.gemm_w8a8(xq, sx, q, np.ones((1, K // 128), np.float32))
+    assert np.array_equal(y64, (xi @ wi.T).astype(np.float64)), "W8A8 integer case != int64 matmul"
+
+
 ALL_PINS = [
     pin_e4m3_all_codes, pin_e4m3_golden, pin_f16_decode_all, pin_bf16_decode_all, pin_16bit_golden,
     pin_f16_rne, pin_bf16_rne, pin_fp8_dequant, pin_lut_dequant, pin_lut_rejects_bad_code,
     pin_gemm_fp8_exact, pin_gemm_lut3_exact, pin_integer_exact, pin_closed_form,
     pin_scale_linearity, pin_strides_rows_cols_threads,
+    pin_e4m3_encode, pin_quantize_x, pin_gemm_w8a8_exact, pin_w8a8_integer_exact,
 ]

@@ -41,6 +41,21 @@ MUTANTS = [
     ("gemm_row_zero_only", "const double* xr = j->x + m * j->K;", "const double* xr = j->x;", None),
     ("gemm_output_transposed", "j->y[m * j->ncols + ci] = acc;", "j->y[ci * j->M + m] = acc;", None),
     ("x_stride_ignored", "x_bits[m * ldx + k]", "x_bits[m * K + k]", None),
+    ("e4m3enc_ties_away", "double q = nearbyint(ldexp(a, 3 - E));", "double q = round(ldexp(a, 3 - E));", None),
+    ("e4m3enc_truncates", "double q = nearbyint(ldexp(a, 3 - E));", "double q = floor(ldexp(a, 3 - E));", None),
+    ("e4m3enc_sub_truncates", "double m = nearbyint(ldexp(a, 9));", "double m = floor(ldexp(a, 9));", None),
+    ("e4m3enc_sub_threshold", "if (a < ldexp(1.0, -6)) {", "if (a < ldexp(1.0, -7)) {", None),
+    ("e4m3enc_bias", "((E + 7) << 3)", "((E + 8) << 3)", None),
+    ("e4m3enc_carry_lost", "q = 8.0;\n        E += 1;", "q = 15.0;", None),
+    ("e4m3enc_sign_dropped", "uint8_t sign = signbit(v) ? 0x80 : 0x00;", "uint8_t sign = 0x00;", None),
+    ("quant_scale_const", "amax / 448.0f", "amax / 447.0f", None),
+    ("quant_zero_group", "amax > 0.0f ? amax / 448.0f : 1.0f", "amax > 0.0f ? amax / 448.0f : 0.5f", None),
+    ("quant_amax_signed", "float a = fabsf((float)wqo_bf16_value(xr[i]));", "float a = (float)wqo_bf16_value(xr[i]);", None),
+    ("quant_x_stride", "x_bf16 + m * ldx + kb * WQO_BLOCK", "x_bf16 + m * K + kb * WQO_BLOCK", None),
+    ("quant_multiplies", "(float)wqo_bf16_value(xr[i]) / s;", "(float)wqo_bf16_value(xr[i]) * (1.0f / s);", None),
+    ("w8a8_sx_group", "sx[m * kb_n + k / WQO_BLOCK]", "sx[m * kb_n]", None),
+    ("w8a8_sx_row", "sx[m * kb_n + k / WQO_BLOCK]", "sx[k / WQO_BLOCK]", None),
+    ("w8a8_x_stride", "xq[m * ldxq + k]", "xq[m * K + k]", None),
 ]
 
 
