@@ -50,7 +50,7 @@ def algorithmic_bytes(fmt: str, N: int, K: int, M: int) -> int:
 
 def kernel_src_sha() -> str:
     h = hashlib.sha256()
-    for f in ("wq_kernels.hip", "wq_device.hpp", "wq_internal.h", "wq_api.cpp"):
+    for f in ("wq_kernels.hip", "wq_w8a8.hip", "wq_device.hpp", "wq_internal.h", "wq_api.cpp"):
         with open(os.path.join(ROOT, "weight_only_quantized_fp8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

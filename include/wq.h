@@ -201,6 +201,44 @@ wq_status wq_gemm_lut3_dense(const void* packed, int64_t N, int64_t K,
                              uint16_t* y, int64_t ldy, int64_t M,
                              void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* ------------------------------------------------------------------ W8A8 */
+/* The W8A8 block-scaled tier above the decode band (atlas "Module m16_tc",
+ * "ARM ORDER" rung 6): activations are quantised to FP8 (the arc PR, "Worth a
+ * separate change": block-scaled FP8 needs an activation quantiser) and
+ * multiplied with the packed FP8 weights on the FP8 matrix cores.
+ *
+ * Quantiser reading (the pages give none): one FP32 scale per (row, 128-wide
+ * K group), s = amax/448 in binary32 (1 for an all-zero group), code = E4M3
+ * nearest-even of clamp(x/s, -448, 448) with x/s in binary32 -- the rule of
+ * the weights' block quantiser.  x must be finite. */
+
+/* Bytes of a packed FP8 activation buffer: Mpad*K codes + 4*Mpad*(K/128)
+ * scale bytes, Mpad = 16*ceil(M/16).  0 for an unsupported shape (K not a
+ * positive multiple of 128, M < 1, or 2 GiB or more). */
+size_t wq_x_fp8_packed_bytes(int64_t M, int64_t K);
+
+/* Quantise BF16 activations into the packed FP8 activation layout.
+ *   x_bf16  device, [M][ldx] BF16 bits; ldx >= K, ldx % 8 == 0, 16-byte aligned
+ *   xq      device, wq_x_fp8_packed_bytes(M, K) bytes, 16-byte aligned
+ * M == 0 queues nothing.  Asynchronous on hip_stream. */
+wq_status wq_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int64_t K,
+                            void* xq, void* hip_stream);
+
+/* y = dequant(xq) . dequant(W)^T with both operands FP8.
+ *   packed  device, from wq_pack_fp8_block with the same N, K (the same packed
+ *           matrix serves wq_gemm_fp8_block); N*K < 2^32
+ *   xq      device, from wq_quantize_x_fp8 with the same M, K
+ *   y       device, [M][ldy] BF16 bits (RNE); ldy >= N
+ *   M       any M >= 1 with wq_x_fp8_packed_bytes(M, K) > 0; M == 0 queues nothing
+ * Per 128-K block the FP32 matrix-core sum of e4m3(x)*e4m3(w) is folded onto an
+ * FP32 accumulator times sx[m][kb]*s[n/128][kb].  Every output is within 2 BF16
+ * ULP of the exact result (of the quantised operands) rounded to BF16, or within
+ * 1e-3*sqrt(K)*max|xq*sx|*max|w| of it.  Deterministic; row r of the result
+ * depends only on row r of xq.  workspace: none needed (NULL accepted). */
+wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void* xq, int64_t M,
+                           uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                           void* hip_stream);
+
 /* ------------------------------------------------------------ workspace */
 
 /* Workspace bytes a GEMM of this format and shape needs (the same for every M
@@ -222,6 +260,11 @@ wq_status wq_unpack_fp8_block_f32(const void* packed, int64_t N, int64_t K,
 /* out[n][k] = fp16_rne(qmap[code] * scale[n][k/128]) */
 wq_status wq_unpack_lut3(const void* packed, int64_t N, int64_t K,
                          uint16_t* w_f16, void* hip_stream);
+
+/* Packed FP8 activations back to canonical codes [M][K] (E4M3) and scales
+ * [M][K/128] (FP32, 4-byte aligned). */
+wq_status wq_unpack_x_fp8(const void* xq, int64_t M, int64_t K, uint8_t* codes, float* scales,
+                          void* hip_stream);
 
 /* The same for a matrix packed by wq_pack_lut3_dense. */
 wq_status wq_unpack_lut3_dense(const void* packed, int64_t N, int64_t K,

@@ -143,6 +143,32 @@ def test_pack_unpack_validation(call, expect):
     assert call() == expect
 
 
+def test_w8a8_sizes_and_validation():
+    assert wq.wq_x_fp8_packed_bytes(1, 128) == 16 * 128 + 4 * 16
+    assert wq.wq_x_fp8_packed_bytes(17, 5120) == 32 * 5120 + 4 * 32 * 40
+    assert wq.wq_x_fp8_packed_bytes(16, 100) == 0
+    assert wq.wq_x_fp8_packed_bytes(0, 128) == 0
+    assert wq.wq_x_fp8_packed_bytes(1 << 20, 4096) == 0                       # 2 GiB or more
+    # (x, ldx, M, K, xq)
+    assert L.wq_quantize_x_fp8(None, 512, 0, 512, None, None) == 0             # M == 0: no-op
+    assert L.wq_quantize_x_fp8(None, 512, 4, 512, P, None) == 1
+    assert L.wq_quantize_x_fp8(P, 511, 4, 512, P, None) == 3
+    assert L.wq_quantize_x_fp8(P, 512, 4, 500, P, None) == 2
+    assert L.wq_quantize_x_fp8(P, 516, 4, 512, P, None) == 8
+    assert L.wq_quantize_x_fp8(P + 2, 512, 4, 512, P, None) == 8
+    # (packed, N, K, xq, M, y, ldy, ws, ws_bytes)
+    assert L.wq_gemm_fp8_w8a8(None, 256, 512, None, 0, None, 256, None, 0, None) == 0
+    assert L.wq_gemm_fp8_w8a8(None, 256, 512, P, 4, P, 256, None, 0, None) == 1
+    assert L.wq_gemm_fp8_w8a8(P, 200, 512, P, 4, P, 256, None, 0, None) == 2    # N % 128
+    assert L.wq_gemm_fp8_w8a8(P, 256, 500, P, 4, P, 256, None, 0, None) == 2
+    assert L.wq_gemm_fp8_w8a8(P, 256, 512, P, -1, P, 256, None, 0, None) == 2
+    assert L.wq_gemm_fp8_w8a8(P, 256, 512, P, 4, P, 255, None, 0, None) == 3
+    assert L.wq_gemm_fp8_w8a8(P, 256, 512, P + 8, 4, P, 256, None, 0, None) == 8
+    assert L.wq_gemm_fp8_w8a8(P, 256, 512, P, 4, P + 1, 256, None, 0, None) == 8
+    assert L.wq_unpack_x_fp8(P, 4, 512, P, P + 2, None) == 8
+    assert L.wq_unpack_x_fp8(None, 4, 512, P, P, None) == 1
+
+
 def _has_gpu():
     try:
         import torch
@@ -157,4 +183,6 @@ def test_valid_call_without_device_reports_hip_error():
     assert L.wq_gemm_fp8_block(P, 256, 512, P, 512, P, 256, 1, P, BIG, None) == 7
     assert L.wq_gemm_lut3(P, 48, 512, P, 512, P, 48, 4, P, BIG, None) == 7
     assert L.wq_gemm_lut3_dense(P, 48, 512, P, 512, P, 48, 4, P, BIG, None) == 7
+    assert L.wq_gemm_fp8_w8a8(P, 256, 512, P, 4, P, 256, None, 0, None) == 7
+    assert L.wq_quantize_x_fp8(P, 512, 4, 512, P, None) == 7
     assert L.wq_pack_fp8_block(P, 512, P, 256, 512, P, None) == 7

@@ -1,0 +1,208 @@
+"""W8A8 tier on the GPU (called through the C ABI) against the CPU oracle.
+
+* quantiser: the packed FP8 activations, unpacked by the test hook, equal the
+  oracle's codes and scales bit for bit (the codes are an integer decision made
+  in binary32 on both sides), padding rows are zero;
+* GEMM: every output within 2 BF16 ULP of the oracle's exact sum of the
+  quantised operands, or within the absolute floor, on shapes with ragged row
+  tiles, several column tiles and K blocks, M from 1 to a few hundred and at
+  the FFN gate/up size; integer-exact inputs give exact results; rows are
+  independent of M, results deterministic, y's padding untouched, HIP-graph
+  replays equal the eager result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import gpu_util as U
+from oracle import compare
+
+pytestmark = pytest.mark.gpu
+
+
+def quantize(xbits, K):
+    """GPU-quantised activations of BF16 bits [M, ldx]: (packed buffer, codes, scales)."""
+    wq = U.wqmod()
+    M = xbits.shape[0]
+    x = U.t_u16(xbits, torch.bfloat16)
+    xq = torch.empty(wq.wq_x_fp8_packed_bytes(M, K), dtype=torch.uint8, device=U.DEV)
+    xq.fill_(0xA5)                                        # padding must be written, not left over
+    wq.wq_quantize_x_fp8(x[:, :K] if xbits.shape[1] > K else x, M, K, xq)
+    codes = torch.empty((M, K), dtype=torch.uint8, device=U.DEV)
+    scales = torch.empty((M, K // 128), dtype=torch.float32, device=U.DEV)
+    wq.wq_unpack_x_fp8(xq, M, K, codes, scales)
+    torch.cuda.synchronize()
+    return xq, codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def run(packed, N, K, xq, M, ldy=None, y_init=None):
+    wq = U.wqmod()
+    ldy = N if ldy is None else ldy
+    y = torch.empty((M, ldy), dtype=torch.bfloat16, device=U.DEV)
+    if y_init is not None:
+        y.copy_(U.t_u16(y_init, torch.bfloat16))
+    wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y)
+    torch.cuda.synchronize()
+    full = U.bits_of(y)
+    return full[:, :N], full
+
+
+def floor_w8a8(xc, xs, codes, scales, K):
+    mx = float(np.abs(oracle.e4m3_value(xc) * np.repeat(xs.astype(np.float64), 128, 1)).max())
+    mw = 0.0
+    for r0 in range(0, codes.shape[0], 2048):
+        w = oracle.dequant_fp8(codes[r0:r0 + 2048], scales[r0 // 128:(r0 + 2048) // 128])
+        mw = max(mw, float(np.abs(w).max()))
+    return compare.abs_floor(K, mx, mw)
+
+
+def special_x(M, K, seed, ld=None):
+    """BF16 activations with an all-zero group, a group holding 448 (scale 1), a
+    negative extreme, tiny and huge groups, and NaN canaries in any padding."""
+    x = synth.normal_matrix(M, K, seed)
+    if M > 3 and K >= 256:
+        x[1, 128:256] = 0.0
+        x[2, 0:128] = np.abs(x[2, 0:128])
+        x[2, 5] = -11.0
+        x[3, 0:128] = np.clip(x[3, 0:128] * 50, -447, 447)
+        x[3, 17] = 448.0
+        x[0, 0:128] *= 1e-5
+        x[0, 128:256] *= 2e4
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if ld is not None and ld > K:
+        wide = np.full((M, ld), 0x7FC1, dtype=np.uint16)
+        wide[:, :K] = bits
+        return wide
+    return bits
+
+
+@pytest.mark.parametrize("M,K,ld", [(1, 128, None), (5, 512, None), (16, 384, 392), (37, 1024, None),
+                                    (300, 640, 648)])
+def test_quantizer_matches_oracle_bit_exact(M, K, ld):
+    U.note("w8a8 quantize M=%d K=%d ld=%s" % (M, K, ld))
+    xb = special_x(M, K, 60 + M, ld)
+    xq, codes, scales = quantize(xb, K)
+    oc, osc = oracle.quantize_x_fp8(xb, K=K)
+    assert np.array_equal(scales.view(np.uint32), osc.view(np.uint32)), "scales differ"
+    assert np.array_equal(codes, oc), "codes differ at %s" % (np.argwhere(codes != oc)[:4],)
+    # padding rows: zero codes and zero scales
+    wq = U.wqmod()
+    Mpad = (M + 15) // 16 * 16
+    raw = xq.cpu().numpy()
+    assert raw.size == wq.wq_x_fp8_packed_bytes(M, K) == Mpad * K + 4 * Mpad * (K // 128)
+    sx = raw[Mpad * K:].view(np.float32).reshape(K // 128, Mpad)
+    assert not sx[:, M:].any()
+    if Mpad > M:
+        units = raw[:Mpad * K].reshape(Mpad // 16, K // 128, 2, 64, 16)
+        last = units[-1]                                  # rows 16*(tiles-1) .. Mpad-1
+        lanes = np.arange(64) % 16 + 16 * (Mpad // 16 - 1) >= M
+        assert not last[:, :, lanes, :].any()
+
+
+W8A8_SHAPES = [(256, 512, 1), (384, 1024, 16), (1024, 640, 33), (640, 2048, 130), (256, 256, 300),
+               (512, 1152, 129)]
+
+
+@pytest.mark.parametrize("N,K,M", W8A8_SHAPES)
+def test_w8a8_parity(N, K, M):
+    U.note("w8a8 parity N=%d K=%d M=%d" % (N, K, M))
+    codes, scales = synth.fp8_weights(N, K, 1100 + N + K)
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(M, K, 1200 + M)
+    xq, xc, xs = quantize(xb, K)
+    oc, osc = oracle.quantize_x_fp8(xb)
+    assert np.array_equal(xc, oc) and np.array_equal(xs, osc)
+    y, _ = run(packed, N, K, xq, M)
+    y64 = oracle.gemm_w8a8(oc, osc, codes, scales)
+    r = compare.grade(y, y64, floor_w8a8(oc, osc, codes, scales, K), "bf16")
+    assert r.ok, str(r)
+    assert r.rel_rms < 4e-3, r
+
+
+def test_w8a8_integer_exact():
+    U.note("w8a8 integer exact")
+    rng = np.random.Generator(np.random.PCG64(61))
+    N, K, M = 256, 1024, 40
+    xi = rng.integers(-6, 7, size=(M, K)).astype(np.int64)
+    xi[:, ::128] = 448                                    # every group quantises with scale 1
+    wi = rng.integers(-8, 9, size=(N, K))
+    xb = torch.from_numpy(xi.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q = torch.from_numpy(wi.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    packed = U.pack_fp8(q, np.ones((N // 128, K // 128), np.float32))
+    xq, _, xs = quantize(xb, K)
+    assert np.all(xs == 1.0)
+    y, _ = run(packed, N, K, xq, M)
+    assert np.array_equal(y, oracle.bf16_rne((xi @ wi.T).astype(np.float64)))
+
+
+def test_w8a8_rows_determinism_strides():
+    U.note("w8a8 invariants")
+    N, K, M = 384, 768, 150
+    codes, scales = synth.fp8_weights(N, K, 62)
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(M, K, 63)
+    xq, _, _ = quantize(xb, K)
+    y, _ = run(packed, N, K, xq, M)
+    # row r depends only on row r: a 20-row call and the rows 130.. of the call
+    for lo, hi in ((0, 20), (130, 150), (16, 17)):
+        xq2, _, _ = quantize(xb[lo:hi], K)
+        y2, _ = run(packed, N, K, xq2, hi - lo)
+        assert np.array_equal(y2, y[lo:hi]), (lo, hi)
+    for _ in range(5):
+        assert np.array_equal(run(packed, N, K, xq, M)[0], y)
+    ldy = N + 40
+    canary = np.full((M, ldy), 0x7FAB, dtype=np.uint16)
+    ys, full = run(packed, N, K, xq, M, ldy=ldy, y_init=canary)
+    assert np.array_equal(ys, y) and np.all(full[:, N:] == 0x7FAB)
+
+
+def test_w8a8_graph_replay():
+    """Quantiser and GEMM captured in a HIP graph replay to the eager result."""
+    wq = U.wqmod()
+    U.note("w8a8 graph replay")
+    N, K, M = 512, 1024, 96
+    codes, scales = synth.fp8_weights(N, K, 64)
+    packed = U.pack_fp8(codes, scales)
+    x = U.t_u16(synth.x_bf16(M, K, 65), torch.bfloat16)
+    xq = torch.empty(wq.wq_x_fp8_packed_bytes(M, K), dtype=torch.uint8, device=U.DEV)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=U.DEV)
+    wq.wq_quantize_x_fp8(x, M, K, xq)
+    wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            wq.wq_quantize_x_fp8(x, M, K, xq)
+            wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        y.fill_(3.0)
+        xq.fill_(0x11)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), rep
+
+
+@pytest.mark.parametrize("M", [64, 512])
+def test_w8a8_gate_up_size(M):
+    """The FFN gate/up matrix (17408 x 5120): every column of the first and last
+    128 and 768 random ones in between, all M rows."""
+    U.note("w8a8 gate_up M=%d" % M)
+    fmt, N, K, Ms, (codes, scales) = U.config_inputs("gate_up")
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(M, K, 1301)
+    xq, xc, xs = quantize(xb, K)
+    oc, osc = oracle.quantize_x_fp8(xb)
+    assert np.array_equal(xc, oc) and np.array_equal(xs, osc)
+    y, _ = run(packed, N, K, xq, M)
+    cols = U.sample_cols(N, 66)
+    y64 = oracle.gemm_w8a8(oc, osc, codes, scales, cols=cols)
+    r = compare.grade(y[:, cols], y64, floor_w8a8(oc, osc, codes, scales, K), "bf16")
+    U.note("  %s" % r)
+    assert r.ok, str(r)

@@ -17,7 +17,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", INCLUDE, "-I", CSRC]
-SOURCES = ["wq_kernels.hip", "wq_api.cpp"]
+SOURCES = ["wq_kernels.hip", "wq_w8a8.hip", "wq_api.cpp"]
 
 
 def build(verbose: bool = False) -> str:

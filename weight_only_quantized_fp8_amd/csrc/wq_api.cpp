@@ -505,4 +505,68 @@ wq_status wq_unpack_lut3_dense(const void* packed, int64_t N, int64_t K, uint16_
     return unpack_lut3_common(WQ_FMT_LUT3_DENSE, packed, N, K, w_f16, hip_stream);
 }
 
+// ------------------------------------------------------------------ W8A8
+
+size_t wq_x_fp8_packed_bytes(int64_t M, int64_t K)
+{
+    if (M <= 0 || K <= 0 || K % 128 || M > (int64_t)1 << 24 || K > (int64_t)1 << 24) return 0;
+    const int64_t mpad = (M + 15) / 16 * 16;
+    const int64_t bytes = mpad * K + 4 * mpad * (K / 128);
+    return bytes < ((int64_t)1 << 31) ? (size_t)bytes : 0;
+}
+
+wq_status wq_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int64_t K, void* xq, void* hip_stream)
+{
+    if (M < 0) return WQ_ERR_SHAPE;
+    if (M == 0) return WQ_OK;
+    if (!wq_x_fp8_packed_bytes(M, K)) return WQ_ERR_SHAPE;
+    if (!x_bf16 || !xq) return WQ_ERR_NULL;
+    if (ldx < K) return WQ_ERR_LD;
+    if (!aligned16(x_bf16) || ldx % 8 || !aligned16(xq)) return WQ_ERR_ALIGN;
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    return wq::launch_quantize_x(x_bf16, ldx, (int)M, (int)K, static_cast<uint8_t*>(xq),
+                                 static_cast<hipStream_t>(hip_stream)) == hipSuccess
+               ? WQ_OK
+               : WQ_ERR_HIP;
+}
+
+wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void* xq, int64_t M, uint16_t* y,
+                           int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    (void)workspace;          // every output tile is owned by one work-group: no workspace
+    (void)workspace_bytes;
+    if (M < 0) return WQ_ERR_SHAPE;
+    if (!shape_ok(WQ_FMT_FP8_BLOCK, N, K) || (uint64_t)N * (uint64_t)K >= ((uint64_t)1 << 32)) return WQ_ERR_SHAPE;
+    if (M == 0) return WQ_OK;
+    if (!wq_x_fp8_packed_bytes(M, K)) return WQ_ERR_SHAPE;
+    if (!packed || !xq || !y) return WQ_ERR_NULL;
+    if (ldy < N) return WQ_ERR_LD;
+    if (!aligned16(packed) || !aligned16(xq) || (reinterpret_cast<uintptr_t>(y) & 1)) return WQ_ERR_ALIGN;
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    return wq::launch_w8a8(static_cast<const uint8_t*>(packed), (int)N, (int)K, static_cast<const uint8_t*>(xq),
+                           (int)M, y, ldy, static_cast<hipStream_t>(hip_stream)) == hipSuccess
+               ? WQ_OK
+               : WQ_ERR_HIP;
+}
+
+wq_status wq_unpack_x_fp8(const void* xq, int64_t M, int64_t K, uint8_t* codes, float* scales, void* hip_stream)
+{
+    if (M < 0) return WQ_ERR_SHAPE;
+    if (M == 0) return WQ_OK;
+    if (!wq_x_fp8_packed_bytes(M, K)) return WQ_ERR_SHAPE;
+    if (!xq || !codes || !scales) return WQ_ERR_NULL;
+    if (!aligned16(xq) || (reinterpret_cast<uintptr_t>(scales) & 3)) return WQ_ERR_ALIGN;
+    DevInfo dev;
+    wq_status st = current_device(&dev);
+    if (st != WQ_OK) return st;
+    return wq::launch_unpack_x(static_cast<const uint8_t*>(xq), (int)M, (int)K, codes, scales,
+                               static_cast<hipStream_t>(hip_stream)) == hipSuccess
+               ? WQ_OK
+               : WQ_ERR_HIP;
+}
+
 }  // extern "C"

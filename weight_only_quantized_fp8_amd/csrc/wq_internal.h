@@ -99,4 +99,11 @@ hipError_t launch_unpack_fp8(const uint8_t* packed, int64_t N, int64_t K, void* 
 hipError_t launch_unpack_lut3(const uint8_t* packed, int64_t N, int64_t K, uint16_t* out,
                               bool dense, hipStream_t stream);
 
+// W8A8 tier (wq_w8a8.hip): activation quantiser into the packed activation
+// layout, its test-hook inverse, and the FP8 x FP8 GEMM on packed FP8 weights.
+hipError_t launch_quantize_x(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* xq, hipStream_t stream);
+hipError_t launch_unpack_x(const uint8_t* xq, int M, int K, uint8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
+                       hipStream_t stream);
+
 }  // namespace wq

@@ -19,6 +19,8 @@ __all__ = [
     "wq_lut3_packed_bytes", "wq_pack_lut3", "wq_gemm_lut3",
     "WQ_FMT_LUT3_DENSE", "wq_lut3_dense_packed_bytes", "wq_pack_lut3_dense", "wq_gemm_lut3_dense",
     "wq_unpack_lut3_dense", "pack_lut3_dense", "gemm_lut3_dense",
+    "wq_x_fp8_packed_bytes", "wq_quantize_x_fp8", "wq_gemm_fp8_w8a8", "wq_unpack_x_fp8", "quantize_x_fp8",
+    "gemm_fp8_w8a8",
     "wq_gemm_workspace_bytes", "wq_unpack_fp8_block", "wq_unpack_fp8_block_f32", "wq_unpack_lut3",
     "workspace", "pack_fp8", "pack_lut3", "gemm_fp8", "gemm_lut3",
 ]
@@ -55,6 +57,10 @@ _SIGS = {
     "wq_pack_lut3_dense": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _P]),
     "wq_gemm_lut3_dense": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
     "wq_unpack_lut3_dense": (_INT, [_P, _I64, _I64, _P, _P]),
+    "wq_x_fp8_packed_bytes": (_SZ, [_I64, _I64]),
+    "wq_quantize_x_fp8": (_INT, [_P, _I64, _I64, _I64, _P, _P]),
+    "wq_gemm_fp8_w8a8": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _SZ, _P]),
+    "wq_unpack_x_fp8": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "wq_gemm_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
     "wq_unpack_fp8_block": (_INT, [_P, _I64, _I64, _P, _P]),
     "wq_unpack_fp8_block_f32": (_INT, [_P, _I64, _I64, _P, _P]),
@@ -189,6 +195,23 @@ def wq_unpack_lut3_dense(packed, N: int, K: int, w_f16, stream=None) -> None:
     _check(lib.wq_unpack_lut3_dense(_ptr(packed), N, K, _ptr(w_f16), _stream(stream)), "wq_unpack_lut3_dense")
 
 
+def wq_x_fp8_packed_bytes(M: int, K: int) -> int:
+    return lib.wq_x_fp8_packed_bytes(M, K)
+
+
+def wq_quantize_x_fp8(x, M: int, K: int, xq, stream=None) -> None:
+    _check(lib.wq_quantize_x_fp8(_ptr(x), _ld(x), M, K, _ptr(xq), _stream(stream)), "wq_quantize_x_fp8")
+
+
+def wq_gemm_fp8_w8a8(packed, N: int, K: int, xq, M: int, y, workspace=None, stream=None) -> None:
+    _check(lib.wq_gemm_fp8_w8a8(_ptr(packed), N, K, _ptr(xq), M, _ptr(y), _ld(y), _ptr(workspace),
+                                _nbytes(workspace), _stream(stream)), "wq_gemm_fp8_w8a8")
+
+
+def wq_unpack_x_fp8(xq, M: int, K: int, codes, scales, stream=None) -> None:
+    _check(lib.wq_unpack_x_fp8(_ptr(xq), M, K, _ptr(codes), _ptr(scales), _stream(stream)), "wq_unpack_x_fp8")
+
+
 # -------------------------------------------------------- torch helpers
 
 def workspace(fmt: int, N: int, K: int, device="cuda"):
@@ -249,4 +272,21 @@ def gemm_lut3_dense(packed, N: int, K: int, x, ws=None, stream=None):
     M = x.shape[0]
     y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     wq_gemm_lut3_dense(packed, N, K, x, y, M, ws, stream)
+    return y
+
+
+def quantize_x_fp8(x, stream=None):
+    """Packed FP8 activations (uint8 buffer) of BF16 x [M, K]."""
+    import torch
+    M, K = x.shape[0], x.shape[1]
+    xq = torch.empty(wq_x_fp8_packed_bytes(M, K), dtype=torch.uint8, device=x.device)
+    wq_quantize_x_fp8(x, M, K, xq, stream)
+    return xq
+
+
+def gemm_fp8_w8a8(packed, N: int, K: int, xq, M: int, stream=None):
+    """y [M, N] (bfloat16) = dequant(xq) . dequant(W)^T."""
+    import torch
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    wq_gemm_fp8_w8a8(packed, N, K, xq, M, y, None, stream)
     return y
