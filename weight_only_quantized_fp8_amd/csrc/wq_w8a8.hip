@@ -26,6 +26,8 @@
 // and zero scales.  A weight unit and an activation unit of the same K block
 // therefore put the same k in the same (lane group, byte) slot, which is all
 // the matrix core needs: it sums over the slots.
+#include <cstdlib>
+
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
@@ -151,57 +153,136 @@ __device__ __forceinline__ i32x8_t lds_frag(const uint8_t* unit, int lane)
     return i32x8_t{(int)p.x, (int)p.y, (int)p.z, (int)p.w, (int)q.x, (int)q.y, (int)q.z, (int)q.w};
 }
 
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// LDS address dst + 16 l (dst is wave-uniform; it goes to M0).  The data never
+// passes through VGPRs.  Written as inline assembly on purpose: the compiler
+// then does not treat the instruction as an LDS write and inserts no wait of
+// its own before later LDS reads (it cannot tell the stages apart and would
+// wait for the newest loads); the kernel orders every stage itself with an
+// explicit vmcnt wait and a barrier, and no other vector-memory load is in
+// flight in its loop.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+struct RawBuf {
+    i32x4_t d;                  // buffer descriptor: base, num_records, raw dword3 flags
+};
+
+__device__ __forceinline__ RawBuf raw_buf(const void* base, uint32_t bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return RawBuf{i32x4_t{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), (int)bytes, 0x00020000}};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+__device__ __forceinline__ void dma16(const RawBuf& r, uint32_t dst, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(r.d),
+                   "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory", "m0");
+}
+
 // Work-group tile 128 rows x 128 columns (8 x 8 MFMA tiles, one weight scale
-// block), 4 waves as 2 x 2, each owning 4 x 4 tiles.  Per K block the
-// work-group stages its 8 activation units and 8 weight units (32 KB) in LDS
-// (double-buffered: the next block's units are fetched into registers while
-// the current block is multiplied), then every wave runs 16 MFMAs and folds
-// them onto its FP32 outer accumulators.
+// block), 4 waves as 2 x 2, each owning 4 x 4 tiles.  A K block's operands
+// (8 activation units, 8 weight units: 32 KB) and the 128 rows' activation
+// scales go from memory straight into one of NS LDS stages (buffer loads to
+// LDS, no VGPR staging), NS - 1 blocks ahead of the block being multiplied.
+// Per block every wave waits for its own loads of that stage, the work-group
+// meets at one barrier (after which every wave's loads of the stage have
+// landed and every wave is done with the stage multiplied last), issues the
+// loads of block kb + NS - 1 into that freed stage, and runs its 16 MFMAs,
+// each folded onto the FP32 outer accumulators times sx[m][kb] * sw[nb][kb].
+// The stages are separate LDS arrays and the loop is unrolled by NS, so each
+// read names a fixed stage and the compiler's own waits can tell the stages
+// apart.
 //
 // Work-groups are numbered so that those sharing a weight slab (same column
 // tile, consecutive row tiles) land on the same XCD (the dispatcher deals
 // work-groups to the 8 XCDs round-robin), where the slab stays in that XCD's
 // L2 across the row tiles.
+constexpr int kW8GroupN = 8;                 // column tiles per group of the work order
+constexpr int kW8Ops = 16 * 2048;            // operand bytes of one stage
+constexpr int kW8Stage = kW8Ops + 128 * 4;   // + the activation scales of 128 rows
+
+template <int NS>
 __global__ void __launch_bounds__(256) w8a8_gemm_kernel(W8Args a)
 {
-    constexpr int kStage = 16 * 2048;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    static_assert(NS == 2 || NS == 3, "2 or 3 stages");
+    __shared__ __attribute__((aligned(16))) uint8_t st0[kW8Stage];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[kW8Stage];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[NS == 3 ? kW8Stage : 16];
+
+    // work order: XCD x (work-groups b = x mod 8) takes the contiguous run
+    // [x * per_xcd, (x+1) * per_xcd) of linear indices wl; wl walks groups of
+    // kW8GroupN column tiles, row tile by row tile, so the work-groups an XCD
+    // runs at once cover a rectangle of about 8 x 8 tiles and share each K
+    // slice of both operands through that XCD's L2
     const int b = blockIdx.x;
     const int per_xcd = gridDim.x >> 3;                   // the grid is a multiple of 8
     const int wl = (b & 7) * per_xcd + (b >> 3);
     if (wl >= a.n_wg) return;                             // whole work-group, before any barrier
-    const int nt = wl / a.n_mt, mt = wl - nt * a.n_mt;
+    const int n_nt = a.N >> 7;
+    const int g = wl / (kW8GroupN * a.n_mt), r = wl - g * (kW8GroupN * a.n_mt);
+    const int gn = min(kW8GroupN, n_nt - g * kW8GroupN);  // column tiles in this group
+    const int nt = g * kW8GroupN + r % gn, mt = r / gn;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int KB = a.KB;
-
-    // global -> LDS copy: thread t moves 64 bytes of activation unit t/32 and
-    // 64 bytes of weight unit t/32
-    const int cu = tid >> 5, cofs = (tid & 31) * 64;
     const int m_tiles = a.Mpad >> 4;
-    const buf_t rx = make_buf(a.xq, (uint32_t)((int64_t)m_tiles * KB * 2048));
-    const buf_t rw = make_buf(a.w + (int64_t)(8 * nt + cu) * KB * 2048, (uint32_t)KB * 2048u);
-    const int xt = 8 * mt + cu;                           // activation tile of this thread's copy
-    const uint32_t xoff = xt < m_tiles ? (uint32_t)xt * KB * 2048u + cofs : kBufOutOfRange;
-    const buf_t rsx = make_buf(a.sx, (uint32_t)((int64_t)KB * a.Mpad * 4));
 
-    uint4 px[4], pw[4];
-    auto fetch = [&](int kb) {
+    // Buffer resources are work-group uniform; tile offsets sit in the VGPR
+    // offset, which the bounds check covers: activation tiles and scale rows
+    // past Mpad read zeros.
+    const RawBuf rx = raw_buf(a.xq, (uint32_t)((int64_t)m_tiles * KB * 2048));
+    const RawBuf rw = raw_buf(a.w, (uint32_t)((int64_t)a.N / 16 * KB * 2048));
+    const RawBuf rsx = raw_buf(a.sx, (uint32_t)((int64_t)KB * a.Mpad * 4));
+
+    // copy chunk c = wave + 4i (1 KB each): c < 16 is half c%2 of activation
+    // unit c/2, c >= 16 half c%2 of weight unit (c-16)/2
+    uint32_t voff[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            px[i] = buf_load16(rx, xoff == kBufOutOfRange ? kBufOutOfRange : xoff + 16 * i, (uint32_t)kb * 2048u);
-            pw[i] = buf_load_stream16(rw, cofs + 16 * i, (uint32_t)kb * 2048u);
+    for (int i = 0; i < 8; ++i) {
+        const int c = wave + 4 * i;
+        const int u = (c & 15) >> 1, h = c & 1;
+        if (c < 16) {
+            const int xt = 8 * mt + u;
+            voff[i] = xt < m_tiles ? (uint32_t)xt * KB * 2048u + h * 1024 + lane * 16 : kBufOutOfRange;
+        } else {
+            voff[i] = (uint32_t)(8 * nt + u) * KB * 2048u + h * 1024 + lane * 16;
         }
-    };
-    auto stage = [&](int buf) {
-        uint8_t* s = lds + buf * kStage;
+    }
+    // activation scales: wave w brings rows 32w .. 32w+31 of the tile, 4 a lane, lanes 0..7
+    const int srow = 128 * mt + 32 * wave + 4 * lane;
+    const uint32_t svoff = srow < a.Mpad ? (uint32_t)srow * 4u : kBufOutOfRange;
+
+    // LDS addresses of the stages (M0 operands), computed once
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(st0));
+    const uint32_t lds1 = __builtin_amdgcn_readfirstlane(lds_addr(st1));
+    const uint32_t lds2 = __builtin_amdgcn_readfirstlane(lds_addr(st2));
+    auto issue = [&](int kb, uint32_t st) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<uint4*>(s + cu * 2048 + cofs + 16 * i) = px[i];
-            *reinterpret_cast<uint4*>(s + 8 * 2048 + cu * 2048 + cofs + 16 * i) = pw[i];
+        for (int i = 0; i < 8; ++i) {
+            const int c = wave + 4 * i;
+            dma16(i < 4 ? rx : rw, st + c * 1024, voff[i], (uint32_t)kb * 2048u);
         }
+        if (lane < 8) dma16(rsx, st + kW8Ops + 128 * wave, svoff, (uint32_t)kb * (uint32_t)a.Mpad * 4u);
     };
 
     f32x4_t outer[4][4];
@@ -210,33 +291,22 @@ __global__ void __launch_bounds__(256) w8a8_gemm_kernel(W8Args a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) outer[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // rows of this lane's outputs: 16 * (8mt + 4wm + i) + 4(l/16) + r
-    const int row0 = 16 * (8 * mt + 4 * wm) + 4 * (lane >> 4);
+    const int lrow = 16 * (4 * wm) + 4 * (lane >> 4);     // this lane's first output row in the tile
 
-    fetch(0);
-    stage(0);
-    __syncthreads();
-    for (int kb = 0; kb < KB; ++kb) {
-        if (kb + 1 < KB) fetch(kb + 1);
+    auto compute = [&](int kb, const uint8_t* st) {
         const float swv = load_uniform_f32(a.sw + (int64_t)nt * KB + kb);
         f32x4_t sc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            // the bounds check of a buffer load covers the VGPR offset only, so the
-            // whole offset goes there; rows past Mpad (whole groups of 4) read zeros
-            const int row = row0 + 16 * i;
-            const uint32_t so = row < a.Mpad ? ((uint32_t)kb * (uint32_t)a.Mpad + (uint32_t)row) * 4u : kBufOutOfRange;
-            const uint4 s4 = buf_load16(rsx, so, 0u);
-            sc[i] = f32x4_t{__uint_as_float(s4.x) * swv, __uint_as_float(s4.y) * swv, __uint_as_float(s4.z) * swv,
-                            __uint_as_float(s4.w) * swv};
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + kW8Ops + (lrow + 16 * i) * 4);
+            sc[i] = f32x4_t{v[0] * swv, v[1] * swv, v[2] * swv, v[3] * swv};
         }
-        const uint8_t* s = lds + (kb & 1) * kStage;
         i32x8_t af[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = lds_frag(s + (4 * wm + i) * 2048, lane);
+        for (int i = 0; i < 4; ++i) af[i] = lds_frag(st + (4 * wm + i) * 2048, lane);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const i32x8_t bf = lds_frag(s + (8 + 4 * wn + j) * 2048, lane);
+            const i32x8_t bf = lds_frag(st + (8 + 4 * wn + j) * 2048, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x4_t blk = mfma_fp8(af[i], bf, f32x4_t{0.f, 0.f, 0.f, 0.f});
@@ -244,11 +314,42 @@ __global__ void __launch_bounds__(256) w8a8_gemm_kernel(W8Args a)
                 for (int r = 0; r < 4; ++r) outer[i][j][r] = __builtin_fmaf(blk[r], sc[i][r], outer[i][j][r]);
             }
         }
-        if (kb + 1 < KB) stage((kb + 1) & 1);
-        __syncthreads();
+    };
+
+    // one block: own loads of `cur` done, barrier, refill the stage freed by
+    // the previous block with block kb + NS - 1 (the last block again once past
+    // the end, so every wave always has the same loads in flight), multiply
+    auto step = [&](int kb, const uint8_t* cur, uint32_t nxt) {
+        wait_vmcnt<(NS - 2) * 9>();
+        __builtin_amdgcn_s_barrier();
+        const int kn = kb + NS - 1 < KB ? kb + NS - 1 : KB - 1;
+        issue(kn, nxt);
+        compute(kb, cur);
+    };
+
+    issue(0, lds0);
+    if constexpr (NS == 3) issue(KB > 1 ? 1 : 0, lds1);
+    if constexpr (NS == 2) {
+        for (int kb = 0;; kb += 2) {
+            step(kb, st0, lds1);
+            if (kb + 1 >= KB) break;
+            step(kb + 1, st1, lds0);
+            if (kb + 2 >= KB) break;
+        }
+    } else {
+        for (int kb = 0;; kb += 3) {
+            step(kb, st0, lds2);
+            if (kb + 1 >= KB) break;
+            step(kb + 1, st1, lds0);
+            if (kb + 2 >= KB) break;
+            step(kb + 2, st2, lds1);
+            if (kb + 3 >= KB) break;
+        }
     }
+    wait_vmcnt<0>();                                      // no load left writing LDS
 
     // D of a 16x16 tile: lane l holds rows 4(l/16)..+3 of column l%16
+    const int row0 = 128 * mt + lrow;
     const int col0 = 16 * (8 * nt + 4 * wn) + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -282,6 +383,18 @@ hipError_t launch_unpack_x(const uint8_t* xq, int M, int K, uint8_t* codes, floa
     return hipGetLastError();
 }
 
+// LDS stages of the W8A8 GEMM: 2 (one block in flight, two work-groups per
+// CU: measured faster) unless WQ_W8A8_STAGES=3 (two blocks in flight, one
+// work-group per CU).
+static int w8a8_stages()
+{
+    static const int n = [] {
+        const char* p = std::getenv("WQ_W8A8_STAGES");
+        return (p && std::atoi(p) == 3) ? 3 : 2;
+    }();
+    return n;
+}
+
 hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
                        hipStream_t stream)
 {
@@ -299,11 +412,10 @@ hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq,
     a.n_mt = (a.Mpad + 127) / 128;
     a.n_wg = a.n_mt * (N / 128);
     const int grid = (a.n_wg + 7) & ~7;
-    const size_t lds = 2 * 16 * 2048;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(w8a8_gemm_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(w8a8_gemm_kernel, dim3(grid), dim3(256), lds, stream, a);
+    if (w8a8_stages() == 2)
+        hipLaunchKernelGGL(w8a8_gemm_kernel<2>, dim3(grid), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(w8a8_gemm_kernel<3>, dim3(grid), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
