@@ -101,8 +101,12 @@ def test_quantizer_matches_oracle_bit_exact(M, K, ld):
         assert not last[:, :, lanes, :].any()
 
 
+# M above 4096 runs the 256 x 256 work-group tile (WQ_W8A8_TILE=256 forces it
+# for every M; 384 and 640 columns leave a ragged column tile there), smaller M
+# the 128 x 128 one
 W8A8_SHAPES = [(256, 512, 1), (384, 1024, 16), (1024, 640, 33), (640, 2048, 130), (256, 256, 300),
-               (512, 1152, 129)]
+               (512, 1152, 129), (384, 1024, 700), (640, 768, 530), (1280, 512, 1030), (384, 512, 4100),
+               (640, 256, 4400)]
 
 
 @pytest.mark.parametrize("N,K,M", W8A8_SHAPES)
@@ -152,6 +156,12 @@ def test_w8a8_rows_determinism_strides():
         assert np.array_equal(y2, y[lo:hi]), (lo, hi)
     for _ in range(5):
         assert np.array_equal(run(packed, N, K, xq, M)[0], y)
+    # the 256 x 256 tile (M > 4096) folds the same MFMA blocks in the same
+    # order as the 128 x 128 tile: rows agree bit for bit across the two
+    xbig = np.vstack([xb, synth.x_bf16(4200 - M, K, 64)])
+    xqb, _, _ = quantize(xbig, K)
+    yb, _ = run(packed, N, K, xqb, 4200)
+    assert np.array_equal(yb[:M], y)
     ldy = N + 40
     canary = np.full((M, ldy), 0x7FAB, dtype=np.uint16)
     ys, full = run(packed, N, K, xq, M, ldy=ldy, y_init=canary)
@@ -189,7 +199,7 @@ def test_w8a8_graph_replay():
         assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), rep
 
 
-@pytest.mark.parametrize("M", [64, 512])
+@pytest.mark.parametrize("M", [64, 512, 1024])
 def test_w8a8_gate_up_size(M):
     """The FFN gate/up matrix (17408 x 5120): every column of the first and last
     128 and 768 random ones in between, all M rows."""

@@ -190,175 +190,168 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
 
 __device__ __forceinline__ void dma16(const RawBuf& r, uint32_t dst, uint32_t voff, uint32_t soff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(r.d),
-                   "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "memory", "m0");
+                 : "v"(voff), "s"(r.d), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                   "{m0}"(__builtin_amdgcn_readfirstlane(dst))
+                 : "memory");
 }
 
-// Work-group tile 128 rows x 128 columns (8 x 8 MFMA tiles, one weight scale
-// block), 4 waves as 2 x 2, each owning 4 x 4 tiles.  A K block's operands
-// (8 activation units, 8 weight units: 32 KB) and the 128 rows' activation
-// scales go from memory straight into one of NS LDS stages (buffer loads to
-// LDS, no VGPR staging), NS - 1 blocks ahead of the block being multiplied.
-// Per block every wave waits for its own loads of that stage, the work-group
-// meets at one barrier (after which every wave's loads of the stage have
-// landed and every wave is done with the stage multiplied last), issues the
-// loads of block kb + NS - 1 into that freed stage, and runs its 16 MFMAs,
-// each folded onto the FP32 outer accumulators times sx[m][kb] * sw[nb][kb].
-// The stages are separate LDS arrays and the loop is unrolled by NS, so each
-// read names a fixed stage and the compiler's own waits can tell the stages
-// apart.
+// Work-group tile BM x BN = (16 WMT WVM) x (16 WNT WVN): WVM x WVN waves, each
+// owning WMT x WNT MFMA tiles of 16 x 16.  A K block's operands (BM/16
+// activation units and BN/16 weight units of 2 KB) and the BM rows'
+// activation scales go from memory straight into one of two LDS stages
+// (buffer loads to LDS, no VGPR staging), one block ahead of the block being
+// multiplied.  Per block every wave waits for its own loads of that stage, the
+// work-group meets at one barrier (after which every wave's loads of the stage
+// have landed and every wave is done with the other stage), issues the loads
+// of block kb + 1 into the other stage, and runs its WMT x WNT MFMAs, each
+// folded onto the FP32 outer accumulators times sx[m][kb] * sw[nb][kb].  The
+// stages are separate LDS arrays and the loop is unrolled by two, so each read
+// names a fixed stage.
 //
-// Work-groups are numbered so that those sharing a weight slab (same column
-// tile, consecutive row tiles) land on the same XCD (the dispatcher deals
-// work-groups to the 8 XCDs round-robin), where the slab stays in that XCD's
-// L2 across the row tiles.
-constexpr int kW8GroupN = 8;                 // column tiles per group of the work order
-constexpr int kW8Ops = 16 * 2048;            // operand bytes of one stage
-constexpr int kW8Stage = kW8Ops + 128 * 4;   // + the activation scales of 128 rows
-
-template <int NS>
-__global__ void __launch_bounds__(256) w8a8_gemm_kernel(W8Args a)
+// Work order: XCD x (work-groups b = x mod 8) takes the contiguous run
+// [x * per_xcd, (x+1) * per_xcd) of linear indices; these walk groups of GN
+// column tiles row tile by row tile, so the work-groups an XCD runs at once
+// cover a rectangle of tiles and share each K slice of both operands through
+// that XCD's L2.
+template <int WMT, int WNT, int WVM, int WVN, int GN>
+__global__ void __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(2, 2)))
+w8a8_gemm_kernel(W8Args a)
 {
-    static_assert(NS == 2 || NS == 3, "2 or 3 stages");
-    __shared__ __attribute__((aligned(16))) uint8_t st0[kW8Stage];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[kW8Stage];
-    __shared__ __attribute__((aligned(16))) uint8_t st2[NS == 3 ? kW8Stage : 16];
+    constexpr int WAVES = WVM * WVN;
+    constexpr int TM = WMT * WVM, TN = WNT * WVN;       // 16-row / 16-column tiles of the work-group
+    constexpr int BM = 16 * TM, BN = 16 * TN;
+    constexpr int OPS = (TM + TN) * 2048;               // operand bytes of one stage
+    constexpr int STAGE = OPS + BM * 4;                 // + the activation scales of BM rows
+    constexpr int CPW = 2 * (TM + TN) / WAVES;          // 1 KB copy chunks per wave and stage
+    constexpr int SROWS = BM / WAVES;                   // scale rows each wave copies
+    static_assert(2 * (TM + TN) % WAVES == 0 && SROWS % 4 == 0 && SROWS <= 256, "copy split");
+    static_assert(WNT * 16 <= 128 && 128 % (WNT * 16) == 0, "a wave's columns share one weight scale block");
+    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
 
-    // work order: XCD x (work-groups b = x mod 8) takes the contiguous run
-    // [x * per_xcd, (x+1) * per_xcd) of linear indices wl; wl walks groups of
-    // kW8GroupN column tiles, row tile by row tile, so the work-groups an XCD
-    // runs at once cover a rectangle of about 8 x 8 tiles and share each K
-    // slice of both operands through that XCD's L2
     const int b = blockIdx.x;
     const int per_xcd = gridDim.x >> 3;                   // the grid is a multiple of 8
     const int wl = (b & 7) * per_xcd + (b >> 3);
     if (wl >= a.n_wg) return;                             // whole work-group, before any barrier
-    const int n_nt = a.N >> 7;
-    const int g = wl / (kW8GroupN * a.n_mt), r = wl - g * (kW8GroupN * a.n_mt);
-    const int gn = min(kW8GroupN, n_nt - g * kW8GroupN);  // column tiles in this group
-    const int nt = g * kW8GroupN + r % gn, mt = r / gn;
+    const int n_nt = (a.N + BN - 1) / BN;
+    const int g = wl / (GN * a.n_mt), r = wl - g * (GN * a.n_mt);
+    const int gn = min(GN, n_nt - g * GN);                // column tiles in this group
+    const int nt = g * GN + r % gn, mt = r / gn;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WVN, wn = wave - wm * WVN;
     const int KB = a.KB;
-    const int m_tiles = a.Mpad >> 4;
+    const int m_tiles = a.Mpad >> 4, n_tiles = a.N >> 4;
 
     // Buffer resources are work-group uniform; tile offsets sit in the VGPR
     // offset, which the bounds check covers: activation tiles and scale rows
-    // past Mpad read zeros.
+    // past Mpad, and weight tiles past N, read zeros.
     const RawBuf rx = raw_buf(a.xq, (uint32_t)((int64_t)m_tiles * KB * 2048));
-    const RawBuf rw = raw_buf(a.w, (uint32_t)((int64_t)a.N / 16 * KB * 2048));
+    const RawBuf rw = raw_buf(a.w, (uint32_t)((int64_t)n_tiles * KB * 2048));
     const RawBuf rsx = raw_buf(a.sx, (uint32_t)((int64_t)KB * a.Mpad * 4));
 
-    // copy chunk c = wave + 4i (1 KB each): c < 16 is half c%2 of activation
-    // unit c/2, c >= 16 half c%2 of weight unit (c-16)/2
-    uint32_t voff[8];
+    // copy chunk c = wave + WAVES i (1 KB each): c < 2 TM is half c%2 of
+    // activation unit c/2, the rest half c%2 of weight unit (c - 2 TM)/2
+    uint32_t voff[CPW];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int c = wave + 4 * i;
-        const int u = (c & 15) >> 1, h = c & 1;
-        if (c < 16) {
-            const int xt = 8 * mt + u;
+    for (int i = 0; i < CPW; ++i) {
+        const int c = wave + WAVES * i;
+        const int h = c & 1;
+        if (c < 2 * TM) {
+            const int xt = TM * mt + (c >> 1);
             voff[i] = xt < m_tiles ? (uint32_t)xt * KB * 2048u + h * 1024 + lane * 16 : kBufOutOfRange;
         } else {
-            voff[i] = (uint32_t)(8 * nt + u) * KB * 2048u + h * 1024 + lane * 16;
+            const int wt = TN * nt + ((c - 2 * TM) >> 1);
+            voff[i] = wt < n_tiles ? (uint32_t)wt * KB * 2048u + h * 1024 + lane * 16 : kBufOutOfRange;
         }
     }
-    // activation scales: wave w brings rows 32w .. 32w+31 of the tile, 4 a lane, lanes 0..7
-    const int srow = 128 * mt + 32 * wave + 4 * lane;
+    // activation scales: wave w brings rows SROWS w .. SROWS (w+1) - 1 of the tile, 4 a lane
+    const int srow = BM * mt + SROWS * wave + 4 * lane;
     const uint32_t svoff = srow < a.Mpad ? (uint32_t)srow * 4u : kBufOutOfRange;
 
     // LDS addresses of the stages (M0 operands), computed once
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(st0));
     const uint32_t lds1 = __builtin_amdgcn_readfirstlane(lds_addr(st1));
-    const uint32_t lds2 = __builtin_amdgcn_readfirstlane(lds_addr(st2));
     auto issue = [&](int kb, uint32_t st) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = wave + 4 * i;
-            dma16(i < 4 ? rx : rw, st + c * 1024, voff[i], (uint32_t)kb * 2048u);
+        for (int i = 0; i < CPW; ++i) {
+            const int c = wave + WAVES * i;
+            dma16(c < 2 * TM ? rx : rw, st + c * 1024, voff[i], (uint32_t)kb * 2048u);
         }
-        if (lane < 8) dma16(rsx, st + kW8Ops + 128 * wave, svoff, (uint32_t)kb * (uint32_t)a.Mpad * 4u);
+        if (lane < SROWS / 4)
+            dma16(rsx, st + OPS + SROWS * 4 * wave, svoff, (uint32_t)kb * (uint32_t)a.Mpad * 4u);
     };
 
-    f32x4_t outer[4][4];
+    f32x4_t outer[WMT][WNT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WMT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) outer[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < WNT; ++j) outer[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int lrow = 16 * (4 * wm) + 4 * (lane >> 4);     // this lane's first output row in the tile
+    const int lrow = 16 * WMT * wm + 4 * (lane >> 4);     // this lane's first output row in the tile
+    const int wcol = TN * nt + WNT * wn;                  // the wave's first 16-column tile
+    const int nb = min(wcol >> 3, (a.N >> 7) - 1);        // its weight scale block (clamped past N)
 
     auto compute = [&](int kb, const uint8_t* st) {
-        const float swv = load_uniform_f32(a.sw + (int64_t)nt * KB + kb);
-        f32x4_t sc[4];
+        const float swv = load_uniform_f32(a.sw + (int64_t)nb * KB + kb);
+        f32x4_t sc[WMT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + kW8Ops + (lrow + 16 * i) * 4);
+        for (int i = 0; i < WMT; ++i) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + OPS + (lrow + 16 * i) * 4);
             sc[i] = f32x4_t{v[0] * swv, v[1] * swv, v[2] * swv, v[3] * swv};
         }
-        i32x8_t af[4];
+        i32x8_t af[WMT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = lds_frag(st + (4 * wm + i) * 2048, lane);
+        for (int i = 0; i < WMT; ++i) af[i] = lds_frag(st + (WMT * wm + i) * 2048, lane);
+        // all WMT products of a column tile are issued before any is folded, so
+        // the fold of one waits for an MFMA issued WMT - 1 slots earlier
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const i32x8_t bf = lds_frag(st + (8 + 4 * wn + j) * 2048, lane);
+        for (int j = 0; j < WNT; ++j) {
+            const i32x8_t bf = lds_frag(st + (TM + WNT * wn + j) * 2048, lane);
+            f32x4_t blk[WMT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4_t blk = mfma_fp8(af[i], bf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            for (int i = 0; i < WMT; ++i) blk[i] = mfma_fp8(af[i], bf, f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int r = 0; r < 4; ++r) outer[i][j][r] = __builtin_fmaf(blk[r], sc[i][r], outer[i][j][r]);
-            }
+            for (int i = 0; i < WMT; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) outer[i][j][q] = __builtin_fmaf(blk[i][q], sc[i][q], outer[i][j][q]);
         }
     };
 
-    // one block: own loads of `cur` done, barrier, refill the stage freed by
-    // the previous block with block kb + NS - 1 (the last block again once past
-    // the end, so every wave always has the same loads in flight), multiply
+    // one block: own loads of `cur` done, barrier, refill the other stage with
+    // block kb + 1 (the last block again at the end, so every wave always has
+    // the same loads in flight), multiply
     auto step = [&](int kb, const uint8_t* cur, uint32_t nxt) {
-        wait_vmcnt<(NS - 2) * 9>();
+        wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        const int kn = kb + NS - 1 < KB ? kb + NS - 1 : KB - 1;
-        issue(kn, nxt);
+        issue(kb + 1 < KB ? kb + 1 : KB - 1, nxt);
         compute(kb, cur);
     };
 
     issue(0, lds0);
-    if constexpr (NS == 3) issue(KB > 1 ? 1 : 0, lds1);
-    if constexpr (NS == 2) {
-        for (int kb = 0;; kb += 2) {
-            step(kb, st0, lds1);
-            if (kb + 1 >= KB) break;
-            step(kb + 1, st1, lds0);
-            if (kb + 2 >= KB) break;
-        }
-    } else {
-        for (int kb = 0;; kb += 3) {
-            step(kb, st0, lds2);
-            if (kb + 1 >= KB) break;
-            step(kb + 1, st1, lds0);
-            if (kb + 2 >= KB) break;
-            step(kb + 2, st2, lds1);
-            if (kb + 3 >= KB) break;
-        }
+    for (int kb = 0;; kb += 2) {
+        step(kb, st0, lds1);
+        if (kb + 1 >= KB) break;
+        step(kb + 1, st1, lds0);
+        if (kb + 2 >= KB) break;
     }
     wait_vmcnt<0>();                                      // no load left writing LDS
 
     // D of a 16x16 tile: lane l holds rows 4(l/16)..+3 of column l%16
-    const int row0 = 128 * mt + lrow;
-    const int col0 = 16 * (8 * nt + 4 * wn) + (lane & 15);
+    const int row0 = BM * mt + lrow;
+    const int col0 = 16 * wcol + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WMT; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = row0 + 16 * i + r;
+        for (int q = 0; q < 4; ++q) {
+            const int m = row0 + 16 * i + q;
             if (m < a.M) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) a.y[(int64_t)m * a.ldy + col0 + 16 * j] = f32_to_bf16_rne(outer[i][j][r]);
+                for (int j = 0; j < WNT; ++j)
+                    if (col0 + 16 * j < a.N) a.y[(int64_t)m * a.ldy + col0 + 16 * j] = f32_to_bf16_rne(outer[i][j][q]);
             }
         }
 }
@@ -383,16 +376,22 @@ hipError_t launch_unpack_x(const uint8_t* xq, int M, int K, uint8_t* codes, floa
     return hipGetLastError();
 }
 
-// LDS stages of the W8A8 GEMM: 2 (one block in flight, two work-groups per
-// CU: measured faster) unless WQ_W8A8_STAGES=3 (two blocks in flight, one
-// work-group per CU).
-static int w8a8_stages()
+// Tile per M: 128 x 128 (4 waves of 64 x 64, two work-groups per CU) up to
+// kW8BigM rows, 256 x 256 above (8 waves of 64 x 128: twice the MFMAs per byte
+// read from LDS, one work-group per CU).  Measured on the FFN shapes: the
+// smaller tile is as fast or faster up to M = 4096 (more work-groups, two per
+// CU), the larger one slightly faster at M = 8192.
+constexpr int kW8BigM = 4096;
+
+template <int WMT, int WNT, int WVM, int WVN, int GN>
+static hipError_t launch_w8a8_tile(W8Args a, hipStream_t stream)
 {
-    static const int n = [] {
-        const char* p = std::getenv("WQ_W8A8_STAGES");
-        return (p && std::atoi(p) == 3) ? 3 : 2;
-    }();
-    return n;
+    constexpr int BM = 16 * WMT * WVM, BN = 16 * WNT * WVN;
+    a.n_mt = (a.Mpad + BM - 1) / BM;
+    a.n_wg = a.n_mt * ((a.N + BN - 1) / BN);
+    const int grid = (a.n_wg + 7) & ~7;
+    hipLaunchKernelGGL((w8a8_gemm_kernel<WMT, WNT, WVM, WVN, GN>), dim3(grid), dim3(64 * WVM * WVN), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
@@ -409,14 +408,13 @@ hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq,
     a.sx = reinterpret_cast<const float*>(xq + (int64_t)a.Mpad * K);
     a.y = y;
     a.ldy = ldy;
-    a.n_mt = (a.Mpad + 127) / 128;
-    a.n_wg = a.n_mt * (N / 128);
-    const int grid = (a.n_wg + 7) & ~7;
-    if (w8a8_stages() == 2)
-        hipLaunchKernelGGL(w8a8_gemm_kernel<2>, dim3(grid), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(w8a8_gemm_kernel<3>, dim3(grid), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    static const int forced = [] {          // WQ_W8A8_TILE=128|256: one tile for every M (sweeps)
+        const char* p = std::getenv("WQ_W8A8_TILE");
+        return p ? std::atoi(p) : 0;
+    }();
+    const bool big = forced ? forced == 256 : a.Mpad > kW8BigM;
+    if (big) return launch_w8a8_tile<4, 8, 4, 2, 4>(a, stream);
+    return launch_w8a8_tile<4, 4, 2, 2, 8>(a, stream);
 }
 
 }  // namespace wq
