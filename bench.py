@@ -181,6 +181,68 @@ def time_workload(w: Workload, steps: int, warmup: int, use_graph: bool = True):
     }
 
 
+FP8_MFMA_PEAK_TFLOPS = 5000.0
+
+
+def time_w8a8(name: str, M: int, steps: int = 20, copies: int = 4) -> dict:
+    """The W8A8 tier on an FFN shape at a prefill batch: one step quantises the
+    BF16 activations (wq_quantize_x_fp8) and runs wq_gemm_fp8_w8a8 on a packed
+    FP8 weight matrix; `copies` weight copies (more than the 256 MB Infinity
+    Cache together) rotate over the steps.  The steps are replayed from a HIP
+    graph, timed with HIP events; the two kernels are also timed alone."""
+    import numpy as np
+    import torch
+    import synth
+    from weight_only_quantized_fp8_amd import wq
+    fmt, N, K, _ = synth.CONFIGS[name]
+    dev = "cuda:0"
+    codes, scales = synth.fp8_weights(N, K, synth.SEEDS[name])
+    p0 = wq.pack_fp8(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev))
+    del codes
+    packed = [p0] + [p0.clone() for _ in range(copies - 1)]
+    x = torch.from_numpy(synth.x_bf16(M, K, synth.SEEDS[name] + 100).view(np.int16)).to(dev).view(torch.bfloat16)
+    xq = torch.empty(wq.wq_x_fp8_packed_bytes(M, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        wq.wq_quantize_x_fp8(x, M, K, xq)
+        wq.wq_gemm_fp8_w8a8(packed[i % copies], N, K, xq, M, y)
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev[0].record()
+    g.replay()
+    ev[1].record()
+    for i in range(steps):
+        wq.wq_quantize_x_fp8(x, M, K, xq)
+    ev[2].record()
+    ev[3].record()
+    for i in range(steps):
+        wq.wq_gemm_fp8_w8a8(packed[i % copies], N, K, xq, M, y)
+    ev[4].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
+    q_us = ev[1].elapsed_time(ev[2]) * 1e3 / steps
+    g_us = ev[3].elapsed_time(ev[4]) * 1e3 / steps
+    tf = 2.0 * M * N * K / (g_us * 1e-6) / 1e12
+    del packed, g
+    torch.cuda.empty_cache()
+    return {"us_per_call": round(us, 2), "quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2),
+            "gemm_TFLOPs": round(tf, 1), "pct_of_fp8_mfma_peak": round(100 * tf / FP8_MFMA_PEAK_TFLOPS, 1)}
+
+
 def cpu_baseline(name: str, M: int, min_seconds: float = 3.0, max_reps: int = 20):
     """The oracle as it stands, on the host cores, over the whole workload (all
     outputs), repeated until min_seconds of wall time; the median pass counts."""
@@ -220,6 +282,8 @@ def main(argv=None) -> int:
     ap.add_argument("--all", action="store_true", help="also time every other workload and M")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="launch each step from Python instead of a HIP graph")
+    ap.add_argument("--w8a8", action="store_true",
+                    help="time only the W8A8 tier (quantise + FP8 x FP8 GEMM) on --config at --M and print its line")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -234,6 +298,21 @@ def main(argv=None) -> int:
         return 2
 
     import synth
+    if args.w8a8:
+        fmt, N, K, _ = synth.CONFIGS[args.config]
+        if fmt != "fp8":
+            print("--w8a8 needs an FP8 workload", file=sys.stderr)
+            return 2
+        r = time_w8a8(args.config, args.M, steps=args.steps)
+        print(json.dumps({"metric": "W8A8 GEMM TFLOP/s (quantise + FP8 x FP8 GEMM per step)",
+                          "value": r["gemm_TFLOPs"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                          "higher_is_better": True, "dtype": "fp8", "data": "synthetic",
+                          "config": {"workload": "%s w8a8 N=%d K=%d M=%d" % (args.config, N, K, args.M)},
+                          "roofline": {"bound": "mfma", "achieved": r["gemm_TFLOPs"],
+                                       "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": round(r["gemm_TFLOPs"] / FP8_MFMA_PEAK_TFLOPS, 4)},
+                          "timing": r}), flush=True)
+        return 0
     print("bench: preparing %s M=%d" % (args.config, args.M), file=sys.stderr, flush=True)
     w = Workload(args.config, args.M)
     r = time_workload(w, args.steps, args.warmup, use_graph=not args.eager)
@@ -291,6 +370,10 @@ def main(argv=None) -> int:
                     "passes": wk.launches_per_step()}
                 del wk
                 torch.cuda.empty_cache()
+        for name in ("gate_up", "down"):
+            for M in (512, 2048, 4096):
+                print("bench: w8a8 %s M=%d" % (name, M), file=sys.stderr, flush=True)
+                extra["w8a8_%s_M%d" % (name, M)] = time_w8a8(name, M)
         out["extra"] = extra
 
     if not args.no_cpu:
