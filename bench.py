@@ -287,9 +287,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the kernel is "
-              "sized for one GPU's share; see DESIGN.md for how it would shard). Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (its kernels are sized for "
+              "one GPU's share of a projection). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
