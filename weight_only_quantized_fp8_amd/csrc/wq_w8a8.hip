@@ -306,18 +306,27 @@ w8a8_gemm_kernel(W8Args a)
         i32x8_t af[WMT];
 #pragma unroll
         for (int i = 0; i < WMT; ++i) af[i] = lds_frag(st + (WMT * wm + i) * 2048, lane);
-        // all WMT products of a column tile are issued before any is folded, so
-        // the fold of one waits for an MFMA issued WMT - 1 slots earlier
+        // software-pipelined over column tiles: the products of column tile j + 1
+        // are issued before those of tile j are folded, so a fold never waits
+        // for an MFMA issued just before it
+        f32x4_t blk[2][WMT];
+        {
+            const i32x8_t bf = lds_frag(st + (TM + WNT * wn) * 2048, lane);
+#pragma unroll
+            for (int i = 0; i < WMT; ++i) blk[0][i] = mfma_fp8(af[i], bf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        }
 #pragma unroll
         for (int j = 0; j < WNT; ++j) {
-            const i32x8_t bf = lds_frag(st + (TM + WNT * wn + j) * 2048, lane);
-            f32x4_t blk[WMT];
+            if (j + 1 < WNT) {
+                const i32x8_t bf = lds_frag(st + (TM + WNT * wn + j + 1) * 2048, lane);
 #pragma unroll
-            for (int i = 0; i < WMT; ++i) blk[i] = mfma_fp8(af[i], bf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                for (int i = 0; i < WMT; ++i) blk[(j + 1) & 1][i] = mfma_fp8(af[i], bf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            }
 #pragma unroll
             for (int i = 0; i < WMT; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) outer[i][j][q] = __builtin_fmaf(blk[i][q], sc[i][q], outer[i][j][q]);
+                for (int q = 0; q < 4; ++q)
+                    outer[i][j][q] = __builtin_fmaf(blk[j & 1][i][q], sc[i][q], outer[i][j][q]);
         }
     };
 
