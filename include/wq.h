@@ -51,6 +51,8 @@
  *   WQ_SN           = 1 .. 8              column-waves sharing staged activations
  *   WQ_SPLIT        = 1 .. 16             waves per work-group (SN x K-groups)
  *   WQ_WAVES_PER_CU = 1 .. 32             resident waves per CU the plan aims for (4)
+ *   WQ_W8A8_TILE    = 128 | 256           W8A8 work-group tile for every M (default: 128 x 128
+ *                                         up to M = 4096, 256 x 256 above)
  */
 #ifndef WQ_H_
 #define WQ_H_
