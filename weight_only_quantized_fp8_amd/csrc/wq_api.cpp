@@ -128,11 +128,11 @@ struct TableEntry {
 constexpr TableEntry kTable[] = {
     {wq::KIND_MFMA_FP8, 17408, 5120, 1, 5, 5},    // FFN gate/up
     {wq::KIND_MFMA_FP8, 5120, 17408, 1, 2, 8},    // FFN down
-    {wq::KIND_MFMA_FP8, 6144, 5120, 1, 2, 4},     // attention Q
+    {wq::KIND_MFMA_FP8, 6144, 5120, 1, 2, 8},     // attention Q
     {wq::KIND_MFMA_FP8, 1024, 5120, 1, 1, 4},     // attention K, V
     {wq::KIND_MFMA_FP8, 5120, 6144, 1, 2, 8},     // attention output
     {wq::KIND_MFMA_LUT, 28672, 8192, 1, 7, 14},   // 3-bit LUT 28672x8192 (two K groups)
-    {wq::KIND_MFMA_LUT3D, 28672, 8192, 1, 8, 8},  // 3-bit LUT 28672x8192, dense codes
+    {wq::KIND_MFMA_LUT3D, 28672, 8192, 1, 8, 16}, // 3-bit LUT 28672x8192, dense codes (two K groups)
     {wq::KIND_GEMV_FP8, 6144, 5120, 1, 2, 8},     // attention Q (other GEMV shapes: the FP8 rows)
     {wq::KIND_GEMV_FP8, 1024, 5120, 1, 2, 8},     // attention K, V
 };

@@ -25,21 +25,26 @@ enum Kind : int {
 
 constexpr bool is_lut_kind(int kind) { return kind == KIND_MFMA_LUT || kind == KIND_MFMA_LUT3D; }
 
-// K blocks of activations staged per chunk (the K group synchronises once
-// per chunk).
-constexpr int kChunkBlocks = 4;
+// Size of an activation chunk (the K group synchronises once per chunk) in
+// 16-row K blocks, per kernel kind and row tiles MT (a 32-row chunk holds
+// half as many K blocks).  Measured on MI355X: the FP8 MFMA tile runs best
+// with two K blocks per chunk at any M -- 6-15% faster than four at M <= 16
+// for the low-N projections, while one 32-row block per chunk costs 8-19% at
+// M = 32 -- and the LUT tile with four 16-row blocks, its 7-wave work-groups
+// running 7% slower with two.
+constexpr int chunk_blocks16(int kind, int mt) { return kind == KIND_MFMA_FP8 ? 2 * mt : 4; }
 
 // Each K group of an MFMA work-group double-buffers one activation chunk in
-// LDS (2 x 4 K blocks x 16 rows x 272 bytes = 34816 bytes); the 160 KiB of LDS
-// of a compute unit bound the K groups of one work-group at 4.
+// LDS (at most 2 x 4 K blocks x 16 rows x 272 bytes = 34816 bytes); the 160
+// KiB of LDS of a compute unit bound the K groups of one work-group at 4.
 constexpr int kMaxKGroups = 4;
 
 // 16-byte activation pieces each lane loads per chunk when SN column-waves
-// share it: ceil(chunk pieces / (64 * SN)); a chunk is 4 K blocks x 16 rows x
-// 16 pieces for the MFMA tiles, 4 K blocks x 4 rows x 16 pieces for the GEMV.
-constexpr int x_pieces_per_lane(int kind, int sn)
+// share it: ceil(chunk pieces / (64 * SN)); a chunk is chunk_blocks16 blocks
+// x 16 rows x 16 pieces for the MFMA tiles, x 4 rows x 16 pieces for the GEMV.
+constexpr int x_pieces_per_lane(int kind, int sn, int mt = 1)
 {
-    const int pieces = kChunkBlocks * (kind == KIND_GEMV_FP8 ? 4 : 16) * 16;
+    const int pieces = chunk_blocks16(kind, mt) * (kind == KIND_GEMV_FP8 ? 4 : 16) * 16;
     return (pieces + 64 * sn - 1) / (64 * sn);
 }
 

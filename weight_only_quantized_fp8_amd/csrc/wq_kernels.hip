@@ -60,7 +60,8 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_page[4096];
 // ======================================================================
 
 // ---- activation staging for the MFMA tiles ---------------------------------
-// x is staged through LDS in chunks of kChunkBlocks K blocks.  The SN
+// x is staged through LDS in chunks of chunk_blocks16(kind, MT) 16-row K
+// blocks.  The SN
 // column-waves of a K group share every chunk: its 16-byte pieces are dealt
 // round-robin over the group's SN*64 lanes, consecutive lanes taking
 // consecutive pieces of one row, so each load instruction reads whole
@@ -76,12 +77,14 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_page[4096];
 // chunk holds half as many K blocks, so the chunk's bytes and pieces stay the
 // same.
 constexpr int kXRowBytes = 128 * 2 + 16;                    // padded LDS row of one K block
-constexpr int kXChunkPieces = kChunkBlocks * 16 * 16;       // 16-byte pieces per chunk
 
-template <int XPL, int MT>   // pieces per lane: >= kXChunkPieces / (64 * SN); row tiles
+// XPL: pieces per lane, >= kXChunkPieces / (64 * SN); MT: row tiles; CB: the
+// chunk size in 16-row K blocks
+template <int XPL, int MT, int CB>
 struct XChunk {
+    static constexpr int kXChunkPieces = CB * 16 * 16;      // 16-byte pieces per chunk
     static constexpr int kRows = 16 * MT;
-    static constexpr int kBlocks = kChunkBlocks / MT;       // K blocks per chunk
+    static constexpr int kBlocks = CB / MT;                 // K blocks per chunk
     static constexpr int kBlockBytes = kRows * kXRowBytes;
     static constexpr int kChunkBytes = kBlocks * kBlockBytes;
     static_assert(kBlocks * kRows * 16 == kXChunkPieces, "a chunk has the same pieces for every MT");
@@ -134,12 +137,13 @@ __device__ __forceinline__ uint4 x_frag(const uint8_t* blk, int lane, int k, int
 // once per use), loaded as 4 rows x 256-byte runs per instruction.
 constexpr int kGemvRows = 4;
 constexpr int kGemvBlockBytes = kGemvRows * 128 * 4;
-constexpr int kGemvChunkPieces = kChunkBlocks * kGemvRows * 16;   // 16-byte BF16 pieces per chunk
+constexpr int kGemvChunkBlocks = chunk_blocks16(KIND_GEMV_FP8, 1);
+constexpr int kGemvChunkPieces = kGemvChunkBlocks * kGemvRows * 16;   // 16-byte BF16 pieces per chunk
 
 template <int XPL>   // pieces per lane: >= kGemvChunkPieces / (64 * SN)
 struct XChunkF32 {
-    static constexpr int kBlocks = kChunkBlocks;
-    static constexpr int kChunkBytes = kChunkBlocks * kGemvBlockBytes;
+    static constexpr int kBlocks = kGemvChunkBlocks;
+    static constexpr int kChunkBytes = kGemvChunkBlocks * kGemvBlockBytes;
     static constexpr int kBlockBytes = kGemvBlockBytes;
     buf_t rx;
     uint32_t vo[XPL];
@@ -239,7 +243,7 @@ struct MfmaFp8 : Fp8Stream<NT> {
     static constexpr int NTILES = NT;
     static constexpr int ROWS = 16 * MT;
     static constexpr int KALIGN = 1;      // K-group ranges start at any K block
-    template <int XPL> using Stage = XChunk<XPL, MT>;
+    template <int XPL> using Stage = XChunk<XPL, MT, chunk_blocks16(KIND_MFMA_FP8, MT)>;
     using typename Fp8Stream<NT>::Unit;
     using Fp8Stream<NT>::lane;
     using Fp8Stream<NT>::ntiles;
@@ -333,7 +337,7 @@ struct MfmaLut {
     static constexpr int NTILES = NT;
     static constexpr int ROWS = 16 * MT;
     static constexpr int KALIGN = 8;      // K blocks per group-scale load
-    template <int XPL> using Stage = XChunk<XPL, MT>;
+    template <int XPL> using Stage = XChunk<XPL, MT, chunk_blocks16(KIND, MT)>;
     struct Unit {
         uint4 w[NT];
         uint4 gv[NT];        // FP16 group scales of 8 K blocks (loaded by a run's first unit only)
@@ -821,24 +825,41 @@ static hipError_t launch_one(const GemmArgs& a, int split, hipStream_t s)
     return hipGetLastError();
 }
 
+// whether some SN in 1..8 stages XPL activation pieces per lane for this kind
+// and row-tile count (only those kernels are built)
+constexpr bool xpl_used(int kind, int mt, int xpl)
+{
+    for (int sn = 1; sn <= 8; ++sn)
+        if (x_pieces_per_lane(kind, sn, mt) == xpl) return true;
+    return false;
+}
+
 template <int NT, int MT, int XPL>
 static hipError_t launch_mfma(int kind, const GemmArgs& a, int split, hipStream_t s)
 {
-    if (kind == KIND_MFMA_FP8) return launch_one<MfmaFp8<NT, MT>, kDepthMfmaFp8, XPL, false>(a, split, s);
-    if (kind == KIND_MFMA_LUT3D) return launch_one<MfmaLut<NT, MT, true>, kDepthMfmaLut, XPL, true>(a, split, s);
-    return launch_one<MfmaLut<NT, MT, false>, kDepthMfmaLut, XPL, true>(a, split, s);
+    if (kind == KIND_MFMA_FP8) {
+        if constexpr (xpl_used(KIND_MFMA_FP8, MT, XPL))
+            return launch_one<MfmaFp8<NT, MT>, kDepthMfmaFp8, XPL, false>(a, split, s);
+        return hipErrorInvalidValue;
+    }
+    if constexpr (xpl_used(KIND_MFMA_LUT, MT, XPL)) {
+        if (kind == KIND_MFMA_LUT3D) return launch_one<MfmaLut<NT, MT, true>, kDepthMfmaLut, XPL, true>(a, split, s);
+        return launch_one<MfmaLut<NT, MT, false>, kDepthMfmaLut, XPL, true>(a, split, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int NT, int MT>
 static hipError_t launch_nt(int kind, const GemmArgs& a, int split, hipStream_t s)
 {
-    switch (x_pieces_per_lane(kind, a.sn)) {
+    switch (x_pieces_per_lane(kind, a.sn, MT)) {
     case 16: return launch_mfma<NT, MT, 16>(kind, a, split, s);
     case 8: return launch_mfma<NT, MT, 8>(kind, a, split, s);
     case 6: return launch_mfma<NT, MT, 6>(kind, a, split, s);
     case 4: return launch_mfma<NT, MT, 4>(kind, a, split, s);
     case 3: return launch_mfma<NT, MT, 3>(kind, a, split, s);
     case 2: return launch_mfma<NT, MT, 2>(kind, a, split, s);
+    case 1: return launch_mfma<NT, MT, 1>(kind, a, split, s);
     default: return hipErrorInvalidValue;
     }
 }
