@@ -110,6 +110,8 @@ class Workload:
             self.ws = wq.workspace(wq.WQ_FMT_LUT3_DENSE if dense else wq.WQ_FMT_LUT3, N, K, dev)
             gemm = wq.wq_gemm_lut3_dense if dense else wq.wq_gemm_lut3
             self._call = lambda p: gemm(p, N, K, self.x, self.y, M, self.ws)
+        # K parts the shape's workspace plan splits K into (1: no workspace needed)
+        self.k_parts = max(1, self.ws.numel() // (32 * N * 4))
         self.packed = [p0] + [p0.clone() for _ in range(copies - 1)]
         torch.cuda.synchronize()
         self.i = 0
@@ -119,8 +121,10 @@ class Workload:
         self.i += 1
 
     def launches_per_step(self) -> int:
-        # the per-shape plans run one tile per wave, which serves M = 17..32 in
-        # a single launch (both 16-row halves share each dequantised operand)
+        # passes over the weights per step: the per-shape plans run one tile
+        # per wave, which serves M = 17..32 in a single pass (both 16-row
+        # halves share each dequantised operand); a K split across
+        # work-groups adds a small kernel that sums the parts, not a pass
         return 1
 
 
@@ -366,7 +370,7 @@ def main(argv=None) -> int:
                     "us_per_call": round(rk["ms_per_step"] * 1e3, 2),
                     "us_per_launch": round(rk["launch_ms_mean"] * 1e3, 2),
                     "stream_GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-                    "passes": wk.launches_per_step()}
+                    "passes": wk.launches_per_step(), "k_parts": wk.k_parts}
                 del wk
                 torch.cuda.empty_cache()
         for name in ("gate_up", "down"):

@@ -51,6 +51,8 @@
  *   WQ_SN           = 1 .. 8              column-waves sharing staged activations
  *   WQ_SPLIT        = 1 .. 16             waves per work-group (SN x K-groups)
  *   WQ_WAVES_PER_CU = 1 .. 32             resident waves per CU the plan aims for (4)
+ *   WQ_KPARTS       = 1 .. 32             K parts across work-groups for calls that pass a
+ *                                         workspace (default: per shape)
  *   WQ_W8A8_TILE    = 128 | 256           W8A8 work-group tile for every M (default: 128 x 128
  *                                         up to M = 4096, 256 x 256 above)
  */
@@ -69,7 +71,7 @@ typedef enum {
     WQ_ERR_NULL = 1,       /* a required pointer is NULL                              */
     WQ_ERR_SHAPE = 2,      /* M, N or K outside what the format/path supports         */
     WQ_ERR_LD = 3,         /* a leading dimension is smaller than the row length      */
-    WQ_ERR_WORKSPACE = 4,  /* workspace smaller than wq_gemm_workspace_bytes() (unused) */
+    WQ_ERR_WORKSPACE = 4,  /* workspace given but smaller than wq_gemm_workspace_bytes() */
     WQ_ERR_CODE = 5,       /* a LUT packer found a code > 7 (packed buffer not valid) */
     WQ_ERR_DEVICE = 6,     /* current device is not gfx950                            */
     WQ_ERR_HIP = 7,        /* a HIP runtime call failed (includes: no device)         */
@@ -112,6 +114,13 @@ int wq_packed_format_version(void);
  * to be called while GEMMs are being queued from other threads. */
 wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu);
 
+/* Tuning and test hook: the number of K parts (1..32) that later calls which
+ * pass a workspace split K into across work-groups; 0 selects the per-shape
+ * choice.  Replaces WQ_KPARTS.  Parts are clamped so that each keeps at least
+ * one K block (8 for the LUT formats).  wq_gemm_workspace_bytes follows the
+ * setting.  Same thread rule as wq_set_tuning. */
+wq_status wq_set_kparts(int kp);
+
 /* ------------------------------------------------------------ FP8 block */
 
 /* Bytes of the packed FP8 matrix: N*K code bytes + 4*(N/128)*(K/128) scale
@@ -133,13 +142,21 @@ wq_status wq_pack_fp8_block(const uint8_t* w_e4m3, int64_t ldw, const float* sca
  *   x          device, [M][ldx] BF16 bits; ldx >= K, ldx % 8 == 0, x 16-byte aligned
  *   y          device, [M][ldy] BF16 bits (RNE); ldy >= N; only columns < N are written
  *   M          0 .. 32; M == 0 queues nothing and returns WQ_OK
- *   workspace  device scratch of wq_gemm_workspace_bytes(...) bytes; that size is 0
- *              in this version (every output is reduced inside one work-group), so
- *              NULL is accepted.  Kept in the interface for schedules that need one.
+ *   workspace  NULL, or device scratch of at least wq_gemm_workspace_bytes(...)
+ *              bytes, 16-byte aligned, owned by the caller (contents on entry do not
+ *              matter; they are overwritten).  With NULL every output is reduced
+ *              inside one work-group.  With a workspace, a shape whose column
+ *              groups leave CUs idle (the low-N projections) also splits K across
+ *              work-groups: each K part's work-group writes FP32 partial sums to
+ *              the workspace and a second kernel on the same stream adds the parts
+ *              in a fixed order and rounds once (the pages' split-K for low-N
+ *              grids).  A workspace smaller than required returns
+ *              WQ_ERR_WORKSPACE; a misaligned one WQ_ERR_ALIGN.
  * Numerics: every output is within 2 BF16 ULP of the exact result rounded to
  * BF16, or within 1e-3*sqrt(K)*max|x|*max|w| of the exact result.  Results are
  * deterministic, and row r of an M-row call equals row r of any other call on
- * the same path with the same row r of x, bit for bit. */
+ * the same path with the same row r of x, bit for bit, when both calls pass a
+ * workspace or both pass NULL (the two schedules may round differently). */
 wq_status wq_gemm_fp8_block(const void* packed, int64_t N, int64_t K,
                             const uint16_t* x, int64_t ldx,
                             uint16_t* y, int64_t ldy, int64_t M,
@@ -243,8 +260,11 @@ wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void*
 
 /* ------------------------------------------------------------ workspace */
 
-/* Workspace bytes a GEMM of this format and shape needs (the same for every M
- * and path).  0 for every shape in this version. */
+/* Workspace bytes a GEMM of this format and shape needs to run its
+ * K-split schedule (the same for every M and path; the FP8 GEMV path never
+ * uses it).  0 when the shape's plan keeps K inside one work-group, and for an
+ * unsupported shape or when no gfx950 device is current; NULL may then be
+ * passed.  Queries the current device (cached). */
 size_t wq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* ----------------------------------------------------------- test hooks */

@@ -62,7 +62,10 @@ def pack_fp8(codes, scales, ldw=None):
 
 
 def run_fp8(packed, N, K, xbits, M=None, path=0, ws=None, ldy=None, y_init=None):
-    """xbits: uint16 [M, ldx] (ldx >= K).  Returns (y bits [M, N], full y buffer bits)."""
+    """xbits: uint16 [M, ldx] (ldx >= K).  ws: None (no workspace: every output
+    reduced in its work-group), "auto" (wq.workspace for the shape: K parts
+    where its plan splits K across work-groups) or a buffer.  Returns (y bits
+    [M, N], full y buffer bits)."""
     wq = wqmod()
     M = xbits.shape[0] if M is None else M
     x = t_u16(xbits, torch.bfloat16)
@@ -70,7 +73,7 @@ def run_fp8(packed, N, K, xbits, M=None, path=0, ws=None, ldy=None, y_init=None)
     y = torch.empty((max(M, 1), ldy), dtype=torch.bfloat16, device=DEV)
     if y_init is not None:
         y.copy_(t_u16(y_init, torch.bfloat16))
-    ws = wq.workspace(wq.WQ_FMT_FP8_BLOCK, N, K, DEV) if ws is None else ws
+    ws = wq.workspace(wq.WQ_FMT_FP8_BLOCK, N, K, DEV) if isinstance(ws, str) else ws
     wq.wq_gemm_fp8_block_path(packed, N, K, x, y, M, ws, path)
     torch.cuda.synchronize()
     full = bits_of(y)
@@ -108,6 +111,7 @@ def pack_lut3(codes, qmap, scales, dense=False):
 
 
 def run_lut3(packed, N, K, xbits, M=None, ws=None, ldy=None, y_init=None, dense=False):
+    """As run_fp8 for the LUT formats (dense: the 3-bit code layout)."""
     wq = wqmod()
     M = xbits.shape[0] if M is None else M
     x = t_u16(xbits, torch.float16)
@@ -116,7 +120,7 @@ def run_lut3(packed, N, K, xbits, M=None, ws=None, ldy=None, y_init=None, dense=
     if y_init is not None:
         y.copy_(t_u16(y_init, torch.float16))
     fmt = wq.WQ_FMT_LUT3_DENSE if dense else wq.WQ_FMT_LUT3
-    ws = wq.workspace(fmt, N, K, DEV) if ws is None else ws
+    ws = wq.workspace(fmt, N, K, DEV) if isinstance(ws, str) else ws
     (wq.wq_gemm_lut3_dense if dense else wq.wq_gemm_lut3)(packed, N, K, x, y, M, ws)
     torch.cuda.synchronize()
     full = bits_of(y)

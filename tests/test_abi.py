@@ -45,9 +45,21 @@ def test_status_strings():
     assert wq.wq_status_str(1234) == "WQ_ERR_UNKNOWN"
 
 
-def test_workspace_is_empty():
-    for fmt, N, K in ((0, 17408, 5120), (0, 256, 512), (1, 28672, 8192), (1, 48, 256), (2, 28672, 8192)):
+def test_workspace_bytes_without_a_device_are_zero():
+    """The workspace size depends on the device's plan; with no gfx950 device
+    current (this host) the query returns 0, and so it does for bad shapes."""
+    for fmt, N, K in ((0, 17408, 5120), (0, 5120, 17408), (0, 256, 512), (1, 28672, 8192), (1, 48, 256),
+                      (2, 28672, 8192), (0, 100, 512), (1, 48, 100), (7, 256, 512)):
         assert wq.wq_gemm_workspace_bytes(fmt, 16, N, K) == 0
+
+
+def test_kparts_hook_validates():
+    with pytest.raises(wq.WqError):
+        wq.wq_set_kparts(-1)
+    with pytest.raises(wq.WqError):
+        wq.wq_set_kparts(33)
+    for kp in (0, 1, 32, 0):
+        wq.wq_set_kparts(kp)
 
 
 def test_sizes_are_host_arithmetic():

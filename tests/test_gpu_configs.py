@@ -1,5 +1,6 @@
-"""Parity at the full workload sizes, in the launch configuration the benchmark
-times.  The oracle computes every column of the first and last 128 and 768
+"""Parity at the full workload sizes, in the launch configurations the
+benchmark times (with the workspace the shape asks for, which splits K across
+work-groups for the FFN down projection, and without one).  The oracle computes every column of the first and last 128 and 768
 random columns in between (all M rows each); the comparison rule is the same
 as at small sizes."""
 import numpy as np
@@ -10,26 +11,33 @@ import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-CASES = [(name, M) for name, (fmt, N, K, Ms) in synth.CONFIGS.items() for M in Ms]
+CASES = [(name, M, ws) for name, (fmt, N, K, Ms) in synth.CONFIGS.items() for M in Ms
+         for ws in (None, "auto")]
 
 
-@pytest.mark.parametrize("name,M", CASES, ids=["%s-M%d" % c for c in CASES])
-def test_config_parity(name, M):
+@pytest.mark.parametrize("name,M,ws", CASES, ids=["%s-M%d-%s" % (n, m, w or "nows") for n, m, w in CASES])
+def test_config_parity(name, M, ws):
+    """ws None: no workspace (one K part); "auto": the workspace the shape asks
+    for, as the benchmark passes (skipped where that is none)."""
     fmt, N, K, Ms, data = U.config_inputs(name)
-    U.note("config %s %s N=%d K=%d M=%d" % (name, fmt, N, K, M))
+    wq = U.wqmod()
+    wfmt = {"fp8": wq.WQ_FMT_FP8_BLOCK, "lut3": wq.WQ_FMT_LUT3, "lut3d": wq.WQ_FMT_LUT3_DENSE}[fmt]
+    if ws and wq.wq_gemm_workspace_bytes(wfmt, M, N, K) == 0:
+        pytest.skip("the shape's plan keeps K in one work-group: same launch as without a workspace")
+    U.note("config %s %s N=%d K=%d M=%d ws=%s" % (name, fmt, N, K, M, ws))
     cols = U.sample_cols(N, 7 + M)
     if fmt == "fp8":
         codes, scales = data
         xbits = synth.x_bf16(M, K, synth.SEEDS[name] + 100)
         packed = _packed(name, lambda: U.pack_fp8(codes, scales))
-        y, _ = U.run_fp8(packed, N, K, xbits)
+        y, _ = U.run_fp8(packed, N, K, xbits, ws=ws)
         r = U.grade_fp8(y, xbits, codes, scales, K, cols=cols)
     else:
         codes, qmap, g = data
         xbits = synth.x_f16(M, K, synth.SEEDS[name] + 100)
         dense = fmt == "lut3d"
         packed = _packed(name, lambda: U.pack_lut3(codes, qmap, g, dense=dense))
-        y, _ = U.run_lut3(packed, N, K, xbits, dense=dense)
+        y, _ = U.run_lut3(packed, N, K, xbits, ws=ws, dense=dense)
         r = U.grade_lut3(y, xbits, codes, qmap, g, K, cols=cols)
     U.note("  %s" % r)
     assert r.ok, str(r)

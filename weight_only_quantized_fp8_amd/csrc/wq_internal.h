@@ -25,6 +25,10 @@ enum Kind : int {
 
 constexpr bool is_lut_kind(int kind) { return kind == KIND_MFMA_LUT || kind == KIND_MFMA_LUT3D; }
 
+// K ranges of K groups and K parts start at multiples of this many K blocks:
+// a LUT wave loads a row's group scales for 8 K blocks at once.
+constexpr int k_align(int kind) { return is_lut_kind(kind) ? 8 : 1; }
+
 // Size of an activation chunk (the K group synchronises once per chunk) in
 // 16-row K blocks, per kernel kind and row tiles MT (a 32-row chunk holds
 // half as many K blocks).  Measured on MI355X: the FP8 MFMA tile runs best
@@ -38,6 +42,9 @@ constexpr int chunk_blocks16(int kind, int mt) { return kind == KIND_MFMA_FP8 ? 
 // LDS (at most 2 x 4 K blocks x 16 rows x 272 bytes = 34816 bytes); the 160
 // KiB of LDS of a compute unit bound the K groups of one work-group at 4.
 constexpr int kMaxKGroups = 4;
+
+// Most K parts a GEMM splits across work-groups (grid y).
+constexpr int kMaxKParts = 32;
 
 // 16-byte activation pieces each lane loads per chunk when SN column-waves
 // share it: ceil(chunk pieces / (64 * SN)); a chunk is chunk_blocks16 blocks
@@ -85,12 +92,16 @@ struct GemmArgs {
     int N;                    // output columns
     int KB;                   // K / 128
     int n_tiles;              // N / 16
-    int n_cg;                 // column groups = grid size
+    int n_cg;                 // column groups (grid x)
     int sn;                   // column-waves per work-group sharing activations
+    int kp;                   // K parts across work-groups (grid y); > 1: partials go to ws
+    float* ws;                // kp > 1: FP32 partial outputs [kp][rows][N]
 };
 
 // nt: tiles per wave; a.sn: column-waves sharing activations (split % sn == 0);
-// split: waves per work-group; the grid has a.n_cg = ceil(n_tiles/(nt*sn)) groups.
+// split: waves per work-group; the grid has a.n_cg = ceil(n_tiles/(nt*sn))
+// column groups times a.kp K parts.  With a.kp > 1 the GEMM writes FP32
+// partials to a.ws and a second kernel sums the parts in order into y.
 hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream);
 
 hipError_t launch_pack_fp8(const uint8_t* w, int64_t ldw, const float* scales, int64_t N,

@@ -242,7 +242,7 @@ struct MfmaFp8 : Fp8Stream<NT> {
     static constexpr int KIND = KIND_MFMA_FP8;
     static constexpr int NTILES = NT;
     static constexpr int ROWS = 16 * MT;
-    static constexpr int KALIGN = 1;      // K-group ranges start at any K block
+    static constexpr int KALIGN = k_align(KIND);   // K-group ranges start at any K block
     template <int XPL> using Stage = XChunk<XPL, MT, chunk_blocks16(KIND_MFMA_FP8, MT)>;
     using typename Fp8Stream<NT>::Unit;
     using Fp8Stream<NT>::lane;
@@ -323,6 +323,21 @@ struct MfmaFp8 : Fp8Stream<NT> {
                 *reinterpret_cast<f32x4_t*>(slot + m * NT * 16 + t * 16 + n4) = outer[t][h];
         }
     }
+
+    // one K part's FP32 sums of this wave's tiles into dst[m][n] (row stride N)
+    __device__ __forceinline__ void store_part(float* dst, const GemmArgs& a, int tile0) const
+    {
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const int m = 16 * h + (lane & 15);
+            if (m >= a.rows) continue;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (t < ntiles)
+                    *reinterpret_cast<f32x4_t*>(dst + (int64_t)m * a.N + (tile0 + t) * 16 + (lane >> 4) * 4) =
+                        outer[t][h];
+        }
+    }
 };
 
 // ---- 3-bit LUT weights, 16-row FP16 MFMA tile -------------------------------
@@ -336,7 +351,7 @@ struct MfmaLut {
     static constexpr uint32_t kUnitBytes = DENSE ? 768u : 1024u;
     static constexpr int NTILES = NT;
     static constexpr int ROWS = 16 * MT;
-    static constexpr int KALIGN = 8;      // K blocks per group-scale load
+    static constexpr int KALIGN = k_align(KIND);   // K blocks per group-scale load
     template <int XPL> using Stage = XChunk<XPL, MT, chunk_blocks16(KIND, MT)>;
     struct Unit {
         uint4 w[NT];
@@ -445,6 +460,21 @@ struct MfmaLut {
                 *reinterpret_cast<f32x4_t*>(slot + m * NT * 16 + t * 16 + n4) = acc[t][h];
         }
     }
+
+    // one K part's FP32 sums of this wave's tiles into dst[m][n] (row stride N)
+    __device__ __forceinline__ void store_part(float* dst, const GemmArgs& a, int tile0) const
+    {
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const int m = 16 * h + (lane & 15);
+            if (m >= a.rows) continue;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (t < ntiles)
+                    *reinterpret_cast<f32x4_t*>(dst + (int64_t)m * a.N + (tile0 + t) * 16 + (lane >> 4) * 4) =
+                        acc[t][h];
+        }
+    }
 };
 
 // ---- FP8 weights, strict-K-order GEMV (MR <= 4 rows) ------------------------
@@ -537,6 +567,18 @@ struct GemvFp8 : Fp8Stream<1> {
             for (int m = 0; m < MR; ++m) slot[m * 16 + lane] = v[m];
         }
     }
+
+    // one K part's FP32 sums of this wave's columns into dst[m][n] (row stride N)
+    __device__ __forceinline__ void store_part(float* dst, const GemmArgs& a, int tile0) const
+    {
+        float v[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) v[m] = column_sum(m);
+        if (lane >= 16 || ntiles < 1) return;
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            if (m < a.rows) dst[(int64_t)m * a.N + tile0 * 16 + lane] = v[m];
+    }
 };
 
 // ======================================================================
@@ -575,12 +617,18 @@ gemm_kernel(GemmArgs a)
     const int SN = a.sn;
     const int SK = S / SN;
     const int cw = wave % SN, kg = wave / SN;
-    // K group kg covers K blocks [kb0, kb1); ranges start at multiples of KALIGN
+    // The work-group's K part (grid y) covers aligned K blocks [pa0, pa1) and
+    // its K group kg covers K blocks [kb0, kb1) of that; ranges start at
+    // multiples of KALIGN
     constexpr int KA = Pol::KALIGN;
     const int KBA = (a.KB + KA - 1) / KA;
-    const int kb0 = KA * ((KBA * kg) / SK), kb1 = min(a.KB, KA * ((KBA * (kg + 1)) / SK));
+    const int kpart = blockIdx.y;
+    const int pa0 = (KBA * kpart) / a.kp, pa1 = (KBA * (kpart + 1)) / a.kp;
+    const int PBA = pa1 - pa0;
+    const int kb0 = min(a.KB, KA * (pa0 + (PBA * kg) / SK));
+    const int kb1 = min(a.KB, KA * (pa0 + (PBA * (kg + 1)) / SK));
     const int len = kb1 - kb0;
-    const int steps = KA * ((KBA + SK - 1) / SK);      // the longest K range; every wave runs it
+    const int steps = KA * ((PBA + SK - 1) / SK);      // the longest K range; every wave runs it
     const int tile0 = (blockIdx.x * SN + cw) * NT;
 
     Pol pol(a, lane, tile0);
@@ -613,8 +661,10 @@ gemm_kernel(GemmArgs a)
             }
         }
     }
+    float* const wsp = a.ws + (int64_t)kpart * a.rows * a.N;  // this K part's partials (a.kp > 1)
     if (SK == 1) {
-        pol.template store_direct<F16_OUT>(a, tile0);
+        if (a.kp == 1) pol.template store_direct<F16_OUT>(a, tile0);
+        else pol.store_part(wsp, a, tile0);
         return;
     }
     __syncthreads();   // every wave is done with the staging buffers
@@ -631,7 +681,10 @@ gemm_kernel(GemmArgs a)
         float v = p[0];
         for (int k = 1; k < SK; ++k) v += p[(int64_t)k * SN * PR * TW];
         const int64_t n = (int64_t)blockIdx.x * cols + c;
-        if (n < a.N) a.y[m * a.ldy + n] = F16_OUT ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
+        if (n < a.N) {
+            if (a.kp == 1) a.y[m * a.ldy + n] = F16_OUT ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
+            else wsp[m * a.N + n] = v;
+        }
     }
 }
 
@@ -807,6 +860,29 @@ __global__ void unpack_lut3_kernel(const uint8_t* __restrict__ packed, int64_t N
         *reinterpret_cast<uint4*>(o + 32 * s) = __builtin_bit_cast(uint4, lut_decode8(d[s], pl));
 }
 
+// ----------------------------------------------------------- K-part sum
+// y[m][n] = the sum of the K parts' FP32 partials ws[p][m][n] taken in order
+// p = 0, 1, .., kp-1, rounded once (RNE) to BF16 or FP16.  A thread takes 4
+// consecutive columns (N is a multiple of 16).
+__global__ void __launch_bounds__(256) reduce_parts_kernel(const float* __restrict__ ws, int kp, int rows, int N,
+                                                           uint16_t* __restrict__ y, int64_t ldy, int f16_out)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4-column group
+    const int64_t groups = (int64_t)N / 4;
+    if (q >= (int64_t)rows * groups) return;
+    const int64_t m = q / groups, n = (q - m * groups) * 4;
+    const float* p = ws + m * N + n;
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
+    for (int k = 1; k < kp; ++k) {
+        const f32x4_t w = *reinterpret_cast<const f32x4_t*>(p + (int64_t)k * rows * N);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += w[i];
+    }
+    uint16_t* yp = y + m * ldy + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yp[i] = f16_out ? f32_to_f16_rne(v[i]) : f32_to_bf16_rne(v[i]);
+}
+
 // ======================================================================
 // Launchers
 // ======================================================================
@@ -821,7 +897,7 @@ static hipError_t launch_one(const GemmArgs& a, int split, hipStream_t s)
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fn, dim3(a.n_cg), dim3(split * 64), lds, s, a);
+    hipLaunchKernelGGL(fn, dim3(a.n_cg, a.kp), dim3(split * 64), lds, s, a);
     return hipGetLastError();
 }
 
@@ -875,7 +951,22 @@ static hipError_t launch_gemv(const GemmArgs& a, int split, hipStream_t s)
     }
 }
 
+static hipError_t launch_gemm_parts(int kind, int nt, int gemv_rows, const GemmArgs& a, int split,
+                                    hipStream_t stream);
+
 hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int split, hipStream_t stream)
+{
+    if (a.kp < 1 || a.kp > kMaxKParts || (a.kp > 1 && !a.ws)) return hipErrorInvalidValue;
+    hipError_t e = launch_gemm_parts(kind, nt, gemv_rows, a, split, stream);
+    if (e != hipSuccess || a.kp == 1) return e;
+    const int64_t groups = (int64_t)a.rows * (a.N / 4);
+    hipLaunchKernelGGL(reduce_parts_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, a.ws, a.kp,
+                       a.rows, a.N, a.y, a.ldy, (int)is_lut_kind(kind));
+    return hipGetLastError();
+}
+
+static hipError_t launch_gemm_parts(int kind, int nt, int gemv_rows, const GemmArgs& a, int split,
+                                    hipStream_t stream)
 {
     if (!split_ok(kind, nt, a.sn, split)) return hipErrorInvalidValue;
     if (kind == KIND_GEMV_FP8) {

@@ -4,7 +4,9 @@
 
 For one format and shape it runs every candidate tiling (tiles per wave,
 column-waves sharing activations, waves per work-group) through the library's
-own tuning hook (``wq_set_tuning``).  A candidate is timed only if its output
+own tuning hook (``wq_set_tuning``); with ``--kparts`` it also sweeps the
+number of K parts split across work-groups (``wq_set_kparts``), passing each
+call a workspace of ``wq_gemm_workspace_bytes``.  A candidate is timed only if its output
 passes the library's tolerance against an FP32 reference built from the
 library's own dequantised weights (``wq_unpack_*``) and a torch matmul: every
 output within 2 BF16 ULP of the reference or within 1e-3*sqrt(K)*max|x|*max|w|.
@@ -51,7 +53,7 @@ def _inputs(fmt: str, N: int, K: int, M: int, dev: str, seed: int, path: int):
         wd = torch.empty(N, K, dtype=torch.float32, device=dev)
         wq.wq_unpack_fp8_block_f32(packed, N, K, wd)
         wd = (wd.view(N // 128, 128, K // 128, 128) * scales.to(dev)[:, None, :, None]).view(N, K)
-        call = lambda p, y: wq.wq_gemm_fp8_block_path(p, N, K, x, y, M, None, path)
+        call = lambda p, y, ws=None: wq.wq_gemm_fp8_block_path(p, N, K, x, y, M, ws, path)
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     else:
         codes = torch.randint(0, 8, (N, K), generator=g, dtype=torch.uint8)
@@ -64,7 +66,7 @@ def _inputs(fmt: str, N: int, K: int, M: int, dev: str, seed: int, path: int):
         (wq.wq_unpack_lut3_dense if dense else wq.wq_unpack_lut3)(packed, N, K, wh)
         wd = wh.float()
         gemm = wq.wq_gemm_lut3_dense if dense else wq.wq_gemm_lut3
-        call = lambda p, y: gemm(p, N, K, x, y, M)
+        call = lambda p, y, ws=None: gemm(p, N, K, x, y, M, ws)
         y = torch.empty(M, N, dtype=torch.float16, device=dev)
     ref = x.float() @ wd.t()
     floor = FLOOR_COEF * math.sqrt(K) * x.float().abs().max().item() * wd.abs().max().item()
@@ -96,13 +98,13 @@ def _time(call, copies, y, calls: int = 100, reps: int = 5) -> float:
     return sorted(out)[reps // 2]
 
 
-def candidates(fmt: str, gemv: bool = False):
+def candidates(fmt: str, gemv: bool = False, kp: int = 1):
     """(nt, sn, split) triples the kernels are built for: sn <= 8, at most 4
     K groups, and at most 8 waves per work-group except the GEMV and one-tile
     LUT groups whose waves hold at most 4 activation pieces per lane
     (sn >= 4), built for 16.  The GEMV always runs one tile per wave."""
     out = []
-    for nt in ((1,) if gemv else (1, 2)):
+    for nt in ((1,) if gemv or kp > 1 else (1, 2)):
         for sn in range(1, 9):
             pieces = math.ceil(16 / sn)
             max_split = 16 if (gemv or (fmt in ("lut3", "lut3d") and nt == 1 and pieces <= 4)) else 8
@@ -122,6 +124,8 @@ def main(argv=None) -> int:
     ap.add_argument("--top", type=int, default=8)
     ap.add_argument("--seed", type=int, default=7)
     ap.add_argument("--path", choices=("mfma", "gemv"), default="mfma", help="FP8 arm to tune (gemv: M <= 4)")
+    ap.add_argument("--kparts", default="1",
+                    help="comma-separated K-part counts to sweep (> 1: K split across work-groups, with a workspace)")
     args = ap.parse_args(argv)
     if not torch.cuda.is_available():
         print("tune needs a GPU", file=sys.stderr)
@@ -132,32 +136,38 @@ def main(argv=None) -> int:
     # rotate copies totalling > the 256 MB Infinity Cache, so calls stream from HBM
     n_copies = min(64, max(2, math.ceil((1 << 30) / packed.numel())))
     copies = [packed] + [packed.clone() for _ in range(n_copies - 1)]
+    fmt_id = {"fp8": wq.WQ_FMT_FP8_BLOCK, "lut3": wq.WQ_FMT_LUT3, "lut3d": wq.WQ_FMT_LUT3_DENSE}[args.fmt]
     results, rejected = [], []
     try:
-        for t in candidates(args.fmt, args.path == "gemv"):
-            wq.wq_set_tuning(t[0], t[1], t[2], 0)
-            y.zero_()
-            call(packed, y)
-            torch.cuda.synchronize()
-            if not _passes(y, ref, floor):
-                rejected.append(t)
-                continue
-            results.append((_time(call, copies, y), t))
+        for kp in (int(v) for v in args.kparts.split(",")):
+            wq.wq_set_kparts(kp)
+            ws = wq.workspace(fmt_id, args.N, args.K, dev) if kp > 1 else None
+            for t in candidates(args.fmt, args.path == "gemv", kp):
+                wq.wq_set_tuning(t[0], t[1], t[2], 0)
+                y.zero_()
+                call(packed, y, ws)
+                torch.cuda.synchronize()
+                if not _passes(y, ref, floor):
+                    rejected.append(t + (kp,))
+                    continue
+                results.append((_time(lambda p, yy: call(p, yy, ws), copies, y), t + (kp,)))
     finally:
         wq.wq_set_tuning(0, 0, 0, 0)
+        wq.wq_set_kparts(0)
     results.sort()
     wb = packed.numel()
     print("%s N=%d K=%d M=%d: %d candidates pass, %d rejected" % (args.fmt, args.N, args.K, args.M,
                                                                  len(results), len(rejected)))
-    for us, (nt, sn, split) in results[: args.top]:
-        print("  nt=%d sn=%d split=%-2d  %7.2f us  %6.0f GB/s" % (nt, sn, split, us, wb / us / 1e3))
+    for us, (nt, sn, split, kp) in results[: args.top]:
+        print("  nt=%d sn=%d split=%-2d kp=%-2d %7.2f us  %6.0f GB/s" % (nt, sn, split, kp, us, wb / us / 1e3))
     if rejected:
         print("  rejected:", rejected)
     if results:
-        nt, sn, split = results[0][1]
+        nt, sn, split, kp = results[0][1]
         kind = ("wq::KIND_GEMV_FP8" if args.path == "gemv" else "wq::KIND_MFMA_FP8") if args.fmt == "fp8" \
             else ("wq::KIND_MFMA_LUT3D" if args.fmt == "lut3d" else "wq::KIND_MFMA_LUT")
-        print("table row: {%s, %d, %d, %d, %d, %d}," % (kind, args.N, args.K, nt, sn, split))
+        print("table row (%s): {%s, %d, %d, %d, %d, %d, %d}," % ("kSplitTable" if kp > 1 else "kTable", kind,
+                                                                 args.N, args.K, nt, sn, split, kp))
     return 0 if results else 1
 
 

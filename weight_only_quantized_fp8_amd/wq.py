@@ -14,7 +14,7 @@ import os
 __all__ = [
     "WqError", "LIB_PATH", "lib",
     "WQ_OK", "WQ_FMT_FP8_BLOCK", "WQ_FMT_LUT3", "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA",
-    "wq_status_str", "wq_packed_format_version", "wq_set_tuning",
+    "wq_status_str", "wq_packed_format_version", "wq_set_tuning", "wq_set_kparts",
     "wq_fp8_block_packed_bytes", "wq_pack_fp8_block", "wq_gemm_fp8_block", "wq_gemm_fp8_block_path",
     "wq_lut3_packed_bytes", "wq_pack_lut3", "wq_gemm_lut3",
     "WQ_FMT_LUT3_DENSE", "wq_lut3_dense_packed_bytes", "wq_pack_lut3_dense", "wq_gemm_lut3_dense",
@@ -46,6 +46,7 @@ _SIGS = {
     "wq_status_str": (ctypes.c_char_p, [_INT]),
     "wq_packed_format_version": (_INT, []),
     "wq_set_tuning": (_INT, [_INT, _INT, _INT, _INT]),
+    "wq_set_kparts": (_INT, [_INT]),
     "wq_fp8_block_packed_bytes": (_SZ, [_I64, _I64]),
     "wq_pack_fp8_block": (_INT, [_P, _I64, _P, _I64, _I64, _P, _P]),
     "wq_gemm_fp8_block": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
@@ -122,6 +123,10 @@ def wq_packed_format_version() -> int:
 
 def wq_set_tuning(nt: int = 0, sn: int = 0, split: int = 0, waves_per_cu: int = 0) -> None:
     _check(lib.wq_set_tuning(nt, sn, split, waves_per_cu), "wq_set_tuning")
+
+
+def wq_set_kparts(kp: int = 0) -> None:
+    _check(lib.wq_set_kparts(kp), "wq_set_kparts")
 
 
 def wq_fp8_block_packed_bytes(N: int, K: int) -> int:
@@ -215,7 +220,8 @@ def wq_unpack_x_fp8(xq, M: int, K: int, codes, scales, stream=None) -> None:
 # -------------------------------------------------------- torch helpers
 
 def workspace(fmt: int, N: int, K: int, device="cuda"):
-    """Workspace for GEMMs of this format and shape (any M, any path); it may be empty."""
+    """Workspace for GEMMs of this format and shape (any M, any path); empty (passed
+    as NULL) when the shape keeps K inside one work-group."""
     import torch
     nbytes = wq_gemm_workspace_bytes(fmt, 1, N, K)
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
