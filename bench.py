@@ -10,8 +10,9 @@ weight matrix, and the copies together exceed the 256 MB Infinity Cache, so the
 weight bytes of every step come from HBM.
 
 Reported value: weight-stream GB/s = (packed code bytes + scale bytes) per step
-divided by the time per step (the pages count stored weight bytes, see
-the design doc).  The JSON line also carries the dominant kernel's roofline (bytes
+divided by the time per step (the pages count stored weight bytes: one byte an
+FP8 code, half a byte a nibble-packed 3-bit code, 3/8 a dense one, plus the
+scales).  The JSON line also carries the dominant kernel's roofline (bytes
 per launch over the mean launch duration, from HIP events on the library's
 stream), the CPU oracle timed on the host as a baseline, and (with --all) the
 other workloads' numbers.

@@ -107,10 +107,11 @@ wq_status current_device(DevInfo* info, int* dev_out = nullptr)
 // its part of x once), so a plan takes as many tiles per work-group as still
 // leaves about one work-group per compute unit, and adds K groups where that
 // leaves too few waves.  Without a workspace KP = 1 and every output is
-// reduced inside its work-group.  With one, a low-N shape splits K across
-// work-groups as well (KP > 1, the benchmark spec's split-K for low-N grids):
-// each K part's work-group writes FP32 partials and a second kernel adds the
-// parts in order, so the grid can cover every CU without thinning the
+// reduced inside its work-group.  With one, a low-N shape with a long K
+// splits K across work-groups as well (KP > 1; atlas "Module m16_tc", "WHY
+// THE FFN ARM LOSES": the low-N projections' grids against the machine's
+// slots): each K part's work-group writes FP32 partials and a second kernel
+// adds the parts in order, so the grid can cover the CUs without thinning the
 // activation sharing.
 struct Plan {
     int kind = 0;

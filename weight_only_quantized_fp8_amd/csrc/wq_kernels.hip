@@ -31,17 +31,19 @@
 //         follow as in LUT3.
 //
 // GEMM schedule.  One work-group owns one column group (SN column-waves of
-// NT tiles of 16 output columns) over the whole of K.  Its waves form SK
-// K groups that split the K blocks into contiguous ranges (split-K), so a
-// low-N projection still puts enough waves on the chip; SN and SK are chosen
-// per shape by the host.  Each wave walks its range with the next D units'
-// loads in flight (a register ring) while the column-waves of a K group
-// share activation chunks staged in LDS.  Every 128-K block is folded onto
-// FP32 accumulators.  With one K group each wave stores its own outputs;
-// otherwise the work-group sums the K groups' partial tiles in LDS in a fixed
-// order.  No two work-groups share an output, so there is no cross-work-group
-// traffic, no workspace and no fence, and every sum has a fixed order:
-// results are deterministic and do not depend on M.
+// NT tiles of 16 output columns) over the whole of K, or over one of KP K
+// parts.  Its waves form SK K groups that split its K blocks into contiguous
+// ranges (split-K), so a low-N projection still puts enough waves on the
+// chip; SN, SK and KP are chosen per shape by the host.  Each wave walks its
+// range with the next D units' loads in flight (a register ring) while the
+// column-waves of a K group share activation chunks staged in LDS.  Every
+// 128-K block is folded onto FP32 accumulators.  With one K group each wave
+// stores its own outputs; otherwise the work-group sums the K groups' partial
+// tiles in LDS in a fixed order.  With KP = 1 no two work-groups share an
+// output: no cross-work-group traffic, no workspace, no fence.  With KP > 1
+// (the caller passed a workspace) each K part's work-group stores FP32 sums
+// to the workspace and a second kernel adds the parts in order.  Every sum
+// has a fixed order: results are deterministic and do not depend on M.
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
@@ -582,14 +584,16 @@ struct GemvFp8 : Fp8Stream<1> {
 };
 
 // ======================================================================
-// The GEMM kernel.  Grid: one work-group per column group of SN*NT tiles.
-// Block: S = SN*SK waves; wave w is column-wave cw = w % SN (tiles
-// cw*NT .. +NT of the group) in K group kg = w / SN (K blocks
-// KB*kg/SK .. KB*(kg+1)/SK).  Each wave streams its units through a ring of
-// D+1 register slots with D units in flight.  The SN waves of a K group share
-// staged activation chunks (see XChunk).  After the K loop every wave parks
-// its partial tile in LDS and the work-group sums the SK partials of each
-// column in K-group order.
+// The GEMM kernel.  Grid: one work-group per column group of SN*NT tiles
+// (x) and K part (y).  Block: S = SN*SK waves; wave w is column-wave
+// cw = w % SN (tiles cw*NT .. +NT of the group) in K group kg = w / SN (the
+// kg-th of SK contiguous runs of the part's K blocks).  Each wave streams its
+// units through a ring of D+1 register slots with D units in flight.  The SN
+// waves of a K group share staged activation chunks (see XChunk).  After the
+// K loop every wave stores its tiles (SK = 1) or parks its partial tile in
+// LDS and the work-group sums the SK partials of each column in K-group
+// order; the result is rounded into y (KP = 1) or stored as FP32 to the
+// part's slab of the workspace.
 // ======================================================================
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
