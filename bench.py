@@ -208,10 +208,14 @@ def time_w8a8(name: str, M: int, steps: int = 20, copies: int = 4) -> dict:
     x = torch.from_numpy(synth.x_bf16(M, K, synth.SEEDS[name] + 100).view(np.int16)).to(dev).view(torch.bfloat16)
     xq = torch.empty(wq.wq_x_fp8_packed_bytes(M, K), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    # the workspace lets a thin grid split K across work-groups (FFN down at small M)
+    ws_bytes = wq.wq_w8a8_workspace_bytes(M, N, K)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    k_parts = ws_bytes // (M * N * 4) if ws_bytes else 1
 
     def step(i):
         wq.wq_quantize_x_fp8(x, M, K, xq)
-        wq.wq_gemm_fp8_w8a8(packed[i % copies], N, K, xq, M, y)
+        wq.wq_gemm_fp8_w8a8(packed[i % copies], N, K, xq, M, y, ws)
 
     for i in range(3):
         step(i)
@@ -235,7 +239,7 @@ def time_w8a8(name: str, M: int, steps: int = 20, copies: int = 4) -> dict:
     ev[2].record()
     ev[3].record()
     for i in range(steps):
-        wq.wq_gemm_fp8_w8a8(packed[i % copies], N, K, xq, M, y)
+        wq.wq_gemm_fp8_w8a8(packed[i % copies], N, K, xq, M, y, ws)
     ev[4].record()
     torch.cuda.synchronize()
     us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
@@ -245,7 +249,8 @@ def time_w8a8(name: str, M: int, steps: int = 20, copies: int = 4) -> dict:
     del packed, g
     torch.cuda.empty_cache()
     return {"us_per_call": round(us, 2), "quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2),
-            "gemm_TFLOPs": round(tf, 1), "pct_of_fp8_mfma_peak": round(100 * tf / FP8_MFMA_PEAK_TFLOPS, 1)}
+            "gemm_TFLOPs": round(tf, 1), "pct_of_fp8_mfma_peak": round(100 * tf / FP8_MFMA_PEAK_TFLOPS, 1),
+            "k_parts": k_parts}
 
 
 def cpu_baseline(name: str, M: int, min_seconds: float = 3.0, max_reps: int = 20):
@@ -375,7 +380,7 @@ def main(argv=None) -> int:
                 del wk
                 torch.cuda.empty_cache()
         for name in ("gate_up", "down"):
-            for M in (512, 2048, 4096):
+            for M in (256, 512, 2048, 4096):
                 print("bench: w8a8 %s M=%d" % (name, M), file=sys.stderr, flush=True)
                 extra["w8a8_%s_M%d" % (name, M)] = time_w8a8(name, M)
         out["extra"] = extra

@@ -115,9 +115,10 @@ int wq_packed_format_version(void);
 wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu);
 
 /* Tuning and test hook: the number of K parts (1..32) that later calls which
- * pass a workspace split K into across work-groups; 0 selects the per-shape
- * choice.  Replaces WQ_KPARTS.  Parts are clamped so that each keeps at least
- * one K block (8 for the LUT formats).  wq_gemm_workspace_bytes follows the
+ * pass a workspace split K into across work-groups (the decode GEMMs and
+ * wq_gemm_fp8_w8a8); 0 selects the per-shape choice.  Replaces WQ_KPARTS.
+ * Parts are clamped so that each keeps at least one K block (8 for the LUT
+ * formats).  wq_gemm_workspace_bytes and wq_w8a8_workspace_bytes follow the
  * setting.  Same thread rule as wq_set_tuning. */
 wq_status wq_set_kparts(int kp);
 
@@ -231,6 +232,12 @@ wq_status wq_gemm_lut3_dense(const void* packed, int64_t N, int64_t K,
  * nearest-even of clamp(x/s, -448, 448) with x/s in binary32 -- the rule of
  * the weights' block quantiser.  x must be finite. */
 
+/* Workspace bytes of a W8A8 GEMM of this M, N, K that splits K across
+ * work-groups (kp * M * N * 4 for kp parts, following wq_set_kparts); 0 when
+ * it keeps K inside one work-group, for an invalid shape, or with no gfx950
+ * device current. */
+size_t wq_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 /* Bytes of a packed FP8 activation buffer: Mpad*K codes + 4*Mpad*(K/128)
  * scale bytes, Mpad = 16*ceil(M/16).  0 for an unsupported shape (K not a
  * positive multiple of 128, M < 1, or 2 GiB or more). */
@@ -252,8 +259,17 @@ wq_status wq_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int6
  * Per 128-K block the FP32 matrix-core sum of e4m3(x)*e4m3(w) is folded onto an
  * FP32 accumulator times sx[m][kb]*s[n/128][kb].  Every output is within 2 BF16
  * ULP of the exact result (of the quantised operands) rounded to BF16, or within
- * 1e-3*sqrt(K)*max|xq*sx|*max|w| of it.  Deterministic; row r of the result
- * depends only on row r of xq.  workspace: none needed (NULL accepted). */
+ * 1e-3*sqrt(K)*max|xq*sx|*max|w| of it.  Deterministic.
+ *   workspace  NULL, or device scratch of at least wq_w8a8_workspace_bytes(M, N, K)
+ *           bytes, 16-byte aligned, contents on entry irrelevant.  With NULL
+ *           every output is reduced inside one work-group and row r of the result
+ *           depends only on row r of xq.  With a workspace, an M whose output
+ *           tiles leave CUs idle also splits K across work-groups: FP32 partial
+ *           sums go to the workspace and a second kernel on the same stream adds
+ *           them in a fixed order (results stay deterministic for a given M, N, K;
+ *           the split, and so the rounding of a row, may differ between Ms).  A
+ *           workspace smaller than required returns WQ_ERR_WORKSPACE, a misaligned
+ *           one WQ_ERR_ALIGN. */
 wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void* xq, int64_t M,
                            uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                            void* hip_stream);

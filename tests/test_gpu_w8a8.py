@@ -8,7 +8,10 @@
   tiles, several column tiles and K blocks, M from 1 to a few hundred and at
   the FFN gate/up size; integer-exact inputs give exact results; rows are
   independent of M, results deterministic, y's padding untouched, HIP-graph
-  replays equal the eager result.
+  replays equal the eager result;
+* K split across work-groups (a workspace passed): forced part counts against
+  the oracle (NaN-filled workspace), the automatic split of the FFN down
+  projection, workspace errors, determinism and graph replay.
 """
 import numpy as np
 import pytest
@@ -37,13 +40,17 @@ def quantize(xbits, K):
     return xq, codes.cpu().numpy(), scales.cpu().numpy()
 
 
-def run(packed, N, K, xq, M, ldy=None, y_init=None):
+def run(packed, N, K, xq, M, ldy=None, y_init=None, ws=None):
+    """ws: None (no workspace), "auto" (wq_w8a8_workspace_bytes, NaN-filled) or a buffer."""
     wq = U.wqmod()
     ldy = N if ldy is None else ldy
     y = torch.empty((M, ldy), dtype=torch.bfloat16, device=U.DEV)
     if y_init is not None:
         y.copy_(U.t_u16(y_init, torch.bfloat16))
-    wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y)
+    if isinstance(ws, str):
+        nb = wq.wq_w8a8_workspace_bytes(M, N, K)
+        ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=U.DEV) if nb else None
+    wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y, ws)
     torch.cuda.synchronize()
     full = U.bits_of(y)
     return full[:, :N], full
@@ -216,3 +223,104 @@ def test_w8a8_gate_up_size(M):
     r = compare.grade(y[:, cols], y64, floor_w8a8(oc, osc, codes, scales, K), "bf16")
     U.note("  %s" % r)
     assert r.ok, str(r)
+
+
+# ---------------------------------------------------------- K parts (workspace)
+
+@pytest.fixture
+def kparts_reset():
+    yield
+    U.wqmod().wq_set_kparts(0)
+
+
+@pytest.mark.parametrize("kp", [2, 3, 7])
+@pytest.mark.parametrize("N,K,M", [(384, 1024, 16), (640, 2048, 130), (1280, 1152, 300), (384, 3072, 4100)])
+def test_w8a8_parts_match_oracle(N, K, M, kp, kparts_reset):
+    wq = U.wqmod()
+    wq.wq_set_kparts(kp)
+    U.note("w8a8 parts N=%d K=%d M=%d kp=%d" % (N, K, M, kp))
+    assert wq.wq_w8a8_workspace_bytes(M, N, K) == min(kp, K // 128) * M * N * 4
+    codes, scales = synth.fp8_weights(N, K, 1400 + N + K)
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(M, K, 1500 + M)
+    xq, xc, xs = quantize(xb, K)
+    y, _ = run(packed, N, K, xq, M, ws="auto")
+    y64 = oracle.gemm_w8a8(xc, xs, codes, scales)
+    r = compare.grade(y, y64, floor_w8a8(xc, xs, codes, scales, K), "bf16")
+    assert r.ok, str(r)
+    for _ in range(3):                                    # deterministic, whatever the workspace held
+        assert np.array_equal(run(packed, N, K, xq, M, ws="auto")[0], y)
+
+
+def test_w8a8_down_splits_k(kparts_reset):
+    """FFN down 5120 x 17408 at M = 256: the automatic plan splits K in 3 parts
+    (sampled columns against the oracle)."""
+    wq = U.wqmod()
+    fmt, N, K, Ms, (codes, scales) = U.config_inputs("down")
+    M = 256
+    assert wq.wq_w8a8_workspace_bytes(M, N, K) == 3 * M * N * 4
+    assert wq.wq_w8a8_workspace_bytes(M, 17408, 5120) == 0        # gate/up keeps K whole
+    U.note("w8a8 down M=%d with a workspace" % M)
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(M, K, 1601)
+    xq, xc, xs = quantize(xb, K)
+    y, _ = run(packed, N, K, xq, M, ws="auto")
+    cols = U.sample_cols(N, 67)
+    y64 = oracle.gemm_w8a8(xc, xs, codes, scales, cols=cols)
+    r = compare.grade(y[:, cols], y64, floor_w8a8(xc, xs, codes, scales, K), "bf16")
+    U.note("  %s" % r)
+    assert r.ok, str(r)
+
+
+def test_w8a8_workspace_errors(kparts_reset):
+    wq = U.wqmod()
+    wq.wq_set_kparts(3)
+    N, K, M = 384, 1024, 40
+    codes, scales = synth.fp8_weights(N, K, 1700)
+    packed = U.pack_fp8(codes, scales)
+    xq, _, _ = quantize(synth.x_bf16(M, K, 1701), K)
+    need = wq.wq_w8a8_workspace_bytes(M, N, K)
+    assert need == 3 * M * N * 4
+    big = torch.zeros(need + 64, dtype=torch.uint8, device=U.DEV)
+    y = torch.full((M, N), 5.0, dtype=torch.bfloat16, device=U.DEV)
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y, big[:need - 4])
+    assert e.value.status == 4
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y, big[8:8 + need])
+    assert e.value.status == 8
+    torch.cuda.synchronize()
+    assert bool((y.float() == 5.0).all())
+
+
+def test_w8a8_graph_replay_with_parts(kparts_reset):
+    """Quantiser, split GEMM and parts sum captured in a HIP graph replay to the eager result."""
+    wq = U.wqmod()
+    wq.wq_set_kparts(4)
+    U.note("w8a8 graph replay with parts")
+    N, K, M = 512, 2048, 96
+    codes, scales = synth.fp8_weights(N, K, 1800)
+    packed = U.pack_fp8(codes, scales)
+    x = U.t_u16(synth.x_bf16(M, K, 1801), torch.bfloat16)
+    xq = torch.empty(wq.wq_x_fp8_packed_bytes(M, K), dtype=torch.uint8, device=U.DEV)
+    ws = torch.empty(wq.wq_w8a8_workspace_bytes(M, N, K), dtype=torch.uint8, device=U.DEV)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=U.DEV)
+    wq.wq_quantize_x_fp8(x, M, K, xq)
+    wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y, ws)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            wq.wq_quantize_x_fp8(x, M, K, xq)
+            wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        y.fill_(3.0)
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), rep

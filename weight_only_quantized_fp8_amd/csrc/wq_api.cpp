@@ -577,6 +577,54 @@ wq_status wq_unpack_lut3_dense(const void* packed, int64_t N, int64_t K, uint16_
 
 // ------------------------------------------------------------------ W8A8
 
+}  // extern "C"
+
+namespace {
+
+// K blocks per W8A8 K part of the automatic rule.
+constexpr int kW8PartBlocks = 40;
+
+// K parts of a W8A8 call that brings a workspace: the wq_set_kparts value, or,
+// when the 128 x 128 output tiles give fewer than 4 work-groups per CU, one part per
+// kW8PartBlocks K blocks, but no more parts than bring the grid to 4
+// work-groups per CU.  Measured on MI355X (GEMM + parts sum): FFN down
+// 5120 x 17408 at M = 256 / 512 / 1024 / 2048 runs 116 / 118 / 143 / 239 us
+// in one part and 51 / 74 / 124 / 224 us in 3, 3, 3 and 2 parts; gate/up
+// (K = 5120) is fastest in one part at every M.
+int w8a8_kparts(int64_t M, int64_t N, int64_t K, int cu)
+{
+    int forced;
+    {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        forced = g_opts.kp;
+    }
+    const int KB = (int)(K / 128);
+    int kp = 1;
+    if (forced) kp = forced;
+    else {
+        const int64_t mpad = (M + 15) / 16 * 16;
+        const int64_t e = wq::w8a8_tile_edge((int)mpad);
+        const int64_t tiles = (mpad + e - 1) / e * ((N + e - 1) / e);
+        if (e == 128 && tiles < 4 * cu)   // the 256 x 256 tile (M > 4096) keeps K whole
+            kp = (int)std::min<int64_t>(KB / kW8PartBlocks, (4 * cu + tiles - 1) / tiles);
+    }
+    return std::max(1, std::min(kp, std::min(KB, wq::kMaxKParts)));
+}
+
+size_t w8a8_workspace_bytes(int64_t M, int64_t N, int kp) { return kp > 1 ? (size_t)kp * M * N * 4 : 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t wq_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || !shape_ok(WQ_FMT_FP8_BLOCK, N, K) || !wq_x_fp8_packed_bytes(M, K)) return 0;
+    DevInfo dev;
+    if (current_device(&dev) != WQ_OK) return 0;
+    return w8a8_workspace_bytes(M, N, w8a8_kparts(M, N, K, dev.cu));
+}
+
 size_t wq_x_fp8_packed_bytes(int64_t M, int64_t K)
 {
     if (M <= 0 || K <= 0 || K % 128 || M > (int64_t)1 << 24 || K > (int64_t)1 << 24) return 0;
@@ -605,8 +653,6 @@ wq_status wq_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int6
 wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void* xq, int64_t M, uint16_t* y,
                            int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream)
 {
-    (void)workspace;          // every output tile is owned by one work-group: no workspace
-    (void)workspace_bytes;
     if (M < 0) return WQ_ERR_SHAPE;
     if (!shape_ok(WQ_FMT_FP8_BLOCK, N, K) || (uint64_t)N * (uint64_t)K >= ((uint64_t)1 << 32)) return WQ_ERR_SHAPE;
     if (M == 0) return WQ_OK;
@@ -617,8 +663,15 @@ wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void*
     DevInfo dev;
     wq_status st = current_device(&dev);
     if (st != WQ_OK) return st;
+    // with a workspace, K may be split across work-groups (FP32 partials there)
+    const int kp = workspace ? w8a8_kparts(M, N, K, dev.cu) : 1;
+    if (kp > 1) {
+        if (workspace_bytes < w8a8_workspace_bytes(M, N, kp)) return WQ_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return WQ_ERR_ALIGN;
+    }
     return wq::launch_w8a8(static_cast<const uint8_t*>(packed), (int)N, (int)K, static_cast<const uint8_t*>(xq),
-                           (int)M, y, ldy, static_cast<hipStream_t>(hip_stream)) == hipSuccess
+                           (int)M, y, ldy, kp, kp > 1 ? static_cast<float*>(workspace) : nullptr,
+                           static_cast<hipStream_t>(hip_stream)) == hipSuccess
                ? WQ_OK
                : WQ_ERR_HIP;
 }

@@ -119,7 +119,19 @@ hipError_t launch_unpack_lut3(const uint8_t* packed, int64_t N, int64_t K, uint1
 // layout, its test-hook inverse, and the FP8 x FP8 GEMM on packed FP8 weights.
 hipError_t launch_quantize_x(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* xq, hipStream_t stream);
 hipError_t launch_unpack_x(const uint8_t* xq, int M, int K, uint8_t* codes, float* scales, hipStream_t stream);
+// kp > 1: K split into kp parts across work-groups, FP32 partials in ws [kp][M][N]
+// summed in order into y by launch_sum_parts
 hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
-                       hipStream_t stream);
+                       int kp, float* ws, hipStream_t stream);
+
+// y[m][n] = the parts ws[p][m][n] (p = 0 .. kp-1, [kp][rows][N] FP32) added in
+// order and rounded once (RNE) to BF16, or FP16 with f16_out; N % 16 == 0.
+hipError_t launch_sum_parts(const float* ws, int kp, int rows, int N, uint16_t* y, int64_t ldy, bool f16_out,
+                            hipStream_t stream);
+
+// W8A8 work-group tile edge (rows and columns) for an M (the launcher's own
+// choice; a K-split plan counts its tiles with it)
+constexpr int kW8BigM = 4096;
+constexpr int w8a8_tile_edge(int Mpad) { return Mpad > kW8BigM ? 256 : 128; }
 
 }  // namespace wq

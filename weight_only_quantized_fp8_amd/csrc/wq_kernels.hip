@@ -963,9 +963,15 @@ hipError_t launch_gemm(int kind, int nt, int gemv_rows, const GemmArgs& a, int s
     if (a.kp < 1 || a.kp > kMaxKParts || (a.kp > 1 && !a.ws)) return hipErrorInvalidValue;
     hipError_t e = launch_gemm_parts(kind, nt, gemv_rows, a, split, stream);
     if (e != hipSuccess || a.kp == 1) return e;
-    const int64_t groups = (int64_t)a.rows * (a.N / 4);
-    hipLaunchKernelGGL(reduce_parts_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, a.ws, a.kp,
-                       a.rows, a.N, a.y, a.ldy, (int)is_lut_kind(kind));
+    return launch_sum_parts(a.ws, a.kp, a.rows, a.N, a.y, a.ldy, is_lut_kind(kind), stream);
+}
+
+hipError_t launch_sum_parts(const float* ws, int kp, int rows, int N, uint16_t* y, int64_t ldy, bool f16_out,
+                            hipStream_t stream)
+{
+    const int64_t groups = (int64_t)rows * (N / 4);
+    hipLaunchKernelGGL(reduce_parts_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, ws, kp,
+                       rows, N, y, ldy, (int)f16_out);
     return hipGetLastError();
 }
 

@@ -133,7 +133,9 @@ struct W8Args {
     uint16_t* y;            // [M][ldy] BF16
     int64_t ldy;
     int M, Mpad, N, KB;
-    int n_mt, n_wg;         // 128-row tiles, work-groups with work
+    int n_mt, n_tw, n_wg;   // row tiles, output tiles, work-groups with work (n_tw * kp)
+    int kp;                 // K parts across work-groups (> 1: FP32 partials to ws)
+    float* ws;              // kp > 1: partial outputs [kp][M][N]
 };
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
@@ -214,7 +216,9 @@ __device__ __forceinline__ void dma16(const RawBuf& r, uint32_t dst, uint32_t vo
 // [x * per_xcd, (x+1) * per_xcd) of linear indices; these walk groups of GN
 // column tiles row tile by row tile, so the work-groups an XCD runs at once
 // cover a rectangle of tiles and share each K slice of both operands through
-// that XCD's L2.
+// that XCD's L2.  With kp K parts the part is the outermost index: work-group
+// (part, tile) multiplies the part-th of kp contiguous runs of K blocks and
+// stores its FP32 sums to the part's slab of the workspace.
 template <int WMT, int WNT, int WVM, int WVN, int GN>
 __global__ void __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 w8a8_gemm_kernel(W8Args a)
@@ -235,8 +239,10 @@ w8a8_gemm_kernel(W8Args a)
     const int per_xcd = gridDim.x >> 3;                   // the grid is a multiple of 8
     const int wl = (b & 7) * per_xcd + (b >> 3);
     if (wl >= a.n_wg) return;                             // whole work-group, before any barrier
+    const int kpart = wl / a.n_tw, wt0 = wl - kpart * a.n_tw;
+    const int kbb = (a.KB * kpart) / a.kp, kbe = (a.KB * (kpart + 1)) / a.kp;   // this part's K blocks
     const int n_nt = (a.N + BN - 1) / BN;
-    const int g = wl / (GN * a.n_mt), r = wl - g * (GN * a.n_mt);
+    const int g = wt0 / (GN * a.n_mt), r = wt0 - g * (GN * a.n_mt);
     const int gn = min(GN, n_nt - g * GN);                // column tiles in this group
     const int nt = g * GN + r % gn, mt = r / gn;
 
@@ -331,27 +337,28 @@ w8a8_gemm_kernel(W8Args a)
     };
 
     // one block: own loads of `cur` done, barrier, refill the other stage with
-    // block kb + 1 (the last block again at the end, so every wave always has
-    // the same loads in flight), multiply
+    // block kb + 1 (the part's last block again at the end, so every wave
+    // always has the same loads in flight), multiply
     auto step = [&](int kb, const uint8_t* cur, uint32_t nxt) {
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        issue(kb + 1 < KB ? kb + 1 : KB - 1, nxt);
+        issue(kb + 1 < kbe ? kb + 1 : kbe - 1, nxt);
         compute(kb, cur);
     };
 
-    issue(0, lds0);
-    for (int kb = 0;; kb += 2) {
+    issue(kbb, lds0);
+    for (int kb = kbb;; kb += 2) {
         step(kb, st0, lds1);
-        if (kb + 1 >= KB) break;
+        if (kb + 1 >= kbe) break;
         step(kb + 1, st1, lds0);
-        if (kb + 2 >= KB) break;
+        if (kb + 2 >= kbe) break;
     }
     wait_vmcnt<0>();                                      // no load left writing LDS
 
     // D of a 16x16 tile: lane l holds rows 4(l/16)..+3 of column l%16
     const int row0 = BM * mt + lrow;
     const int col0 = 16 * wcol + (lane & 15);
+    float* const wsp = a.ws + (int64_t)kpart * a.M * a.N;   // this part's partials (kp > 1)
 #pragma unroll
     for (int i = 0; i < WMT; ++i)
 #pragma unroll
@@ -360,7 +367,10 @@ w8a8_gemm_kernel(W8Args a)
             if (m < a.M) {
 #pragma unroll
                 for (int j = 0; j < WNT; ++j)
-                    if (col0 + 16 * j < a.N) a.y[(int64_t)m * a.ldy + col0 + 16 * j] = f32_to_bf16_rne(outer[i][j][q]);
+                    if (col0 + 16 * j < a.N) {
+                        if (a.kp == 1) a.y[(int64_t)m * a.ldy + col0 + 16 * j] = f32_to_bf16_rne(outer[i][j][q]);
+                        else wsp[(int64_t)m * a.N + col0 + 16 * j] = outer[i][j][q];
+                    }
             }
         }
 }
@@ -385,28 +395,33 @@ hipError_t launch_unpack_x(const uint8_t* xq, int M, int K, uint8_t* codes, floa
     return hipGetLastError();
 }
 
-// Tile per M: 128 x 128 (4 waves of 64 x 64, two work-groups per CU) up to
-// kW8BigM rows, 256 x 256 above (8 waves of 64 x 128: twice the MFMAs per byte
-// read from LDS, one work-group per CU).  Measured on the FFN shapes: the
-// smaller tile is as fast or faster up to M = 4096 (more work-groups, two per
-// CU), the larger one slightly faster at M = 8192.
-constexpr int kW8BigM = 4096;
+// Tile per M (w8a8_tile_edge): 128 x 128 (4 waves of 64 x 64, two
+// work-groups per CU) up to kW8BigM rows, 256 x 256 above (8 waves of
+// 64 x 128: twice the MFMAs per byte read from LDS, one work-group per CU).
+// Measured on the FFN shapes: the smaller tile is as fast or faster up to
+// M = 4096 (more work-groups, two per CU), the larger one slightly faster at
+// M = 8192; 128 x 64, 64 x 128 and 64 x 64 tiles are no faster at M = 256 ..
+// 2048 (K parts across work-groups serve the grids those would fill).
 
 template <int WMT, int WNT, int WVM, int WVN, int GN>
 static hipError_t launch_w8a8_tile(W8Args a, hipStream_t stream)
 {
     constexpr int BM = 16 * WMT * WVM, BN = 16 * WNT * WVN;
     a.n_mt = (a.Mpad + BM - 1) / BM;
-    a.n_wg = a.n_mt * ((a.N + BN - 1) / BN);
+    a.n_tw = a.n_mt * ((a.N + BN - 1) / BN);
+    a.n_wg = a.n_tw * a.kp;
     const int grid = (a.n_wg + 7) & ~7;
     hipLaunchKernelGGL((w8a8_gemm_kernel<WMT, WNT, WVM, WVN, GN>), dim3(grid), dim3(64 * WVM * WVN), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
-                       hipStream_t stream)
+                       int kp, float* ws, hipStream_t stream)
 {
+    if (kp < 1 || kp > K / 128 || kp > kMaxKParts || (kp > 1 && !ws)) return hipErrorInvalidValue;
     W8Args a{};
+    a.kp = kp;
+    a.ws = ws;
     a.KB = K / 128;
     a.N = N;
     a.M = M;
@@ -421,9 +436,10 @@ hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq,
         const char* p = std::getenv("WQ_W8A8_TILE");
         return p ? std::atoi(p) : 0;
     }();
-    const bool big = forced ? forced == 256 : a.Mpad > kW8BigM;
-    if (big) return launch_w8a8_tile<4, 8, 4, 2, 4>(a, stream);
-    return launch_w8a8_tile<4, 4, 2, 2, 8>(a, stream);
+    const bool big = forced ? forced == 256 : w8a8_tile_edge(a.Mpad) == 256;
+    hipError_t e = big ? launch_w8a8_tile<4, 8, 4, 2, 4>(a, stream) : launch_w8a8_tile<4, 4, 2, 2, 8>(a, stream);
+    if (e != hipSuccess || kp == 1) return e;
+    return launch_sum_parts(ws, kp, M, N, y, ldy, false, stream);
 }
 
 }  // namespace wq

@@ -19,7 +19,7 @@ __all__ = [
     "wq_lut3_packed_bytes", "wq_pack_lut3", "wq_gemm_lut3",
     "WQ_FMT_LUT3_DENSE", "wq_lut3_dense_packed_bytes", "wq_pack_lut3_dense", "wq_gemm_lut3_dense",
     "wq_unpack_lut3_dense", "pack_lut3_dense", "gemm_lut3_dense",
-    "wq_x_fp8_packed_bytes", "wq_quantize_x_fp8", "wq_gemm_fp8_w8a8", "wq_unpack_x_fp8", "quantize_x_fp8",
+    "wq_x_fp8_packed_bytes", "wq_w8a8_workspace_bytes", "wq_quantize_x_fp8", "wq_gemm_fp8_w8a8", "wq_unpack_x_fp8", "quantize_x_fp8",
     "gemm_fp8_w8a8",
     "wq_gemm_workspace_bytes", "wq_unpack_fp8_block", "wq_unpack_fp8_block_f32", "wq_unpack_lut3",
     "workspace", "pack_fp8", "pack_lut3", "gemm_fp8", "gemm_lut3",
@@ -59,6 +59,7 @@ _SIGS = {
     "wq_gemm_lut3_dense": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
     "wq_unpack_lut3_dense": (_INT, [_P, _I64, _I64, _P, _P]),
     "wq_x_fp8_packed_bytes": (_SZ, [_I64, _I64]),
+    "wq_w8a8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "wq_quantize_x_fp8": (_INT, [_P, _I64, _I64, _I64, _P, _P]),
     "wq_gemm_fp8_w8a8": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _SZ, _P]),
     "wq_unpack_x_fp8": (_INT, [_P, _I64, _I64, _P, _P, _P]),
@@ -204,6 +205,10 @@ def wq_x_fp8_packed_bytes(M: int, K: int) -> int:
     return lib.wq_x_fp8_packed_bytes(M, K)
 
 
+def wq_w8a8_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib.wq_w8a8_workspace_bytes(M, N, K)
+
+
 def wq_quantize_x_fp8(x, M: int, K: int, xq, stream=None) -> None:
     _check(lib.wq_quantize_x_fp8(_ptr(x), _ld(x), M, K, _ptr(xq), _stream(stream)), "wq_quantize_x_fp8")
 
@@ -290,9 +295,10 @@ def quantize_x_fp8(x, stream=None):
     return xq
 
 
-def gemm_fp8_w8a8(packed, N: int, K: int, xq, M: int, stream=None):
-    """y [M, N] (bfloat16) = dequant(xq) . dequant(W)^T."""
+def gemm_fp8_w8a8(packed, N: int, K: int, xq, M: int, ws=None, stream=None):
+    """y [M, N] (bfloat16) = dequant(xq) . dequant(W)^T (ws: optional workspace of
+    wq_w8a8_workspace_bytes(M, N, K) bytes)."""
     import torch
     y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
-    wq_gemm_fp8_w8a8(packed, N, K, xq, M, y, None, stream)
+    wq_gemm_fp8_w8a8(packed, N, K, xq, M, y, ws, stream)
     return y
