@@ -34,6 +34,7 @@ METRIC = "weight-stream GB/s (% of HBM peak) for quantized GEMM at M=1/8/16/32"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 ROTATE_TARGET_BYTES = 1 << 30
+WARM_SECONDS = 0.2
 
 
 def weight_bytes(fmt: str, N: int, K: int) -> int:
@@ -136,7 +137,7 @@ def time_workload(w: Workload, steps: int, warmup: int, use_graph: bool = True):
     hipLaunchKernel) does not sit between the kernels; the graph's output is
     checked bit for bit against an eager call first."""
     import torch
-    for _ in range(warmup):
+    for _ in range(min(warmup, 20)):
         w.step()
     torch.cuda.synchronize()
     graph = None
@@ -163,6 +164,20 @@ def time_workload(w: Workload, steps: int, warmup: int, use_graph: bool = True):
             # the last captured step used copy (steps-1) % copies, identical bytes to copy 0
             if not torch.equal(w.y.view(torch.int16), ref.view(torch.int16)):
                 raise RuntimeError("graph replay %d differs from the eager result" % rep)
+    # The rest of the warm-up: at least `warmup` steps in all and at least
+    # WARM_SECONDS of back-to-back work, so the part's clock has settled to
+    # its sustained value before the timed steps (it ramps over the first
+    # milliseconds of load).
+    done, t_warm = min(warmup, 20), time.perf_counter()
+    while done < warmup or time.perf_counter() - t_warm < WARM_SECONDS:
+        if graph is not None:
+            graph.replay()
+            done += steps
+        else:
+            for _ in range(100):
+                w.step()
+            done += 100
+        torch.cuda.synchronize()          # keeps the host's clock on the GPU's work
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)

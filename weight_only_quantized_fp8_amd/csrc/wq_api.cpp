@@ -345,10 +345,12 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // One-tile MFMA waves serve M = 17..32 in one pass (each dequantised
-    // operand feeds both 16-row halves); two-tile waves run the rows 0..15
-    // and 16..M-1 as two passes.  Either way every row sees the same
-    // arithmetic as in a call of at most 16 rows.
-    const int64_t rows_per_launch = (kind != wq::KIND_GEMV_FP8 && p.nt == 1) ? 32 : 16;
+    // operand feeds both 16-row halves) -- for the LUT tile where its 32-row
+    // chunks fit; otherwise the rows 0..15 and 16..M-1 run as two passes.
+    // Either way every row sees the same arithmetic as in a call of at most
+    // 16 rows.
+    const bool single_pass = p.nt == 1 && (kind == wq::KIND_MFMA_FP8 || wq::lut_single_pass(kind, p.sn, p.split));
+    const int64_t rows_per_launch = single_pass ? 32 : 16;
     for (int64_t r0 = 0; r0 < M; r0 += rows_per_launch) {
         const int rows = (int)std::min<int64_t>(rows_per_launch, M - r0);
         a.x = x + r0 * ldx;

@@ -68,10 +68,10 @@ struct LutPlanes {
     uint32_t hi0, hi1;   // high bytes of entries 0..3 / 4..7
 };
 
-// q[i] holds map entries (2i, 2i+1) as an FP16 pair; g is the group scale.
-__device__ __forceinline__ LutPlanes lut_scaled_planes(const uint32_t q[4], _Float16 g)
+// q[i] holds map entries (2i, 2i+1) as an FP16 pair; gg is the group scale
+// in both halves.
+__device__ __forceinline__ LutPlanes lut_scaled_planes2(const uint32_t q[4], f16x2_t gg)
 {
-    f16x2_t gg = {g, g};
     uint32_t e[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -83,6 +83,11 @@ __device__ __forceinline__ LutPlanes lut_scaled_planes(const uint32_t q[4], _Flo
     p.lo1 = __builtin_amdgcn_perm(e[3], e[2], 0x06040200u);
     p.hi1 = __builtin_amdgcn_perm(e[3], e[2], 0x07050301u);
     return p;
+}
+
+__device__ __forceinline__ LutPlanes lut_scaled_planes(const uint32_t q[4], _Float16 g)
+{
+    return lut_scaled_planes2(q, f16x2_t{g, g});
 }
 
 // One packed dword = eight 3-bit codes: byte b carries code e=b in its low

@@ -30,18 +30,26 @@ constexpr bool is_lut_kind(int kind) { return kind == KIND_MFMA_LUT || kind == K
 constexpr int k_align(int kind) { return is_lut_kind(kind) ? 8 : 1; }
 
 // Size of an activation chunk (the K group synchronises once per chunk) in
-// 16-row K blocks, per kernel kind and row tiles MT (a 32-row chunk holds
-// half as many K blocks).  Measured on MI355X: the FP8 MFMA tile runs best
-// with two K blocks per chunk at any M -- 6-15% faster than four at M <= 16
-// for the low-N projections, while one 32-row block per chunk costs 8-19% at
-// M = 32 -- and the LUT tile with four 16-row blocks, its 7-wave work-groups
-// running 7% slower with two.
-constexpr int chunk_blocks16(int kind, int mt) { return kind == KIND_MFMA_FP8 ? 2 * mt : 4; }
+// 16-row K blocks, per kernel kind and row tiles MT.  Measured on MI355X: the
+// FP8 MFMA tile runs best with two K blocks per chunk at any M -- 6-15%
+// faster than four at M <= 16 for the low-N projections, while one 32-row
+// block per chunk costs 8-19% at M = 32.  The LUT tile's chunk is one quad of
+// four K blocks at any M (its lane groups read four blocks at once); the GEMV
+// stages four 4-row blocks.
+constexpr int chunk_blocks16(int kind, int mt)
+{
+    return kind == KIND_MFMA_FP8 ? 2 * mt : is_lut_kind(kind) ? 4 * mt : 4;
+}
+
+// LDS bytes of one staged activation chunk (16-row blocks, rows padded to 272 bytes)
+constexpr int chunk_lds_bytes(int kind, int mt) { return chunk_blocks16(kind, mt) * 16 * (128 * 2 + 16); }
 
 // Each K group of an MFMA work-group double-buffers one activation chunk in
-// LDS (at most 2 x 4 K blocks x 16 rows x 272 bytes = 34816 bytes); the 160
-// KiB of LDS of a compute unit bound the K groups of one work-group at 4.
+// LDS; at M <= 16 that is at most 2 x 4 K blocks x 16 rows x 272 bytes =
+// 34816 bytes, so the 160 KiB of LDS of a compute unit bound the K groups of
+// one work-group at 4.
 constexpr int kMaxKGroups = 4;
+constexpr int kLdsBytes = 160 * 1024;
 
 // Most K parts a GEMM splits across work-groups (grid y).
 constexpr int kMaxKParts = 32;
@@ -68,6 +76,20 @@ constexpr int max_split_xpl(int kind, int nt, int xpl)
     return ((is_lut_kind(kind) && nt == 1 && xpl <= 4) || kind == KIND_GEMV_FP8) ? 16 : 8;
 }
 constexpr int max_split(int kind, int nt, int sn) { return max_split_xpl(kind, nt, x_pieces_per_lane(kind, sn)); }
+
+// Whether a one-tile LUT tiling also runs M = 17..32 in one pass (both
+// 16-row halves share each dequantised operand).  Its 32-row quad chunks take
+// twice the LDS and activation pieces of the 16-row ones: the pieces per lane
+// must be a built count (4, 6 or 8) within the work-group's launch bound and
+// the double-buffered chunks of its K groups must fit in LDS.  Otherwise the
+// host runs rows 0..15 and 16..M-1 as two passes.
+constexpr bool lut_single_pass(int kind, int sn, int split)
+{
+    if (!is_lut_kind(kind) || sn < 1 || split < sn) return false;
+    const int xpl = x_pieces_per_lane(kind, sn, 2);
+    return (xpl == 4 || xpl == 6 || xpl == 8) && split <= max_split_xpl(kind, 1, xpl) &&
+           (split / sn) * 2 * chunk_lds_bytes(kind, 2) <= kLdsBytes;
+}
 
 // Whether (nt, sn, split) is a launchable tiling for this kernel kind.
 constexpr bool split_ok(int kind, int nt, int sn, int split)

@@ -219,6 +219,8 @@ struct Fp8Stream {
         srow = reinterpret_cast<const float*>(a.scales) + (int64_t)(min(tile0, a.n_tiles - 1) * 16 / 128) * a.KB;
     }
 
+    __device__ __forceinline__ void set_range(int) {}
+
     __device__ __forceinline__ void load(Unit& r, int kb, bool valid, int) const
     {
 #pragma unroll
@@ -343,18 +345,33 @@ struct MfmaFp8 : Fp8Stream<NT> {
 };
 
 // ---- 3-bit LUT weights, 16-row FP16 MFMA tile -------------------------------
+// Quad schedule.  A wave takes the K blocks of its range four at a time (a
+// quad; ranges start at multiples of 8 blocks).  Lane group g = lane/16 works
+// on block qb+g of quad qb at all four of the quad's loop positions
+// p = 0..3: at position p it loads piece p of that block's unit -- the 32
+// codes the packed layout gives lane 16p + lane%16, i.e. k = 32s + 8p .. +7
+// for MFMA steps s = 0..3 -- and takes the matching activations from block
+// qb+g of the staged chunk (a chunk is exactly one quad).  An MFMA sums over
+// all 32 of its k slots, so the four lane groups may feed k values of four
+// different blocks.  What this buys: a lane meets one (row, group scale) pair
+// per quad instead of one per unit, so it scales the map and splits it into
+// byte planes once per 4 units (the decode itself is unchanged).
 // Group scales come as one 16-byte load per row and run of 8 K blocks, issued
-// with the weights of the run's first unit; K-group ranges start at multiples
-// of 8 blocks, so a unit's place in its run is its (compile-time) position in
-// the unrolled loop.  DENSE selects the 3-bit-per-code unit layout.
+// with the weights of the run's first unit; a unit's place in its run is its
+// compile-time position in the unrolled loop, and a lane picks its block's
+// scale from the run with one byte permute.  DENSE selects the
+// 3-bit-per-code unit layout.
 template <int NT, int MT, bool DENSE>
 struct MfmaLut {
     static constexpr int KIND = DENSE ? KIND_MFMA_LUT3D : KIND_MFMA_LUT;
     static constexpr uint32_t kUnitBytes = DENSE ? 768u : 1024u;
+    static constexpr uint32_t kPiece = DENSE ? 12u : 16u;     // one lane's bytes of a unit
     static constexpr int NTILES = NT;
     static constexpr int ROWS = 16 * MT;
     static constexpr int KALIGN = k_align(KIND);   // K blocks per group-scale load
+    static constexpr int kXBlock = 16 * MT * kXRowBytes;     // LDS bytes of one staged K block
     template <int XPL> using Stage = XChunk<XPL, MT, chunk_blocks16(KIND, MT)>;
+    static_assert(chunk_blocks16(KIND, MT) == 4 * MT, "an activation chunk holds one quad of K blocks");
     struct Unit {
         uint4 w[NT];
         uint4 gv[NT];        // FP16 group scales of 8 K blocks (loaded by a run's first unit only)
@@ -363,14 +380,19 @@ struct MfmaLut {
     int KB;
     int KB8;
     int ntiles;
-    buf_t rw;                // code units of the wave's tiles (zero bytes past N)
+    int kb_end;              // end of the wave's K range
+    buf_t rw;                // code units of the wave's tiles
     buf_t rg;                // group scales of the wave's tiles
     buf_t rnull;             // zero bytes: loads return zeros
     uint32_t q[4];           // map entries as FP16 pairs
+    uint32_t vq;             // this lane's piece 0 in its block of a quad: row lane%16, block g
+    uint32_t vqc[NT];        // vq for the current quad, or out of range (block past the K range or tile past N)
+    uint32_t gsel;           // byte-permute selector: FP16 element g of four, as a pair
     uint4 gcur[NT];          // group scales of the current run
+    LutPlanes pl[NT];        // scaled map of the current quad's block, as byte planes
     f32x4_t acc[NT][MT];
 
-    __device__ MfmaLut(const GemmArgs& a, int l, int tile0) : lane(l), KB(a.KB), KB8((a.KB + 7) / 8)
+    __device__ MfmaLut(const GemmArgs& a, int l, int tile0) : lane(l), KB(a.KB), KB8((a.KB + 7) / 8), kb_end(0)
     {
         ntiles = max(0, min(NT, a.n_tiles - tile0));
         const int t0 = min(tile0, a.n_tiles);
@@ -378,6 +400,9 @@ struct MfmaLut {
         rg = make_buf(reinterpret_cast<const uint8_t*>(a.scales) + (int64_t)t0 * KB8 * 256,
                       (uint32_t)(ntiles * KB8) * 256u);
         rnull = make_buf(a.codes, 0);
+        const uint32_t g = (uint32_t)(l >> 4);
+        vq = (uint32_t)(l & 15) * kPiece + g * kUnitBytes;
+        gsel = (2 * g) | ((2 * g + 1) << 8) | ((2 * g) << 16) | ((2 * g + 1) << 24);
         const uint32_t* qm = reinterpret_cast<const uint32_t*>(a.qmap);
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = qm[i];
@@ -386,46 +411,63 @@ struct MfmaLut {
 #pragma unroll
             for (int h = 0; h < MT; ++h) acc[t][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             gcur[t] = make_uint4(0, 0, 0, 0);
+            vqc[t] = kBufOutOfRange;
         }
     }
 
-    // pos: the unit's position in the unrolled loop, == kb (mod 8)
-    __device__ __forceinline__ void load(Unit& r, int kb, bool valid, int pos) const
+    __device__ __forceinline__ void set_range(int kb1) { kb_end = kb1; }
+
+    // pos: the unit's position in the unrolled loop, == kb (mod 8).  The
+    // lane's block is past the K range only in the last, partial quad of K;
+    // its loads then return zeros (valid is not used for the codes: a lane
+    // whose block lies inside the range loads at all four positions of its
+    // quad, whether or not the position's own block does).
+    __device__ __forceinline__ void load(Unit& r, int kb, bool valid, int pos)
     {
+        const int p = pos & 3;
+        const int qb = kb - p;                           // first K block of the quad
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const bool ok = valid && t < ntiles;
-            const uint32_t soff = (uint32_t)(t * KB + kb) * kUnitBytes;
-            r.w[t] = DENSE ? buf_load_stream12(ok ? rw : rnull, lane * 12, soff)
-                           : buf_load_stream16(ok ? rw : rnull, lane * 16, soff);
+            if (p == 0) vqc[t] = (t < ntiles && qb + (lane >> 4) < kb_end) ? vq : kBufOutOfRange;
+            const uint32_t soff = (uint32_t)(t * KB + (qb < KB ? qb : 0)) * kUnitBytes;
+            const uint32_t vo = vqc[t] + (uint32_t)p * 16u * kPiece;
+            r.w[t] = DENSE ? buf_load_stream12(rw, vo, soff) : buf_load_stream16(rw, vo, soff);
             if ((pos & 7) == 0)
-                r.gv[t] = buf_load16(ok ? rg : rnull, (lane & 15) * 16, (uint32_t)(t * KB8 + (kb >> 3)) * 256u);
+                r.gv[t] = buf_load16((valid && t < ntiles) ? rg : rnull, (lane & 15) * 16,
+                                     (uint32_t)(t * KB8 + (kb >> 3)) * 256u);
         }
     }
 
+    // xblk: the staged block of position pos; its quad's chunk starts p blocks earlier
     __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk, int pos)
     {
         const int e = pos & 7;
+        const int p = pos & 3;
         if (e == 0) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) gcur[t] = r.gv[t];
         }
+        // MFMA step s: lane group g holds k = 32s + 8p .. +7 of block qb+g
+        const uint8_t* xq = xblk + ((lane >> 4) - p) * kXBlock + (lane & 15) * kXRowBytes + p * 16;
         f16x8_t b[MT][4];
 #pragma unroll
         for (int h = 0; h < MT; ++h)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)   // MFMA step s: lane group g holds k = 32s + 8g + e
-                b[h][s] = __builtin_bit_cast(f16x8_t, x_frag(xblk, lane, s * 32 + (lane >> 4) * 8, h));
+            for (int s = 0; s < 4; ++s)
+                b[h][s] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(xq + h * 16 * kXRowBytes + s * 64));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const uint32_t gd = e < 2 ? gcur[t].x : e < 4 ? gcur[t].y : e < 6 ? gcur[t].z : gcur[t].w;
-            const uint16_t gbits = (uint16_t)((e & 1) ? gd >> 16 : gd & 0xFFFFu);
-            const LutPlanes pl = lut_scaled_planes(q, __builtin_bit_cast(_Float16, gbits));
+            if (p == 0) {
+                // this lane's group scale (block qb+g: element (e + g) of the run) as an FP16 pair
+                const uint32_t gp = e == 0 ? __builtin_amdgcn_perm(gcur[t].y, gcur[t].x, gsel)
+                                           : __builtin_amdgcn_perm(gcur[t].w, gcur[t].z, gsel);
+                pl[t] = lut_scaled_planes2(q, __builtin_bit_cast(f16x2_t, gp));
+            }
             const uint32_t w3 = DENSE ? lut3d_step3_word(r.w[t].x, r.w[t].y, r.w[t].z) : r.w[t].w;
             const uint32_t wd[4] = {r.w[t].x, r.w[t].y, r.w[t].z, w3};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const f16x8_t av = lut_decode8(wd[s], pl);
+                const f16x8_t av = lut_decode8(wd[s], pl[t]);
 #pragma unroll
                 for (int h = 0; h < MT; ++h) acc[t][h] = mfma_f16(av, b[h][s], acc[t][h]);
             }
@@ -636,6 +678,7 @@ gemm_kernel(GemmArgs a)
     const int tile0 = (blockIdx.x * SN + cw) * NT;
 
     Pol pol(a, lane, tile0);
+    pol.set_range(kb1);
     {
         typename Pol::Unit r[R];
         uint8_t* xb = lds + kg * 2 * XS::kChunkBytes;   // this K group's two chunk buffers
@@ -922,7 +965,8 @@ static hipError_t launch_mfma(int kind, const GemmArgs& a, int split, hipStream_
             return launch_one<MfmaFp8<NT, MT>, kDepthMfmaFp8, XPL, false>(a, split, s);
         return hipErrorInvalidValue;
     }
-    if constexpr (xpl_used(KIND_MFMA_LUT, MT, XPL)) {
+    // 32-row LUT tiles run only where lut_single_pass allows (4, 6 or 8 pieces)
+    if constexpr (xpl_used(KIND_MFMA_LUT, MT, XPL) && (MT == 1 || XPL == 4 || XPL == 6 || XPL == 8)) {
         if (kind == KIND_MFMA_LUT3D) return launch_one<MfmaLut<NT, MT, true>, kDepthMfmaLut, XPL, true>(a, split, s);
         return launch_one<MfmaLut<NT, MT, false>, kDepthMfmaLut, XPL, true>(a, split, s);
     }
