@@ -114,9 +114,10 @@ struct XChunk {
     // rows >= M and pieces past the chunk read zeros.
     __device__ __forceinline__ void load(int kb, int kb_end)
     {
+        const int lim = kb_end - kb;    // blocks of this chunk inside the range (wave-uniform)
 #pragma unroll
         for (int i = 0; i < XPL; ++i)
-            r[i] = buf_load16(rx, kb + blk[i] < kb_end ? vo[i] : kBufOutOfRange, (uint32_t)kb * 256u);
+            r[i] = buf_load16(rx, blk[i] < lim ? vo[i] : kBufOutOfRange, (uint32_t)kb * 256u);
     }
 
     __device__ __forceinline__ void stage(uint8_t* buf) const
@@ -169,9 +170,10 @@ struct XChunkF32 {
 
     __device__ __forceinline__ void load(int kb, int kb_end)
     {
+        const int lim = kb_end - kb;    // blocks of this chunk inside the range (wave-uniform)
 #pragma unroll
         for (int i = 0; i < XPL; ++i)
-            r[i] = buf_load16(rx, kb + blk[i] < kb_end ? vo[i] : kBufOutOfRange, (uint32_t)kb * 256u);
+            r[i] = buf_load16(rx, blk[i] < lim ? vo[i] : kBufOutOfRange, (uint32_t)kb * 256u);
     }
 
     // BF16 -> FP32 is exact: the BF16 bits become the top half of the FP32 word
@@ -428,7 +430,7 @@ struct MfmaLut {
         const int qb = kb - p;                           // first K block of the quad
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            if (p == 0) vqc[t] = (t < ntiles && qb + (lane >> 4) < kb_end) ? vq : kBufOutOfRange;
+            if (p == 0) vqc[t] = (t < ntiles && (lane >> 4) < kb_end - qb) ? vq : kBufOutOfRange;
             const uint32_t soff = (uint32_t)(t * KB + (qb < KB ? qb : 0)) * kUnitBytes;
             const uint32_t vo = vqc[t] + (uint32_t)p * 16u * kPiece;
             r.w[t] = DENSE ? buf_load_stream12(rw, vo, soff) : buf_load_stream16(rw, vo, soff);
