@@ -246,6 +246,7 @@ struct Fp8Stream {
 template <int NT, int MT>
 struct MfmaFp8 : Fp8Stream<NT> {
     static constexpr int KIND = KIND_MFMA_FP8;
+    static constexpr bool kSumInRegisters = true;   // K groups combine through add_partial
     static constexpr int NTILES = NT;
     static constexpr int ROWS = 16 * MT;
     static constexpr int KALIGN = k_align(KIND);   // K-group ranges start at any K block
@@ -330,6 +331,19 @@ struct MfmaFp8 : Fp8Stream<NT> {
         }
     }
 
+    // add another K group's partial tile (slot as written by store_partial)
+    __device__ __forceinline__ void add_partial(const float* slot)
+    {
+        const int n4 = (lane >> 4) * 4;
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const int m = 16 * h + (lane & 15);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                outer[t][h] += *reinterpret_cast<const f32x4_t*>(slot + m * NT * 16 + t * 16 + n4);
+        }
+    }
+
     // one K part's FP32 sums of this wave's tiles into dst[m][n] (row stride N)
     __device__ __forceinline__ void store_part(float* dst, const GemmArgs& a, int tile0) const
     {
@@ -366,6 +380,7 @@ struct MfmaFp8 : Fp8Stream<NT> {
 template <int NT, int MT, bool DENSE>
 struct MfmaLut {
     static constexpr int KIND = DENSE ? KIND_MFMA_LUT3D : KIND_MFMA_LUT;
+    static constexpr bool kSumInRegisters = true;   // K groups combine through add_partial
     static constexpr uint32_t kUnitBytes = DENSE ? 768u : 1024u;
     static constexpr uint32_t kPiece = DENSE ? 12u : 16u;     // one lane's bytes of a unit
     static constexpr int NTILES = NT;
@@ -507,6 +522,19 @@ struct MfmaLut {
         }
     }
 
+    // add another K group's partial tile (slot as written by store_partial)
+    __device__ __forceinline__ void add_partial(const float* slot)
+    {
+        const int n4 = (lane >> 4) * 4;
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const int m = 16 * h + (lane & 15);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t][h] += *reinterpret_cast<const f32x4_t*>(slot + m * NT * 16 + t * 16 + n4);
+        }
+    }
+
     // one K part's FP32 sums of this wave's tiles into dst[m][n] (row stride N)
     __device__ __forceinline__ void store_part(float* dst, const GemmArgs& a, int tile0) const
     {
@@ -537,6 +565,7 @@ struct MfmaLut {
 template <int MR>
 struct GemvFp8 : Fp8Stream<1> {
     static constexpr int KIND = KIND_GEMV_FP8;
+    static constexpr bool kSumInRegisters = false;  // K groups combine in LDS by all threads
     static constexpr int NTILES = 1;
     static constexpr int ROWS = 16;       // rows of the partial-tile slot (MR used)
     static constexpr int KALIGN = 1;
@@ -711,7 +740,19 @@ gemm_kernel(GemmArgs a)
         }
     }
     float* const wsp = a.ws + (int64_t)kpart * a.rows * a.N;  // this K part's partials (a.kp > 1)
-    if (SK == 1) {
+    if constexpr (Pol::kSumInRegisters) if (SK > 1) {
+        // K groups 1..SK-1 park their partial tiles in LDS; each K-group-0
+        // wave adds those of its columns in K-group order and stores its
+        // tiles itself: ((kg0 + kg1) + kg2) + ..., the same sums, in the same
+        // order, as an all-thread reduction, without its second pass over LDS
+        __syncthreads();   // every wave is done with the staging buffers
+        float* part = reinterpret_cast<float*>(lds);           // [S][PR][TW]
+        if (kg > 0) pol.store_partial(part + wave * PR * TW);
+        __syncthreads();
+        if (kg > 0) return;
+        for (int k = 1; k < SK; ++k) pol.add_partial(part + (k * SN + cw) * PR * TW);
+    }
+    if (Pol::kSumInRegisters || SK == 1) {
         if (a.kp == 1) pol.template store_direct<F16_OUT>(a, tile0);
         else pol.store_part(wsp, a, tile0);
         return;
