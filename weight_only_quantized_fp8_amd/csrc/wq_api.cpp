@@ -141,7 +141,7 @@ struct TableEntry {
 };
 constexpr TableEntry kTable[] = {
     {wq::KIND_MFMA_FP8, 17408, 5120, 1, 5, 5, 1},    // FFN gate/up
-    {wq::KIND_MFMA_FP8, 5120, 17408, 1, 2, 8, 1},    // FFN down
+    {wq::KIND_MFMA_FP8, 5120, 17408, 1, 2, 6, 1},    // FFN down
     {wq::KIND_MFMA_FP8, 6144, 5120, 1, 2, 6, 1},     // attention Q
     {wq::KIND_MFMA_FP8, 1024, 5120, 1, 1, 4, 1},     // attention K, V
     {wq::KIND_MFMA_FP8, 5120, 6144, 1, 2, 6, 1},     // attention output

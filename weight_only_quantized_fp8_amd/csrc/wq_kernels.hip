@@ -716,6 +716,12 @@ gemm_kernel(GemmArgs a)
         XS xc;
         xc.init(a, lane, cw, SN);
         xc.load(kb0, kb1);
+        // FP8 tile: let the first activation chunk's requests reach memory
+        // ahead of the weight ring's first burst, which they would otherwise
+        // queue behind (~256 cycles; attention K/V 7.7 -> 7.2 us, the large
+        // shapes within 1%; the LUT tile, whose burst is smaller per wave,
+        // gains nothing from it)
+        if constexpr (Pol::KIND == KIND_MFMA_FP8) __builtin_amdgcn_s_sleep(4);
 #pragma unroll
         for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len, i);
         xc.stage(xb);
