@@ -334,6 +334,36 @@ def test_every_tiling_matches_oracle(nt, sn, split, tuning_reset):
             assert np.array_equal(yd, y), "lut3 dense N=%d K=%d M=%d" % (N, K, M)
 
 
+# Tilings whose 32-row LUT chunks fit, so M = 17..32 runs in one pass with
+# both 16-row halves fed by each dequantised operand (the host's single-pass
+# rule: 4, 6 or 8 activation pieces per lane within the launch bound, and the
+# K groups' double-buffered 32-row chunks within LDS), and one that does not.
+LUT_SINGLE_PASS = [(1, 8, 8), (1, 8, 16), (1, 6, 6), (1, 4, 8), (1, 7, 14)]
+
+
+@pytest.mark.parametrize("nt,sn,split", LUT_SINGLE_PASS, ids=["sn%d-s%d" % t[1:] for t in LUT_SINGLE_PASS])
+@pytest.mark.parametrize("dense", [False, True], ids=["nibble", "dense"])
+def test_lut3_single_pass_rows_equal_16_row_calls(nt, sn, split, dense, tuning_reset):
+    """A 32-row LUT call (one pass or two) gives each row the bits of the
+    16-row call holding that row, and passes the oracle; K = 1152 ends in a
+    partial quad of K blocks."""
+    wq = U.wqmod()
+    wq.wq_set_tuning(nt, sn, split, 0)
+    U.note("lut3 single pass sn=%d split=%d dense=%d" % (sn, split, dense))
+    N, K = 400, 1152
+    c, q, g = synth.lut3_weights(N, K, 910)
+    packed = U.pack_lut3(c, q, g, dense=dense)
+    x32 = synth.x_f16(32, K, 911)
+    y32, _ = U.run_lut3(packed, N, K, x32, dense=dense)
+    ya, _ = U.run_lut3(packed, N, K, x32[:16], dense=dense)
+    yb, _ = U.run_lut3(packed, N, K, x32[16:], dense=dense)
+    assert np.array_equal(y32, np.vstack([ya, yb]))
+    y20, _ = U.run_lut3(packed, N, K, x32[:20], dense=dense)
+    assert np.array_equal(y20, y32[:20])
+    r = U.grade_lut3(y32, x32, c, q, g, K)
+    assert r.ok, str(r)
+
+
 def test_hip_graph_replays_match_eager():
     """The GEMM captured in a HIP graph (no memset nodes: the library queues
     kernels only) replays to the eager result every time, with eager work and
