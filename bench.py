@@ -24,6 +24,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -51,10 +52,15 @@ def algorithmic_bytes(fmt: str, N: int, K: int, M: int) -> int:
 
 
 def kernel_src_sha() -> str:
+    """Hash of the library's sources with comments and layout removed, so a
+    change to a comment does not orphan counter data taken on the same code."""
     h = hashlib.sha256()
     for f in ("wq_kernels.hip", "wq_w8a8.hip", "wq_device.hpp", "wq_internal.h", "wq_api.cpp"):
-        with open(os.path.join(ROOT, "weight_only_quantized_fp8_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "weight_only_quantized_fp8_amd", "csrc", f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

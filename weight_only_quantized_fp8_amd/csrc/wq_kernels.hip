@@ -38,8 +38,9 @@
 // range with the next D units' loads in flight (a register ring) while the
 // column-waves of a K group share activation chunks staged in LDS.  Every
 // 128-K block is folded onto FP32 accumulators.  With one K group each wave
-// stores its own outputs; otherwise the work-group sums the K groups' partial
-// tiles in LDS in a fixed order.  With KP = 1 no two work-groups share an
+// stores its own outputs; otherwise the other K groups' partial tiles pass
+// through LDS and K group 0 adds them in a fixed order and stores (the GEMV:
+// the work-group sums them in LDS in the same fixed order).  With KP = 1 no two work-groups share an
 // output: no cross-work-group traffic, no workspace, no fence.  With KP > 1
 // (the caller passed a workspace) each K part's work-group stores FP32 sums
 // to the workspace and a second kernel adds the parts in order.  Every sum
@@ -719,8 +720,7 @@ gemm_kernel(GemmArgs a)
         // FP8 tile: let the first activation chunk's requests reach memory
         // ahead of the weight ring's first burst, which they would otherwise
         // queue behind (~256 cycles; attention K/V 7.7 -> 7.2 us, the large
-        // shapes within 1%; the LUT tile, whose burst is smaller per wave,
-        // gains nothing from it)
+        // shapes within 1%; the LUT tile measured no gain from it)
         if constexpr (Pol::KIND == KIND_MFMA_FP8) __builtin_amdgcn_s_sleep(4);
 #pragma unroll
         for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len, i);
