@@ -274,9 +274,10 @@ def time_w8a8(name: str, M: int, steps: int = 20, copies: int = 4) -> dict:
             "k_parts": k_parts}
 
 
-def cpu_baseline(name: str, M: int, min_seconds: float = 3.0, max_reps: int = 20):
+def cpu_baseline(name: str, M: int, min_seconds: float = 10.0, max_reps: int = 500):
     """The oracle as it stands, on the host cores, over the whole workload (all
-    outputs), repeated until min_seconds of wall time; the median pass counts."""
+    outputs), repeated until about min_seconds of CPU wall time (at least 3
+    passes); the median pass counts."""
     import oracle
     import synth
     fmt, N, K, _ = synth.CONFIGS[name]
@@ -298,8 +299,9 @@ def cpu_baseline(name: str, M: int, min_seconds: float = 3.0, max_reps: int = 20
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[len(times) // 2]
     return {"value": weight_bytes(fmt, N, K) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "whole %s workload N=%d K=%d M=%d, all %d outputs; median of %d passes, %.3f s each"
-                      % (name, N, K, M, M * N, len(times), dt),
+            "sample": "whole %s workload N=%d K=%d M=%d, all %d outputs; median of %d passes "
+                      "(%.1f s of CPU work in all), %.3f s each"
+                      % (name, N, K, M, M * N, len(times), sum(times), dt),
             "seconds": dt}
 
 
