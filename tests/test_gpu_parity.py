@@ -285,6 +285,39 @@ def test_zero_rows_and_zero_matrix():
         assert not (y & 0x7FFF).any()
 
 
+def test_nan_codes_poison_exactly_their_columns():
+    """E4M3 NaN codes (0x7F, 0xFF) in W: every output of a column whose row
+    of W holds one is NaN on every path (GEMV, MFMA tile, K parts across
+    work-groups, 32-row single pass), every other output is finite and passes
+    the oracle."""
+    U.note("nan codes")
+    N, K = 512, 2048
+    codes, scales = synth.fp8_weights(N, K, 57)
+    codes = codes.copy()
+    bad = [3, 130, 257, 511]
+    for i, n in enumerate(bad):
+        codes[n, (97 * i + 5) % K] = 0x7F if i % 2 == 0 else 0xFF
+    packed = U.pack_fp8(codes, scales)
+    wq = U.wqmod()
+    for path, M in ((GEMV, 1), (GEMV, 4), (MFMA, 16), (MFMA, 32)):
+        for ws in (None, "auto"):
+            wq.wq_set_kparts(4 if ws else 0)
+            try:
+                xbits = synth.x_bf16(M, K, 58)
+                y, _ = U.run_fp8(packed, N, K, xbits, path=path, ws=ws)
+            finally:
+                wq.wq_set_kparts(0)
+            nan = np.isnan(oracle.bf16_value(y))
+            expect = np.zeros(N, dtype=bool)
+            expect[bad] = True
+            assert np.array_equal(nan, np.broadcast_to(expect, nan.shape)), (path, M, ws)
+            ok = ~expect
+            y64 = oracle.gemm_fp8(xbits, codes, scales, K=K)
+            assert np.all(np.isnan(y64[:, expect])) and np.all(np.isfinite(y64[:, ok]))
+            g = U.compare.grade(y, y64, U.floor_fp8(xbits, codes, scales, K), "bf16")
+            assert g.ok, (path, M, ws, str(g))
+
+
 # ------------------------------------------------------ every kernel variant
 
 # (nt, sn, split): every activation-piece count per lane the kernels are built
