@@ -369,9 +369,10 @@ def test_every_tiling_matches_oracle(nt, sn, split, tuning_reset):
 
 # Tilings whose 32-row LUT chunks fit, so M = 17..32 runs in one pass with
 # both 16-row halves fed by each dequantised operand (the host's single-pass
-# rule: 4, 6 or 8 activation pieces per lane within the launch bound, and the
-# K groups' double-buffered 32-row chunks within LDS), and one that does not.
-LUT_SINGLE_PASS = [(1, 8, 8), (1, 8, 16), (1, 6, 6), (1, 4, 8), (1, 7, 14)]
+# rule: 4, 5, 6 or 8 activation pieces per lane within the launch bound, and
+# the K groups' double-buffered 32-row chunks within LDS), and two that do
+# not (16 pieces per lane; 16 pieces and 4 K groups).
+LUT_SINGLE_PASS = [(1, 8, 8), (1, 8, 16), (1, 6, 6), (1, 4, 8), (1, 7, 14), (1, 2, 4), (1, 2, 8)]
 
 
 @pytest.mark.parametrize("nt,sn,split", LUT_SINGLE_PASS, ids=["sn%d-s%d" % t[1:] for t in LUT_SINGLE_PASS])

@@ -68,26 +68,26 @@ constexpr int x_pieces_per_lane(int kind, int sn, int mt = 1)
 // kernels are built for work-groups of at most 8 waves, which lets a wave
 // hold up to 256 VGPRs: the register ring, the activation pieces in flight
 // and the unrolled MFMA steps of a chunk need more than 128.  One-tile LUT
-// waves with at most 4 activation pieces per lane fit in 128 and are built
-// for up to 16 waves, so a work-group can split K across more waves than it
-// has SIMDs.
+// waves with at most 5 activation pieces per lane (5 only occurs for 32-row
+// chunks shared by 7 column-waves) fit in 128 and are built for up to 16
+// waves, so a work-group can split K across more waves than it has SIMDs.
 constexpr int max_split_xpl(int kind, int nt, int xpl)
 {
-    return ((is_lut_kind(kind) && nt == 1 && xpl <= 4) || kind == KIND_GEMV_FP8) ? 16 : 8;
+    return ((is_lut_kind(kind) && nt == 1 && xpl <= 5) || kind == KIND_GEMV_FP8) ? 16 : 8;
 }
 constexpr int max_split(int kind, int nt, int sn) { return max_split_xpl(kind, nt, x_pieces_per_lane(kind, sn)); }
 
 // Whether a one-tile LUT tiling also runs M = 17..32 in one pass (both
 // 16-row halves share each dequantised operand).  Its 32-row quad chunks take
 // twice the LDS and activation pieces of the 16-row ones: the pieces per lane
-// must be a built count (4, 6 or 8) within the work-group's launch bound and
+// must be a built count (4, 5, 6 or 8) within the work-group's launch bound and
 // the double-buffered chunks of its K groups must fit in LDS.  Otherwise the
 // host runs rows 0..15 and 16..M-1 as two passes.
 constexpr bool lut_single_pass(int kind, int sn, int split)
 {
     if (!is_lut_kind(kind) || sn < 1 || split < sn) return false;
     const int xpl = x_pieces_per_lane(kind, sn, 2);
-    return (xpl == 4 || xpl == 6 || xpl == 8) && split <= max_split_xpl(kind, 1, xpl) &&
+    return (xpl == 4 || xpl == 5 || xpl == 6 || xpl == 8) && split <= max_split_xpl(kind, 1, xpl) &&
            (split / sn) * 2 * chunk_lds_bytes(kind, 2) <= kLdsBytes;
 }
 

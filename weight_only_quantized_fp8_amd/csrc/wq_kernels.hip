@@ -1014,8 +1014,8 @@ static hipError_t launch_mfma(int kind, const GemmArgs& a, int split, hipStream_
             return launch_one<MfmaFp8<NT, MT>, kDepthMfmaFp8, XPL, false>(a, split, s);
         return hipErrorInvalidValue;
     }
-    // 32-row LUT tiles run only where lut_single_pass allows (4, 6 or 8 pieces)
-    if constexpr (xpl_used(KIND_MFMA_LUT, MT, XPL) && (MT == 1 || XPL == 4 || XPL == 6 || XPL == 8)) {
+    // 32-row LUT tiles run only where lut_single_pass allows (4, 5, 6 or 8 pieces)
+    if constexpr (xpl_used(KIND_MFMA_LUT, MT, XPL) && (MT == 1 || (XPL >= 4 && XPL <= 6) || XPL == 8)) {
         if (kind == KIND_MFMA_LUT3D) return launch_one<MfmaLut<NT, MT, true>, kDepthMfmaLut, XPL, true>(a, split, s);
         return launch_one<MfmaLut<NT, MT, false>, kDepthMfmaLut, XPL, true>(a, split, s);
     }
@@ -1029,6 +1029,7 @@ static hipError_t launch_nt(int kind, const GemmArgs& a, int split, hipStream_t 
     case 16: return launch_mfma<NT, MT, 16>(kind, a, split, s);
     case 8: return launch_mfma<NT, MT, 8>(kind, a, split, s);
     case 6: return launch_mfma<NT, MT, 6>(kind, a, split, s);
+    case 5: return launch_mfma<NT, MT, 5>(kind, a, split, s);
     case 4: return launch_mfma<NT, MT, 4>(kind, a, split, s);
     case 3: return launch_mfma<NT, MT, 3>(kind, a, split, s);
     case 2: return launch_mfma<NT, MT, 2>(kind, a, split, s);
