@@ -89,11 +89,11 @@ typedef enum { WQ_FMT_FP8_BLOCK = 0, WQ_FMT_LUT3 = 1, WQ_FMT_LUT3_DENSE = 2 } wq
  * (one mainloop across the decode band, as in the FLUTE PR's "Results").
  * M = 17..32 runs the MFMA tile on the two contiguous row halves 0..15 and
  * 16..M-1 ("ARM ORDER"): in one pass, each dequantised weight operand feeding
- * both halves, when the plan has one tile per wave (every built-in FP8 plan;
- * for the LUT formats also only where the plan's 32-row activation chunks fit
- * in LDS and its launch bound, e.g. the dense 28672x8192 plan but not the
- * nibble one), and as two passes otherwise.  Either way each row gets the
- * arithmetic of a 16-row call. */
+ * both halves, when the plan has one tile per wave (every built-in plan; for
+ * the LUT formats also only where the plan's 32-row activation chunks fit in
+ * LDS and its launch bound, which the built-in LUT plans do), and as two
+ * passes otherwise.  Either way each row gets the arithmetic of a 16-row
+ * call. */
 typedef enum { WQ_PATH_AUTO = 0, WQ_PATH_GEMV = 1, WQ_PATH_MFMA = 2 } wq_path;
 
 /* Human-readable name of a status code (static storage, never NULL). */
