@@ -56,49 +56,65 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v)
     return sign | code;
 }
 
-// One lane per 8 consecutive k of one (row, K group); the 16 lanes of a group
-// are adjacent in the wave and find the group's amax with a butterfly.
+// One wave per activation unit (16 rows x one 128-K block), laid out by its
+// output: lane l writes the two 16-byte pieces it owns in the unit -- piece l
+// of each 1 KiB chunk j, i.e. the codes of row r = l%16 at k = 32(2j + h) +
+// 8g + e (g = l/16, h = 0, 1, e = 0..7) -- so each store instruction writes a
+// whole 1 KiB chunk.  The lane reads those 32 activations with four 16-byte
+// loads (the four 8-wide runs k = 8g + 32q, q = 0..3, of its row); the four
+// lanes of a row (l = r, r+16, r+32, r+48) hold its whole K group and find
+// the group's amax with two exchanges.  Per value the arithmetic is that of
+// the quantiser rule above: s = amax / 448, code = e4m3_rne(clamp(x / s)).
 __global__ void __launch_bounds__(256) quantize_x_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                          int Mpad, int KB, uint8_t* __restrict__ xq)
 {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t grp = idx >> 4;
-    const int j = (int)(idx & 15);
-    if (grp >= (int64_t)Mpad * KB) return;       // whole groups of 16 exit together
-    const int m = (int)(grp / KB), kb = (int)(grp - (int64_t)m * KB);
-    float v[8];
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (row tile, kb), kb fastest
+    if (unit >= (int64_t)(Mpad >> 4) * KB) return;                       // whole waves exit together
+    const int lane = threadIdx.x & 63;
+    const int mt = (int)(unit / KB), kb = (int)(unit - (int64_t)mt * KB);
+    const int r = lane & 15, g = lane >> 4;
+    const int m = 16 * mt + r;
+    float v[4][8];                      // run q: k = 128kb + 32q + 8g + e
     float amax = 0.f;
     if (m < M) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(x + (int64_t)m * ldx + kb * 128 + 8 * j);
-        const uint32_t d[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint16_t* row = x + (int64_t)m * ldx + kb * 128 + 8 * g;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(d[i] << 16);
-            v[2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
+        for (int q = 0; q < 4; ++q) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(row + 32 * q);
+            const uint32_t d[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[q][2 * i] = __uint_as_float(d[i] << 16);
+                v[q][2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[q][e]));
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    }
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+            for (int e = 0; e < 8; ++e) v[q][e] = 0.f;
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
     const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-    uint32_t lo = 0, hi = 0;
+    uint32_t c[4][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float q = fminf(fmaxf(v[i] / s, -448.0f), 448.0f);
-        const uint32_t c = m < M ? e4m3_rne(q) : 0u;
-        if (i < 4) lo |= c << (8 * i);
-        else hi |= c << (8 * (i - 4));
+    for (int q = 0; q < 4; ++q) {
+        c[q][0] = c[q][1] = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float qv = fminf(fmaxf(v[q][e] / s, -448.0f), 448.0f);
+            const uint32_t code = m < M ? e4m3_rne(qv) : 0u;
+            c[q][e >> 2] |= code << (8 * (e & 3));
+        }
     }
-    // k = 128kb + 8j + e sits in MFMA step js = j/4, lane group g = j%4: chunk
-    // js/2, lane 16g + m%16, byte 8(js%2) + e
-    const int js = j >> 2, g = j & 3;
-    uint8_t* unit = xq + ((int64_t)(m >> 4) * KB + kb) * 2048;
-    *reinterpret_cast<uint2*>(unit + (js >> 1) * 1024 + (16 * g + (m & 15)) * 16 + 8 * (js & 1)) = make_uint2(lo, hi);
-    if (j == 0) {
+    // chunk j holds runs q = 2j (bytes 0..7) and q = 2j + 1 (bytes 8..15)
+    uint8_t* u = xq + unit * 2048 + lane * 16;
+    *reinterpret_cast<uint4*>(u) = make_uint4(c[0][0], c[0][1], c[1][0], c[1][1]);
+    *reinterpret_cast<uint4*>(u + 1024) = make_uint4(c[2][0], c[2][1], c[3][0], c[3][1]);
+    if (g == 0) {
         float* sx = reinterpret_cast<float*>(xq + (int64_t)Mpad * KB * 128);
         sx[(int64_t)kb * Mpad + m] = m < M ? s : 0.f;
     }
@@ -382,8 +398,9 @@ static unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
 hipError_t launch_quantize_x(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* xq, hipStream_t stream)
 {
     const int Mpad = (M + 15) & ~15, KB = K / 128;
-    hipLaunchKernelGGL(quantize_x_kernel, dim3(blocks_of((int64_t)Mpad * KB * 16)), dim3(256), 0, stream, x, ldx, M,
-                       Mpad, KB, xq);
+    const int64_t units = (int64_t)(Mpad / 16) * KB;
+    hipLaunchKernelGGL(quantize_x_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, x, ldx, M, Mpad,
+                       KB, xq);
     return hipGetLastError();
 }
 
