@@ -42,6 +42,7 @@ SEEDS = {
     "tiny": 1000, "gate_up": 1001, "down": 1002, "lut3": 1003,
     "attn_q": 1004, "attn_k": 1005, "attn_v": 1006, "attn_o": 1007,
     "lut3d": 1003,     # the "lut3" matrix and activations, stored densely (3 bits a code)
+    "attn_qkv": 1008,  # the Q, K and V projections stacked into one 8192-row matrix
 }
 
 # name -> (format, N, K, M sweep); format "lut3d" is the LUT format with the
@@ -56,6 +57,7 @@ CONFIGS = {
     "attn_v":  ("fp8", 1024, 5120, (16,)),
     "attn_o":  ("fp8", 5120, 6144, (16,)),
     "lut3d":   ("lut3d", 28672, 8192, (1, 2, 4, 8, 16)),
+    "attn_qkv": ("fp8", 8192, 5120, (16,)),
 }
 
 _BLOCK = 128

@@ -144,6 +144,7 @@ constexpr TableEntry kTable[] = {
     {wq::KIND_MFMA_FP8, 5120, 17408, 1, 2, 6, 1},    // FFN down
     {wq::KIND_MFMA_FP8, 6144, 5120, 1, 2, 6, 1},     // attention Q
     {wq::KIND_MFMA_FP8, 1024, 5120, 1, 1, 4, 1},     // attention K, V
+    {wq::KIND_MFMA_FP8, 8192, 5120, 1, 2, 6, 1},     // attention Q, K and V stacked in one matrix
     {wq::KIND_MFMA_FP8, 5120, 6144, 1, 2, 6, 1},     // attention output
     {wq::KIND_MFMA_LUT, 28672, 8192, 1, 7, 14, 1},   // 3-bit LUT 28672x8192 (two K groups)
     {wq::KIND_MFMA_LUT3D, 28672, 8192, 1, 8, 16, 1}, // 3-bit LUT 28672x8192, dense codes (two K groups)
