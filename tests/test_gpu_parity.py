@@ -143,6 +143,23 @@ def test_gemm_lut3_parity(N, K, M, dense):
     assert r.rel_rms < 4e-3, r
 
 
+@pytest.mark.parametrize("K", [128, 640, 1664])
+@pytest.mark.parametrize("dense", [False, True], ids=["nibble", "dense"])
+def test_lut3_partial_quads(K, dense):
+    """K blocks not a multiple of 4 (one block; a quad plus one; 13 blocks over
+    two K groups): the lanes whose block of the last quad lies past K load
+    zeros, every M from 1 to 32 passes the oracle."""
+    N = 112
+    U.note("lut3 partial quads K=%d dense=%d" % (K, dense))
+    c, q, g = synth.lut3_weights(N, K, 930 + K)
+    packed = U.pack_lut3(c, q, g, dense=dense)
+    for M in (1, 3, 16, 17, 32):
+        xh = synth.x_f16(M, K, 931 + M)
+        y, _ = U.run_lut3(packed, N, K, xh, dense=dense)
+        r = U.grade_lut3(y, xh, c, q, g, K)
+        assert r.ok, "K=%d M=%d: %s" % (K, M, r)
+
+
 @pytest.mark.parametrize("N,K", [(48, 256), (528, 2048), (1024, 1152)])
 def test_dense_lut3_gives_the_nibble_bits(N, K):
     """The two storage layouts feed the same decode and the same arithmetic, so
