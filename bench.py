@@ -64,6 +64,42 @@ def kernel_src_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def sysfs_gpu_state(node: str) -> dict:
+    """Current shader clock level (the DPM table line marked '*') and hwmon
+    temperatures and clocks of the PCI device node `node`; {} where absent."""
+    import glob
+    st = {}
+    try:
+        if os.path.exists(node + "/pp_dpm_sclk"):
+            with open(node + "/pp_dpm_sclk") as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        st["sclk_level"] = line.split(":", 1)[1].strip(" *\n")
+        for path in sorted(glob.glob(node + "/hwmon/hwmon*/temp*_input") + glob.glob(node + "/hwmon/hwmon*/freq*_input")):
+            label = path[:-len("_input")] + "_label"
+            name = open(label).read().strip() if os.path.exists(label) else os.path.basename(path)[:-len("_input")]
+            v = int(open(path).read())
+            if os.path.basename(path).startswith("temp"):
+                st["temp_%s_C" % name] = v / 1000.0          # millidegrees
+            else:
+                st["%s_MHz" % name] = round(v / 1e6)          # Hz
+    except (OSError, ValueError):
+        pass
+    return st
+
+
+def gpu_state() -> dict:
+    """sysfs_gpu_state of cuda:0 (found by its PCI address).  Reads files only:
+    no tool is started."""
+    try:
+        import torch
+        pr = torch.cuda.get_device_properties(0)
+    except Exception:
+        return {}
+    return sysfs_gpu_state("/sys/bus/pci/devices/%04x:%02x:%02x.0" % (pr.pci_domain_id, pr.pci_bus_id,
+                                                                      pr.pci_device_id))
+
+
 def load_traffic(workload_key: str):
     """HBM traffic per launch measured with rocprofv3 PMC counters for this kernel
     source (profiles/traffic.json); None when absent or the kernel changed."""
@@ -347,7 +383,9 @@ def main(argv=None) -> int:
         return 0
     print("bench: preparing %s M=%d" % (args.config, args.M), file=sys.stderr, flush=True)
     w = Workload(args.config, args.M)
+    state_before = gpu_state()
     r = time_workload(w, args.steps, args.warmup, use_graph=not args.eager)
+    state_after = gpu_state()
     value = w.wbytes / (r["ms_per_step"] * 1e-3) / 1e9
     achieved = w.abytes / (r["launch_ms_mean"] * 1e-3) / 1e9
     key = "%s_M%d" % (args.config, args.M)
@@ -377,7 +415,8 @@ def main(argv=None) -> int:
         "timing": {"us_per_step": round(r["ms_per_step"] * 1e3, 3),
                    "host_us_per_step": round(r["host_ms_per_step"] * 1e3, 3),
                    "hip_graph": r["graph"],
-                   "method": "HIP events around %d back-to-back steps on the library's stream" % args.steps},
+                   "method": "HIP events around %d back-to-back steps on the library's stream" % args.steps,
+                   "gpu_before": state_before, "gpu_after": state_after},
     }
     del w
     torch.cuda.empty_cache()
@@ -400,6 +439,10 @@ def main(argv=None) -> int:
                     "us_per_launch": round(rk["launch_ms_mean"] * 1e3, 2),
                     "stream_GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                     "passes": wk.launches_per_step(), "k_parts": wk.k_parts}
+                if fmt in ("lut3", "lut3d"):
+                    # 3 bits of information per code, plus the group scales and the map
+                    info = N * K * 3 // 8 + 2 * N * (K // 128) + 16
+                    extra["%s_M%d" % (name, M)]["info_GBps"] = round(info / (rk["ms_per_step"] * 1e-3) / 1e9, 1)
                 del wk
                 torch.cuda.empty_cache()
         for name in ("gate_up", "down"):
