@@ -43,6 +43,10 @@
  *     the default stream).  Results are valid once the stream reaches them.
  *   - Calls are thread-safe.  Calls that share a workspace must be ordered
  *     (same stream, or synchronised): concurrent calls on one workspace race.
+ *   - Size limits (the kernels address with 32-bit buffer offsets): N and K at
+ *     most 2^24 and N*K at most 2^35, else WQ_ERR_SHAPE (size queries return
+ *     0); for the decode GEMMs a call's activation span, ((min(M, 32) - 1) *
+ *     ldx + K) * 2 bytes, under 4 GiB, else WQ_ERR_LD.
  *
  * Environment options, read once at the first call that needs them (for
  * sweeps without a rebuild; the defaults are the per-shape plan):

@@ -103,6 +103,23 @@ def test_fp8_gemm_validation(args, expect):
     assert L.wq_gemm_fp8_block(*args, None) == expect
 
 
+def test_size_limits():
+    # N, K at most 2^24 and N*K at most 2^35: the kernels' 32-bit buffer offsets
+    assert wq.wq_fp8_block_packed_bytes(1 << 24, 128) > 0
+    assert wq.wq_fp8_block_packed_bytes((1 << 24) + 128, 128) == 0
+    assert wq.wq_fp8_block_packed_bytes(128, (1 << 24) + 128) == 0
+    assert wq.wq_fp8_block_packed_bytes(1 << 24, 1 << 11) > 0          # 2^35 codes
+    assert wq.wq_fp8_block_packed_bytes(1 << 24, (1 << 11) + 128) == 0
+    assert wq.wq_lut3_packed_bytes(1 << 24, (1 << 11) + 128) == 0
+    assert L.wq_gemm_fp8_block(P, (1 << 24) + 128, 512, P, 512, P, 1 << 25, 1, P, BIG, None) == 2
+    assert L.wq_gemm_lut3(P, 1 << 24, 1 << 12, P, 1 << 12, P, 1 << 24, 1, P, BIG, None) == 2
+    # activation span ((min(M, 32) - 1) * ldx + K) * 2 bytes under 4 GiB
+    ld = 1 << 27
+    assert L.wq_gemm_fp8_block(P, 256, 512, P, ld, P, 256, 32, P, BIG, None) == 3   # 31 * 2^28 + 1 KiB
+    assert L.wq_gemm_lut3(P, 48, 512, P, ld, P, 48, 17, P, BIG, None) == 3      # 16 * 2^28 + 1 KiB
+    assert L.wq_gemm_fp8_block(P, 256, 512, P, 1 << 60, P, 256, 1, P, BIG, None) == 3
+
+
 def test_m_zero_is_a_no_op():
     # M == 0 queues nothing and returns WQ_OK before looking at the pointers
     assert L.wq_gemm_fp8_block(None, 256, 512, None, 512, None, 256, 0, None, 0, None) == 0
@@ -198,3 +215,11 @@ def test_valid_call_without_device_reports_hip_error():
     assert L.wq_gemm_fp8_w8a8(P, 256, 512, P, 4, P, 256, None, 0, None) == 7
     assert L.wq_quantize_x_fp8(P, 512, 4, 512, P, None) == 7
     assert L.wq_pack_fp8_block(P, 512, P, 256, 512, P, None) == 7
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-device path")
+def test_large_stride_within_limits_passes_validation():
+    # 31 rows of 2^26 BF16 elements + 1 KiB: just under 4 GiB; one row of any
+    # stride.  The calls get past validation and fail only for want of a device
+    assert L.wq_gemm_fp8_block(P, 256, 512, P, 1 << 26, P, 256, 32, P, BIG, None) == 7
+    assert L.wq_gemm_fp8_block(P, 256, 512, P, 1 << 30, P, 256, 1, P, BIG, None) == 7

@@ -264,10 +264,17 @@ Plan cached_plan(int kind, int64_t N, int64_t K, int cu, bool ws)
     return p;
 }
 
+// Size limits keep every offset the kernels form within its width: a wave's
+// run of tiles (at most 2 x 2^17 K blocks x 2 KiB) within a 32-bit buffer
+// range, and the pack/unpack launches (one work-item per 16 or 32 codes)
+// under 2^32 work-items.
+constexpr int64_t kMaxDim = (int64_t)1 << 24;
+constexpr int64_t kMaxCodes = (int64_t)1 << 35;
+
 bool shape_ok(int fmt, int64_t N, int64_t K)
 {
     if (N <= 0 || K <= 0 || K % 128) return false;
-    if (N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return false;
+    if (N > kMaxDim || K > kMaxDim || N * K > kMaxCodes) return false;
     if (fmt == WQ_FMT_FP8_BLOCK) return N % 128 == 0;
     if (fmt == WQ_FMT_LUT3 || fmt == WQ_FMT_LUT3_DENSE) return N % 16 == 0;
     return false;
@@ -297,6 +304,8 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
     if (M == 0) return WQ_OK;
     if (!packed || !x || !y) return WQ_ERR_NULL;
     if (ldx < K || ldy < N) return WQ_ERR_LD;
+    // the kernels address one launch's activations (up to 32 rows) with 32-bit byte offsets
+    if (ldx > kMaxCodes || ((std::min<int64_t>(M, 32) - 1) * ldx + K) * 2 >= ((int64_t)1 << 32)) return WQ_ERR_LD;
     if (!aligned16(packed) || !aligned16(x) || ldx % 8) return WQ_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(y) & 1) return WQ_ERR_ALIGN;
 
