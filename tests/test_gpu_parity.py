@@ -10,7 +10,9 @@
   M=1 calls, MFMA rows = the M=16 call, determinism over repeats, strides and
   canaries, workspace left zeroed, pack determinism;
 * the dense 3-bit LUT layout passes every LUT test and gives the nibble
-  layout's GEMM bits exactly.
+  layout's GEMM bits exactly;
+* special values: NaN weight codes and infinite or NaN activations give NaN
+  and infinities exactly where the oracle's sum has them.
 """
 import numpy as np
 import pytest
@@ -333,6 +335,72 @@ def test_nan_codes_poison_exactly_their_columns():
             assert np.all(np.isnan(y64[:, expect])) and np.all(np.isfinite(y64[:, ok]))
             g = U.compare.grade(y, y64, U.floor_fp8(xbits, codes, scales, K), "bf16")
             assert g.ok, (path, M, ws, str(g))
+
+
+def _check_nonfinite(yv, y64, ybits, floor, out_dtype, what):
+    """NaN exactly where the oracle's sum is NaN, infinities with the oracle's
+    sign, every finite output graded against the oracle."""
+    assert np.array_equal(np.isnan(yv), np.isnan(y64)), what
+    assert np.array_equal(np.isposinf(yv), np.isposinf(y64)), what
+    assert np.array_equal(np.isneginf(yv), np.isneginf(y64)), what
+    fin = np.isfinite(y64)
+    g = U.compare.grade(ybits[fin], y64[fin], floor, out_dtype)
+    assert g.ok, (what, str(g))
+
+
+def test_nonfinite_activations_follow_ieee():
+    """Infinite and NaN activations (BF16 for FP8 weights, FP16 for the LUT):
+    an infinity times a nonzero weight is an infinity of the product's sign, an
+    infinity times a zero weight (an E4M3 +0/-0 code, a zero group scale) and
+    opposite infinities in one sum are NaN, a NaN activation makes its row NaN,
+    on every path (GEMV, MFMA tile, K parts across work-groups, the 32-row
+    single pass); the oracle decides each output's class."""
+    U.note("non-finite activations")
+    wq = U.wqmod()
+    N, K = 512, 2048
+    codes, scales = synth.fp8_weights(N, K, 61)
+    codes = codes.copy()
+    codes[7, 100] = 0x00          # +0 and -0 weights under the row-0 infinity
+    codes[300, 100] = 0x80
+    specials = {(0, 100): 0x7F80, (1, 700): 0x7FC0, (2, 5): 0x7F80, (2, 1500): 0xFF80, (3, 2047): 0xFF80}
+    packed = U.pack_fp8(codes, scales)
+    for path, M in ((GEMV, 1), (GEMV, 4), (MFMA, 5), (MFMA, 16), (MFMA, 32)):
+        xbits = synth.x_bf16(M, K, 62).copy()
+        fin_x = xbits.copy()
+        for (m, k), b in specials.items():
+            if m < M:
+                xbits[m, k] = b
+                fin_x[m, k] = 0
+        y64 = oracle.gemm_fp8(xbits, codes, scales, K=K)
+        assert np.isnan(y64[0, [7, 300]]).all() and np.isinf(y64[0, 0])
+        floor = U.floor_fp8(fin_x, codes, scales, K)
+        for ws in (None, "auto"):
+            wq.wq_set_kparts(4 if ws else 0)
+            try:
+                y, _ = U.run_fp8(packed, N, K, xbits, path=path, ws=ws)
+            finally:
+                wq.wq_set_kparts(0)
+            _check_nonfinite(oracle.bf16_value(y), y64, y, floor, "bf16", ("fp8", path, M, ws))
+
+    N, K = 528, 1152
+    codes, qmap, g = synth.lut3_weights(N, K, 63)
+    g = g.copy()
+    g[9, 0] = 0                   # a zero group scale under the row-0 infinity
+    lut_specials = {(0, 100): 0x7C00, (1, 700): 0x7E00, (2, 5): 0x7C00, (2, 1000): 0xFC00, (3, 1151): 0xFC00}
+    for dense in (False, True):
+        packed = U.pack_lut3(codes, qmap, g, dense=dense)
+        for M in (1, 4, 16, 17, 32):
+            xbits = synth.x_f16(M, K, 64).copy()
+            fin_x = xbits.copy()
+            for (m, k), b in lut_specials.items():
+                if m < M:
+                    xbits[m, k] = b
+                    fin_x[m, k] = 0
+            y64 = oracle.gemm_lut3(xbits, codes, qmap, g, K=K)
+            assert np.isnan(y64[0, 9]) and np.isinf(y64[0, 0])
+            floor = U.floor_lut3(fin_x, codes, qmap, g, K)
+            y, _ = U.run_lut3(packed, N, K, xbits, dense=dense)
+            _check_nonfinite(oracle.f16_value(y), y64, y, floor, "f16", ("lut3", dense, M))
 
 
 # ------------------------------------------------------ every kernel variant
