@@ -36,6 +36,7 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 ROTATE_TARGET_BYTES = 1 << 30
 WARM_SECONDS = 0.2
+SPREAD_WINDOWS = 9
 
 
 def weight_bytes(fmt: str, N: int, K: int) -> int:
@@ -235,11 +236,25 @@ def time_workload(w: Workload, steps: int, warmup: int, use_graph: bool = True):
     torch.cuda.synchronize()
     host_s = time.perf_counter() - h0
     total_ms = t0.elapsed_time(t1)
+    # Spread: SPREAD_WINDOWS more windows of the same steps after the timed
+    # one (reported beside it; the value is the timed window alone).
+    windows = [total_ms / steps]
+    if graph is not None:
+        for _ in range(SPREAD_WINDOWS):
+            t0.record(stream)
+            graph.replay()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            windows.append(t0.elapsed_time(t1) / steps)
+    q = sorted(windows)
+    pick = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))]
     return {
         "ms_per_step": total_ms / steps,
         "host_ms_per_step": host_s * 1e3 / steps,
         "launch_ms_mean": total_ms / steps / w.launches_per_step(),
         "graph": graph is not None,
+        "windows_us": {"n": len(q), "p10": round(pick(0.1) * 1e3, 3), "median": round(pick(0.5) * 1e3, 3),
+                       "p90": round(pick(0.9) * 1e3, 3)},
     }
 
 
@@ -416,6 +431,7 @@ def main(argv=None) -> int:
                    "host_us_per_step": round(r["host_ms_per_step"] * 1e3, 3),
                    "hip_graph": r["graph"],
                    "method": "HIP events around %d back-to-back steps on the library's stream" % args.steps,
+                   "windows_us_per_step": r["windows_us"],
                    "gpu_before": state_before, "gpu_after": state_after},
     }
     del w
