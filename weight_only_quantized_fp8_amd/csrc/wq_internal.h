@@ -9,11 +9,14 @@
 namespace wq {
 
 // Prefetch depth: weight units in flight per wave beyond the one being
-// computed (the register ring has depth + 1 slots).  Depths 3 to 7 measured
-// within noise of each other for both formats; 3 keeps the most registers
-// free.
+// computed (the register ring has depth + 1 slots).  FP8 and the GEMV: depths
+// 3 to 7 within noise of each other, 3 keeps the most registers free.  LUT
+// tile with the quad schedule, 28672 x 8192 (medians of 15 interleaved
+// windows): nibbles 5 units 0.4-0.55 us faster than 3 at M = 1, 8 and 16 (7
+// slower); dense codes 5 units 0.3 us slower than 3 at M = 16.
 constexpr int kDepthMfmaFp8 = 3;
-constexpr int kDepthMfmaLut = 3;
+constexpr int kDepthMfmaLut = 5;       // nibble layout
+constexpr int kDepthMfmaLut3D = 3;     // dense 3-bit layout
 constexpr int kDepthGemv = 3;
 
 enum Kind : int {
