@@ -9,15 +9,16 @@
 namespace wq {
 
 // Prefetch depth: weight units in flight per wave beyond the one being
-// computed (the register ring has depth + 1 slots).  FP8 and the GEMV: depths
-// 3 to 7 within noise of each other, 3 keeps the most registers free.  LUT
-// tile with the quad schedule, 28672 x 8192 (medians of 15 interleaved
-// windows): nibbles 5 units 0.4-0.55 us faster than 3 at M = 1, 8 and 16 (7
-// slower); dense codes 5 units 0.3 us slower than 3 at M = 16.
+// computed (the register ring has depth + 1 slots).  FP8 tile and GEMV: 3
+// (5 gains 0.07 us on gate/up and loses 0.24 us on attention Q; 3 to 7 were
+// within noise before).  LUT tile with the quad schedule, 28672 x 8192, M = 16
+// (medians of 15 interleaved windows of 200 graph-replayed calls): one-tile
+// waves at 4 units, nibbles 24.0 us against 24.5 at 5, 25.0 at 6 and ~24.9
+// at 3, dense codes 23.2 us against 23.5 at 3 and 24.5 at 2; two-tile waves
+// keep 3 (at 4 their 16-piece kernel spills).
 constexpr int kDepthMfmaFp8 = 3;
-constexpr int kDepthMfmaLut = 5;       // nibble layout
-constexpr int kDepthMfmaLut3D = 3;     // dense 3-bit layout
 constexpr int kDepthGemv = 3;
+constexpr int lut_depth(int nt) { return nt == 1 ? 4 : 3; }
 
 enum Kind : int {
     KIND_MFMA_FP8 = 0,   // 16-row BF16 MFMA tile, FP8 block-scaled weights

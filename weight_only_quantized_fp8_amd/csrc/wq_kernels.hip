@@ -1016,8 +1016,8 @@ static hipError_t launch_mfma(int kind, const GemmArgs& a, int split, hipStream_
     }
     // 32-row LUT tiles run only where lut_single_pass allows (4, 5, 6 or 8 pieces)
     if constexpr (xpl_used(KIND_MFMA_LUT, MT, XPL) && (MT == 1 || (XPL >= 4 && XPL <= 6) || XPL == 8)) {
-        if (kind == KIND_MFMA_LUT3D) return launch_one<MfmaLut<NT, MT, true>, kDepthMfmaLut3D, XPL, true>(a, split, s);
-        return launch_one<MfmaLut<NT, MT, false>, kDepthMfmaLut, XPL, true>(a, split, s);
+        if (kind == KIND_MFMA_LUT3D) return launch_one<MfmaLut<NT, MT, true>, lut_depth(NT), XPL, true>(a, split, s);
+        return launch_one<MfmaLut<NT, MT, false>, lut_depth(NT), XPL, true>(a, split, s);
     }
     return hipErrorInvalidValue;
 }
