@@ -9,14 +9,17 @@
 namespace wq {
 
 // Prefetch depth: weight units in flight per wave beyond the one being
-// computed (the register ring has depth + 1 slots).  FP8 tile and GEMV: 3
-// (5 gains 0.07 us on gate/up and loses 0.24 us on attention Q; 3 to 7 were
-// within noise before).  LUT tile with the quad schedule, 28672 x 8192, M = 16
+// computed (the register ring has depth + 1 slots).  FP8 16-row tile: 4 where
+// each wave streams its K range alone (one K group per work-group: gate/up
+// 17.45 -> 17.24 us, FFN down in 4 parts 19.61 -> 19.56), 3 where K groups
+// split it (attention output 9.84 us at 3, 10.01 at 4, 10.20 at 5).  GEMV
+// and 32-row tiles: 3.  LUT tile with the quad schedule, 28672 x 8192, M = 16
 // (medians of 15 interleaved windows of 200 graph-replayed calls): one-tile
 // waves at 4 units, nibbles 24.0 us against 24.5 at 5, 25.0 at 6 and ~24.9
 // at 3, dense codes 23.2 us against 23.5 at 3 and 24.5 at 2; two-tile waves
 // keep 3 (at 4 their 16-piece kernel spills).
 constexpr int kDepthMfmaFp8 = 3;
+constexpr int kDepthMfmaFp8Solo = 4;   // one K group per work-group
 constexpr int kDepthGemv = 3;
 constexpr int lut_depth(int nt) { return nt == 1 ? 4 : 3; }
 

@@ -1010,8 +1010,12 @@ template <int NT, int MT, int XPL>
 static hipError_t launch_mfma(int kind, const GemmArgs& a, int split, hipStream_t s)
 {
     if (kind == KIND_MFMA_FP8) {
-        if constexpr (xpl_used(KIND_MFMA_FP8, MT, XPL))
+        if constexpr (xpl_used(KIND_MFMA_FP8, MT, XPL)) {
+            if constexpr (MT == 1)
+                if (split == a.sn)   // one K group: each wave streams its whole K part alone
+                    return launch_one<MfmaFp8<NT, MT>, kDepthMfmaFp8Solo, XPL, false>(a, split, s);
             return launch_one<MfmaFp8<NT, MT>, kDepthMfmaFp8, XPL, false>(a, split, s);
+        }
         return hipErrorInvalidValue;
     }
     // 32-row LUT tiles run only where lut_single_pass allows (4, 5, 6 or 8 pieces)
