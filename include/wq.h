@@ -100,11 +100,20 @@ typedef enum { WQ_FMT_FP8_BLOCK = 0, WQ_FMT_LUT3 = 1, WQ_FMT_LUT3_DENSE = 2 } wq
  * call. */
 typedef enum { WQ_PATH_AUTO = 0, WQ_PATH_GEMV = 1, WQ_PATH_MFMA = 2 } wq_path;
 
-/* Human-readable name of a status code (static storage, never NULL). */
+/* Human-readable name of a status code (static storage, never NULL).
+ * Source: arc PR "fix(ArcKernels): FP8 bank conflict + the dispatch
+ * threshold's provenance", section "The threshold" (the eligibility of a
+ * weight matrix for the block-scaled arm, which these codes report when a
+ * call is refused); the pages give no error convention, the codes are this
+ * library's reading. */
 const char* wq_status_str(wq_status s);
 
 /* Version of the packed layouts written by wq_pack_*; a packed buffer is a
- * deterministic, byte-for-byte function of the pack inputs and this number. */
+ * deterministic, byte-for-byte function of the pack inputs and this number.
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Core contributions" item 2 (weights packed once, offline, in the order
+ * the kernel loads them: the layout is a contract between packer and
+ * kernel). */
 int wq_packed_format_version(void);
 
 /* Tuning and test hook: override the per-shape plan of later calls.  nt =
@@ -117,7 +126,11 @@ int wq_packed_format_version(void);
  * WQ_NT / WQ_SN / WQ_SPLIT / WQ_WAVES_PER_CU environment values.  The FP8
  * GEMV path always runs one tile per wave (it ignores nt).  Results stay within the documented tolerance
  * for every setting, but bit patterns may differ between settings.  Not meant
- * to be called while GEMMs are being queued from other threads. */
+ * to be called while GEMMs are being queued from other threads.
+ * Source: arc PR "fix(ArcKernels): FP8 bank conflict + the dispatch
+ * threshold's provenance", "The threshold" (every arm selectable on one
+ * binary without a rebuild); atlas docs "Module m16_tc", struct M16TcLevers
+ * (levers resolved once). */
 wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu);
 
 /* Tuning and test hook: the number of K parts (1..32) that later calls which
@@ -125,14 +138,21 @@ wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu);
  * wq_gemm_fp8_w8a8); 0 selects the per-shape choice.  Replaces WQ_KPARTS.
  * Parts are clamped so that each keeps at least one K block (8 for the LUT
  * formats).  wq_gemm_workspace_bytes and wq_w8a8_workspace_bytes follow the
- * setting.  Same thread rule as wq_set_tuning. */
+ * setting.  Same thread rule as wq_set_tuning.
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Core contributions" (striped stream-K adopted from Marlin); atlas docs
+ * "Module m16_tc", "WHY THE FFN ARM LOSES" (low-N grids against the
+ * machine's slots). */
 wq_status wq_set_kparts(int kp);
 
 /* ------------------------------------------------------------ FP8 block */
 
 /* Bytes of the packed FP8 matrix: N*K code bytes + 4*(N/128)*(K/128) scale
  * bytes.  Returns 0 for an unsupported shape (N or K not a positive multiple
- * of 128). */
+ * of 128).
+ * Source: atlas docs "Module m16_tc", WHY (an 89 MB FP8 matrix: one byte a
+ * weight); arc PR "fix(ArcKernels): FP8 bank conflict + the dispatch
+ * threshold's provenance", "The threshold" (block geometry [128, 128]). */
 size_t wq_fp8_block_packed_bytes(int64_t N, int64_t K);
 
 /* Pack an FP8 weight matrix.
@@ -140,7 +160,12 @@ size_t wq_fp8_block_packed_bytes(int64_t N, int64_t K);
  *   scales  device, [N/128][K/128] FP32, row-major, contiguous
  *   packed  device, wq_fp8_block_packed_bytes(N, K) bytes, 16-byte aligned
  * N and K must be positive multiples of 128.  Every byte value is accepted
- * (NaN codes decode to NaN).  Asynchronous on hip_stream. */
+ * (NaN codes decode to NaN).  Asynchronous on hip_stream.
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Core contributions" item 2 (offline pack in matrix-fragment order, one
+ * coalesced 16-byte load per lane); arc PR "fix(ArcKernels): FP8 bank
+ * conflict + the dispatch threshold's provenance", "The threshold" (128 x
+ * 128 scale blocks). */
 wq_status wq_pack_fp8_block(const uint8_t* w_e4m3, int64_t ldw, const float* scales,
                             int64_t N, int64_t K, void* packed, void* hip_stream);
 
@@ -163,7 +188,9 @@ wq_status wq_pack_fp8_block(const uint8_t* w_e4m3, int64_t ldw, const float* sca
  * BF16, or within 1e-3*sqrt(K)*max|x|*max|w| of the exact result.  Results are
  * deterministic, and row r of an M-row call equals row r of any other call on
  * the same path with the same row r of x, bit for bit, when both calls pass a
- * workspace or both pass NULL (the two schedules may round differently). */
+ * workspace or both pass NULL (the two schedules may round differently).
+ * Source: atlas docs "Module m16_tc", WHY, NUMERICS (two-level fold, 2 BF16
+ * ULP) and ARM ORDER (the batch ladder, row halves for M = 17..32). */
 wq_status wq_gemm_fp8_block(const void* packed, int64_t N, int64_t K,
                             const uint16_t* x, int64_t ldx,
                             uint16_t* y, int64_t ldy, int64_t M,
@@ -172,7 +199,10 @@ wq_status wq_gemm_fp8_block(const void* packed, int64_t N, int64_t K,
 /* Same as wq_gemm_fp8_block with an explicit path (WQ_PATH_GEMV serves
  * M <= 4 only; WQ_PATH_MFMA serves M <= 32; AUTO as above).  Used to sweep
  * the GEMV/MFMA crossover (arc PR, section "The threshold": one binary, arms
- * toggled without a rebuild). */
+ * toggled without a rebuild).
+ * Source: arc PR "fix(ArcKernels): FP8 bank conflict + the dispatch
+ * threshold's provenance", "The threshold" (three arms on one binary,
+ * toggled without a rebuild); atlas docs "Module m16_tc", ARM ORDER. */
 wq_status wq_gemm_fp8_block_path(const void* packed, int64_t N, int64_t K,
                                  const uint16_t* x, int64_t ldx,
                                  uint16_t* y, int64_t ldy, int64_t M,
@@ -184,7 +214,9 @@ wq_status wq_gemm_fp8_block_path(const void* packed, int64_t N, int64_t K,
 /* Bytes of the packed LUT matrix: N*K/2 nibble bytes + 16*N*ceil(K/1024)
  * scale bytes (K blocks padded to a multiple of 8) + 32 bytes (map and pack
  * status).  Returns 0 for an unsupported shape (N not a positive multiple of
- * 16 or K not of 128). */
+ * 16 or K not of 128).
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Core contributions" item 2 (one 3-bit code per nibble). */
 size_t wq_lut3_packed_bytes(int64_t N, int64_t K);
 
 /* Pack a 3-bit LUT weight matrix.
@@ -193,7 +225,10 @@ size_t wq_lut3_packed_bytes(int64_t N, int64_t K);
  *   scales  device, FP16 bits [N][K/128], row-major, contiguous
  *   packed  device, wq_lut3_packed_bytes(N, K) bytes, 16-byte aligned
  * This call synchronises hip_stream: it reads back whether any code exceeded
- * 7 and then returns WQ_ERR_CODE (the packed buffer is then not valid). */
+ * 7 and then returns WQ_ERR_CODE (the packed buffer is then not valid).
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Core contributions" items 1 and 2 (learned 8-entry map, group scales,
+ * nibble + fragment-order offline pack). */
 wq_status wq_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* qmap,
                        const uint16_t* scales, int64_t N, int64_t K,
                        void* packed, void* hip_stream);
@@ -202,7 +237,11 @@ wq_status wq_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* qmap,
  *   x  device, [M][ldx] FP16 bits; ldx >= K, ldx % 8 == 0, x 16-byte aligned
  *   y  device, [M][ldy] FP16 bits (RNE); ldy >= N
  * Other arguments, limits and guarantees as wq_gemm_fp8_block (the ULP
- * criterion is applied after rounding the FP16 result to BF16). */
+ * criterion is applied after rounding the FP16 result to BF16).
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Core contributions" item 1 (byte-permute lookup of the learned map) and
+ * "Results" (the dequant rounds to FP16 before the accumulate; one mainloop
+ * for M = 1..16). */
 wq_status wq_gemm_lut3(const void* packed, int64_t N, int64_t K,
                        const uint16_t* x, int64_t ldx,
                        uint16_t* y, int64_t ldy, int64_t M,
@@ -215,13 +254,22 @@ wq_status wq_gemm_lut3(const void* packed, int64_t N, int64_t K,
  * the three calls are those of wq_pack_lut3 / wq_gemm_lut3 / wq_unpack_lut3;
  * a GEMM on a dense matrix returns the same bits as on the nibble-packed
  * matrix of the same inputs (the layouts differ only in how the codes are
- * stored, the arithmetic is the same). */
+ * stored, the arithmetic is the same).
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Why this exists" (FLUTE's own bit-sliced 3-bit storage, which the nibble
+ * pack trades away). */
 size_t wq_lut3_dense_packed_bytes(int64_t N, int64_t K);
 
+/* Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Why this exists" (3-bit storage) and "Core contributions" item 2 (offline
+ * pack). */
 wq_status wq_pack_lut3_dense(const uint8_t* codes, int64_t ldc, const uint16_t* qmap,
                              const uint16_t* scales, int64_t N, int64_t K,
                              void* packed, void* hip_stream);
 
+/* Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Why this exists" and "Core contributions" item 1 (same lookup as the
+ * nibble layout). */
 wq_status wq_gemm_lut3_dense(const void* packed, int64_t N, int64_t K,
                              const uint16_t* x, int64_t ldx,
                              uint16_t* y, int64_t ldy, int64_t M,
@@ -236,23 +284,34 @@ wq_status wq_gemm_lut3_dense(const void* packed, int64_t N, int64_t K,
  * Quantiser reading (the pages give none): one FP32 scale per (row, 128-wide
  * K group), s = amax/448 in binary32 (1 for an all-zero group), code = E4M3
  * nearest-even of clamp(x/s, -448, 448) with x/s in binary32 -- the rule of
- * the weights' block quantiser.  x must be finite. */
+ * the weights' block quantiser.  A group holding an infinity or a NaN gets
+ * a NaN scale and the E4M3 NaN code 0x7F for all its values, so every output
+ * of that row is NaN (the weight-only paths give NaN or an infinity there). */
 
 /* Workspace bytes of a W8A8 GEMM of this M, N, K that splits K across
  * work-groups (kp * M * N * 4 for kp parts, following wq_set_kparts); 0 when
  * it keeps K inside one work-group, for an invalid shape, or with no gfx950
- * device current. */
+ * device current.
+ * Source: atlas docs "Module m16_tc", ARM ORDER rung 6 (W8A8 block-scaled
+ * prefill); FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Core contributions" (stream-K for thin grids). */
 size_t wq_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Bytes of a packed FP8 activation buffer: Mpad*K codes + 4*Mpad*(K/128)
  * scale bytes, Mpad = 16*ceil(M/16).  0 for an unsupported shape (K not a
- * positive multiple of 128, M < 1, or 2 GiB or more). */
+ * positive multiple of 128, M < 1, or 2 GiB or more).
+ * Source: arc PR "fix(ArcKernels): FP8 bank conflict + the dispatch
+ * threshold's provenance", "Worth a separate change" (block-scaled FP8 needs
+ * the activations in FP8: an activation quantiser). */
 size_t wq_x_fp8_packed_bytes(int64_t M, int64_t K);
 
 /* Quantise BF16 activations into the packed FP8 activation layout.
  *   x_bf16  device, [M][ldx] BF16 bits; ldx >= K, ldx % 8 == 0, 16-byte aligned
  *   xq      device, wq_x_fp8_packed_bytes(M, K) bytes, 16-byte aligned
- * M == 0 queues nothing.  Asynchronous on hip_stream. */
+ * M == 0 queues nothing.  Asynchronous on hip_stream.
+ * Source: arc PR "fix(ArcKernels): FP8 bank conflict + the dispatch
+ * threshold's provenance", "Worth a separate change" (an activation
+ * quantiser for the block-scaled FP8 product). */
 wq_status wq_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int64_t K,
                             void* xq, void* hip_stream);
 
@@ -275,7 +334,11 @@ wq_status wq_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int6
  *           them in a fixed order (results stay deterministic for a given M, N, K;
  *           the split, and so the rounding of a row, may differ between Ms).  A
  *           workspace smaller than required returns WQ_ERR_WORKSPACE, a misaligned
- *           one WQ_ERR_ALIGN. */
+ *           one WQ_ERR_ALIGN.
+ * Source: atlas docs "Module m16_tc", ARM ORDER rung 6 (W8A8 block-scaled
+ * prefill) and NUMERICS (the two-level fold); arc PR "fix(ArcKernels): FP8
+ * bank conflict + the dispatch threshold's provenance", "Worth a separate
+ * change". */
 wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void* xq, int64_t M,
                            uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                            void* hip_stream);
@@ -286,31 +349,47 @@ wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void*
  * K-split schedule (the same for every M and path; the FP8 GEMV path never
  * uses it).  0 when the shape's plan keeps K inside one work-group, and for an
  * unsupported shape or when no gfx950 device is current; NULL may then be
- * passed.  Queries the current device (cached). */
+ * passed.  Queries the current device (cached).
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Core contributions" (striped stream-K with a serial reduction of the
+ * partial sums); atlas docs "Module m16_tc", "WHY THE FFN ARM LOSES". */
 size_t wq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* ----------------------------------------------------------- test hooks */
 /* Decode a packed matrix back to canonical row-major [N][K] with the same
  * device dequant code the GEMM runs.  Asynchronous on hip_stream. */
 
-/* out[n][k] = BF16(e4m3(code)) -- unscaled; the MFMA path's converter. */
+/* out[n][k] = BF16(e4m3(code)) -- unscaled; the MFMA path's converter.
+ * Source: atlas docs "Module m16_tc", module oracle (one numerics contract
+ * evaluated against the device and a host model: the device dequant checked
+ * bit for bit). */
 wq_status wq_unpack_fp8_block(const void* packed, int64_t N, int64_t K,
                               uint16_t* w_bf16, void* hip_stream);
 
-/* out[n][k] = FP32(e4m3(code)) -- unscaled; the GEMV path's converter. */
+/* out[n][k] = FP32(e4m3(code)) -- unscaled; the GEMV path's converter.
+ * Source: atlas docs "Module m16_tc", module oracle (as wq_unpack_fp8_block;
+ * the GEMV arm's converter). */
 wq_status wq_unpack_fp8_block_f32(const void* packed, int64_t N, int64_t K,
                                   float* w_f32, void* hip_stream);
 
-/* out[n][k] = fp16_rne(qmap[code] * scale[n][k/128]) */
+/* out[n][k] = fp16_rne(qmap[code] * scale[n][k/128])
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Results" (the dequant rounds to FP16 before the accumulate; exactness-
+ * gated kernels) and atlas docs "Module m16_tc", module oracle. */
 wq_status wq_unpack_lut3(const void* packed, int64_t N, int64_t K,
                          uint16_t* w_f16, void* hip_stream);
 
 /* Packed FP8 activations back to canonical codes [M][K] (E4M3) and scales
- * [M][K/128] (FP32, 4-byte aligned). */
+ * [M][K/128] (FP32, 4-byte aligned).
+ * Source: arc PR "fix(ArcKernels): FP8 bank conflict + the dispatch
+ * threshold's provenance", "Worth a separate change" (the activation
+ * quantiser, checked bit for bit against the host rule). */
 wq_status wq_unpack_x_fp8(const void* xq, int64_t M, int64_t K, uint8_t* codes, float* scales,
                           void* hip_stream);
 
-/* The same for a matrix packed by wq_pack_lut3_dense. */
+/* The same for a matrix packed by wq_pack_lut3_dense.
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * "Why this exists" (3-bit storage) and "Results" (FP16 dequant). */
 wq_status wq_unpack_lut3_dense(const void* packed, int64_t N, int64_t K,
                                uint16_t* w_f16, void* hip_stream);
 

@@ -304,7 +304,12 @@ static uint8_t e4m3_rne_code(float v)
 uint8_t wqo_e4m3_rne(float v) { return e4m3_rne_code(v); }
 
 /* codes [M][K] and scales [M][K/128] of BF16 x [M][ldx]:
- * s = amax/448 (binary32; 1 for an all-zero group), code = e4m3_rne(clamp(x/s)). */
+ * s = amax/448 (binary32; 1 for an all-zero group), code = e4m3_rne(clamp(x/s)).
+ * A group holding an infinity or a NaN has no finite amax; reading taken (the
+ * pages define no quantiser, let alone for non-finite input): its scale is NaN
+ * and every code of the group is the E4M3 NaN 0x7F, so every product that
+ * uses the group is NaN, as an infinite or NaN activation makes the
+ * weight-only paths' sums non-finite. */
 int wqo_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int64_t K,
                        uint8_t* codes, float* scales)
 {
@@ -314,9 +319,16 @@ int wqo_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int64_t K
         for (int64_t kb = 0; kb < kb_n; ++kb) {
             const uint16_t* xr = x_bf16 + m * ldx + kb * WQO_BLOCK;
             float amax = 0.0f;
+            int nonfinite = 0;
             for (int i = 0; i < WQO_BLOCK; ++i) {
                 float a = fabsf((float)wqo_bf16_value(xr[i]));
-                if (a > amax) amax = a;
+                if (!isfinite(a)) nonfinite = 1;
+                else if (a > amax) amax = a;
+            }
+            if (nonfinite) {
+                scales[m * kb_n + kb] = NAN;
+                for (int i = 0; i < WQO_BLOCK; ++i) codes[m * K + kb * WQO_BLOCK + i] = 0x7F;
+                continue;
             }
             float s = amax > 0.0f ? amax / 448.0f : 1.0f;
             scales[m * kb_n + kb] = s;

@@ -8,6 +8,8 @@
  * the FP64 result rounded to BF16, or within 1e-3*sqrt(K)*max|x|*max|w| of it.
  * It also checks a few validation errors that need no device work.
  *
+ * With --selftest it checks only its own acceptance rule, on the CPU.
+ *
  * Exit status 0: every check passed; 1: a check failed; 2: no usable device.
  */
 #include <math.h>
@@ -84,22 +86,56 @@ static uint16_t f16_bits_unit(void)
 
 static int64_t bf16_ord(uint16_t b) { return (b & 0x8000) ? -(int64_t)(b & 0x7FFF) : (int64_t)b; }
 
-/* every output: 2 BF16 ULP of bf16(y64), or within the absolute floor */
+/* the absolute floor of the acceptance rule: 1e-3 * sqrt(K) * max|x| * max|w| */
+static double abs_floor(int64_t K, double xmax, double wmax) { return 1e-3 * sqrt((double)K) * xmax * wmax; }
+
+/* one output: finite, and within 2 BF16 ULP of bf16(y64) or within the floor of y64 */
+static int element_ok(uint16_t gb, int is_f16, double r, double floor_abs)
+{
+    const double g = is_f16 ? wqo_f16_value(gb) : wqo_bf16_value(gb);
+    const uint16_t g16 = is_f16 ? wqo_bf16_rne(g) : gb;
+    const int ulp_ok = llabs(bf16_ord(g16) - bf16_ord(wqo_bf16_rne(r))) <= 2;
+    const int abs_ok = fabs(g - r) <= floor_abs;
+    return isfinite(g) && (ulp_ok || abs_ok);
+}
+
 static void grade(const char* what, const uint16_t* y_bits, int is_f16, const double* y64, int64_t M, int64_t N,
                   int64_t ldy, double floor_abs)
 {
     int64_t bad = 0;
     for (int64_t m = 0; m < M; ++m)
-        for (int64_t n = 0; n < N; ++n) {
-            const uint16_t gb = y_bits[m * ldy + n];
-            const double g = is_f16 ? wqo_f16_value(gb) : wqo_bf16_value(gb);
-            const double r = y64[m * N + n];
-            const uint16_t g16 = is_f16 ? wqo_bf16_rne(g) : gb;
-            const int ulp_ok = llabs(bf16_ord(g16) - bf16_ord(wqo_bf16_rne(r))) <= 2;
-            const int abs_ok = fabs(g - r) <= floor_abs;
-            if (!isfinite(g) || !(ulp_ok || abs_ok)) ++bad;
-        }
+        for (int64_t n = 0; n < N; ++n)
+            if (!element_ok(y_bits[m * ldy + n], is_f16, y64[m * N + n], floor_abs)) ++bad;
     CHECK(bad == 0, "%s: %lld of %lld outputs outside the tolerance", what, (long long)bad, (long long)(M * N));
+}
+
+/* CPU self-test of the rule above (no device): the floor at points where it
+ * is a short decimal, and the element rule on both sides of the floor and of
+ * the 2-ULP budget.  BF16 1.0 = 0x3F80; one ULP there is 2^-7. */
+static int selftest(void)
+{
+    static const double pts[][4] = {  /* K, max|x|, max|w|, floor */
+        {10000, 2.0, 0.5, 0.1}, {1, 1.0, 1.0, 0.001}, {16, 1.0, 1.0, 0.004},
+        {256, 3.0, 0.25, 0.012}, {4, 0.5, 8.0, 0.008}, {1024, 1.0, 1.0, 0.032},
+    };
+    for (size_t i = 0; i < sizeof(pts) / sizeof(pts[0]); ++i) {
+        const double f = abs_floor((int64_t)pts[i][0], pts[i][1], pts[i][2]);
+        CHECK(fabs(f - pts[i][3]) <= 1e-15 * pts[i][3], "floor(%g, %g, %g) = %.17g, want %g", pts[i][0], pts[i][1],
+              pts[i][2], f, pts[i][3]);
+    }
+    CHECK(element_ok(0x3F82, 0, 1.0, 0.0), "2 ULP above 1.0 must pass");
+    CHECK(!element_ok(0x3F83, 0, 1.0, 0.0), "3 ULP above 1.0 must fail with no floor");
+    const double e10 = 10.0 / 128.0;           /* 0x3F8A = 1 + 10 * 2^-7 */
+    CHECK(element_ok(0x3F8A, 0, 1.0, e10 / 0.99), "10 ULP inside the floor must pass");
+    CHECK(element_ok(0x3F8A, 0, 1.0, e10), "10 ULP at the floor must pass");
+    CHECK(!element_ok(0x3F8A, 0, 1.0, e10 / 1.01), "10 ULP outside the floor must fail");
+    CHECK(!element_ok(0x7F80, 0, 1.0, 1e30), "an infinity must fail");
+    CHECK(!element_ok(0x7F80, 0, INFINITY, 1e30), "an infinity must fail where the sum is infinite too");
+    CHECK(element_ok(0x3C00, 1, 1.0, 0.0), "FP16 1.0 must pass");
+    CHECK(element_ok(0x3C08, 1, 1.0, 0.0), "FP16 1 + 8 ULP (1 BF16 ULP) must pass");
+    CHECK(!element_ok(0x3C28, 1, 1.0, 0.0), "FP16 1 + 40 ULP (5 BF16 ULP) must fail");
+    printf("%s: %d failed checks (self-test)\n", failures ? "FAIL" : "OK", failures);
+    return failures ? 1 : 0;
 }
 
 static void test_fp8(void)
@@ -125,7 +161,7 @@ static void test_fp8(void)
     for (int64_t i = 0; i < N * K; ++i)
         if (fabs(w[i]) > wmax) wmax = fabs(w[i]);
     free(w);
-    const double floor_abs = 1e-3 * sqrt((double)K) * xmax * wmax;
+    const double floor_abs = abs_floor(K, xmax, wmax);
 
     uint8_t *d_codes, *d_packed;
     float* d_scales;
@@ -189,7 +225,7 @@ static void test_lut3(int dense)
     for (int64_t i = 0; i < N * K; ++i)
         if (fabs(w[i]) > wmax) wmax = fabs(w[i]);
     free(w);
-    const double floor_abs = 1e-3 * sqrt((double)K) * xmax * wmax;
+    const double floor_abs = abs_floor(K, xmax, wmax);
 
     const size_t pbytes = dense ? wq_lut3_dense_packed_bytes(N, K) : wq_lut3_packed_bytes(N, K);
     uint8_t *d_codes, *d_packed;
@@ -234,8 +270,9 @@ static void test_lut3(int dense)
     hipFree(d_codes), hipFree(d_qmap), hipFree(d_g), hipFree(d_packed), hipFree(d_x), hipFree(d_y);
 }
 
-int main(void)
+int main(int argc, char** argv)
 {
+    if (argc > 1 && !strcmp(argv[1], "--selftest")) return selftest();
     int n = 0;
     if (hipGetDeviceCount(&n) != hipSuccess || n < 1) {
         fprintf(stderr, "no HIP device\n");

@@ -144,6 +144,28 @@ def grade_lut3(ybits, xbits, codes, qmap, scales, K, cols=None, floor=None):
     return compare.grade(yb, y64, floor, "f16")
 
 
+# Beyond the contract: at most this fraction of the outputs may lie beyond 2
+# BF16 ULP (such outputs pass only through the absolute floor).  The floor is
+# wide at large K (2.7% of the output RMS at the FFN gate/up size), so without
+# this bound a fault that shifts outputs by a few per cent -- a wrong block
+# scale, a lost K block -- could still pass element by element.  The atlas
+# m16_tc docs' own M=32 receipt had 5 of 557,056 outputs over the budget, all
+# cancellations.
+OVER_BUDGET_FRAC = 1e-4
+# rel_rms bounds by output type: BF16 rounding alone gives ~1.5e-3, FP16 ~2e-4
+REL_RMS_MAX = {"bf16": 4e-3, "f16": 1e-3}
+
+
+def check(r, what: str = "", out_dtype: str = "bf16") -> None:
+    """Assert a receipt: every output within the contract, at most
+    OVER_BUDGET_FRAC of them beyond 2 ULP, no sign flips, rel_rms bounded."""
+    tag = ("%s: " % what if what else "") + str(r)
+    assert r.ok, tag
+    assert r.n_over_budget <= int(OVER_BUDGET_FRAC * r.n), "over budget: " + tag
+    assert r.sign_flips == 0, tag
+    assert np.isfinite(r.rel_rms) and r.rel_rms < REL_RMS_MAX[out_dtype], "rel_rms: " + tag
+
+
 def sample_cols(N: int, seed: int, n: int = 768) -> np.ndarray:
     """Every column of the first and last 128, plus n random ones in between."""
     rng = np.random.Generator(np.random.PCG64(seed))

@@ -507,6 +507,31 @@ def pin_quantize_x():
     assert np.array_equal(c2, codes) and np.array_equal(s2, sc), "x stride"
 
 
+def pin_quantize_x_nonfinite():
+    """A K group holding +Inf, -Inf or NaN gets scale NaN and the E4M3 NaN
+    code 0x7F everywhere (the reading for non-finite input); the row's other
+    groups and the other rows quantise as without it."""
+    xb, K = _quant_fixture(47)
+    base_c, base_s = oracle.quantize_x_fp8(xb)
+    bad = xb.copy()
+    bad[0, 5] = 0x7F80        # +Inf in row 0, group 0
+    bad[2, 300] = 0xFF80      # -Inf in row 2, group 2
+    bad[4, 511] = 0x7FC1      # NaN in row 4, group 3
+    c, s = oracle.quantize_x_fp8(bad)
+    hit = {(0, 0), (2, 2), (4, 3)}
+    for m in range(xb.shape[0]):
+        for kb in range(K // 128):
+            blk = slice(kb * 128, (kb + 1) * 128)
+            if (m, kb) in hit:
+                assert np.isnan(s[m, kb]) and np.all(c[m, blk] == 0x7F), (m, kb)
+            else:
+                assert s[m, kb] == base_s[m, kb] and np.array_equal(c[m, blk], base_c[m, blk]), (m, kb)
+    # the product: every output of a row with such a group is NaN, the others are finite
+    q = np.full((128, K), 0x38, dtype=np.uint8)       # E4M3 1.0
+    y = oracle.gemm_w8a8(c, s, q, np.ones((1, K // 128), dtype=np.float32))
+    assert np.all(np.isnan(y[[0, 2, 4]])) and np.all(np.isfinite(y[[1, 3]]))
+
+
 def pin_gemm_w8a8_exact():
     rng = np.random.Generator(np.random.PCG64(42))
     M, N, K = 2, 256, 256
@@ -557,5 +582,5 @@ ALL_PINS = [
     pin_f16_rne, pin_bf16_rne, pin_fp8_dequant, pin_lut_dequant, pin_lut_rejects_bad_code,
     pin_gemm_fp8_exact, pin_gemm_lut3_exact, pin_integer_exact, pin_closed_form,
     pin_scale_linearity, pin_strides_rows_cols_threads,
-    pin_e4m3_encode, pin_quantize_x, pin_gemm_w8a8_exact, pin_w8a8_integer_exact,
+    pin_e4m3_encode, pin_quantize_x, pin_quantize_x_nonfinite, pin_gemm_w8a8_exact, pin_w8a8_integer_exact,
 ]

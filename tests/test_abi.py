@@ -28,6 +28,30 @@ def test_header_declares_the_boundary():
         assert required in names
 
 
+PAGES = ("atlas docs", "FLUTE PR", "arc PR", "strata PR")
+
+
+def test_every_declaration_cites_its_source():
+    """Each declared call has its own comment directly above it, and the
+    comment names the passage that defines the operation ("Source:" and a
+    page); a call that exists for callers rather than for a passage says so
+    ("Callers:")."""
+    text = open(HEADER).read()
+    decl = re.compile(r"^(?:const char\*|int|wq_status|size_t)\s+(wq_[a-z0-9_]+)\(", re.M)
+    found = 0
+    for m in decl.finditer(text):
+        found += 1
+        before = text[:m.start()].rstrip()
+        assert before.endswith("*/"), "%s has no comment directly above it" % m.group(1)
+        comment = before[before.rfind("/*"):]
+        if "Callers:" in comment:
+            continue
+        assert "Source:" in comment, "%s: no Source: line" % m.group(1)
+        cite = " ".join(comment[comment.find("Source:"):].split())
+        assert any(p in cite for p in PAGES), "%s: the Source line names no page" % m.group(1)
+    assert found == len(declared_functions())
+
+
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(wq.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(lib, n)]

@@ -61,7 +61,7 @@ def test_fp8_parts_match_oracle(kp, reset):
             xb = synth.x_bf16(M, K, 950 + M)
             y, _ = U.run_fp8(packed, N, K, xb, path=MFMA, ws=ws)
             r = U.grade_fp8(y, xb, codes, scales, K)
-            assert r.ok, "N=%d K=%d M=%d: %s" % (N, K, M, r)
+            U.check(r, "N=%d K=%d M=%d" % (N, K, M))
 
 
 @pytest.mark.parametrize("dense", [False, True], ids=["nibble", "dense"])
@@ -81,7 +81,7 @@ def test_lut3_parts_match_oracle(kp, dense, reset):
             xh = synth.x_f16(M, K, 970 + M)
             y, _ = U.run_lut3(packed, N, K, xh, ws=ws, dense=dense)
             r = U.grade_lut3(y, xh, c, q, g, K)
-            assert r.ok, "N=%d K=%d M=%d: %s" % (N, K, M, r)
+            U.check(r, "N=%d K=%d M=%d" % (N, K, M), "f16")
 
 
 # every kernel variant with K parts: one- and two-tile waves, 1..8 column-waves,
@@ -103,7 +103,7 @@ def test_every_tiling_with_parts(nt, sn, split, reset):
         xb = synth.x_bf16(M, K, 981 + M)
         y, _ = U.run_fp8(packed, N, K, xb, path=MFMA, ws=ws)
         r = U.grade_fp8(y, xb, codes, scales, K)
-        assert r.ok, "fp8 M=%d: %s" % (M, r)
+        U.check(r, "fp8 M=%d" % M)
     N, K = 272, 3072
     c, q, g = synth.lut3_weights(N, K, 982)
     packed = U.pack_lut3(c, q, g)
@@ -112,7 +112,7 @@ def test_every_tiling_with_parts(nt, sn, split, reset):
         xh = synth.x_f16(M, K, 983 + M)
         y, _ = U.run_lut3(packed, N, K, xh, ws=ws)
         r = U.grade_lut3(y, xh, c, q, g, K)
-        assert r.ok, "lut3 M=%d: %s" % (M, r)
+        U.check(r, "lut3 M=%d" % M, "f16")
 
 
 def test_host_rules(reset):
@@ -218,4 +218,4 @@ def test_down_projection_table_plan(M, reset):
     cols = U.sample_cols(N, 17 + M)
     r = U.grade_fp8(y, xb, codes, scales, K, cols=cols)
     U.note("  %s" % r)
-    assert r.ok, str(r)
+    U.check(r)

@@ -124,8 +124,7 @@ def test_gemm_fp8_parity(N, K, M):
     for path in paths:
         y, _ = U.run_fp8(packed, N, K, xbits, path=path)
         r = U.grade_fp8(y, xbits, codes, scales, K)
-        assert r.ok, "path %d: %s" % (path, r)
-        assert r.rel_rms < 4e-3, r
+        U.check(r, "path %d" % path)
 
 
 LUT_SHAPES = [(48, 256), (272, 1024), (1024, 384), (528, 2048)]
@@ -141,8 +140,7 @@ def test_gemm_lut3_parity(N, K, M, dense):
     packed = U.pack_lut3(c, q, g, dense=dense)
     y, _ = U.run_lut3(packed, N, K, xbits, dense=dense)
     r = U.grade_lut3(y, xbits, c, q, g, K)
-    assert r.ok, str(r)
-    assert r.rel_rms < 4e-3, r
+    U.check(r, out_dtype="f16")
 
 
 @pytest.mark.parametrize("K", [128, 640, 1664])
@@ -159,7 +157,7 @@ def test_lut3_partial_quads(K, dense):
         xh = synth.x_f16(M, K, 931 + M)
         y, _ = U.run_lut3(packed, N, K, xh, dense=dense)
         r = U.grade_lut3(y, xh, c, q, g, K)
-        assert r.ok, "K=%d M=%d: %s" % (K, M, r)
+        U.check(r, "K=%d M=%d" % (K, M), "f16")
 
 
 @pytest.mark.parametrize("N,K", [(48, 256), (528, 2048), (1024, 1152)])
@@ -199,6 +197,71 @@ def test_integer_exact_results_are_exact():
     for dense in (False, True):
         yl, _ = U.run_lut3(U.pack_lut3(ci, qmap, g, dense=dense), N, K, xh, dense=dense)
         assert np.array_equal(yl, exact_l), dense
+
+
+@pytest.mark.parametrize("dense", [False, True], ids=["nibble", "dense"])
+def test_lut3_subnormal_weights_are_exact(dense):
+    """Map {-4..3} and every group scale 2^-24 (FP16 bits 0x0001): each
+    dequantised weight q * 2^-24 is an exact FP16 subnormal, and the FP16
+    matrix core must take it unflushed.  With x in {-2..2} every product and
+    every partial sum is an integer times 2^-24 (|sum| < 2^24), exact in FP32
+    in any order, so each output must be fp16_rne(exact) bit for bit; the
+    oracle's binary64 sum is the exact value itself.  K = 1152 ends in a
+    partial quad of K blocks; M = 20 and 32 take the 32-row pass."""
+    N, K = 272, 1152
+    U.note("lut3 subnormal weights dense=%d" % dense)
+    rng = np.random.Generator(np.random.PCG64(1701))
+    ci = rng.integers(0, 8, size=(N, K)).astype(np.uint8)
+    qmap = np.arange(-4, 4).astype(np.float16).view(np.uint16)
+    g = np.full((N, K // 128), 0x0001, dtype=np.uint16)
+    wq = U.wqmod()
+    packed = U.pack_lut3(ci, qmap, g, dense=dense)
+    w = torch.empty((N, K), dtype=torch.float16, device=U.DEV)
+    (wq.wq_unpack_lut3_dense if dense else wq.wq_unpack_lut3)(packed, N, K, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(oracle.f16_value(U.bits_of(w)), (ci.astype(np.int64) - 4) * 2.0 ** -24)
+    for M in (1, 5, 16, 20, 32):
+        xi = rng.integers(-2, 3, size=(M, K))
+        xh = xi.astype(np.float16).view(np.uint16)
+        S = xi @ (ci.astype(np.int64) - 4).T
+        exact = S.astype(np.float64) * 2.0 ** -24
+        y, _ = U.run_lut3(packed, N, K, xh, dense=dense)
+        assert np.array_equal(y, oracle.f16_rne(exact)), M
+        assert np.array_equal(oracle.gemm_lut3(xh, ci, qmap, g), exact), M
+
+
+def test_fp8_subnormal_activations_are_exact():
+    """BF16-subnormal activations x = j * 2^-133 (|j| <= 127) against E4M3
+    weights that are small integers, block scale 2^110: every product and
+    every 128-K block sum is an integer times 2^-133, an FP32 number exactly
+    (FP32 subnormals reach 2^-149), the fold times 2^110 is exact and the
+    output S * 2^-23 (|S| < 2^24) is a BF16 normal.  The matrix core and the
+    GEMV must take the subnormal operands unflushed: every output equals
+    bf16_rne(exact) bit for bit on every path, with and without K parts."""
+    N, K = 256, 1024
+    U.note("fp8 subnormal activations")
+    rng = np.random.Generator(np.random.PCG64(1702))
+    wi = rng.integers(-8, 9, size=(N, K))
+    codes = oracle.e4m3_rne(wi.astype(np.float32))
+    assert np.array_equal(oracle.e4m3_value(codes), wi)
+    scales = np.full((N // 128, K // 128), 2.0 ** 110, dtype=np.float32)
+    packed = U.pack_fp8(codes, scales)
+    wq = U.wqmod()
+    for M in (1, 4, 16, 32):
+        xi = rng.integers(-127, 128, size=(M, K))
+        xbits = (np.abs(xi) | np.where(xi < 0, 0x8000, 0)).astype(np.uint16)
+        assert np.array_equal(oracle.bf16_value(xbits), xi * 2.0 ** -133)
+        exact = (xi @ wi.T).astype(np.float64) * 2.0 ** -23
+        want = oracle.bf16_rne(exact)
+        assert np.array_equal(oracle.gemm_fp8(xbits, codes, scales), exact), M
+        for path in ([GEMV, MFMA] if M <= 4 else [MFMA]):
+            for kp in (0, 3):
+                wq.wq_set_kparts(kp)
+                try:
+                    y, _ = U.run_fp8(packed, N, K, xbits, path=path, ws="auto" if kp else None)
+                finally:
+                    wq.wq_set_kparts(0)
+                assert np.array_equal(y, want), (M, path, kp)
 
 
 def test_invariants_fp8():
@@ -282,15 +345,17 @@ def test_strides_and_canaries():
     canary = np.full((M, ldy), 0x7FAB, dtype=np.uint16)
     for path in (AUTO, MFMA):
         y, full = U.run_fp8(packed, N, K, xs, path=path, ldy=ldy, y_init=canary)
-        assert U.grade_fp8(y, xs, codes, scales, K).ok
+        U.check(U.grade_fp8(y, xs, codes, scales, K), "path %d" % path)
         assert np.all(full[:, N:] == 0x7FAB)
     y4, full4 = U.run_fp8(packed, N, K, xs[:4], path=GEMV, ldy=ldy, y_init=canary[:4])
-    assert U.grade_fp8(y4, xs[:4], codes, scales, K).ok and np.all(full4[:, N:] == 0x7FAB)
+    U.check(U.grade_fp8(y4, xs[:4], codes, scales, K), "gemv")
+    assert np.all(full4[:, N:] == 0x7FAB)
     c, q, g = synth.lut3_weights(N, K, 51)
     xh = synth.x_f16(M, K, 52, ld=K + 8)
     for dense in (False, True):
         yl, fl = U.run_lut3(U.pack_lut3(c, q, g, dense=dense), N, K, xh, ldy=ldy, y_init=canary, dense=dense)
-        assert U.grade_lut3(yl, xh, c, q, g, K).ok and np.all(fl[:, N:] == 0x7FAB), dense
+        U.check(U.grade_lut3(yl, xh, c, q, g, K), "dense=%d" % dense, "f16")
+        assert np.all(fl[:, N:] == 0x7FAB), dense
 
 
 def test_zero_rows_and_zero_matrix():
@@ -334,7 +399,7 @@ def test_nan_codes_poison_exactly_their_columns():
             y64 = oracle.gemm_fp8(xbits, codes, scales, K=K)
             assert np.all(np.isnan(y64[:, expect])) and np.all(np.isfinite(y64[:, ok]))
             g = U.compare.grade(y, y64, U.floor_fp8(xbits, codes, scales, K), "bf16")
-            assert g.ok, (path, M, ws, str(g))
+            U.check(g, "path %d M=%d ws=%s" % (path, M, ws))
 
 
 def _check_nonfinite(yv, y64, ybits, floor, out_dtype, what):
@@ -345,7 +410,7 @@ def _check_nonfinite(yv, y64, ybits, floor, out_dtype, what):
     assert np.array_equal(np.isneginf(yv), np.isneginf(y64)), what
     fin = np.isfinite(y64)
     g = U.compare.grade(ybits[fin], y64[fin], floor, out_dtype)
-    assert g.ok, (what, str(g))
+    U.check(g, str(what), out_dtype)
 
 
 def test_nonfinite_activations_follow_ieee():
@@ -433,12 +498,12 @@ def test_every_tiling_matches_oracle(nt, sn, split, tuning_reset):
             xbits = synth.x_bf16(M, K, 600 + M)
             y, _ = U.run_fp8(packed, N, K, xbits, path=MFMA)
             r = U.grade_fp8(y, xbits, codes, scales, K)
-            assert r.ok, "fp8 N=%d K=%d M=%d: %s" % (N, K, M, r)
+            U.check(r, "fp8 N=%d K=%d M=%d" % (N, K, M))
         for M in (1, 3):   # the GEMV takes the same (sn, split); it always runs one tile per wave
             xbits = synth.x_bf16(M, K, 650 + M)
             y, _ = U.run_fp8(packed, N, K, xbits, path=GEMV)
             r = U.grade_fp8(y, xbits, codes, scales, K)
-            assert r.ok, "fp8 gemv N=%d K=%d M=%d: %s" % (N, K, M, r)
+            U.check(r, "fp8 gemv N=%d K=%d M=%d" % (N, K, M))
     for N, K in ((48, 384), (272, 1152)):
         c, q, g = synth.lut3_weights(N, K, 700 + N)
         packed = U.pack_lut3(c, q, g)
@@ -447,7 +512,7 @@ def test_every_tiling_matches_oracle(nt, sn, split, tuning_reset):
             xh = synth.x_f16(M, K, 800 + M)
             y, _ = U.run_lut3(packed, N, K, xh)
             r = U.grade_lut3(y, xh, c, q, g, K)
-            assert r.ok, "lut3 N=%d K=%d M=%d: %s" % (N, K, M, r)
+            U.check(r, "lut3 N=%d K=%d M=%d" % (N, K, M), "f16")
             yd, _ = U.run_lut3(packed_d, N, K, xh, dense=True)
             assert np.array_equal(yd, y), "lut3 dense N=%d K=%d M=%d" % (N, K, M)
 
@@ -480,7 +545,7 @@ def test_lut3_single_pass_rows_equal_16_row_calls(nt, sn, split, dense, tuning_r
     y20, _ = U.run_lut3(packed, N, K, x32[:20], dense=dense)
     assert np.array_equal(y20, y32[:20])
     r = U.grade_lut3(y32, x32, c, q, g, K)
-    assert r.ok, str(r)
+    U.check(r, out_dtype="f16")
 
 
 def test_hip_graph_replays_match_eager():

@@ -56,6 +56,8 @@ MUTANTS = [
     ("w8a8_sx_group", "sx[m * kb_n + k / WQO_BLOCK]", "sx[m * kb_n]", None),
     ("w8a8_sx_row", "sx[m * kb_n + k / WQO_BLOCK]", "sx[k / WQO_BLOCK]", None),
     ("w8a8_x_stride", "xq[m * ldxq + k]", "xq[m * K + k]", None),
+    ("quant_nonfinite_ignored", "if (!isfinite(a)) nonfinite = 1;", "if (0) nonfinite = 1;", None),
+    ("quant_nonfinite_scale_one", "scales[m * kb_n + kb] = NAN;", "scales[m * kb_n + kb] = 1.0f;", None),
 ]
 
 

@@ -45,6 +45,8 @@
 // (the caller passed a workspace) each K part's work-group stores FP32 sums
 // to the workspace and a second kernel adds the parts in order.  Every sum
 // has a fixed order: results are deterministic and do not depend on M.
+#include <atomic>
+
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
@@ -983,16 +985,32 @@ __global__ void __launch_bounds__(256) reduce_parts_kernel(const float* __restri
 // Launchers
 // ======================================================================
 
+// A launch with more than 64 KiB of dynamic LDS needs the kernel's limit
+// raised first.  It is raised once per kernel instantiation and device, to the
+// whole 160 KiB of a compute unit (a limit, not a reservation), and later
+// launches only test a bit: no runtime call on the hot path.  `done` is the
+// instantiation's own mask of devices already set.
+static hipError_t allow_big_lds(const void* fn, size_t lds, std::atomic<uint64_t>& done)
+{
+    if (lds <= 64 * 1024) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 template <class Pol, int D, int XPL, bool F16>
 static hipError_t launch_one(const GemmArgs& a, int split, hipStream_t s)
 {
     auto fn = gemm_kernel<Pol, D, XPL, F16>;
+    static std::atomic<uint64_t> big_lds_set{0};
     const size_t lds = (size_t)gemm_lds_bytes<Pol, XPL>(split, a.sn);
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    hipError_t e = allow_big_lds(reinterpret_cast<const void*>(fn), lds, big_lds_set);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, dim3(a.n_cg, a.kp), dim3(split * 64), lds, s, a);
     return hipGetLastError();
 }

@@ -9,7 +9,8 @@
 //   quantiser  x (BF16) -> codes + one FP32 scale per (row, 128-wide K group):
 //              s = amax / 448 (IEEE binary32 division; 1 for an all-zero
 //              group), code = E4M3 nearest-even of clamp(x / s, -448, 448),
-//              the rule of the weights' own 128x128 block quantiser.
+//              the rule of the weights' own 128x128 block quantiser; a group
+//              holding an infinity or a NaN gets a NaN scale and NaN codes.
 //   GEMM       y[m,n] = sum over K blocks kb of sx[m][kb] * sw[n/128][kb] *
 //              (sum over the block of e4m3(xq) * e4m3(w)); one
 //              v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-K block of a
@@ -76,6 +77,7 @@ __global__ void __launch_bounds__(256) quantize_x_kernel(const uint16_t* __restr
     const int m = 16 * mt + r;
     float v[4][8];                      // run q: k = 128kb + 32q + 8g + e
     float amax = 0.f;
+    uint32_t expmax = 0u;               // largest BF16 exponent field seen (0xFF: Inf or NaN)
     if (m < M) {
         const uint16_t* row = x + (int64_t)m * ldx + kb * 128 + 8 * g;
 #pragma unroll
@@ -86,6 +88,7 @@ __global__ void __launch_bounds__(256) quantize_x_kernel(const uint16_t* __restr
             for (int i = 0; i < 4; ++i) {
                 v[q][2 * i] = __uint_as_float(d[i] << 16);
                 v[q][2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
+                expmax = max(expmax, max((d[i] >> 7) & 0xFFu, (d[i] >> 23) & 0xFFu));
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[q][e]));
@@ -98,7 +101,12 @@ __global__ void __launch_bounds__(256) quantize_x_kernel(const uint16_t* __restr
     }
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    expmax = max(expmax, (uint32_t)__shfl_xor((int)expmax, 16));
+    expmax = max(expmax, (uint32_t)__shfl_xor((int)expmax, 32));
+    // a group holding an infinity or a NaN: NaN scale and the E4M3 NaN code
+    // everywhere, so every product that uses the group is NaN
+    const bool nonfinite = expmax == 0xFFu;
+    const float s = nonfinite ? __uint_as_float(0x7FC00000u) : amax > 0.f ? amax / 448.0f : 1.0f;
     uint32_t c[4][2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -106,7 +114,7 @@ __global__ void __launch_bounds__(256) quantize_x_kernel(const uint16_t* __restr
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float qv = fminf(fmaxf(v[q][e] / s, -448.0f), 448.0f);
-            const uint32_t code = m < M ? e4m3_rne(qv) : 0u;
+            const uint32_t code = m < M ? (nonfinite ? 0x7Fu : e4m3_rne(qv)) : 0u;
             c[q][e >> 2] |= code << (8 * (e & 3));
         }
     }
@@ -180,6 +188,10 @@ __device__ __forceinline__ void wait_vmcnt()
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+
+// Wait until no vector-memory operation and no LDS access of this wave is
+// outstanding (vmcnt = 0, lgkmcnt = 0; expcnt left at its maximum).
+__device__ __forceinline__ void wait_vmcnt_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(7 << 4); }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
 // LDS address dst + 16 l (dst is wave-uniform; it goes to M0).  The data never
@@ -354,10 +366,19 @@ w8a8_gemm_kernel(W8Args a)
 
     // one block: own loads of `cur` done, barrier, refill the other stage with
     // block kb + 1 (the part's last block again at the end, so every wave
-    // always has the same loads in flight), multiply
+    // always has the same loads in flight), multiply.
+    // Ordering of the stage reuse: the loads that fill `nxt` overwrite what
+    // every wave read from it in the previous block.  Before the barrier each
+    // wave waits for its own loads into `cur` (vmcnt) and for its own LDS
+    // reads of `nxt` (lgkmcnt), and the workgroup-scope release/acquire
+    // fences keep the compiler from moving any LDS access across the
+    // barrier; so when a wave issues the refill after the barrier, every
+    // wave's reads of that stage have returned.
     auto step = [&](int kb, const uint8_t* cur, uint32_t nxt) {
-        wait_vmcnt<0>();
+        wait_vmcnt_lgkmcnt0();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         issue(kb + 1 < kbe ? kb + 1 : kbe - 1, nxt);
         compute(kb, cur);
     };
