@@ -28,6 +28,10 @@ from . import bf16_rne, bf16_value, f16_rne, f16_value
 
 MAX_ULP = 2
 FLOOR_COEF = 1e-3
+# Smallest FP16 normal.  Below it FP16's spacing is a fixed 2^-24, wider than
+# 2 BF16 ULP of any value under 2^-16, so an FP16 output there can miss the
+# ULP budget even when it is the correctly rounded result.
+F16_MIN_NORMAL = 2.0 ** -14
 
 
 def bf16_ord(bits) -> np.ndarray:
@@ -49,6 +53,8 @@ class Receipt:
     n_fail: int
     max_ulp: int
     n_over_budget: int          # elements beyond MAX_ULP (they may still pass via the floor)
+    n_over_budget_resolvable: int  # of those, the ones the output format resolves to MAX_ULP
+                                   # (FP16 output: |y64| at or above FP16's smallest normal)
     max_err_over_floor: float
     rel_rms: float
     sign_flips: int
@@ -61,9 +67,10 @@ class Receipt:
         return self.n_fail == 0
 
     def __str__(self) -> str:
-        s = ("n=%d fail=%d max_ulp=%d over_2ulp=%d max_err/floor=%.3g rel_rms=%.3g sign_flips=%d floor=%.3g"
-             % (self.n, self.n_fail, self.max_ulp, self.n_over_budget, self.max_err_over_floor,
-                self.rel_rms, self.sign_flips, self.floor))
+        s = ("n=%d fail=%d max_ulp=%d over_2ulp=%d (resolvable %d) max_err/floor=%.3g rel_rms=%.3g "
+             "sign_flips=%d floor=%.3g"
+             % (self.n, self.n_fail, self.max_ulp, self.n_over_budget, self.n_over_budget_resolvable,
+                self.max_err_over_floor, self.rel_rms, self.sign_flips, self.floor))
         if self.max_f16_ulp is not None:
             s += " max_f16_ulp=%d" % self.max_f16_ulp
         if self.first_fail is not None:
@@ -99,6 +106,7 @@ def grade(y_bits: np.ndarray, y64: np.ndarray, floor: float, out_dtype: str = "b
     abs_ok = err <= floor
     ok = (finite & (ulp_ok | abs_ok)) | both_nan
     fin = finite & np.isfinite(y64)
+    resolvable = fin & (np.abs(y64) >= F16_MIN_NORMAL) if out_dtype == "f16" else fin
     denom = math.sqrt(float(np.sum(y64[fin] ** 2))) if fin.any() else 0.0
     rel_rms = math.sqrt(float(np.sum((g[fin] - y64[fin]) ** 2))) / denom if denom > 0 else 0.0
     big = fin & (np.abs(y64) > floor)
@@ -111,5 +119,6 @@ def grade(y_bits: np.ndarray, y64: np.ndarray, floor: float, out_dtype: str = "b
     return Receipt(
         n=int(y64.size), n_fail=int((~ok).sum()),
         max_ulp=int(ulp[fin].max(initial=0)), n_over_budget=int((fin & ~ulp_ok).sum()),
+        n_over_budget_resolvable=int((resolvable & ~ulp_ok).sum()),
         max_err_over_floor=float(err[fin].max(initial=0.0) / floor) if floor > 0 else float("inf"),
         rel_rms=rel_rms, sign_flips=flips, floor=floor, max_f16_ulp=max_f16, first_fail=first)

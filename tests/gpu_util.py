@@ -151,17 +151,23 @@ def grade_lut3(ybits, xbits, codes, qmap, scales, K, cols=None, floor=None):
 # scale, a lost K block -- could still pass element by element.  The atlas
 # m16_tc docs' own M=32 receipt had 5 of 557,056 outputs over the budget, all
 # cancellations.
+# FP16 outputs below FP16's smallest normal are not counted: FP16's spacing
+# there is coarser than 2 BF16 ULP, so even a correctly rounded value can be
+# over the budget (Receipt.n_over_budget_resolvable).
 OVER_BUDGET_FRAC = 1e-4
 # rel_rms bounds by output type: BF16 rounding alone gives ~1.5e-3, FP16 ~2e-4
 REL_RMS_MAX = {"bf16": 4e-3, "f16": 1e-3}
 
 
-def check(r, what: str = "", out_dtype: str = "bf16") -> None:
+def check(r, what: str = "", out_dtype: str = "bf16", max_over: int | None = None) -> None:
     """Assert a receipt: every output within the contract, at most
-    OVER_BUDGET_FRAC of them beyond 2 ULP, no sign flips, rel_rms bounded."""
+    OVER_BUDGET_FRAC of them (or max_over) beyond 2 ULP, no sign flips,
+    rel_rms bounded."""
     tag = ("%s: " % what if what else "") + str(r)
     assert r.ok, tag
-    assert r.n_over_budget <= int(OVER_BUDGET_FRAC * r.n), "over budget: " + tag
+    if max_over is None:
+        max_over = int(OVER_BUDGET_FRAC * r.n)
+    assert r.n_over_budget_resolvable <= max_over, "over budget: " + tag
     assert r.sign_flips == 0, tag
     assert np.isfinite(r.rel_rms) and r.rel_rms < REL_RMS_MAX[out_dtype], "rel_rms: " + tag
 

@@ -138,6 +138,26 @@ def pin_f16_output_graded_after_bf16_rounding(C):
     assert r3.ok and r3.max_ulp == 1
 
 
+def pin_f16_resolvable_budget(C):
+    """An FP16 output below FP16's smallest normal (2^-14) is counted over
+    the budget but not as resolvable; at or above it, both.  At 2^-18 one
+    FP16 step (2^-24) is 2 BF16 ULP, so 3 FP16 steps are 6 BF16 ULP."""
+    y64 = np.array([[2.0 ** -18, 1.0]])
+    h = oracle.f16_rne(y64)
+    h[0, 0] += 3                                # 3 FP16 steps of 2^-24 above 2^-18
+    h[0, 1] += 40                               # 40 FP16 ULP at 1.0 = 5 BF16 ULP
+    r = C.grade(h, y64, floor=1.0, out_dtype="f16")
+    assert r.ok and r.max_ulp == 6
+    assert r.n_over_budget == 2 and r.n_over_budget_resolvable == 1
+    rb = C.grade(bits(np.array([[1.0 + 5 * 2 ** -7, 2.0 ** -18 * (1 + 5 * 2 ** -7)]])),
+                 np.array([[1.0, 2.0 ** -18]]), floor=1.0)
+    assert rb.n_over_budget == rb.n_over_budget_resolvable == 2      # BF16 output: every element
+    y_edge = np.array([[2.0 ** -14]])           # the smallest normal itself is resolvable
+    he = oracle.f16_rne(y_edge) + 40
+    re_ = C.grade(he, y_edge, floor=1.0, out_dtype="f16")
+    assert re_.n_over_budget_resolvable == 1
+
+
 def pin_sign_flips_counted_only_above_floor(C):
     y64 = np.array([[2.0, 1e-8]])
     g = bits(np.array([[-2.0, -1e-8]]))
@@ -157,7 +177,8 @@ def pin_rel_rms(C):
 COMPARE_PINS = [pin_floor_values, pin_floor_boundary, pin_exact_and_two_ulp_pass_three_fail,
                 pin_criteria_are_or_ed, pin_ord_is_monotone_and_signed_zero_agnostic,
                 pin_cancellation_passes_through_the_floor, pin_non_finite,
-                pin_f16_output_graded_after_bf16_rounding, pin_sign_flips_counted_only_above_floor, pin_rel_rms]
+                pin_f16_output_graded_after_bf16_rounding, pin_f16_resolvable_budget,
+                pin_sign_flips_counted_only_above_floor, pin_rel_rms]
 
 
 @pytest.mark.parametrize("pin", COMPARE_PINS, ids=[p.__name__ for p in COMPARE_PINS])
@@ -188,6 +209,10 @@ MUTANTS = [
      "rel_rms = float(np.sum((g[fin] - y64[fin]) ** 2)) / denom", None),
     ("flips_everywhere", "big = fin & (np.abs(y64) > floor)", "big = fin", None),
     ("over_budget_counts_fails", "n_over_budget=int((fin & ~ulp_ok).sum())", "n_over_budget=int((~ok).sum())", None),
+    ("resolvable_everything", "resolvable = fin & (np.abs(y64) >= F16_MIN_NORMAL) if", "resolvable = fin if", None),
+    ("resolvable_threshold_bf16", "F16_MIN_NORMAL = 2.0 ** -14", "F16_MIN_NORMAL = 2.0 ** -126", None),
+    ("resolvable_threshold_high", "F16_MIN_NORMAL = 2.0 ** -14", "F16_MIN_NORMAL = 2.0 ** -13", None),
+    ("resolvable_for_bf16_too", 'if out_dtype == "f16" else fin', "", None),
 ]
 
 
