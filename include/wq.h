@@ -80,7 +80,8 @@ typedef enum {
     WQ_ERR_DEVICE = 6,     /* current device is not gfx950                            */
     WQ_ERR_HIP = 7,        /* a HIP runtime call failed (includes: no device)         */
     WQ_ERR_ALIGN = 8,      /* pointer or leading dimension breaks a 16-byte alignment */
-    WQ_ERR_PATH = 9        /* requested path cannot serve this format / M             */
+    WQ_ERR_PATH = 9,       /* requested path cannot serve this format / M             */
+    WQ_ERR_SCRATCH = 10    /* the no-allocation GEMM's plan needs more than its static scratch */
 } wq_status;
 
 typedef enum { WQ_FMT_FP8_BLOCK = 0, WQ_FMT_LUT3 = 1, WQ_FMT_LUT3_DENSE = 2 } wq_format;
@@ -208,6 +209,29 @@ wq_status wq_gemm_fp8_block_path(const void* packed, int64_t N, int64_t K,
                                  uint16_t* y, int64_t ldy, int64_t M,
                                  void* workspace, size_t workspace_bytes,
                                  int path, void* hip_stream);
+
+/* The FP8 GEMM without allocation and without a workspace argument: the
+ * same computation, plan and result bits as wq_gemm_fp8_block called with a
+ * workspace of wq_gemm_workspace_bytes(...) bytes, but the K-split partials
+ * go to a static device array of the library (wq_noalloc_scratch_bytes()
+ * bytes, 4 MiB; each device holds its own copy until the process ends).  The
+ * call makes no allocation of any kind; the caller passes inputs and outputs
+ * only.  A shape whose K-split plan needs more scratch than that returns
+ * WQ_ERR_SCRATCH and queues nothing.  Every call on one device shares that
+ * device's array: calls that overlap on one device (other streams, other
+ * threads) race and must be ordered by the caller.  Arguments, validation,
+ * numerics and determinism otherwise as wq_gemm_fp8_block.
+ * Callers: code that cannot call hipMalloc -- work under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. */
+wq_status wq_gemm_fp8_block_noalloc(const void* packed, int64_t N, int64_t K,
+                                    const uint16_t* x, int64_t ldx,
+                                    uint16_t* y, int64_t ldy, int64_t M, void* hip_stream);
+
+/* Bytes of the static device scratch that wq_gemm_fp8_block_noalloc uses
+ * (the largest K-split workspace it can serve).
+ * Callers: those of wq_gemm_fp8_block_noalloc, to check a shape ahead
+ * against wq_gemm_workspace_bytes. */
+size_t wq_noalloc_scratch_bytes(void);
 
 /* ----------------------------------------------------------------- LUT3 */
 

@@ -247,3 +247,16 @@ def test_large_stride_within_limits_passes_validation():
     # stride.  The calls get past validation and fail only for want of a device
     assert L.wq_gemm_fp8_block(P, 256, 512, P, 1 << 26, P, 256, 32, P, BIG, None) == 7
     assert L.wq_gemm_fp8_block(P, 256, 512, P, 1 << 30, P, 256, 1, P, BIG, None) == 7
+
+
+def test_noalloc_validates_before_the_device():
+    """The no-allocation GEMM: M == 0 queues nothing; host validation errors come
+    before any device work; the scratch bound is a constant."""
+    assert wq.wq_noalloc_scratch_bytes() == 4 << 20
+    f = wq.lib.wq_gemm_fp8_block_noalloc
+    assert f(None, 256, 512, None, 512, None, 256, 0, None) == 0                    # M == 0
+    assert f(None, 256, 512, None, 512, None, 256, 1, None) == 1                    # WQ_ERR_NULL
+    assert f(16, 256, 500, 16, 512, 16, 256, 1, None) == 2                          # K % 128
+    assert f(16, 256, 512, 16, 256, 16, 256, 1, None) == 3                          # ldx < K
+    assert f(16, 256, 512, 16, 512, 16, 256, 33, None) == 2                         # M > 32
+    assert wq.wq_status_str(wq.WQ_ERR_SCRATCH).startswith("WQ_ERR_SCRATCH")

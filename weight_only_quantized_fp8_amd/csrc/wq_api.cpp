@@ -292,10 +292,12 @@ size_t lut3_scale_bytes(int64_t N, int64_t K) { return (size_t)(N / 16) * (size_
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Shared front end of the GEMMs.
+// Shared front end of the GEMMs.  static_scratch: the no-allocation entry
+// point -- the workspace is the library's static device scratch of the
+// current device (the caller passes none), planned as a call with a workspace.
 wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                       uint16_t* y, int64_t ldy, int64_t M, void* workspace, size_t workspace_bytes, int path,
-                      void* stream)
+                      void* stream, bool static_scratch = false)
 {
     // ---- validation that needs no HIP call
     if (M < 0 || M > 32) return WQ_ERR_SHAPE;
@@ -326,9 +328,19 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
 
     // ---- device and workspace
     DevInfo dev;
-    wq_status st = current_device(&dev);
+    int dev_index = -1;
+    wq_status st = current_device(&dev, &dev_index);
     if (st != WQ_OK) return st;
-    const Plan p = cached_plan(kind, N, K, dev.cu, workspace != nullptr);
+    const Plan p = cached_plan(kind, N, K, dev.cu, static_scratch || workspace != nullptr);
+    if (static_scratch) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (p.kp > 1) {
+            if (plan_workspace_bytes(p, N) > wq::kScratchBytes) return WQ_ERR_SCRATCH;
+            if (wq::scratch_address(dev_index, &workspace) != hipSuccess) return WQ_ERR_HIP;
+            workspace_bytes = wq::kScratchBytes;
+        }
+    }
     if (p.kp > 1) {   // K parts across work-groups: FP32 partials in the workspace
         if (workspace_bytes < plan_workspace_bytes(p, N)) return WQ_ERR_WORKSPACE;
         if (!aligned16(workspace)) return WQ_ERR_ALIGN;
@@ -429,6 +441,7 @@ const char* wq_status_str(wq_status s)
     case WQ_ERR_HIP: return "WQ_ERR_HIP: HIP runtime call failed";
     case WQ_ERR_ALIGN: return "WQ_ERR_ALIGN: pointer or leading dimension misaligned";
     case WQ_ERR_PATH: return "WQ_ERR_PATH: path cannot serve this format or M";
+    case WQ_ERR_SCRATCH: return "WQ_ERR_SCRATCH: the shape's K-split plan needs more than the static scratch";
     }
     return "WQ_ERR_UNKNOWN";
 }
@@ -508,6 +521,15 @@ wq_status wq_gemm_fp8_block_path(const void* packed, int64_t N, int64_t K, const
     return gemm_common(WQ_FMT_FP8_BLOCK, packed, N, K, x, ldx, y, ldy, M, workspace, workspace_bytes, path,
                        hip_stream);
 }
+
+wq_status wq_gemm_fp8_block_noalloc(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                                    uint16_t* y, int64_t ldy, int64_t M, void* hip_stream)
+{
+    return gemm_common(WQ_FMT_FP8_BLOCK, packed, N, K, x, ldx, y, ldy, M, nullptr, 0, WQ_PATH_AUTO, hip_stream,
+                       true);
+}
+
+size_t wq_noalloc_scratch_bytes(void) { return wq::kScratchBytes; }
 
 wq_status wq_pack_lut3(const uint8_t* codes, int64_t ldc, const uint16_t* qmap, const uint16_t* scales, int64_t N,
                        int64_t K, void* packed, void* hip_stream)

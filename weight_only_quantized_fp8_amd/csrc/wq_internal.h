@@ -158,6 +158,15 @@ hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq,
 hipError_t launch_sum_parts(const float* ws, int kp, int rows, int N, uint16_t* y, int64_t ldy, bool f16_out,
                             hipStream_t stream);
 
+// Static device scratch for callers that cannot allocate (the no-allocation
+// FP8 GEMM entry point): the K-split plan's FP32 partials go there instead of
+// a caller's workspace.  kScratchBytes bounds the plan it can serve (FFN down
+// 5120 x 17408 in 4 K parts needs 4 x 32 x 5120 x 4 = 2.6 MB).
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+// Device address of the current device's copy of that array (dev = the
+// current device's index); looked up once per device, with it current.
+hipError_t scratch_address(int dev, void** out);
+
 // W8A8 work-group tile edge (rows and columns) for an M (the launcher's own
 // choice; a K-split plan counts its tiles with it)
 constexpr int kW8BigM = 4096;

@@ -46,6 +46,7 @@
 // to the workspace and a second kernel adds the parts in order.  Every sum
 // has a fixed order: results are deterministic and do not depend on M.
 #include <atomic>
+#include <mutex>
 
 #include "wq_device.hpp"
 #include "wq_internal.h"
@@ -55,6 +56,38 @@ namespace wq {
 // 4 KiB of zeros: the source of the block-scale load of a unit with nothing
 // to fetch (vector loads use a zero-byte buffer resource instead).
 __device__ __attribute__((aligned(256))) uint8_t g_zero_page[4096];
+
+// Scratch of the no-allocation GEMM entry point: each device that runs the
+// library holds its own copy until the process ends.  In host code the name
+// `scratch` is only a host-side handle of the symbol, not a device address;
+// scratch_address() returns the device address (hipGetSymbolAddress with the
+// device current), and only that address is ever passed to a kernel.  Every
+// call on one device shares that device's copy: calls that overlap on one
+// device race, and the array keeps whatever the last call left in it (every
+// slot a call reads, it has written first).
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static constexpr int kScratchDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kScratchDevices];
+static std::mutex g_scratch_mu;
+
+hipError_t scratch_address(int dev, void** out)
+{
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 // ======================================================================
 // Policies: per-unit loads and compute for each kernel kind.  A policy is

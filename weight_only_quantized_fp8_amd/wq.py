@@ -16,6 +16,7 @@ __all__ = [
     "WQ_OK", "WQ_FMT_FP8_BLOCK", "WQ_FMT_LUT3", "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA",
     "wq_status_str", "wq_packed_format_version", "wq_set_tuning", "wq_set_kparts",
     "wq_fp8_block_packed_bytes", "wq_pack_fp8_block", "wq_gemm_fp8_block", "wq_gemm_fp8_block_path",
+    "wq_gemm_fp8_block_noalloc", "wq_noalloc_scratch_bytes", "WQ_ERR_SCRATCH",
     "wq_lut3_packed_bytes", "wq_pack_lut3", "wq_gemm_lut3",
     "WQ_FMT_LUT3_DENSE", "wq_lut3_dense_packed_bytes", "wq_pack_lut3_dense", "wq_gemm_lut3_dense",
     "wq_unpack_lut3_dense", "pack_lut3_dense", "gemm_lut3_dense",
@@ -38,6 +39,7 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 WQ_OK = 0
+WQ_ERR_SCRATCH = 10
 WQ_FMT_FP8_BLOCK, WQ_FMT_LUT3, WQ_FMT_LUT3_DENSE = 0, 1, 2
 WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 
@@ -51,6 +53,8 @@ _SIGS = {
     "wq_pack_fp8_block": (_INT, [_P, _I64, _P, _I64, _I64, _P, _P]),
     "wq_gemm_fp8_block": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
     "wq_gemm_fp8_block_path": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _INT, _P]),
+    "wq_gemm_fp8_block_noalloc": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P]),
+    "wq_noalloc_scratch_bytes": (_SZ, []),
     "wq_lut3_packed_bytes": (_SZ, [_I64, _I64]),
     "wq_pack_lut3": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _P]),
     "wq_gemm_lut3": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
@@ -162,6 +166,15 @@ def wq_gemm_fp8_block_path(packed, N: int, K: int, x, y, M: int, workspace=None,
     _check(lib.wq_gemm_fp8_block_path(_ptr(packed), N, K, _ptr(x), _ld(x), _ptr(y), _ld(y), M, _ptr(workspace),
                                       _nbytes(workspace), path, _stream(stream)),
            "wq_gemm_fp8_block_path")
+
+
+def wq_gemm_fp8_block_noalloc(packed, N: int, K: int, x, y, M: int, stream=None) -> None:
+    _check(lib.wq_gemm_fp8_block_noalloc(_ptr(packed), N, K, _ptr(x), _ld(x), _ptr(y), _ld(y), M,
+                                         _stream(stream)), "wq_gemm_fp8_block_noalloc")
+
+
+def wq_noalloc_scratch_bytes() -> int:
+    return lib.wq_noalloc_scratch_bytes()
 
 
 def wq_pack_lut3(codes, qmap, scales, N: int, K: int, packed, stream=None) -> None:
