@@ -14,8 +14,10 @@ divided by the time per step (the pages count stored weight bytes: one byte an
 FP8 code, half a byte a nibble-packed 3-bit code, 3/8 a dense one, plus the
 scales).  The JSON line also carries the dominant kernel's roofline (bytes
 per launch over the mean launch duration, from HIP events on the library's
-stream), the CPU oracle timed on the host as a baseline, and (with --all) the
-other workloads' numbers.
+stream), the CPU oracle timed on the host as a baseline, and an "extra" block
+with the other M=16 target (3-bit LUT 28672 x 8192, both storage layouts), the
+FFN down projection at M = 16 and 32 and gate/up at M = 1 and 8 (--no-extra
+skips it; --all times every workload, M and the W8A8 tier).
 """
 from __future__ import annotations
 
@@ -260,6 +262,36 @@ def time_workload(w: Workload, steps: int, warmup: int, use_graph: bool = True):
 
 FP8_MFMA_PEAK_TFLOPS = 5000.0
 
+# Workloads a default run times beside the headline one, by the same method
+# (HIP graph of the steps, weight copies rotated beyond the Infinity Cache):
+# the other M=16 target (3-bit LUT 28672 x 8192, both storage layouts), the
+# FFN down projection at M = 16 and 32, and gate/up at M = 1 and 8.
+DEFAULT_EXTRA = [("lut3", 16), ("lut3d", 16), ("down", 16), ("down", 32), ("gate_up", 1), ("gate_up", 8)]
+
+
+def time_extra(name: str, M: int, steps: int, warmup: int, eager: bool) -> dict:
+    """One more workload timed like the headline one; its line of the extra block."""
+    import synth
+    import torch
+    fmt, N, K, _ = synth.CONFIGS[name]
+    print("bench: %s M=%d" % (name, M), file=sys.stderr, flush=True)
+    wk = Workload(name, M)
+    rk = time_workload(wk, steps, warmup, use_graph=not eager)
+    state = gpu_state()
+    gbs = wk.wbytes * wk.launches_per_step() / (rk["ms_per_step"] * 1e-3) / 1e9
+    e = {"us_per_call": round(rk["ms_per_step"] * 1e3, 2),
+         "windows_us": rk["windows_us"],
+         "stream_GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+         "roofline_frac": round(wk.abytes / (rk["launch_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+         "passes": wk.launches_per_step(), "k_parts": wk.k_parts, "sclk_after": state.get("sclk_level")}
+    if fmt in ("lut3", "lut3d"):
+        # 3 bits of information per code, plus the group scales and the map
+        info = N * K * 3 // 8 + 2 * N * (K // 128) + 16
+        e["info_GBps"] = round(info / (rk["ms_per_step"] * 1e-3) / 1e9, 1)
+    del wk
+    torch.cuda.empty_cache()
+    return e
+
 
 def time_w8a8(name: str, M: int, steps: int = 20, copies: int = 4) -> dict:
     """The W8A8 tier on an FFN shape at a prefill batch: one step quantises the
@@ -363,7 +395,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="gate_up")
     ap.add_argument("--M", type=int, default=16)
-    ap.add_argument("--all", action="store_true", help="also time every other workload and M")
+    ap.add_argument("--all", action="store_true", help="also time every other workload and M, and the W8A8 tier")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only the headline workload (skip the default extra block)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="launch each step from Python instead of a HIP graph")
     ap.add_argument("--w8a8", action="store_true",
@@ -437,34 +471,21 @@ def main(argv=None) -> int:
     del w
     torch.cuda.empty_cache()
 
+    extra_list = []
     if args.all:
+        extra_list = [(name, M) for name, (fmt, N, K, Ms) in synth.CONFIGS.items() if name != "tiny" for M in Ms]
+    elif not args.no_extra:
+        extra_list = list(DEFAULT_EXTRA)
+    extra_list = [(n, m) for n, m in extra_list if not (n == args.config and m == args.M)]
+    if extra_list or args.all:
         extra = {}
-        for name, (fmt, N, K, Ms) in synth.CONFIGS.items():
-            if name == "tiny":
-                continue
-            for M in Ms:
-                if name == args.config and M == args.M:
-                    continue
-                print("bench: %s M=%d" % (name, M), file=sys.stderr, flush=True)
-                wk = Workload(name, M)
-                rk = time_workload(wk, max(20, args.steps // 4), max(5, args.warmup // 4),
-                                   use_graph=not args.eager)
-                gbs = wk.wbytes * wk.launches_per_step() / (rk["ms_per_step"] * 1e-3) / 1e9
-                extra["%s_M%d" % (name, M)] = {
-                    "us_per_call": round(rk["ms_per_step"] * 1e3, 2),
-                    "us_per_launch": round(rk["launch_ms_mean"] * 1e3, 2),
-                    "stream_GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-                    "passes": wk.launches_per_step(), "k_parts": wk.k_parts}
-                if fmt in ("lut3", "lut3d"):
-                    # 3 bits of information per code, plus the group scales and the map
-                    info = N * K * 3 // 8 + 2 * N * (K // 128) + 16
-                    extra["%s_M%d" % (name, M)]["info_GBps"] = round(info / (rk["ms_per_step"] * 1e-3) / 1e9, 1)
-                del wk
-                torch.cuda.empty_cache()
-        for name in ("gate_up", "down"):
-            for M in (256, 512, 2048, 4096):
-                print("bench: w8a8 %s M=%d" % (name, M), file=sys.stderr, flush=True)
-                extra["w8a8_%s_M%d" % (name, M)] = time_w8a8(name, M)
+        for name, M in extra_list:
+            extra["%s_M%d" % (name, M)] = time_extra(name, M, args.steps, args.warmup, args.eager)
+        if args.all:
+            for name in ("gate_up", "down"):
+                for M in (256, 512, 2048, 4096):
+                    print("bench: w8a8 %s M=%d" % (name, M), file=sys.stderr, flush=True)
+                    extra["w8a8_%s_M%d" % (name, M)] = time_w8a8(name, M)
         out["extra"] = extra
 
     if not args.no_cpu:
