@@ -357,6 +357,99 @@ def time_w8a8(name: str, M: int, steps: int = 20, copies: int = 4) -> dict:
             "k_parts": k_parts}
 
 
+def graph_time_us(step, steps: int = 100, windows: int = 9) -> dict:
+    """Median (and p10/p90) microseconds per step of `step(i)` over `windows`
+    replays of a HIP graph holding `steps` calls, after a settling warm-up."""
+    import torch
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    t_end = time.perf_counter() + WARM_SECONDS
+    while time.perf_counter() < t_end:
+        g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    v = []
+    for _ in range(windows):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        v.append(e0.elapsed_time(e1) * 1e3 / steps)
+    v.sort()
+    pick = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+    del g
+    return {"median": round(pick(0.5), 2), "p10": round(pick(0.1), 2), "p90": round(pick(0.9), 2)}
+
+
+def crossover() -> dict:
+    """The arms of the decode ladder on one binary (the arc PR's "The threshold":
+    every arm timed on the same build, the crossover taken from the data).
+    (1) FP8 strict-order GEMV against the 16-row MFMA tile at M = 1..4 on the
+    FFN and attention shapes; (2) the W8A8 tier (quantise + FP8 x FP8 GEMM,
+    with its workspace) against the decode tile run as 32-row calls
+    (ceil(M/32) calls on consecutive row blocks) at M = 16 .. 128.  Weight
+    copies rotate beyond the Infinity Cache in both."""
+    import numpy as np
+    import torch
+    import synth
+    from weight_only_quantized_fp8_amd import wq
+    dev = "cuda:0"
+    out = {"gemv_vs_mfma": {}, "w8a8_vs_decode": {}}
+    for name in ("gate_up", "down", "attn_q", "attn_o", "attn_k"):
+        fmt, N, K, _ = synth.CONFIGS[name]
+        codes, scales = synth.fp8_weights(N, K, synth.SEEDS[name])
+        p0 = wq.pack_fp8(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev))
+        del codes
+        copies = max(2, math.ceil(ROTATE_TARGET_BYTES / p0.numel()))
+        packed = [p0] + [p0.clone() for _ in range(copies - 1)]
+        ws = wq.workspace(wq.WQ_FMT_FP8_BLOCK, N, K, dev)
+        ws = ws if ws.numel() else None
+        row = {}
+        for M in (1, 2, 3, 4):
+            x = torch.from_numpy(synth.x_bf16(M, K, synth.SEEDS[name] + 100).view(np.int16)).to(dev).view(torch.bfloat16)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            for path, tag in ((wq.WQ_PATH_GEMV, "gemv"), (wq.WQ_PATH_MFMA, "mfma")):
+                print("bench: crossover %s M=%d %s" % (name, M, tag), file=sys.stderr, flush=True)
+                st = lambda i, x=x, y=y, path=path: wq.wq_gemm_fp8_block_path(packed[i % copies], N, K, x, y, M, ws,
+                                                                              path)
+                row["M%d_%s_us" % (M, tag)] = graph_time_us(st)["median"]
+        out["gemv_vs_mfma"][name] = row
+        if name in ("gate_up", "down"):
+            r2 = {}
+            for M in (16, 32, 64, 128):
+                x = torch.from_numpy(synth.x_bf16(M, K, synth.SEEDS[name] + 100).view(np.int16)).to(dev).view(
+                    torch.bfloat16)
+                y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                print("bench: crossover %s M=%d decode vs w8a8" % (name, M), file=sys.stderr, flush=True)
+
+                def dec(i, x=x, y=y, M=M):
+                    for r0 in range(0, M, 32):
+                        wq.wq_gemm_fp8_block(packed[i % copies], N, K, x[r0:r0 + 32], y[r0:r0 + 32], min(32, M - r0), ws)
+                xq = torch.empty(wq.wq_x_fp8_packed_bytes(M, K), dtype=torch.uint8, device=dev)
+                nb = wq.wq_w8a8_workspace_bytes(M, N, K)
+                w8ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+
+                def w8(i, x=x, y=y, M=M, xq=xq, w8ws=w8ws):
+                    wq.wq_quantize_x_fp8(x, M, K, xq)
+                    wq.wq_gemm_fp8_w8a8(packed[i % copies], N, K, xq, M, y, w8ws)
+                d_us, w_us = graph_time_us(dec)["median"], graph_time_us(w8)["median"]
+                r2["M%d" % M] = {"decode_us": d_us, "decode_calls": (M + 31) // 32, "w8a8_us": w_us,
+                                 "faster": "decode" if d_us < w_us else "w8a8"}
+            out["w8a8_vs_decode"][name] = r2
+        del packed, p0
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(name: str, M: int, min_seconds: float = 10.0, max_reps: int = 500):
     """The oracle as it stands, on the host cores, over the whole workload (all
     outputs), repeated until about min_seconds of CPU wall time (at least 3
@@ -400,6 +493,9 @@ def main(argv=None) -> int:
                     help="time only the headline workload (skip the default extra block)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="launch each step from Python instead of a HIP graph")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time the ladder's arms on one binary (GEMV vs MFMA at M=1..4, W8A8 vs the decode tile at "
+                         "M=16..128) and print that table as one JSON line")
     ap.add_argument("--w8a8", action="store_true",
                     help="time only the W8A8 tier (quantise + FP8 x FP8 GEMM) on --config at --M and print its line")
     args = ap.parse_args(argv)
@@ -415,6 +511,9 @@ def main(argv=None) -> int:
         return 2
 
     import synth
+    if args.crossover:
+        print(json.dumps({"crossover": crossover()}), flush=True)
+        return 0
     if args.w8a8:
         fmt, N, K, _ = synth.CONFIGS[args.config]
         if fmt != "fp8":

@@ -88,9 +88,11 @@ typedef enum { WQ_FMT_FP8_BLOCK = 0, WQ_FMT_LUT3 = 1, WQ_FMT_LUT3_DENSE = 2 } wq
 
 /* Kernel path for the GEMM.  AUTO follows the batch ladder of the atlas
  * "Module m16_tc" docs (section ARM ORDER) with the crossover measured on
- * MI355X (arc PR, "The threshold"): FP8 uses the strict-K-order GEMV for
- * M = 1 and the 16-row MFMA tile for M = 2..16 (the GEMV serves M <= 4 when
- * asked for explicitly); the LUT format uses the MFMA tile for every M = 1..16
+ * MI355X (arc PR, "The threshold": both arms swept on one binary): the 16-row
+ * MFMA tile serves every M = 1..16 for FP8 (it ties or beats the strict-K-order
+ * GEMV already at M = 1 on every decode shape, and the GEMV slows with each
+ * row; the GEMV serves M <= 4 when asked for explicitly); the LUT format uses
+ * the MFMA tile for every M = 1..16
  * (one mainloop across the decode band, as in the FLUTE PR's "Results").
  * M = 17..32 runs the MFMA tile on the two contiguous row halves 0..15 and
  * 16..M-1 ("ARM ORDER"): in one pass, each dequantised weight operand feeding

@@ -122,13 +122,21 @@ struct Plan {
     int n_tiles = 0, n_cg = 0, KB = 0;
 };
 
-// Largest M the automatic ladder sends to the FP8 GEMV.  Measured on MI355X
-// over the FFN and attention shapes: the strict-order FP32 GEMV is faster
-// than the MFMA tile at M = 1 (by 5-15%), about even at M = 2 and slower
-// from M = 3 on, where its FP32 FMAs (M per weight) outweigh the stream; the
-// MFMA tile's time does not change with M.  (The arc PR, "The threshold":
-// the crossover is a measured lever, not a constant of the method.)
-constexpr int64_t kGemvAutoMaxM = 1;
+// Largest M the automatic ladder sends to the FP8 GEMV: none.  Both arms
+// timed on one build (python bench.py --crossover; HIP graphs, weight copies
+// rotated past the Infinity Cache), M = 1 / 2 / 3 / 4 in us, GEMV vs MFMA
+// tile: FFN gate/up 16.8 / 21.2 / 27.0 / 32.9 vs 16.9 / 16.9 / 16.8 / 16.8;
+// FFN down 19.8 / 26.7 / 33.6 / 40.3 vs 19.1 / 19.2 / 19.2 / 19.5; attention
+// Q 9.3 / 10.6 / 12.4 / 14.3 vs 9.0 for every M; attention K/V 7.9 / 9.8 /
+// 11.7 / 13.4 vs 6.5 / 6.6.  The tile's time does not change with M, the
+// GEMV's FP32 FMAs grow with it, and at M = 1 the tile ties or wins (it also
+// takes the shape's K-split plan).  So the first M at which the GEMV beats
+// the better arm does not exist, and AUTO takes the tile for every M; the
+// GEMV stays selectable (WQ_PATH_GEMV, WQ_FORCE_PATH=gemv) for M <= 4, for
+// callers that want its strict K order.  (The arc PR, "The threshold": the
+// crossover is a measured lever, taken from a sweep of all arms on one
+// binary, not a constant of the method.)
+constexpr int64_t kGemvAutoMaxM = 0;
 
 // Tilings measured fastest on MI355X (256 CUs) for the decode shapes of the
 // FFN and attention projections (per-shape dispatch, as in the FLUTE PR's
