@@ -425,7 +425,7 @@ def crossover() -> dict:
         out["gemv_vs_mfma"][name] = row
         if name in ("gate_up", "down"):
             r2 = {}
-            for M in (16, 32, 64, 128):
+            for M in (16, 32, 48, 64, 96, 128):
                 x = torch.from_numpy(synth.x_bf16(M, K, synth.SEEDS[name] + 100).view(np.int16)).to(dev).view(
                     torch.bfloat16)
                 y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -582,7 +582,7 @@ def main(argv=None) -> int:
             extra["%s_M%d" % (name, M)] = time_extra(name, M, args.steps, args.warmup, args.eager)
         if args.all:
             for name in ("gate_up", "down"):
-                for M in (256, 512, 2048, 4096):
+                for M in (64, 128, 256, 512, 2048, 4096):
                     print("bench: w8a8 %s M=%d" % (name, M), file=sys.stderr, flush=True)
                     extra["w8a8_%s_M%d" % (name, M)] = time_w8a8(name, M)
         out["extra"] = extra

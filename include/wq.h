@@ -148,6 +148,19 @@ wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu);
  * machine's slots). */
 wq_status wq_set_kparts(int kp);
 
+/* Tuning and test hook: the LDS pipeline depth of later wq_gemm_fp8_w8a8
+ * calls -- 2 (one K block in flight per work-group, two work-groups per CU)
+ * or 4 (three in flight, one work-group per CU; the 128 x 128 tile only, the
+ * 256 x 256 tile of M > 4096 keeps 2) -- or 0 for the automatic choice (4
+ * where the grid has at most one work-group per CU).  The depth changes no
+ * arithmetic: outputs are bitwise the same at either.  Returns WQ_ERR_SHAPE
+ * for any other value.  Same thread rule as wq_set_tuning.
+ * Source: atlas docs "Module m16_tc", ARM ORDER rung 6 (the W8A8 prefill
+ * rung) and struct M16TcLevers (levers resolved once); arc PR "fix(ArcKernels):
+ * FP8 bank conflict + the dispatch threshold's provenance", "The threshold"
+ * (every arm selectable on one binary). */
+wq_status wq_set_w8a8_stages(int stages);
+
 /* ------------------------------------------------------------ FP8 block */
 
 /* Bytes of the packed FP8 matrix: N*K code bytes + 4*(N/128)*(K/128) scale
@@ -312,7 +325,10 @@ wq_status wq_gemm_lut3_dense(const void* packed, int64_t N, int64_t K,
  * nearest-even of clamp(x/s, -448, 448) with x/s in binary32 -- the rule of
  * the weights' block quantiser.  A group holding an infinity or a NaN gets
  * a NaN scale and the E4M3 NaN code 0x7F for all its values, so every output
- * of that row is NaN (the weight-only paths give NaN or an infinity there). */
+ * of that row is NaN (the weight-only paths give NaN or an infinity there).
+ *
+ * Measured on MI355X at the FFN sizes, quantiser + GEMM with the workspace
+ * overtake the decode GEMM run as 32-row calls from M = 48 on. */
 
 /* Workspace bytes of a W8A8 GEMM of this M, N, K that splits K across
  * work-groups (kp * M * N * 4 for kp parts, following wq_set_kparts); 0 when

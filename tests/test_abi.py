@@ -86,6 +86,14 @@ def test_kparts_hook_validates():
         wq.wq_set_kparts(kp)
 
 
+def test_w8a8_stages_hook_validates():
+    for bad in (-1, 1, 3, 5, 8):
+        with pytest.raises(wq.WqError):
+            wq.wq_set_w8a8_stages(bad)
+    for ns in (0, 2, 4, 0):
+        wq.wq_set_w8a8_stages(ns)
+
+
 def test_sizes_are_host_arithmetic():
     assert wq.wq_packed_format_version() == 3
     assert wq.wq_fp8_block_packed_bytes(17408, 5120) == 17408 * 5120 + 4 * 136 * 40

@@ -9,6 +9,9 @@
   the FFN gate/up size; integer-exact inputs give exact results; rows are
   independent of M, results deterministic, y's padding untouched, HIP-graph
   replays equal the eager result;
+* LDS pipeline depth: two and four stages give bitwise equal outputs, and at
+  the FFN sizes small-M calls (four stages) equal the first rows of an
+  M = 2048 call (two stages);
 * K split across work-groups (a workspace passed): forced part counts against
   the oracle (NaN-filled workspace), the automatic split of the FFN down
   projection, workspace errors, determinism and graph replay.
@@ -263,6 +266,55 @@ def test_w8a8_gate_up_size(M):
     check_w8a8(r)
 
 
+# ------------------------------------------------------------ pipeline depth
+
+@pytest.fixture
+def stages_reset():
+    yield
+    U.wqmod().wq_set_w8a8_stages(0)
+    U.wqmod().wq_set_kparts(0)
+
+
+@pytest.mark.parametrize("N,K,M,kp", [(256, 512, 1, 0), (384, 1024, 16, 0), (640, 2048, 130, 0),
+                                      (1280, 512, 1030, 0), (384, 1024, 700, 3), (640, 2048, 33, 5)])
+def test_w8a8_pipeline_depths_agree(N, K, M, kp, stages_reset):
+    """Two and four LDS stages run the same arithmetic: bitwise equal outputs
+    (with and without K parts), and the automatic choice agrees with both."""
+    wq = U.wqmod()
+    U.note("w8a8 stages N=%d K=%d M=%d kp=%d" % (N, K, M, kp))
+    codes, scales = synth.fp8_weights(N, K, 1600 + N + K)
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(M, K, 1700 + M)
+    xq, xc, xs = quantize(xb, K)
+    wq.wq_set_kparts(kp)
+    out = {}
+    for ns in (2, 4, 0):
+        wq.wq_set_w8a8_stages(ns)
+        out[ns] = run(packed, N, K, xq, M, ws="auto" if kp else None)[0]
+    assert np.array_equal(out[2], out[4]) and np.array_equal(out[0], out[2])
+    y64 = oracle.gemm_w8a8(xc, xs, codes, scales)
+    check_w8a8(compare.grade(out[4], y64, floor_w8a8(xc, xs, codes, scales, K), "bf16"))
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_w8a8_small_grid_rows_equal_large_grid(name, stages_reset):
+    """At the FFN sizes a small M runs the four-stage pipeline (at most one
+    work-group per CU) and M = 2048 the two-stage one; rows depend only on
+    their own activations, so the small calls equal the first rows of the
+    large one bit for bit."""
+    fmt, N, K, Ms, (codes, scales) = U.config_inputs(name)
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(2048, K, 1801)
+    xq, _, _ = quantize(xb, K)
+    U.note("w8a8 %s M=2048 (two stages)" % name)
+    ybig, _ = run(packed, N, K, xq, 2048)
+    for M in (48, 128):
+        U.note("w8a8 %s M=%d (four stages)" % (name, M))
+        xq2, _, _ = quantize(xb[:M], K)
+        y, _ = run(packed, N, K, xq2, M)
+        assert np.array_equal(y, ybig[:M]), M
+
+
 # ---------------------------------------------------------- K parts (workspace)
 
 @pytest.fixture
@@ -290,15 +342,17 @@ def test_w8a8_parts_match_oracle(N, K, M, kp, kparts_reset):
         assert np.array_equal(run(packed, N, K, xq, M, ws="auto")[0], y)
 
 
-def test_w8a8_down_splits_k(kparts_reset):
-    """FFN down 5120 x 17408 at M = 256: the automatic plan splits K in 3 parts
-    (sampled columns against the oracle)."""
+@pytest.mark.parametrize("name,M,kp", [("down", 256, 3), ("down", 64, 6), ("gate_up", 64, 3)])
+def test_w8a8_automatic_split(name, M, kp, kparts_reset):
+    """The automatic plan at the FFN sizes: FFN down at M = 256 in 3 K parts
+    (80 tiles, one work-group per CU), at M = 64 in 6 (40 tiles); gate/up at
+    M = 64 in 3 (136 tiles, two work-groups per CU) and with K whole from
+    M = 256 on (sampled columns against the oracle)."""
     wq = U.wqmod()
-    fmt, N, K, Ms, (codes, scales) = U.config_inputs("down")
-    M = 256
-    assert wq.wq_w8a8_workspace_bytes(M, N, K) == 3 * M * N * 4
-    assert wq.wq_w8a8_workspace_bytes(M, 17408, 5120) == 0        # gate/up keeps K whole
-    U.note("w8a8 down M=%d with a workspace" % M)
+    fmt, N, K, Ms, (codes, scales) = U.config_inputs(name)
+    assert wq.wq_w8a8_workspace_bytes(M, N, K) == kp * M * N * 4
+    assert wq.wq_w8a8_workspace_bytes(256, 17408, 5120) == 0        # gate/up keeps K whole
+    U.note("w8a8 %s M=%d with a workspace (%d parts)" % (name, M, kp))
     packed = U.pack_fp8(codes, scales)
     xb = synth.x_bf16(M, K, 1601)
     xq, xc, xs = quantize(xb, K)

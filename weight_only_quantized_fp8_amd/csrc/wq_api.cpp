@@ -27,6 +27,7 @@ struct Options {
     int split = 0;           // 0 = per-shape choice
     int waves_per_cu = 4;    // target resident waves per compute unit
     int kp = 0;              // K parts across work-groups with a workspace; 0 = per-shape choice
+    int w8a8_stages = 0;     // W8A8 LDS pipeline depth (2 or 4); 0 = per-grid choice
 };
 
 Options g_opts;
@@ -482,6 +483,15 @@ wq_status wq_set_kparts(int kp)
     return WQ_OK;
 }
 
+wq_status wq_set_w8a8_stages(int stages)
+{
+    if (stages != 0 && stages != 2 && stages != 4) return WQ_ERR_SHAPE;
+    options();
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    g_opts.w8a8_stages = stages;
+    return WQ_OK;
+}
+
 size_t wq_fp8_block_packed_bytes(int64_t N, int64_t K)
 {
     if (!shape_ok(WQ_FMT_FP8_BLOCK, N, K)) return 0;
@@ -623,16 +633,25 @@ wq_status wq_unpack_lut3_dense(const void* packed, int64_t N, int64_t K, uint16_
 
 namespace {
 
-// K blocks per W8A8 K part of the automatic rule.
+// K blocks per W8A8 K part of the automatic rule for grids of more than one
+// 128 x 128 tile per CU, and the fewest K blocks a part keeps for smaller ones.
 constexpr int kW8PartBlocks = 40;
+constexpr int kW8MinPartBlocks = 12;
 
-// K parts of a W8A8 call that brings a workspace: the wq_set_kparts value, or,
-// when the 128 x 128 output tiles give fewer than 4 work-groups per CU, one part per
-// kW8PartBlocks K blocks, but no more parts than bring the grid to 4
-// work-groups per CU.  Measured on MI355X (GEMM + parts sum): FFN down
-// 5120 x 17408 at M = 256 / 512 / 1024 / 2048 runs 116 / 118 / 143 / 239 us
-// in one part and 51 / 74 / 124 / 224 us in 3, 3, 3 and 2 parts; gate/up
-// (K = 5120) is fastest in one part at every M.
+// K parts of a W8A8 call that brings a workspace: the wq_set_kparts value, or:
+// - at most one 128 x 128 output tile per CU: the part count that best fills
+//   the work-group slots (one per CU for grids the four-stage pipeline runs,
+//   two per CU for the two-stage one), each part keeping at least
+//   kW8MinPartBlocks K blocks; a larger count must fill 5% more slots.
+//   Measured on MI355X (GEMM + parts sum, M = 32 / 64 / 128): FFN down
+//   (40 tiles) 99.8 / 101.4 / 102.0 us in one part, 26.7 / 29.1 / 31.2 in 6;
+//   gate/up (136 tiles) 34.1 / 36.0 / 36.8 in one part, 25.0 / 29.4 / 36.0
+//   in 3;
+// - below 4 tiles per CU: one part per kW8PartBlocks K blocks, but no more
+//   parts than bring the grid to 4 work-groups per CU.  Measured: FFN down at
+//   M = 256 / 512 / 1024 / 2048 runs 116 / 118 / 143 / 239 us in one part and
+//   51 / 74 / 124 / 224 us in 3, 3, 3 and 2 parts; gate/up (K = 5120) is
+//   fastest in one part from M = 256 on.
 int w8a8_kparts(int64_t M, int64_t N, int64_t K, int cu)
 {
     int forced;
@@ -647,8 +666,20 @@ int w8a8_kparts(int64_t M, int64_t N, int64_t K, int cu)
         const int64_t mpad = (M + 15) / 16 * 16;
         const int64_t e = wq::w8a8_tile_edge((int)mpad);
         const int64_t tiles = (mpad + e - 1) / e * ((N + e - 1) / e);
-        if (e == 128 && tiles < 4 * cu)   // the 256 x 256 tile (M > 4096) keeps K whole
+        if (e == 128 && tiles <= cu) {
+            double best = (double)tiles / cu;
+            for (int k = 2; k <= KB / kW8MinPartBlocks && k <= wq::kMaxKParts; ++k) {
+                const int64_t n = tiles * k;
+                if (n > 2 * (int64_t)cu) break;
+                const double fill = n <= cu ? (double)n / cu : (double)n / (2.0 * cu);
+                if (fill > best + 0.05) {
+                    best = fill;
+                    kp = k;
+                }
+            }
+        } else if (e == 128 && tiles < 4 * cu) {   // the 256 x 256 tile (M > 4096) keeps K whole
             kp = (int)std::min<int64_t>(KB / kW8PartBlocks, (4 * cu + tiles - 1) / tiles);
+        }
     }
     return std::max(1, std::min(kp, std::min(KB, wq::kMaxKParts)));
 }
@@ -707,12 +738,17 @@ wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void*
     if (st != WQ_OK) return st;
     // with a workspace, K may be split across work-groups (FP32 partials there)
     const int kp = workspace ? w8a8_kparts(M, N, K, dev.cu) : 1;
+    int stages;
+    {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        stages = g_opts.w8a8_stages;
+    }
     if (kp > 1) {
         if (workspace_bytes < w8a8_workspace_bytes(M, N, kp)) return WQ_ERR_WORKSPACE;
         if (!aligned16(workspace)) return WQ_ERR_ALIGN;
     }
     return wq::launch_w8a8(static_cast<const uint8_t*>(packed), (int)N, (int)K, static_cast<const uint8_t*>(xq),
-                           (int)M, y, ldy, kp, kp > 1 ? static_cast<float*>(workspace) : nullptr,
+                           (int)M, y, ldy, kp, kp > 1 ? static_cast<float*>(workspace) : nullptr, dev.cu, stages,
                            static_cast<hipStream_t>(hip_stream)) == hipSuccess
                ? WQ_OK
                : WQ_ERR_HIP;

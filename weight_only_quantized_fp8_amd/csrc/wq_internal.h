@@ -149,9 +149,11 @@ hipError_t launch_unpack_lut3(const uint8_t* packed, int64_t N, int64_t K, uint1
 hipError_t launch_quantize_x(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* xq, hipStream_t stream);
 hipError_t launch_unpack_x(const uint8_t* xq, int M, int K, uint8_t* codes, float* scales, hipStream_t stream);
 // kp > 1: K split into kp parts across work-groups, FP32 partials in ws [kp][M][N]
-// summed in order into y by launch_sum_parts
+// summed in order into y by launch_sum_parts; cu: the device's compute units;
+// stages: the LDS pipeline depth (2 or 4), 0 = 4 where the grid has at most
+// one work-group per CU
 hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
-                       int kp, float* ws, hipStream_t stream);
+                       int kp, float* ws, int cu, int stages, hipStream_t stream);
 
 // y[m][n] = the parts ws[p][m][n] (p = 0 .. kp-1, [kp][rows][N] FP32) added in
 // order and rounded once (RNE) to BF16, or FP16 with f16_out; N % 16 == 0.

@@ -189,9 +189,14 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until no vector-memory operation and no LDS access of this wave is
-// outstanding (vmcnt = 0, lgkmcnt = 0; expcnt left at its maximum).
-__device__ __forceinline__ void wait_vmcnt_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(7 << 4); }
+// Wait until at most N vector-memory operations and no LDS access of this
+// wave are outstanding (lgkmcnt = 0; expcnt left at its maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkmcnt0()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
 // LDS address dst + 16 l (dst is wave-uniform; it goes to M0).  The data never
@@ -230,15 +235,19 @@ __device__ __forceinline__ void dma16(const RawBuf& r, uint32_t dst, uint32_t vo
 // Work-group tile BM x BN = (16 WMT WVM) x (16 WNT WVN): WVM x WVN waves, each
 // owning WMT x WNT MFMA tiles of 16 x 16.  A K block's operands (BM/16
 // activation units and BN/16 weight units of 2 KB) and the BM rows'
-// activation scales go from memory straight into one of two LDS stages
-// (buffer loads to LDS, no VGPR staging), one block ahead of the block being
-// multiplied.  Per block every wave waits for its own loads of that stage, the
-// work-group meets at one barrier (after which every wave's loads of the stage
-// have landed and every wave is done with the other stage), issues the loads
-// of block kb + 1 into the other stage, and runs its WMT x WNT MFMAs, each
-// folded onto the FP32 outer accumulators times sx[m][kb] * sw[nb][kb].  The
-// stages are separate LDS arrays and the loop is unrolled by two, so each read
-// names a fixed stage.
+// activation scales go from memory straight into one of NS LDS stages
+// (buffer loads to LDS, no VGPR staging), NS - 1 blocks ahead of the block
+// being multiplied.  Per block every wave waits for its own loads of that
+// stage (the later blocks' loads stay in flight), the work-group meets at one
+// barrier (after which every wave's loads of the stage have landed and every
+// wave is done with the stage it multiplied last), issues the loads of block
+// kb + NS - 1 into that stage, and runs its WMT x WNT MFMAs, each folded onto
+// the FP32 outer accumulators times sx[m][kb] * sw[nb][kb].  The stages are
+// separate LDS arrays and the loop is unrolled by NS, so each read names a
+// fixed stage.  NS = 2 lets two work-groups share a CU; NS = 4 (132 KB of LDS
+// at 128 x 128) serves grids of at most one work-group per CU, where a
+// work-group with one block in flight would wait out the memory latency on
+// every block.
 //
 // Work order: XCD x (work-groups b = x mod 8) takes the contiguous run
 // [x * per_xcd, (x+1) * per_xcd) of linear indices; these walk groups of GN
@@ -247,8 +256,8 @@ __device__ __forceinline__ void dma16(const RawBuf& r, uint32_t dst, uint32_t vo
 // that XCD's L2.  With kp K parts the part is the outermost index: work-group
 // (part, tile) multiplies the part-th of kp contiguous runs of K blocks and
 // stores its FP32 sums to the part's slab of the workspace.
-template <int WMT, int WNT, int WVM, int WVN, int GN>
-__global__ void __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int WMT, int WNT, int WVM, int WVN, int GN, int NS>
+__global__ void __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(NS == 2 ? 2 : 1, 2)))
 w8a8_gemm_kernel(W8Args a)
 {
     constexpr int WAVES = WVM * WVN;
@@ -260,8 +269,10 @@ w8a8_gemm_kernel(W8Args a)
     constexpr int SROWS = BM / WAVES;                   // scale rows each wave copies
     static_assert(2 * (TM + TN) % WAVES == 0 && SROWS % 4 == 0 && SROWS <= 256, "copy split");
     static_assert(WNT * 16 <= 128 && 128 % (WNT * 16) == 0, "a wave's columns share one weight scale block");
-    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+    static_assert(NS >= 2 && NS * STAGE <= kLdsBytes, "stages fit in LDS");
+    constexpr int LPS = CPW + 1;                        // loads a wave issues per stage (copies + scale row)
+    static_assert((NS - 2) * LPS < 64, "the loads of NS - 2 stages fit the vmcnt field");
+    __shared__ __attribute__((aligned(16))) uint8_t st[NS][STAGE];
 
     const int b = blockIdx.x;
     const int per_xcd = gridDim.x >> 3;                   // the grid is a multiple of 8
@@ -307,16 +318,19 @@ w8a8_gemm_kernel(W8Args a)
     const uint32_t svoff = srow < a.Mpad ? (uint32_t)srow * 4u : kBufOutOfRange;
 
     // LDS addresses of the stages (M0 operands), computed once
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(st0));
-    const uint32_t lds1 = __builtin_amdgcn_readfirstlane(lds_addr(st1));
-    auto issue = [&](int kb, uint32_t st) {
+    uint32_t lds_st[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) lds_st[s] = __builtin_amdgcn_readfirstlane(lds_addr(st[s]));
+    // the LPS loads of block kb into the stage at LDS address sa (every lane
+    // range is non-empty, so each wave issues every one of them)
+    auto issue = [&](int kb, uint32_t sa) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int c = wave + WAVES * i;
-            dma16(c < 2 * TM ? rx : rw, st + c * 1024, voff[i], (uint32_t)kb * 2048u);
+            dma16(c < 2 * TM ? rx : rw, sa + c * 1024, voff[i], (uint32_t)kb * 2048u);
         }
         if (lane < SROWS / 4)
-            dma16(rsx, st + OPS + SROWS * 4 * wave, svoff, (uint32_t)kb * (uint32_t)a.Mpad * 4u);
+            dma16(rsx, sa + OPS + SROWS * 4 * wave, svoff, (uint32_t)kb * (uint32_t)a.Mpad * 4u);
     };
 
     f32x4_t outer[WMT][WNT];
@@ -364,32 +378,37 @@ w8a8_gemm_kernel(W8Args a)
         }
     };
 
-    // one block: own loads of `cur` done, barrier, refill the other stage with
-    // block kb + 1 (the part's last block again at the end, so every wave
-    // always has the same loads in flight), multiply.
+    // one block: own loads of `cur` done (those of the NS - 2 later blocks may
+    // still be in flight: a wave's loads complete in order), barrier, refill
+    // the stage multiplied last with block kb + NS - 1 (the part's last block
+    // again near the end, so every wave always has the same loads in flight),
+    // multiply.
     // Ordering of the stage reuse: the loads that fill `nxt` overwrite what
     // every wave read from it in the previous block.  Before the barrier each
     // wave waits for its own loads into `cur` (vmcnt) and for its own LDS
-    // reads of `nxt` (lgkmcnt), and the workgroup-scope release/acquire
-    // fences keep the compiler from moving any LDS access across the
-    // barrier; so when a wave issues the refill after the barrier, every
-    // wave's reads of that stage have returned.
+    // reads (lgkmcnt), and the workgroup-scope release/acquire fences keep
+    // the compiler from moving any LDS access across the barrier; so when a
+    // wave issues the refill after the barrier, every wave's reads of that
+    // stage have returned.
     auto step = [&](int kb, const uint8_t* cur, uint32_t nxt) {
-        wait_vmcnt_lgkmcnt0();
+        wait_vmcnt_lgkmcnt0<(NS - 2) * LPS>();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        issue(kb + 1 < kbe ? kb + 1 : kbe - 1, nxt);
+        issue(min(kb + NS - 1, kbe - 1), nxt);
         compute(kb, cur);
     };
 
-    issue(kbb, lds0);
-    for (int kb = kbb;; kb += 2) {
-        step(kb, st0, lds1);
-        if (kb + 1 >= kbe) break;
-        step(kb + 1, st1, lds0);
-        if (kb + 2 >= kbe) break;
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(min(kbb + s, kbe - 1), lds_st[s]);
+    for (int kb = kbb;; kb += NS) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            step(kb + s, st[s], lds_st[(s + NS - 1) % NS]);
+            if (kb + s + 1 >= kbe) goto k_done;      // uniform: every wave leaves here
+        }
     }
+k_done:
     wait_vmcnt<0>();                                      // no load left writing LDS
 
     // D of a 16x16 tile: lane l holds rows 4(l/16)..+3 of column l%16
@@ -441,20 +460,32 @@ hipError_t launch_unpack_x(const uint8_t* xq, int M, int K, uint8_t* codes, floa
 // M = 8192; 128 x 64, 64 x 128 and 64 x 64 tiles are no faster at M = 256 ..
 // 2048 (K parts across work-groups serve the grids those would fill).
 
+// Pipeline depth: 4 stages where the grid has at most one work-group per CU
+// (measured on the FFN shapes at M = 32 .. 256: with 2 stages every K block
+// waits out the memory latency, ~0.85 us a block), else 2 (two work-groups
+// share a CU); stages = 2 or 4 forces one.
 template <int WMT, int WNT, int WVM, int WVN, int GN>
-static hipError_t launch_w8a8_tile(W8Args a, hipStream_t stream)
+static hipError_t launch_w8a8_tile(W8Args a, int cu, int stages, hipStream_t stream)
 {
     constexpr int BM = 16 * WMT * WVM, BN = 16 * WNT * WVN;
     a.n_mt = (a.Mpad + BM - 1) / BM;
     a.n_tw = a.n_mt * ((a.N + BN - 1) / BN);
     a.n_wg = a.n_tw * a.kp;
     const int grid = (a.n_wg + 7) & ~7;
-    hipLaunchKernelGGL((w8a8_gemm_kernel<WMT, WNT, WVM, WVN, GN>), dim3(grid), dim3(64 * WVM * WVN), 0, stream, a);
+    constexpr int kStage = (WMT * WVM + WNT * WVN) * 2048 + BM * 4;   // LDS bytes of one stage
+    if constexpr (4 * kStage <= kLdsBytes) {                          // the 128 x 128 tile
+        if (stages ? stages == 4 : a.n_wg <= cu) {
+            hipLaunchKernelGGL((w8a8_gemm_kernel<WMT, WNT, WVM, WVN, GN, 4>), dim3(grid), dim3(64 * WVM * WVN), 0,
+                               stream, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((w8a8_gemm_kernel<WMT, WNT, WVM, WVN, GN, 2>), dim3(grid), dim3(64 * WVM * WVN), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
-                       int kp, float* ws, hipStream_t stream)
+                       int kp, float* ws, int cu, int stages, hipStream_t stream)
 {
     if (kp < 1 || kp > K / 128 || kp > kMaxKParts || (kp > 1 && !ws)) return hipErrorInvalidValue;
     W8Args a{};
@@ -475,7 +506,8 @@ hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq,
         return p ? std::atoi(p) : 0;
     }();
     const bool big = forced ? forced == 256 : w8a8_tile_edge(a.Mpad) == 256;
-    hipError_t e = big ? launch_w8a8_tile<4, 8, 4, 2, 4>(a, stream) : launch_w8a8_tile<4, 4, 2, 2, 8>(a, stream);
+    hipError_t e = big ? launch_w8a8_tile<4, 8, 4, 2, 4>(a, cu, stages, stream)
+                       : launch_w8a8_tile<4, 4, 2, 2, 8>(a, cu, stages, stream);
     if (e != hipSuccess || kp == 1) return e;
     return launch_sum_parts(ws, kp, M, N, y, ldy, false, stream);
 }

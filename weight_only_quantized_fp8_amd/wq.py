@@ -14,7 +14,7 @@ import os
 __all__ = [
     "WqError", "LIB_PATH", "lib",
     "WQ_OK", "WQ_FMT_FP8_BLOCK", "WQ_FMT_LUT3", "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA",
-    "wq_status_str", "wq_packed_format_version", "wq_set_tuning", "wq_set_kparts",
+    "wq_status_str", "wq_packed_format_version", "wq_set_tuning", "wq_set_kparts", "wq_set_w8a8_stages",
     "wq_fp8_block_packed_bytes", "wq_pack_fp8_block", "wq_gemm_fp8_block", "wq_gemm_fp8_block_path",
     "wq_gemm_fp8_block_noalloc", "wq_noalloc_scratch_bytes", "WQ_ERR_SCRATCH",
     "wq_lut3_packed_bytes", "wq_pack_lut3", "wq_gemm_lut3",
@@ -49,6 +49,7 @@ _SIGS = {
     "wq_packed_format_version": (_INT, []),
     "wq_set_tuning": (_INT, [_INT, _INT, _INT, _INT]),
     "wq_set_kparts": (_INT, [_INT]),
+    "wq_set_w8a8_stages": (_INT, [_INT]),
     "wq_fp8_block_packed_bytes": (_SZ, [_I64, _I64]),
     "wq_pack_fp8_block": (_INT, [_P, _I64, _P, _I64, _I64, _P, _P]),
     "wq_gemm_fp8_block": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
@@ -132,6 +133,10 @@ def wq_set_tuning(nt: int = 0, sn: int = 0, split: int = 0, waves_per_cu: int = 
 
 def wq_set_kparts(kp: int = 0) -> None:
     _check(lib.wq_set_kparts(kp), "wq_set_kparts")
+
+
+def wq_set_w8a8_stages(stages: int = 0) -> None:
+    _check(lib.wq_set_w8a8_stages(stages), "wq_set_w8a8_stages")
 
 
 def wq_fp8_block_packed_bytes(N: int, K: int) -> int:
