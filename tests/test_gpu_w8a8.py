@@ -296,6 +296,28 @@ def test_w8a8_pipeline_depths_agree(N, K, M, kp, stages_reset):
     check_w8a8(compare.grade(out[4], y64, floor_w8a8(xc, xs, codes, scales, K), "bf16"))
 
 
+@pytest.mark.parametrize("M", [2048, 2049])
+def test_w8a8_depth_boundary(M, stages_reset):
+    """N = 2048: M = 2048 gives 16 x 16 = 256 work-groups, the most the
+    four-stage pipeline takes on a 256-CU part; M = 2049 gives 17 x 16 = 272
+    (two stages).  Both against the oracle on sampled columns, and equal to
+    the forced other depth."""
+    wq = U.wqmod()
+    N, K = 2048, 384
+    U.note("w8a8 depth boundary N=%d K=%d M=%d" % (N, K, M))
+    codes, scales = synth.fp8_weights(N, K, 1900)
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(M, K, 1901)
+    xq, xc, xs = quantize(xb, K)
+    y, _ = run(packed, N, K, xq, M)
+    for ns in (2, 4):
+        wq.wq_set_w8a8_stages(ns)
+        assert np.array_equal(run(packed, N, K, xq, M)[0], y), ns
+    cols = U.sample_cols(N, 68)
+    y64 = oracle.gemm_w8a8(xc, xs, codes, scales, cols=cols)
+    check_w8a8(compare.grade(y[:, cols], y64, floor_w8a8(xc, xs, codes, scales, K), "bf16"))
+
+
 @pytest.mark.parametrize("name", ["gate_up", "down"])
 def test_w8a8_small_grid_rows_equal_large_grid(name, stages_reset):
     """At the FFN sizes a small M runs the four-stage pipeline (at most one
