@@ -14,7 +14,9 @@ divided by the time per step (the pages count stored weight bytes: one byte an
 FP8 code, half a byte a nibble-packed 3-bit code, 3/8 a dense one, plus the
 scales).  The JSON line also carries the dominant kernel's roofline (bytes
 per launch over the mean launch duration, from HIP events on the library's
-stream), the CPU oracle timed on the host as a baseline, and an "extra" block
+stream), the CPU oracle timed on the host as a baseline (whose output also
+grades the timed steps' output element by element: "parity" in that object),
+and an "extra" block
 with the other M=16 target (3-bit LUT 28672 x 8192, both storage layouts), the
 FFN down projection at M = 16 and 32 and gate/up at M = 1 and 8 (--no-extra
 skips it; --all times every workload, M and the W8A8 tier).
@@ -450,11 +452,16 @@ def crossover() -> dict:
     return out
 
 
-def cpu_baseline(name: str, M: int, min_seconds: float = 10.0, max_reps: int = 500):
+def cpu_baseline(name: str, M: int, min_seconds: float = 10.0, max_reps: int = 500, gpu_bits=None):
     """The oracle as it stands, on the host cores, over the whole workload (all
     outputs), repeated until about min_seconds of CPU wall time (at least 3
-    passes); the median pass counts."""
+    passes); the median pass counts.  With gpu_bits (the GPU's output of the
+    same seeded workload as BF16/FP16 bits [M, N]) the oracle's output also
+    grades it, element by element under the library's rule (within 2 BF16 ULP
+    or the absolute floor): the receipt comes back as "parity"."""
+    import numpy as np
     import oracle
+    from oracle import compare
     import synth
     fmt, N, K, _ = synth.CONFIGS[name]
     seed = synth.SEEDS[name]
@@ -469,16 +476,32 @@ def cpu_baseline(name: str, M: int, min_seconds: float = 10.0, max_reps: int = 5
         run = lambda: oracle.gemm_lut3(x, codes, qmap, g, nthreads=threads)
     times = []
     start = time.perf_counter()
+    y64 = None
     while len(times) < max_reps and (time.perf_counter() - start < min_seconds or len(times) < 3):
         t0 = time.perf_counter()
-        run()
+        y64 = run()
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[len(times) // 2]
-    return {"value": weight_bytes(fmt, N, K) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "whole %s workload N=%d K=%d M=%d, all %d outputs; median of %d passes "
-                      "(%.1f s of CPU work in all), %.3f s each"
-                      % (name, N, K, M, M * N, len(times), sum(times), dt),
-            "seconds": dt}
+    res = {"value": weight_bytes(fmt, N, K) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": "whole %s workload N=%d K=%d M=%d, all %d outputs; median of %d passes "
+                     "(%.1f s of CPU work in all), %.3f s each"
+                     % (name, N, K, M, M * N, len(times), sum(times), dt),
+           "seconds": dt}
+    if gpu_bits is not None:
+        # floor inputs: max |x| and max |dequantised weight|, the weights in row chunks
+        if fmt == "fp8":
+            mx = float(np.abs(oracle.bf16_value(x)).max())
+            mw = max(float(np.nanmax(np.abs(oracle.dequant_fp8(codes[r:r + 2048], scales[r // 128:(r + 2048) // 128]))))
+                     for r in range(0, N, 2048))
+        else:
+            mx = float(np.abs(oracle.f16_value(x)).max())
+            mw = max(float(np.abs(oracle.dequant_lut3(codes[r:r + 2048], qmap, g[r:r + 2048])).max())
+                     for r in range(0, N, 2048))
+        rc = compare.grade(gpu_bits, y64, compare.abs_floor(K, mx, mw), "bf16" if fmt == "fp8" else "f16")
+        res["parity"] = {"ok": rc.ok, "n": rc.n, "fail": rc.n_fail, "max_ulp": rc.max_ulp,
+                         "over_2ulp": rc.n_over_budget, "max_err_over_floor": round(rc.max_err_over_floor, 4),
+                         "rel_rms": round(rc.rel_rms, 6), "sign_flips": rc.sign_flips}
+    return res
 
 
 def main(argv=None) -> int:
@@ -534,6 +557,10 @@ def main(argv=None) -> int:
     state_before = gpu_state()
     r = time_workload(w, args.steps, args.warmup, use_graph=not args.eager)
     state_after = gpu_state()
+    # the timed steps' output (bit-identical to the eager reference: checked
+    # by time_workload), graded against the oracle in the CPU-baseline leg
+    import numpy as np
+    gpu_bits = w.y.view(torch.int16).cpu().numpy().view(np.uint16)
     value = w.wbytes / (r["ms_per_step"] * 1e-3) / 1e9
     achieved = w.abytes / (r["launch_ms_mean"] * 1e-3) / 1e9
     key = "%s_M%d" % (args.config, args.M)
@@ -589,7 +616,7 @@ def main(argv=None) -> int:
 
     if not args.no_cpu:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cb = cpu_baseline(args.config, args.M)
+        cb = cpu_baseline(args.config, args.M, gpu_bits=gpu_bits)
         out["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cb.items()
                                if k != "seconds"}
     print(json.dumps(out), flush=True)

@@ -38,3 +38,25 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr + r.stdout
+
+
+def test_cpu_baseline_grades_the_gpu_output():
+    """The CPU-baseline leg grades the timed workload's output against the
+    oracle's: the oracle's own RNE result passes with 0 ULP, and one output
+    moved far beyond both criteria fails (tiny config, no GPU needed)."""
+    import numpy as np
+    import oracle
+    import synth
+    fmt, N, K, Ms = synth.CONFIGS["tiny"]
+    M = Ms[0]
+    codes, scales = synth.fp8_weights(N, K, synth.SEEDS["tiny"])
+    x = synth.x_bf16(M, K, synth.SEEDS["tiny"] + 100)
+    good = oracle.bf16_rne(oracle.gemm_fp8(x, codes, scales))
+    r = bench.cpu_baseline("tiny", M, min_seconds=0.0, gpu_bits=good)
+    assert r["kind"] == "oracle" and r["parity"]["ok"] and r["parity"]["max_ulp"] == 0
+    assert r["parity"]["n"] == M * N and r["parity"]["fail"] == 0
+    bad = good.copy()
+    moved = float(oracle.bf16_value(good[:1, 7:8])[0, 0]) + 100.0
+    bad[0, 7] = oracle.bf16_rne(np.array([[moved]]))[0, 0]
+    r = bench.cpu_baseline("tiny", M, min_seconds=0.0, gpu_bits=bad)
+    assert not r["parity"]["ok"] and r["parity"]["fail"] == 1
