@@ -638,50 +638,106 @@ namespace {
 constexpr int kW8PartBlocks = 40;
 constexpr int kW8MinPartBlocks = 12;
 
-// K parts of a W8A8 call that brings a workspace: the wq_set_kparts value, or:
-// - at most one 128 x 128 output tile per CU: the part count that best fills
-//   the work-group slots (one per CU for grids the four-stage pipeline runs,
-//   two per CU for the two-stage one), each part keeping at least
-//   kW8MinPartBlocks K blocks; a larger count must fill 5% more slots.
-//   Measured on MI355X (GEMM + parts sum, M = 32 / 64 / 128): FFN down
-//   (40 tiles) 99.8 / 101.4 / 102.0 us in one part, 26.7 / 29.1 / 31.2 in 6;
-//   gate/up (136 tiles) 34.1 / 36.0 / 36.8 in one part, 25.0 / 29.4 / 36.0
-//   in 3;
-// - below 4 tiles per CU: one part per kW8PartBlocks K blocks, but no more
-//   parts than bring the grid to 4 work-groups per CU.  Measured: FFN down at
-//   M = 256 / 512 / 1024 / 2048 runs 116 / 118 / 143 / 239 us in one part and
-//   51 / 74 / 124 / 224 us in 3, 3, 3 and 2 parts; gate/up (K = 5120) is
-//   fastest in one part from M = 256 on.
-int w8a8_kparts(int64_t M, int64_t N, int64_t K, int cu)
+struct W8Plan {
+    int tile;   // wq::W8Tile
+    int kp;     // K parts across work-groups
+};
+
+// WQ_W8A8_TILE = 128 | 256 | 64 (64 x 128) | 6464 (64 x 64): one tile for
+// every M (sweeps); read once.
+int forced_w8a8_tile()
 {
-    int forced;
+    static const int t = [] {
+        const char* p = std::getenv("WQ_W8A8_TILE");
+        const int v = p ? std::atoi(p) : 0;
+        return v == 128 ? wq::W8_T128 : v == 256 ? wq::W8_T256 : v == 64 ? wq::W8_T64x128
+                                                   : v == 6464 ? wq::W8_T64x64 : -1;
+    }();
+    return t;
+}
+
+// Tile and K parts of a W8A8 call (ws: the call brings a workspace, so K may
+// be split across work-groups; the wq_set_kparts value forces the count):
+// - the tile: 64 x 128 or 64 x 64 for Mpad <= 64, 128 x 128 up to kW8BigM
+//   rows, 256 x 256 above (see the launcher);
+// - where the grid has at most one tile per CU, or the tile has 64 rows:
+//   among the candidate tiles and part counts (each part keeping at least
+//   kW8MinPartBlocks K blocks), the pair that best fills the work-group slots
+//   -- one per CU for a grid the four-stage pipeline runs, two per CU for the
+//   two-stage one; a pair must fill 5% more slots than the best so far, or
+//   as many with fewer parts, and ties go to the larger tile.  Measured on
+//   MI355X (GEMM + parts sum, M = 16 / 32 / 48 / 64, quantised activations
+//   prepared): FFN down takes 64 x 64 in 3 parts, 21.9 / 22.4 / 22.9 /
+//   23.9 us (128 x 128 in 6 parts: 25.9 / 26.6 / 27.7 / 29.4; in one part
+//   ~100); gate/up takes 64 x 128 in 3 parts, 22.2 / 23.5 / 25.7 / 27.5 us
+//   (128 x 128 in 3 parts: 23.3 / 25.2 / 27.1 / 29.5).  At M = 96 / 128 the
+//   128 x 128 tile: down 6 parts 30.8 / 32.9 us, gate/up 3 parts 33.0 /
+//   36.5;
+// - a 128 x 128 grid of 1 to 4 tiles per CU: one part per kW8PartBlocks K
+//   blocks, but no more parts than bring the grid to 4 work-groups per CU.
+//   Measured: FFN down at M = 256 / 512 / 1024 / 2048 runs 116 / 118 / 143 /
+//   239 us in one part and 51 / 74 / 124 / 224 us in 3, 3, 3 and 2 parts;
+//   gate/up (K = 5120) is fastest in one part from M = 256 on;
+// - the 256 x 256 tile keeps K whole.
+W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
+{
+    int forced_kp;
     {
         std::lock_guard<std::mutex> lk(g_plan_mu);
-        forced = g_opts.kp;
+        forced_kp = g_opts.kp;
     }
     const int KB = (int)(K / 128);
-    int kp = 1;
-    if (forced) kp = forced;
-    else {
-        const int64_t mpad = (M + 15) / 16 * 16;
-        const int64_t e = wq::w8a8_tile_edge((int)mpad);
-        const int64_t tiles = (mpad + e - 1) / e * ((N + e - 1) / e);
-        if (e == 128 && tiles <= cu) {
-            double best = (double)tiles / cu;
-            for (int k = 2; k <= KB / kW8MinPartBlocks && k <= wq::kMaxKParts; ++k) {
-                const int64_t n = tiles * k;
-                if (n > 2 * (int64_t)cu) break;
-                const double fill = n <= cu ? (double)n / cu : (double)n / (2.0 * cu);
-                if (fill > best + 0.05) {
-                    best = fill;
-                    kp = k;
-                }
+    const int max_kp = std::max(1, std::min(KB, wq::kMaxKParts));
+    const int64_t mpad = (M + 15) / 16 * 16;
+    int cand[2], nc = 0;
+    if (forced_w8a8_tile() >= 0) cand[nc++] = forced_w8a8_tile();
+    else if (mpad <= 64) {
+        cand[nc++] = wq::W8_T64x128;
+        cand[nc++] = wq::W8_T64x64;
+    } else cand[nc++] = mpad > wq::kW8BigM ? wq::W8_T256 : wq::W8_T128;
+    auto tiles = [&](int t) {
+        const int r = wq::w8_tile_rows(t), c = wq::w8_tile_cols(t);
+        return (mpad + r - 1) / r * ((N + c - 1) / c);
+    };
+    auto fill = [&](int64_t n) {   // share of the work-group slots a grid of n fills
+        return n <= cu ? (double)n / cu : n <= 2 * (int64_t)cu ? (double)n / (2.0 * cu) : 0.0;
+    };
+    W8Plan best{cand[0], 1};
+    if (!ws || forced_kp) {                          // the part count is given: the tile that fills best
+        const int kp = ws ? std::min(forced_kp, max_kp) : 1;
+        double bf = -1.0;
+        for (int i = 0; i < nc; ++i) {
+            const int64_t n = tiles(cand[i]) * kp;
+            const double f = n <= 2 * (int64_t)cu ? fill(n) : 1.0;
+            if (f > bf + 1e-9) {
+                bf = f;
+                best = {cand[i], kp};
             }
-        } else if (e == 128 && tiles < 4 * cu) {   // the 256 x 256 tile (M > 4096) keeps K whole
-            kp = (int)std::min<int64_t>(KB / kW8PartBlocks, (4 * cu + tiles - 1) / tiles);
+        }
+        return best;
+    }
+    if (cand[0] == wq::W8_T256) return best;
+    const int64_t t0 = tiles(cand[0]);
+    if (cand[0] == wq::W8_T128 && t0 > cu) {         // 1 to 4 tiles per CU
+        if (t0 < 4 * (int64_t)cu)
+            best.kp = std::max(1, (int)std::min<int64_t>({(int64_t)KB / kW8PartBlocks, (4 * cu + t0 - 1) / t0,
+                                                          (int64_t)max_kp}));
+        return best;
+    }
+    double bf = fill(t0);
+    for (int i = 0; i < nc; ++i) {
+        const int64_t nt = tiles(cand[i]);
+        for (int k = 1; k <= std::min(max_kp, std::max(1, KB / kW8MinPartBlocks)); ++k) {
+            const int64_t n = nt * k;
+            if (n > 2 * (int64_t)cu) break;
+            const double f = fill(n);
+            if (f > bf + 0.05 || (f >= bf - 0.05 && k < best.kp)) {
+                bf = std::max(bf, f);
+                best = {cand[i], k};
+            }
         }
     }
-    return std::max(1, std::min(kp, std::min(KB, wq::kMaxKParts)));
+    return best;
 }
 
 size_t w8a8_workspace_bytes(int64_t M, int64_t N, int kp) { return kp > 1 ? (size_t)kp * M * N * 4 : 0; }
@@ -695,7 +751,7 @@ size_t wq_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K)
     if (M <= 0 || !shape_ok(WQ_FMT_FP8_BLOCK, N, K) || !wq_x_fp8_packed_bytes(M, K)) return 0;
     DevInfo dev;
     if (current_device(&dev) != WQ_OK) return 0;
-    return w8a8_workspace_bytes(M, N, w8a8_kparts(M, N, K, dev.cu));
+    return w8a8_workspace_bytes(M, N, w8a8_plan(M, N, K, dev.cu, true).kp);
 }
 
 size_t wq_x_fp8_packed_bytes(int64_t M, int64_t K)
@@ -737,7 +793,8 @@ wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void*
     wq_status st = current_device(&dev);
     if (st != WQ_OK) return st;
     // with a workspace, K may be split across work-groups (FP32 partials there)
-    const int kp = workspace ? w8a8_kparts(M, N, K, dev.cu) : 1;
+    const W8Plan plan = w8a8_plan(M, N, K, dev.cu, workspace != nullptr);
+    const int kp = plan.kp;
     int stages;
     {
         std::lock_guard<std::mutex> lk(g_plan_mu);
@@ -748,7 +805,8 @@ wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void*
         if (!aligned16(workspace)) return WQ_ERR_ALIGN;
     }
     return wq::launch_w8a8(static_cast<const uint8_t*>(packed), (int)N, (int)K, static_cast<const uint8_t*>(xq),
-                           (int)M, y, ldy, kp, kp > 1 ? static_cast<float*>(workspace) : nullptr, dev.cu, stages,
+                           (int)M, y, ldy, plan.tile, kp, kp > 1 ? static_cast<float*>(workspace) : nullptr, dev.cu,
+                           stages,
                            static_cast<hipStream_t>(hip_stream)) == hipSuccess
                ? WQ_OK
                : WQ_ERR_HIP;

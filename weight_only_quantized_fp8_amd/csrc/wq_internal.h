@@ -148,12 +148,22 @@ hipError_t launch_unpack_lut3(const uint8_t* packed, int64_t N, int64_t K, uint1
 // layout, its test-hook inverse, and the FP8 x FP8 GEMM on packed FP8 weights.
 hipError_t launch_quantize_x(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* xq, hipStream_t stream);
 hipError_t launch_unpack_x(const uint8_t* xq, int M, int K, uint8_t* codes, float* scales, hipStream_t stream);
-// kp > 1: K split into kp parts across work-groups, FP32 partials in ws [kp][M][N]
-// summed in order into y by launch_sum_parts; cu: the device's compute units;
-// stages: the LDS pipeline depth (2 or 4), 0 = 4 where the grid has at most
-// one work-group per CU
+// W8A8 work-group tiles (rows x columns of output)
+enum W8Tile : int {
+    W8_T128 = 0,      // 128 x 128: 4 waves of 64 x 64
+    W8_T256 = 1,      // 256 x 256: 8 waves of 64 x 128
+    W8_T64x128 = 2,   // 64 x 128: 4 waves of 64 x 32
+    W8_T64x64 = 3,    // 64 x 64: 4 waves of 32 x 32
+};
+constexpr int w8_tile_rows(int t) { return t == W8_T256 ? 256 : t == W8_T128 ? 128 : 64; }
+constexpr int w8_tile_cols(int t) { return t == W8_T256 ? 256 : t == W8_T64x64 ? 64 : 128; }
+
+// tile: a W8Tile; kp > 1: K split into kp parts across work-groups, FP32
+// partials in ws [kp][M][N] summed in order into y by launch_sum_parts; cu:
+// the device's compute units; stages: the LDS pipeline depth (2 or 4), 0 = 4
+// where the grid has at most one work-group per CU
 hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
-                       int kp, float* ws, int cu, int stages, hipStream_t stream);
+                       int tile, int kp, float* ws, int cu, int stages, hipStream_t stream);
 
 // y[m][n] = the parts ws[p][m][n] (p = 0 .. kp-1, [kp][rows][N] FP32) added in
 // order and rounded once (RNE) to BF16, or FP16 with f16_out; N % 16 == 0.
@@ -169,9 +179,7 @@ constexpr size_t kScratchBytes = (size_t)4 << 20;
 // current device's index); looked up once per device, with it current.
 hipError_t scratch_address(int dev, void** out);
 
-// W8A8 work-group tile edge (rows and columns) for an M (the launcher's own
-// choice; a K-split plan counts its tiles with it)
+// Above this many (padded) rows the W8A8 GEMM takes the 256 x 256 tile
 constexpr int kW8BigM = 4096;
-constexpr int w8a8_tile_edge(int Mpad) { return Mpad > kW8BigM ? 256 : 128; }
 
 }  // namespace wq

@@ -27,8 +27,6 @@
 // and zero scales.  A weight unit and an activation unit of the same K block
 // therefore put the same k in the same (lane group, byte) slot, which is all
 // the matrix core needs: it sums over the slots.
-#include <cstdlib>
-
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
@@ -452,13 +450,16 @@ hipError_t launch_unpack_x(const uint8_t* xq, int M, int K, uint8_t* codes, floa
     return hipGetLastError();
 }
 
-// Tile per M (w8a8_tile_edge): 128 x 128 (4 waves of 64 x 64, two
-// work-groups per CU) up to kW8BigM rows, 256 x 256 above (8 waves of
-// 64 x 128: twice the MFMAs per byte read from LDS, one work-group per CU).
-// Measured on the FFN shapes: the smaller tile is as fast or faster up to
-// M = 4096 (more work-groups, two per CU), the larger one slightly faster at
-// M = 8192; 128 x 64, 64 x 128 and 64 x 64 tiles are no faster at M = 256 ..
-// 2048 (K parts across work-groups serve the grids those would fill).
+// Tiles (the host picks one per call, with the K-part count): 128 x 128 (4
+// waves of 64 x 64, two work-groups per CU) for 64 < Mpad <= kW8BigM,
+// 256 x 256 above (8 waves of 64 x 128: twice the MFMAs per byte read from
+// LDS, one work-group per CU), and for Mpad <= 64 a 64-row tile: 64 x 128
+// (4 waves of 64 x 32) or 64 x 64 (4 waves of 32 x 32), whichever fills
+// the work-group slots better.  Measured on the FFN shapes: the 128 x 128
+// tile is as fast or faster than 128 x 64, 64 x 128 and 64 x 64 from M = 96
+// to 4096, the 256 x 256 one slightly faster at M = 8192; at M <= 64 the
+// 64-row tiles are 1-5 us faster (the 128-row tile fetches, stages and
+// multiplies padding rows).
 
 // Pipeline depth: 4 stages where the grid has at most one work-group per CU
 // (measured on the FFN shapes at M = 32 .. 256: with 2 stages every K block
@@ -485,7 +486,7 @@ static hipError_t launch_w8a8_tile(W8Args a, int cu, int stages, hipStream_t str
 }
 
 hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
-                       int kp, float* ws, int cu, int stages, hipStream_t stream)
+                       int tile, int kp, float* ws, int cu, int stages, hipStream_t stream)
 {
     if (kp < 1 || kp > K / 128 || kp > kMaxKParts || (kp > 1 && !ws)) return hipErrorInvalidValue;
     W8Args a{};
@@ -501,13 +502,14 @@ hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq,
     a.sx = reinterpret_cast<const float*>(xq + (int64_t)a.Mpad * K);
     a.y = y;
     a.ldy = ldy;
-    static const int forced = [] {          // WQ_W8A8_TILE=128|256: one tile for every M (sweeps)
-        const char* p = std::getenv("WQ_W8A8_TILE");
-        return p ? std::atoi(p) : 0;
-    }();
-    const bool big = forced ? forced == 256 : w8a8_tile_edge(a.Mpad) == 256;
-    hipError_t e = big ? launch_w8a8_tile<4, 8, 4, 2, 4>(a, cu, stages, stream)
-                       : launch_w8a8_tile<4, 4, 2, 2, 8>(a, cu, stages, stream);
+    hipError_t e;
+    switch (tile) {
+    case W8_T128: e = launch_w8a8_tile<4, 4, 2, 2, 8>(a, cu, stages, stream); break;
+    case W8_T256: e = launch_w8a8_tile<4, 8, 4, 2, 4>(a, cu, stages, stream); break;
+    case W8_T64x128: e = launch_w8a8_tile<4, 2, 1, 4, 8>(a, cu, stages, stream); break;
+    case W8_T64x64: e = launch_w8a8_tile<2, 2, 2, 2, 8>(a, cu, stages, stream); break;
+    default: return hipErrorInvalidValue;
+    }
     if (e != hipSuccess || kp == 1) return e;
     return launch_sum_parts(ws, kp, M, N, y, ldy, false, stream);
 }
