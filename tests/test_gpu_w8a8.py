@@ -364,11 +364,11 @@ def test_w8a8_parts_match_oracle(N, K, M, kp, kparts_reset):
         assert np.array_equal(run(packed, N, K, xq, M, ws="auto")[0], y)
 
 
-@pytest.mark.parametrize("name,M,kp", [("down", 256, 3), ("down", 128, 6), ("down", 64, 3), ("gate_up", 64, 3),
+@pytest.mark.parametrize("name,M,kp", [("down", 256, 6), ("down", 128, 6), ("down", 64, 3), ("gate_up", 64, 3),
                                        ("gate_up", 128, 3)])
 def test_w8a8_automatic_split(name, M, kp, kparts_reset):
-    """The automatic plan at the FFN sizes: FFN down at M = 256 in 3 K parts
-    (80 128 x 128 tiles, one work-group per CU), at M = 128 in 6 (40 tiles),
+    """The automatic plan at the FFN sizes: FFN down at M = 256 in 6 K parts
+    (80 128 x 128 tiles, two work-groups per CU), at M = 128 in 6 (40 tiles),
     at M = 64 in 3 (80 64 x 64 tiles); gate/up at M = 64 in 3 (136 64 x 128
     tiles, two work-groups per CU), at M = 128 in 3 and with K whole from
     M = 256 on (sampled columns against the oracle)."""

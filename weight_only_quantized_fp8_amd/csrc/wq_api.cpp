@@ -665,18 +665,20 @@ int forced_w8a8_tile()
 //   kW8MinPartBlocks K blocks), the pair that best fills the work-group slots
 //   -- one per CU for a grid the four-stage pipeline runs, two per CU for the
 //   two-stage one; a pair must fill 5% more slots than the best so far, or
-//   as many with fewer parts, and ties go to the larger tile.  Measured on
+//   as many with fewer parts (with more parts above 128 rows), and ties go
+//   to the larger tile.  Measured on
 //   MI355X (GEMM + parts sum, M = 16 / 32 / 48 / 64, quantised activations
 //   prepared): FFN down takes 64 x 64 in 3 parts, 21.9 / 22.4 / 22.9 /
 //   23.9 us (128 x 128 in 6 parts: 25.9 / 26.6 / 27.7 / 29.4; in one part
 //   ~100); gate/up takes 64 x 128 in 3 parts, 22.2 / 23.5 / 25.7 / 27.5 us
 //   (128 x 128 in 3 parts: 23.3 / 25.2 / 27.1 / 29.5).  At M = 96 / 128 the
 //   128 x 128 tile: down 6 parts 30.8 / 32.9 us, gate/up 3 parts 33.0 /
-//   36.5;
+//   36.5.  FFN down at M = 192 / 256 (80 tiles): 6 parts, two work-groups
+//   per CU, 38.0 / 45.5 us against 45.0 / 46.4 in 3 with one per CU;
 // - a 128 x 128 grid of 1 to 4 tiles per CU: one part per kW8PartBlocks K
 //   blocks, but no more parts than bring the grid to 4 work-groups per CU.
-//   Measured: FFN down at M = 256 / 512 / 1024 / 2048 runs 116 / 118 / 143 /
-//   239 us in one part and 51 / 74 / 124 / 224 us in 3, 3, 3 and 2 parts;
+//   Measured: FFN down at M = 512 / 1024 / 2048 runs 118 / 143 / 239 us in
+//   one part and 74 / 124 / 224 us in 3, 3 and 2 parts;
 //   gate/up (K = 5120) is fastest in one part from M = 256 on;
 // - the 256 x 256 tile keeps K whole.
 W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
@@ -724,6 +726,10 @@ W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
                                                           (int64_t)max_kp}));
         return best;
     }
+    // equal fills: fewer parts while the tile has at most 128 rows (the
+    // stream binds); more work-groups above (two per CU hide the longer
+    // matrix-core work of each block)
+    const bool more_wgs = mpad > 128;
     double bf = fill(t0);
     for (int i = 0; i < nc; ++i) {
         const int64_t nt = tiles(cand[i]);
@@ -731,7 +737,7 @@ W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
             const int64_t n = nt * k;
             if (n > 2 * (int64_t)cu) break;
             const double f = fill(n);
-            if (f > bf + 0.05 || (f >= bf - 0.05 && k < best.kp)) {
+            if (f > bf + 0.05 || (f >= bf - 0.05 && (more_wgs ? k > best.kp : k < best.kp))) {
                 bf = std::max(bf, f);
                 best = {cand[i], k};
             }
