@@ -4,7 +4,8 @@
  * packs FP8 block-scaled and 3-bit LUT matrices through the C ABI of
  * include/wq.h, runs the GEMMs on both FP8 paths and both LUT layouts, and
  * checks every output against the CPU oracle (liboracle, linked here as the
- * tests' checker) with the comparison rule of the tests: within 2 BF16 ULP of
+ * reference the outputs are compared with) with the comparison rule of the
+ * tests: within 2 BF16 ULP of
  * the FP64 result rounded to BF16, or within 1e-3*sqrt(K)*max|x|*max|w| of it.
  * It also checks a few validation errors that need no device work.
  *
