@@ -127,6 +127,33 @@ def test_gemm_fp8_parity(N, K, M):
         U.check(r, "path %d" % path)
 
 
+@pytest.fixture
+def kparts_reset():
+    yield
+    U.wqmod().wq_set_kparts(0)
+
+
+@pytest.mark.parametrize("N", [128, 256])
+def test_fp8_single_k_block(N, kparts_reset):
+    """The smallest legal shapes: one 128-wide K block (K groups and K parts
+    have nothing to split) and one or two 128-row scale blocks; every path,
+    with and without a workspace, forced part counts clamped to one block."""
+    wq = U.wqmod()
+    K = 128
+    U.note("fp8 single K block N=%d" % N)
+    codes, scales = synth.fp8_weights(N, K, 940 + N)
+    packed = U.pack_fp8(codes, scales)
+    for M in (1, 2, 4, 5, 16, 17, 32):
+        xbits = synth.x_bf16(M, K, 941 + M)
+        for path in [AUTO, MFMA] + ([GEMV] if M <= 4 else []):
+            for kp in (0, 4):
+                wq.wq_set_kparts(kp)
+                for ws in (None, "auto"):
+                    y, _ = U.run_fp8(packed, N, K, xbits, path=path, ws=ws)
+                    U.check(U.grade_fp8(y, xbits, codes, scales, K), "M=%d path=%d kp=%d ws=%s" % (M, path, kp, ws))
+        wq.wq_set_kparts(0)
+
+
 LUT_SHAPES = [(48, 256), (272, 1024), (1024, 384), (528, 2048)]
 
 

@@ -153,7 +153,8 @@ def test_quantizer_nonfinite_groups():
 # M above 4096 runs the 256 x 256 work-group tile (WQ_W8A8_TILE=256 forces it
 # for every M; 384 and 640 columns leave a ragged column tile there), smaller M
 # the 128 x 128 one
-W8A8_SHAPES = [(256, 512, 1), (384, 1024, 16), (1024, 640, 33), (640, 2048, 130), (256, 256, 300),
+W8A8_SHAPES = [(128, 128, 5), (128, 128, 33), (256, 512, 1), (384, 1024, 16), (1024, 640, 33), (640, 2048, 130),
+               (256, 256, 300),
                (512, 1152, 129), (384, 1024, 700), (640, 768, 530), (1280, 512, 1030), (384, 512, 4100),
                (640, 256, 4400)]
 
