@@ -435,6 +435,32 @@ wq_status wq_unpack_x_fp8(const void* xq, int64_t M, int64_t K, uint8_t* codes, 
 wq_status wq_unpack_lut3_dense(const void* packed, int64_t N, int64_t K,
                                uint16_t* w_f16, void* hip_stream);
 
+/* Host-only plan queries: the plan a call would take on a gfx950 device with
+ * `cu` compute units (1..1024), computed on the host without touching any
+ * device, so that the dispatch rules can be checked where no GPU is present.
+ * Both follow wq_set_tuning, wq_set_kparts and the environment levers as the
+ * calls do.  with_workspace != 0 plans a call that passes a workspace (K may
+ * be split across work-groups).  Return WQ_ERR_NULL for a NULL plan,
+ * WQ_ERR_SHAPE where the call would reject the shape or M, or cu is out of
+ * range, and WQ_ERR_PATH where the call would reject the path.  Thread-safe.
+ *
+ * Decode GEMM (wq_gemm_fp8_block[_path], wq_gemm_lut3[_dense]; M = 1..32):
+ * plan[6] = { path run (WQ_PATH_GEMV or WQ_PATH_MFMA), 16-column tiles per
+ * wave, column-waves per work-group, waves per work-group, K parts across
+ * work-groups, launches (rows of x are served 32 or 16 per launch) }.
+ * Source: FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
+ * opening summary (a dispatch table chosen per shape from measurements);
+ * atlas docs "Module m16_tc", "WHY THE FFN ARM LOSES" (grids against the
+ * machine's slots). */
+wq_status wq_query_gemm_plan(int fmt, int path, int64_t M, int64_t N, int64_t K, int cu,
+                             int with_workspace, int* plan);
+
+/* W8A8 (wq_gemm_fp8_w8a8; any M the activation packer accepts):
+ * plan[3] = { output tile rows, tile columns, K parts across work-groups }.
+ * Source: atlas docs "Module m16_tc", ARM ORDER rung 6 (the W8A8 prefill
+ * rung) and "WHY THE FFN ARM LOSES" (grids against the machine's slots). */
+wq_status wq_query_w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, int with_workspace, int* plan);
+
 #ifdef __cplusplus
 }
 #endif

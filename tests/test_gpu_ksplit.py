@@ -219,3 +219,21 @@ def test_down_projection_table_plan(M, reset):
     r = U.grade_fp8(y, xb, codes, scales, K, cols=cols)
     U.note("  %s" % r)
     U.check(r)
+
+
+def test_plan_query_matches_the_device():
+    """The host plan queries, given this device's CU count, give the K parts
+    the calls size their workspaces for (decode GEMMs and W8A8)."""
+    wq = U.wqmod()
+    U.note("ksplit plan query against the device")
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    for fmt, N, K in ((wq.WQ_FMT_FP8_BLOCK, 17408, 5120), (wq.WQ_FMT_FP8_BLOCK, 5120, 17408),
+                      (wq.WQ_FMT_FP8_BLOCK, 1024, 5120), (wq.WQ_FMT_FP8_BLOCK, 1024, 16384),
+                      (wq.WQ_FMT_LUT3, 28672, 8192), (wq.WQ_FMT_LUT3_DENSE, 28672, 8192),
+                      (wq.WQ_FMT_LUT3, 48, 8192)):
+        kp = wq.wq_query_gemm_plan(fmt, 16, N, K, cu, True)["kparts"]
+        assert wq.wq_gemm_workspace_bytes(fmt, 16, N, K) == (kp * 32 * N * 4 if kp > 1 else 0), (fmt, N, K, kp)
+    for M, N, K in ((16, 17408, 5120), (16, 5120, 17408), (128, 5120, 17408), (1024, 5120, 17408),
+                    (8192, 17408, 5120), (300, 1280, 1152)):
+        kp = wq.wq_query_w8a8_plan(M, N, K, cu, True)["kparts"]
+        assert wq.wq_w8a8_workspace_bytes(M, N, K) == (kp * M * N * 4 if kp > 1 else 0), (M, N, K, kp)

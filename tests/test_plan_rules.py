@@ -1,0 +1,237 @@
+"""The dispatch rules, checked on the host through the plan queries (no device).
+
+wq_query_gemm_plan and wq_query_w8a8_plan return the plan a call would take on
+a device with a given number of compute units.  These tests pin the plans the
+library takes for the FFN and attention shapes on MI355X (256 CUs), which were
+chosen from timed sweeps, and check the properties the automatic rules promise
+for any shape and CU count: every K group and K part keeps work, parts are only
+used with a workspace, and a forced lever is honoured.
+"""
+import random
+
+import pytest
+
+wq = pytest.importorskip("weight_only_quantized_fp8_amd.wq")
+
+FP8, LUT, LUTD = wq.WQ_FMT_FP8_BLOCK, wq.WQ_FMT_LUT3, wq.WQ_FMT_LUT3_DENSE
+GEMV, MFMA = wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA
+CU = 256
+
+
+@pytest.fixture
+def levers_reset():
+    yield
+    wq.wq_set_tuning()
+    wq.wq_set_kparts(0)
+
+
+def plan(fmt, M, N, K, cu=CU, ws=False, path=wq.WQ_PATH_AUTO):
+    p = wq.wq_query_gemm_plan(fmt, M, N, K, cu, ws, path)
+    return p["nt"], p["sn"], p["split"], p["kparts"]
+
+
+# (format, N, K): (nt, sn, waves, K parts) without and with a workspace, on 256 CUs
+DECODE_PLANS = {
+    (FP8, 17408, 5120): ((1, 5, 5, 1), (1, 5, 5, 1)),      # FFN gate/up
+    (FP8, 5120, 17408): ((1, 2, 6, 1), (1, 5, 5, 4)),      # FFN down: 4 K parts + the parts sum
+    (FP8, 6144, 5120): ((1, 2, 6, 1), (1, 2, 6, 1)),       # attention Q
+    (FP8, 1024, 5120): ((1, 1, 4, 1), (1, 1, 4, 1)),       # attention K, V
+    (FP8, 8192, 5120): ((1, 2, 6, 1), (1, 2, 6, 1)),       # attention Q, K, V stacked
+    (FP8, 5120, 6144): ((1, 2, 6, 1), (1, 2, 6, 1)),       # attention output
+    (LUT, 28672, 8192): ((1, 7, 14, 1), (1, 7, 14, 1)),    # 3-bit LUT, nibbles: two K groups
+    (LUTD, 28672, 8192): ((1, 8, 16, 1), (1, 8, 16, 1)),   # 3-bit LUT, dense codes: two K groups
+}
+
+
+@pytest.mark.parametrize("key", list(DECODE_PLANS))
+def test_measured_decode_plans(key):
+    fmt, N, K = key
+    no_ws, with_ws = DECODE_PLANS[key]
+    for M in (1, 8, 16, 17, 32):
+        assert plan(fmt, M, N, K) == no_ws
+        assert plan(fmt, M, N, K, ws=True) == with_ws
+        p = wq.wq_query_gemm_plan(fmt, M, N, K, CU, True)
+        assert p["path"] == MFMA
+        assert p["launches"] == 1     # M = 17..32 in one pass on every one-tile table plan
+
+
+def test_table_applies_only_at_256_cus():
+    """The measured plans are for 256 CUs; another count takes the general rule
+    (one tile a wave, as many column-waves as leave a work-group per CU)."""
+    assert plan(FP8, 16, 17408, 5120, cu=255)[:2] == (1, 4)
+    assert plan(FP8, 16, 17408, 5120, cu=304)[:2] == (1, 3)
+    assert plan(FP8, 16, 17408, 5120, cu=128)[:2] == (1, 8)
+    assert plan(FP8, 16, 5120, 17408, cu=255, ws=True)[3] == 1     # 320 work-groups: no room for parts
+
+
+def test_gemv_only_when_asked():
+    """AUTO never takes the GEMV (the tile ties or wins at every M); an explicit
+    GEMV path runs for M <= 4 and is refused above, and for the LUT formats."""
+    for M in (1, 2, 4):
+        assert wq.wq_query_gemm_plan(FP8, M, 6144, 5120, CU)["path"] == MFMA
+        p = wq.wq_query_gemm_plan(FP8, M, 6144, 5120, CU, False, GEMV)
+        assert p["path"] == GEMV and (p["nt"], p["sn"], p["split"], p["kparts"]) == (1, 2, 8, 1)
+        # a GEMV plan with a workspace keeps K inside the work-group
+        assert wq.wq_query_gemm_plan(FP8, M, 5120, 17408, CU, True, GEMV)["kparts"] == 1
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_query_gemm_plan(FP8, 5, 6144, 5120, CU, False, GEMV)
+    assert e.value.status == 9
+    with pytest.raises(wq.WqError):
+        wq.wq_query_gemm_plan(LUT, 1, 28672, 8192, CU, False, GEMV)
+
+
+def test_launch_count_follows_the_tile(levers_reset):
+    """Rows are served 32 per launch by one-tile waves (FP8 always; LUT where
+    its 32-row activation chunks fit), else 16."""
+    wq.wq_set_tuning(1, 1, 0, 0)
+    assert wq.wq_query_gemm_plan(FP8, 32, 17408, 5120, CU)["launches"] == 1
+    assert wq.wq_query_gemm_plan(LUT, 17, 28672, 8192, CU)["launches"] == 2
+    assert wq.wq_query_gemm_plan(LUT, 16, 28672, 8192, CU)["launches"] == 1
+    wq.wq_set_tuning(1, 4, 0, 0)
+    assert wq.wq_query_gemm_plan(LUT, 32, 28672, 8192, CU)["launches"] == 1
+    wq.wq_set_tuning(2, 2, 0, 0)
+    for fmt, N, K in ((FP8, 17408, 5120), (LUT, 28672, 8192), (LUTD, 28672, 8192)):
+        assert wq.wq_query_gemm_plan(fmt, 17, N, K, CU)["launches"] == 2
+        assert wq.wq_query_gemm_plan(fmt, 16, N, K, CU)["launches"] == 1
+
+
+def test_levers_override_the_table(levers_reset):
+    wq.wq_set_tuning(1, 4, 8, 0)
+    assert plan(FP8, 16, 17408, 5120) == (1, 4, 8, 1)
+    assert plan(FP8, 16, 5120, 17408, ws=True)[:3] == (1, 4, 8)
+    wq.wq_set_tuning()
+    wq.wq_set_kparts(3)
+    assert plan(FP8, 16, 17408, 5120, ws=True)[3] == 3
+    assert plan(FP8, 16, 17408, 5120)[3] == 1              # parts need a workspace
+    wq.wq_set_kparts(32)
+    assert plan(FP8, 16, 256, 512, ws=True)[3] == 4        # at most one part per K block
+    assert plan(LUT, 16, 48, 1024, ws=True)[3] == 1        # LUT parts keep 8 K blocks
+
+
+def test_automatic_split_for_low_n_long_k():
+    """With a workspace, a grid of at most half the CUs and a long K splits K
+    into parts of 32 K blocks or more, to about one work-group per CU."""
+    assert plan(FP8, 16, 1024, 16384, ws=True) == (1, 1, 4, 4)
+    assert plan(FP8, 16, 1024, 16384) == (1, 1, 4, 1)
+    assert plan(FP8, 16, 1024, 16384, cu=128, ws=True)[3] == 2
+    assert plan(FP8, 16, 1024, 4096, ws=True)[3] == 1     # 32 K blocks: too short to split
+
+
+def _general_cases(n=400, seed=7):
+    rng = random.Random(seed)
+    for _ in range(n):
+        fmt = rng.choice((FP8, LUT, LUTD))
+        N = rng.choice((128, 256, 384, 1024, 2048, 5120, 8192, 17408, 28672))
+        if fmt != FP8:
+            N = rng.choice((16, 48, N))
+        K = 128 * rng.choice((1, 2, 3, 5, 8, 16, 40, 64, 136, 200))
+        cu = rng.choice((1, 8, 80, 104, 128, 228, 255, 256, 304, 1024))
+        yield fmt, rng.randint(1, 32), N, K, cu, rng.random() < 0.5
+
+
+def test_general_rule_invariants():
+    """For any shape and CU count: the kernels' limits hold, every K group and
+    K part gets at least one (aligned) K block, parts only with a workspace and
+    only where they leave about one work-group per CU with 32 K blocks each."""
+    for fmt, M, N, K, cu, ws in _general_cases():
+        p = wq.wq_query_gemm_plan(fmt, M, N, K, cu, ws)
+        nt, sn, split, kp = p["nt"], p["sn"], p["split"], p["kparts"]
+        where = (fmt, M, N, K, cu, ws, p)
+        kb = K // 128
+        align = 8 if fmt != FP8 else 1
+        kba = -(-kb // align)
+        assert p["path"] == MFMA, where
+        assert nt in (1, 2) and 1 <= sn <= 8, where
+        assert split % sn == 0 and 1 <= split // sn <= 4 and split <= 16, where
+        assert 1 <= kp <= 32 and (split // sn) * kp <= kba, where
+        assert p["launches"] in (-(-M // 32), -(-M // 16)), where
+        if not ws:
+            assert kp == 1, where
+        n_cg = -(-(N // 16) // (nt * sn))
+        if kp > 1 and cu != 256:
+            assert 2 * n_cg <= cu and n_cg * kp <= cu and kb // kp >= 32, where
+
+
+def test_query_validation():
+    assert wq.lib.wq_query_gemm_plan(FP8, 0, 16, 256, 512, CU, 0, None) == 1           # NULL plan
+    assert wq.lib.wq_query_w8a8_plan(16, 256, 512, CU, 0, None) == 1
+    for args in ((FP8, 0, 256, 512, CU), (FP8, 33, 256, 512, CU), (FP8, 16, 100, 512, CU),
+                 (FP8, 16, 256, 500, CU), (LUT, 16, 40, 512, CU), (FP8, 16, 256, 512, 0),
+                 (FP8, 16, 256, 512, 1025), (7, 16, 256, 512, CU)):
+        with pytest.raises(wq.WqError) as e:
+            wq.wq_query_gemm_plan(*args)
+        assert e.value.status == 2, args
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_query_gemm_plan(FP8, 16, 256, 512, CU, False, 3)
+    assert e.value.status == 9
+    for args in ((0, 256, 512, CU), (16, 100, 512, CU), (16, 256, 500, CU), (16, 256, 512, 0),
+                 (16, 65536, 65536, CU), (1 << 25, 256, 512, CU)):
+        with pytest.raises(wq.WqError) as e:
+            wq.wq_query_w8a8_plan(*args)
+        assert e.value.status == 2, args
+
+
+# W8A8 on 256 CUs with a workspace, FFN gate/up (17408 x 5120) and down
+# (5120 x 17408): M -> (tile rows, tile columns, K parts), the choices of the
+# timed sweeps (64-row tiles in 3 parts for small M; 128 x 128 split while the
+# grid is short; one part for gate/up from M = 192 on; 256 x 256 above 4096).
+W8A8_PLANS = {
+    "gate_up": {1: (64, 128, 3), 16: (64, 128, 3), 64: (64, 128, 3), 96: (128, 128, 3), 128: (128, 128, 3),
+                192: (128, 128, 1), 256: (128, 128, 1), 512: (128, 128, 1), 2048: (128, 128, 1),
+                4096: (128, 128, 1), 8192: (256, 256, 1)},
+    "down": {1: (64, 64, 3), 16: (64, 64, 3), 64: (64, 64, 3), 96: (128, 128, 6), 128: (128, 128, 6),
+             192: (128, 128, 6), 256: (128, 128, 6), 512: (128, 128, 3), 1024: (128, 128, 3),
+             2048: (128, 128, 2), 4096: (128, 128, 1), 8192: (256, 256, 1)},
+}
+FFN = {"gate_up": (17408, 5120), "down": (5120, 17408)}
+
+
+@pytest.mark.parametrize("name", list(W8A8_PLANS))
+def test_measured_w8a8_plans(name):
+    N, K = FFN[name]
+    for M, want in W8A8_PLANS[name].items():
+        p = wq.wq_query_w8a8_plan(M, N, K, CU, True)
+        assert p["tile"] + (p["kparts"],) == want, (name, M, p)
+        # without a workspace K stays whole; the tile is the one that fills best
+        q = wq.wq_query_w8a8_plan(M, N, K, CU, False)
+        assert q["kparts"] == 1 and q["tile"][0] == want[0], (name, M, q)
+
+
+def test_w8a8_forced_parts(levers_reset):
+    wq.wq_set_kparts(5)
+    assert wq.wq_query_w8a8_plan(16, 5120, 17408, CU, True)["kparts"] == 5
+    assert wq.wq_query_w8a8_plan(16, 5120, 17408, CU, False)["kparts"] == 1
+    wq.wq_set_kparts(32)
+    assert wq.wq_query_w8a8_plan(16, 256, 512, CU, True)["kparts"] == 4
+
+
+def test_w8a8_rule_invariants():
+    """The tile follows the padded row count; parts keep 12 K blocks or more
+    and need a workspace; a split grid of 64-row tiles, or of a 128 x 128 grid
+    that fits the CUs, stays within two work-groups per CU; a 128 x 128 grid
+    of 1 to 4 tiles per CU adds no part beyond 4 work-groups per CU."""
+    rng = random.Random(11)
+    for _ in range(400):
+        M = rng.choice((1, 7, 16, 33, 64, 65, 100, 128, 129, 200, 256, 300, 512, 1000, 2048, 4096, 4097, 6000))
+        N = 128 * rng.choice((1, 2, 3, 8, 16, 40, 48, 136))
+        K = 128 * rng.choice((1, 2, 12, 24, 40, 64, 136))
+        cu = rng.choice((8, 80, 128, 256, 304))
+        ws = rng.random() < 0.7
+        p = wq.wq_query_w8a8_plan(M, N, K, cu, ws)
+        (r, c), kp = p["tile"], p["kparts"]
+        where = (M, N, K, cu, ws, p)
+        mpad = -(-M // 16) * 16
+        assert r == (64 if mpad <= 64 else 256 if mpad > 4096 else 128), where
+        assert c == (256 if r == 256 else c) and c in (64, 128, 256), where
+        if r != 64:
+            assert c == r, where
+        if not ws or r == 256:
+            assert kp == 1, where
+            continue
+        tiles = -(-mpad // r) * -(-N // c)
+        if kp > 1:
+            assert K // 128 >= 12 * kp or (r == 128 and tiles > cu), where
+            if r == 64 or tiles <= cu:
+                assert tiles * kp <= 2 * cu, where
+            else:
+                assert tiles * (kp - 1) < 4 * cu and K // 128 >= 40 * kp, where

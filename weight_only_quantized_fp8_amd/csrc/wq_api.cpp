@@ -140,8 +140,9 @@ struct Plan {
 constexpr int64_t kGemvAutoMaxM = 0;
 
 // Tilings measured fastest on MI355X (256 CUs) for the decode shapes of the
-// FFN and attention projections (per-shape dispatch, as in the FLUTE PR's
-// "data-driven per-shape dispatch"); other shapes use the rule below.
+// FFN and attention projections (a dispatch table chosen per shape from
+// measurements, as the FLUTE PR's opening summary describes for its kernel);
+// other shapes use the rule below.
 struct TableEntry {
     int kind;
     int64_t N, K;
@@ -280,6 +281,9 @@ Plan cached_plan(int kind, int64_t N, int64_t K, int cu, bool ws)
 constexpr int64_t kMaxDim = (int64_t)1 << 24;
 constexpr int64_t kMaxCodes = (int64_t)1 << 35;
 
+// Largest compute-unit count the plan queries accept.
+constexpr int kMaxQueryCu = 1024;
+
 bool shape_ok(int fmt, int64_t N, int64_t K)
 {
     if (N <= 0 || K <= 0 || K % 128) return false;
@@ -301,6 +305,38 @@ size_t lut3_scale_bytes(int64_t N, int64_t K) { return (size_t)(N / 16) * (size_
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// The kernel family of a decode call: the LUT formats run their MFMA tile;
+// FP8 runs the tile, or the GEMV for M <= 4 where the call or the
+// WQ_FORCE_PATH lever asks for it (AUTO never does: kGemvAutoMaxM).
+wq_status resolve_kind(int fmt, int path, int64_t M, int* kind)
+{
+    if (fmt != WQ_FMT_FP8_BLOCK) {
+        if (path == WQ_PATH_GEMV) return WQ_ERR_PATH;
+        *kind = fmt == WQ_FMT_LUT3_DENSE ? wq::KIND_MFMA_LUT3D : wq::KIND_MFMA_LUT;
+        return WQ_OK;
+    }
+    int eff = path == WQ_PATH_AUTO ? options().force_path : path;
+    if (eff == WQ_PATH_AUTO) eff = M <= kGemvAutoMaxM ? WQ_PATH_GEMV : WQ_PATH_MFMA;
+    if (eff == WQ_PATH_GEMV && M > 4) {
+        if (path == WQ_PATH_GEMV) return WQ_ERR_PATH;
+        eff = WQ_PATH_MFMA;   // a forced GEMV lever only applies where it can run
+    }
+    *kind = eff == WQ_PATH_GEMV ? wq::KIND_GEMV_FP8 : wq::KIND_MFMA_FP8;
+    return WQ_OK;
+}
+
+// Rows of x one launch serves.  One-tile MFMA waves serve M = 17..32 in one
+// pass (each dequantised operand feeds both 16-row halves) -- for the LUT
+// tile where its 32-row chunks fit; otherwise the rows 0..15 and 16..M-1 run
+// as two passes.  Either way every row sees the same arithmetic as in a call
+// of at most 16 rows.
+int plan_rows_per_launch(const Plan& p)
+{
+    const bool single_pass =
+        p.nt == 1 && (p.kind == wq::KIND_MFMA_FP8 || wq::lut_single_pass(p.kind, p.sn, p.split));
+    return single_pass ? 32 : 16;
+}
+
 // Shared front end of the GEMMs.  static_scratch: the no-allocation entry
 // point -- the workspace is the library's static device scratch of the
 // current device (the caller passes none), planned as a call with a workspace.
@@ -320,20 +356,9 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
     if (!aligned16(packed) || !aligned16(x) || ldx % 8) return WQ_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(y) & 1) return WQ_ERR_ALIGN;
 
-    const Options& o = options();
     int kind;
-    if (fmt != WQ_FMT_FP8_BLOCK) {
-        if (path == WQ_PATH_GEMV) return WQ_ERR_PATH;
-        kind = fmt == WQ_FMT_LUT3_DENSE ? wq::KIND_MFMA_LUT3D : wq::KIND_MFMA_LUT;
-    } else {
-        int eff = path == WQ_PATH_AUTO ? o.force_path : path;
-        if (eff == WQ_PATH_AUTO) eff = M <= kGemvAutoMaxM ? WQ_PATH_GEMV : WQ_PATH_MFMA;
-        if (eff == WQ_PATH_GEMV && M > 4) {
-            if (path == WQ_PATH_GEMV) return WQ_ERR_PATH;
-            eff = WQ_PATH_MFMA;   // a forced GEMV lever only applies where it can run
-        }
-        kind = eff == WQ_PATH_GEMV ? wq::KIND_GEMV_FP8 : wq::KIND_MFMA_FP8;
-    }
+    const wq_status ks = resolve_kind(fmt, path, M, &kind);
+    if (ks != WQ_OK) return ks;
 
     // ---- device and workspace
     DevInfo dev;
@@ -375,13 +400,7 @@ wq_status gemm_common(int fmt, const void* packed, int64_t N, int64_t K, const u
     a.ws = p.kp > 1 ? static_cast<float*>(workspace) : nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    // One-tile MFMA waves serve M = 17..32 in one pass (each dequantised
-    // operand feeds both 16-row halves) -- for the LUT tile where its 32-row
-    // chunks fit; otherwise the rows 0..15 and 16..M-1 run as two passes.
-    // Either way every row sees the same arithmetic as in a call of at most
-    // 16 rows.
-    const bool single_pass = p.nt == 1 && (kind == wq::KIND_MFMA_FP8 || wq::lut_single_pass(kind, p.sn, p.split));
-    const int64_t rows_per_launch = single_pass ? 32 : 16;
+    const int64_t rows_per_launch = plan_rows_per_launch(p);
     for (int64_t r0 = 0; r0 < M; r0 += rows_per_launch) {
         const int rows = (int)std::min<int64_t>(rows_per_launch, M - r0);
         a.x = x + r0 * ldx;
@@ -589,6 +608,26 @@ size_t wq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K)
     return plan_workspace_bytes(cached_plan(kind, N, K, dev.cu, true), N);
 }
 
+wq_status wq_query_gemm_plan(int fmt, int path, int64_t M, int64_t N, int64_t K, int cu, int with_workspace,
+                             int* plan)
+{
+    if (!plan) return WQ_ERR_NULL;
+    if (M < 1 || M > 32 || cu < 1 || cu > kMaxQueryCu || !shape_ok(fmt, N, K)) return WQ_ERR_SHAPE;
+    if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_ERR_PATH;
+    int kind;
+    const wq_status ks = resolve_kind(fmt, path, M, &kind);
+    if (ks != WQ_OK) return ks;
+    const Plan p = cached_plan(kind, N, K, cu, with_workspace != 0);
+    const int rows = plan_rows_per_launch(p);
+    plan[0] = kind == wq::KIND_GEMV_FP8 ? WQ_PATH_GEMV : WQ_PATH_MFMA;
+    plan[1] = p.nt;
+    plan[2] = p.sn;
+    plan[3] = p.split;
+    plan[4] = p.kp;
+    plan[5] = (int)((M + rows - 1) / rows);
+    return WQ_OK;
+}
+
 wq_status wq_unpack_fp8_block(const void* packed, int64_t N, int64_t K, uint16_t* w_bf16, void* hip_stream)
 {
     if (!shape_ok(WQ_FMT_FP8_BLOCK, N, K)) return WQ_ERR_SHAPE;
@@ -758,6 +797,19 @@ size_t wq_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K)
     DevInfo dev;
     if (current_device(&dev) != WQ_OK) return 0;
     return w8a8_workspace_bytes(M, N, w8a8_plan(M, N, K, dev.cu, true).kp);
+}
+
+wq_status wq_query_w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, int with_workspace, int* plan)
+{
+    if (!plan) return WQ_ERR_NULL;
+    if (M < 1 || cu < 1 || cu > kMaxQueryCu || !shape_ok(WQ_FMT_FP8_BLOCK, N, K) ||
+        (uint64_t)N * (uint64_t)K >= ((uint64_t)1 << 32) || !wq_x_fp8_packed_bytes(M, K))
+        return WQ_ERR_SHAPE;
+    const W8Plan p = w8a8_plan(M, N, K, cu, with_workspace != 0);
+    plan[0] = wq::w8_tile_rows(p.tile);
+    plan[1] = wq::w8_tile_cols(p.tile);
+    plan[2] = p.kp;
+    return WQ_OK;
 }
 
 size_t wq_x_fp8_packed_bytes(int64_t M, int64_t K)

@@ -23,6 +23,7 @@ __all__ = [
     "wq_x_fp8_packed_bytes", "wq_w8a8_workspace_bytes", "wq_quantize_x_fp8", "wq_gemm_fp8_w8a8", "wq_unpack_x_fp8", "quantize_x_fp8",
     "gemm_fp8_w8a8",
     "wq_gemm_workspace_bytes", "wq_unpack_fp8_block", "wq_unpack_fp8_block_f32", "wq_unpack_lut3",
+    "wq_query_gemm_plan", "wq_query_w8a8_plan",
     "workspace", "pack_fp8", "pack_lut3", "gemm_fp8", "gemm_lut3",
 ]
 
@@ -72,6 +73,8 @@ _SIGS = {
     "wq_unpack_fp8_block": (_INT, [_P, _I64, _I64, _P, _P]),
     "wq_unpack_fp8_block_f32": (_INT, [_P, _I64, _I64, _P, _P]),
     "wq_unpack_lut3": (_INT, [_P, _I64, _I64, _P, _P]),
+    "wq_query_gemm_plan": (_INT, [_INT, _INT, _I64, _I64, _I64, _INT, _INT, ctypes.POINTER(_INT)]),
+    "wq_query_w8a8_plan": (_INT, [_I64, _I64, _I64, _INT, _INT, ctypes.POINTER(_INT)]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -234,6 +237,23 @@ def wq_quantize_x_fp8(x, M: int, K: int, xq, stream=None) -> None:
 def wq_gemm_fp8_w8a8(packed, N: int, K: int, xq, M: int, y, workspace=None, stream=None) -> None:
     _check(lib.wq_gemm_fp8_w8a8(_ptr(packed), N, K, _ptr(xq), M, _ptr(y), _ld(y), _ptr(workspace),
                                 _nbytes(workspace), _stream(stream)), "wq_gemm_fp8_w8a8")
+
+
+def wq_query_gemm_plan(fmt: int, M: int, N: int, K: int, cu: int, with_workspace: bool = False,
+                       path: int = WQ_PATH_AUTO) -> dict:
+    """Host-only: the plan a decode GEMM call would take on a device with `cu`
+    compute units (no device is touched)."""
+    out = (_INT * 6)()
+    _check(lib.wq_query_gemm_plan(fmt, path, M, N, K, cu, int(bool(with_workspace)), out), "wq_query_gemm_plan")
+    return dict(path=out[0], nt=out[1], sn=out[2], split=out[3], kparts=out[4], launches=out[5])
+
+
+def wq_query_w8a8_plan(M: int, N: int, K: int, cu: int, with_workspace: bool = False) -> dict:
+    """Host-only: the tile and K parts a W8A8 call would take on a device with
+    `cu` compute units (no device is touched)."""
+    out = (_INT * 3)()
+    _check(lib.wq_query_w8a8_plan(M, N, K, cu, int(bool(with_workspace)), out), "wq_query_w8a8_plan")
+    return dict(tile=(out[0], out[1]), kparts=out[2])
 
 
 def wq_unpack_x_fp8(xq, M: int, K: int, codes, scales, stream=None) -> None:
