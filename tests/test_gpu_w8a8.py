@@ -321,18 +321,21 @@ def test_w8a8_depth_boundary(M, stages_reset):
 
 @pytest.mark.parametrize("name", ["gate_up", "down"])
 def test_w8a8_small_grid_rows_equal_large_grid(name, stages_reset):
-    """At the FFN sizes a small M runs the four-stage pipeline (at most one
-    work-group per CU) and M = 2048 the two-stage one; rows depend only on
-    their own activations, so the small calls equal the first rows of the
-    large one bit for bit."""
+    """At the FFN sizes M = 2048 runs 128 x 128 tiles on the two-stage
+    pipeline; M = 48 runs 64-row tiles and M = 128 the four-stage pipeline (at
+    most one work-group per CU), and gate/up M = 512 the 256 x 256 tile.  Rows
+    depend only on their own activations, so the smaller calls equal the first
+    rows of the large one bit for bit."""
+    wq = U.wqmod()
     fmt, N, K, Ms, (codes, scales) = U.config_inputs(name)
     packed = U.pack_fp8(codes, scales)
     xb = synth.x_bf16(2048, K, 1801)
     xq, _, _ = quantize(xb, K)
     U.note("w8a8 %s M=2048 (two stages)" % name)
+    assert wq.wq_query_w8a8_plan(2048, N, K, 256, False)["tile"] == (128, 128)
     ybig, _ = run(packed, N, K, xq, 2048)
-    for M in (48, 128):
-        U.note("w8a8 %s M=%d (four stages)" % (name, M))
+    for M in (48, 128, 512):
+        U.note("w8a8 %s M=%d (plan %s)" % (name, M, wq.wq_query_w8a8_plan(M, N, K, 256, False)))
         xq2, _, _ = quantize(xb[:M], K)
         y, _ = run(packed, N, K, xq2, M)
         assert np.array_equal(y, ybig[:M]), M
@@ -366,11 +369,12 @@ def test_w8a8_parts_match_oracle(N, K, M, kp, kparts_reset):
 
 
 @pytest.mark.parametrize("name,M,kp", [("down", 256, 6), ("down", 128, 6), ("down", 64, 3), ("gate_up", 64, 3),
-                                       ("gate_up", 128, 3)])
+                                       ("gate_up", 128, 3), ("down", 1024, 3)])
 def test_w8a8_automatic_split(name, M, kp, kparts_reset):
     """The automatic plan at the FFN sizes: FFN down at M = 256 in 6 K parts
     (80 128 x 128 tiles, two work-groups per CU), at M = 128 in 6 (40 tiles),
-    at M = 64 in 3 (80 64 x 64 tiles); gate/up at M = 64 in 3 (136 64 x 128
+    at M = 64 in 3 (80 64 x 64 tiles), at M = 1024 in 3 on 256 x 256 tiles
+    (80 tiles, one work-group per CU); gate/up at M = 64 in 3 (136 64 x 128
     tiles, two work-groups per CU), at M = 128 in 3 and with K whole from
     M = 256 on (sampled columns against the oracle)."""
     wq = U.wqmod()

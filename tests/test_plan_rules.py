@@ -171,17 +171,22 @@ def test_query_validation():
         assert e.value.status == 2, args
 
 
-# W8A8 on 256 CUs with a workspace, FFN gate/up (17408 x 5120) and down
-# (5120 x 17408): M -> (tile rows, tile columns, K parts), the choices of the
-# timed sweeps (64-row tiles in 3 parts for small M; 128 x 128 split while the
-# grid is short; one part for gate/up from M = 192 on; 256 x 256 above 4096).
+# W8A8 on 256 CUs, FFN gate/up (17408 x 5120) and down (5120 x 17408):
+# M -> (tile rows, tile columns, K parts) with a workspace, and the tile
+# without one (K whole) -- the choices of the timed sweeps: 64-row tiles in
+# 3 parts for small M; 128 x 128 split while the grid is short; one part for
+# gate/up from M = 192 on; 256 x 256 where its coarser rounds still come out
+# ahead (gate/up M = 512 and 4096, down M = 1024 and 2048 in 3 parts) and
+# above M = 4096.
 W8A8_PLANS = {
-    "gate_up": {1: (64, 128, 3), 16: (64, 128, 3), 64: (64, 128, 3), 96: (128, 128, 3), 128: (128, 128, 3),
-                192: (128, 128, 1), 256: (128, 128, 1), 512: (128, 128, 1), 2048: (128, 128, 1),
-                4096: (128, 128, 1), 8192: (256, 256, 1)},
-    "down": {1: (64, 64, 3), 16: (64, 64, 3), 64: (64, 64, 3), 96: (128, 128, 6), 128: (128, 128, 6),
-             192: (128, 128, 6), 256: (128, 128, 6), 512: (128, 128, 3), 1024: (128, 128, 3),
-             2048: (128, 128, 2), 4096: (128, 128, 1), 8192: (256, 256, 1)},
+    "gate_up": {1: ((64, 128, 3), 64), 16: ((64, 128, 3), 64), 64: ((64, 128, 3), 64),
+                96: ((128, 128, 3), 128), 128: ((128, 128, 3), 128), 192: ((128, 128, 1), 128),
+                256: ((128, 128, 1), 128), 512: ((256, 256, 1), 256), 1024: ((128, 128, 1), 128),
+                2048: ((128, 128, 1), 128), 4096: ((256, 256, 1), 256), 8192: ((256, 256, 1), 256)},
+    "down": {1: ((64, 64, 3), 64), 16: ((64, 64, 3), 64), 64: ((64, 64, 3), 64), 96: ((128, 128, 6), 128),
+             128: ((128, 128, 6), 128), 192: ((128, 128, 6), 128), 256: ((128, 128, 6), 128),
+             512: ((128, 128, 3), 128), 1024: ((256, 256, 3), 128), 2048: ((256, 256, 3), 128),
+             4096: ((128, 128, 1), 128), 8192: ((256, 256, 1), 256)},
 }
 FFN = {"gate_up": (17408, 5120), "down": (5120, 17408)}
 
@@ -189,12 +194,23 @@ FFN = {"gate_up": (17408, 5120), "down": (5120, 17408)}
 @pytest.mark.parametrize("name", list(W8A8_PLANS))
 def test_measured_w8a8_plans(name):
     N, K = FFN[name]
-    for M, want in W8A8_PLANS[name].items():
+    for M, (want, rows_no_ws) in W8A8_PLANS[name].items():
         p = wq.wq_query_w8a8_plan(M, N, K, CU, True)
         assert p["tile"] + (p["kparts"],) == want, (name, M, p)
-        # without a workspace K stays whole; the tile is the one that fills best
         q = wq.wq_query_w8a8_plan(M, N, K, CU, False)
-        assert q["kparts"] == 1 and q["tile"][0] == want[0], (name, M, q)
+        assert q["kparts"] == 1 and q["tile"][0] == rows_no_ws, (name, M, q)
+
+
+def test_w8a8_big_tile_only_where_fitted(levers_reset):
+    """The 256 x 256 tile below M = 4097 needs K >= 4096 (the range its cost
+    estimate was fitted on) and no forced tile; a forced part count is kept."""
+    assert wq.wq_query_w8a8_plan(2049, 2048, 384, CU, False)["tile"] == (128, 128)
+    assert wq.wq_query_w8a8_plan(512, 17408, 3968, CU, False)["tile"] == (128, 128)
+    assert wq.wq_query_w8a8_plan(512, 17408, 4096, CU, False)["tile"] == (256, 256)
+    assert wq.wq_query_w8a8_plan(256, 17408, 5120, CU, False)["tile"] == (128, 128)
+    wq.wq_set_kparts(2)
+    p = wq.wq_query_w8a8_plan(1024, 5120, 17408, CU, True)
+    assert p["kparts"] == 2
 
 
 def test_w8a8_forced_parts(levers_reset):
@@ -206,10 +222,13 @@ def test_w8a8_forced_parts(levers_reset):
 
 
 def test_w8a8_rule_invariants():
-    """The tile follows the padded row count; parts keep 12 K blocks or more
-    and need a workspace; a split grid of 64-row tiles, or of a 128 x 128 grid
+    """The tile follows the padded row count (256 x 256 below M = 4097 only
+    above 256 rows and for K >= 4096); parts keep 12 K blocks or more and
+    need a workspace; a split grid of 64-row tiles, or of a 128 x 128 grid
     that fits the CUs, stays within two work-groups per CU; a 128 x 128 grid
-    of 1 to 4 tiles per CU adds no part beyond 4 work-groups per CU."""
+    of 1 to 4 tiles per CU adds no part beyond 4 work-groups per CU; a
+    256 x 256 grid below M = 4097 splits K (into at most 3) only while it has
+    fewer tiles than CUs, and above that keeps K whole."""
     rng = random.Random(11)
     for _ in range(400):
         M = rng.choice((1, 7, 16, 33, 64, 65, 100, 128, 129, 200, 256, 300, 512, 1000, 2048, 4096, 4097, 6000))
@@ -221,14 +240,24 @@ def test_w8a8_rule_invariants():
         (r, c), kp = p["tile"], p["kparts"]
         where = (M, N, K, cu, ws, p)
         mpad = -(-M // 16) * 16
-        assert r == (64 if mpad <= 64 else 256 if mpad > 4096 else 128), where
+        if mpad <= 64:
+            assert r == 64, where
+        elif mpad > 4096:
+            assert r == 256, where
+        elif mpad <= 256 or K < 4096:
+            assert r == 128, where
+        else:
+            assert r in (128, 256), where
         assert c == (256 if r == 256 else c) and c in (64, 128, 256), where
         if r != 64:
             assert c == r, where
-        if not ws or r == 256:
+        tiles = -(-mpad // r) * -(-N // c)
+        if not ws or (r == 256 and (mpad > 4096 or tiles >= cu)):
             assert kp == 1, where
             continue
-        tiles = -(-mpad // r) * -(-N // c)
+        if r == 256:
+            assert kp <= 3 and K // 128 >= 12 * kp, where
+            continue
         if kp > 1:
             assert K // 128 >= 12 * kp or (r == 128 and tiles > cu), where
             if r == 64 or tiles <= cu:

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -682,6 +683,32 @@ struct W8Plan {
     int kp;     // K parts across work-groups
 };
 
+// Estimated microseconds of a GEMM on 128 x 128 or 256 x 256 tiles, for the
+// choice between them at 256 < Mpad <= kW8BigM.  Per K block of a part: a
+// round of 128 x 128 work-groups at two per CU takes ~1.07 us, one at one per
+// CU (the four-stage pipeline) ~0.75 us, a round of 256 x 256 work-groups
+// (one per CU) ~1.75 us; a 128 x 128 grid of several rounds adds ~20 us, and
+// a partial last round costs at least half a round.  K parts add their FP32
+// partials written and read back (~6 TB/s) and the summing kernel (~3 us).
+// Fitted to the FFN shapes at M = 192 ... 8192 (gate/up K = 5120 and down
+// K = 17408, 1-6 K parts, both tiles); on those the estimate ranks the two
+// tiles as measured wherever they differ by more than 3%.
+double w8_estimate_us(int tile, int64_t tiles, int kp, int KB, int64_t M, int64_t N, int cu)
+{
+    const int64_t n = tiles * kp;
+    const double bpp = (double)((KB + kp - 1) / kp);
+    double t;
+    if (tile == wq::W8_T128) {
+        if (n <= cu) t = 0.754 * bpp;
+        else {
+            const double r = (double)n / (2.0 * cu);
+            t = 20.0 + 1.07 * bpp * std::max(r, std::ceil(r) - 0.5);
+        }
+    } else t = std::ceil((double)n / cu) * 1.75 * bpp;
+    if (kp > 1) t += 2.0 * kp * (double)M * (double)N * 4.0 / 6.0e6 + 3.0;
+    return t;
+}
+
 // WQ_W8A8_TILE = 128 | 256 | 64 (64 x 128) | 6464 (64 x 64): one tile for
 // every M (sweeps); read once.
 int forced_w8a8_tile()
@@ -719,7 +746,18 @@ int forced_w8a8_tile()
 //   Measured: FFN down at M = 512 / 1024 / 2048 runs 118 / 143 / 239 us in
 //   one part and 74 / 124 / 224 us in 3, 3 and 2 parts;
 //   gate/up (K = 5120) is fastest in one part from M = 256 on;
-// - the 256 x 256 tile keeps K whole.
+// - at 256 < Mpad <= kW8BigM and K >= 4096 the 256 x 256 tile replaces
+//   that plan where w8_estimate_us puts it 5% lower (its fewer, larger
+//   work-groups do more matrix-core work per byte staged, but fill the CUs
+//   in coarser rounds).  Measured against the 128 x 128 plan (same process,
+//   interleaved): gate/up M = 512 / 768 / 1500 / 2500 / 3500 / 4096 in one
+//   part 72.9 / 77.0 / 146.6 / 228.8 / 309.3 / 372.2 us against 81.0 /
+//   91.8 / 165.3 / 253.8 / 346.1 / 393.0; FFN down M = 800 / 1024 / 1200 /
+//   2048 / 3000 in 3, 3, 2, 3 and 1 parts 93.5 / 104.2 / 123.6 / 198.8 /
+//   246.6 against 109.3 / 126.2 / 157.0 / 226.8 / 316.5; where the 128 x 128
+//   plan stays (gate/up M = 300 / 800 / 1024 / 2048, down M = 300 ... 768
+//   and 3500 / 4096) the two are within 2.5%;
+// - above kW8BigM the 256 x 256 tile, with K whole.
 W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
 {
     int forced_kp;
@@ -743,6 +781,26 @@ W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
     auto fill = [&](int64_t n) {   // share of the work-group slots a grid of n fills
         return n <= cu ? (double)n / cu : n <= 2 * (int64_t)cu ? (double)n / (2.0 * cu) : 0.0;
     };
+    // 256 < Mpad <= kW8BigM and K >= 4096 (the range the estimate was fitted
+    // on): the 256 x 256 tile instead of a 128 x 128 plan where its estimate
+    // is at least 5% lower -- in one K part, or in up to three (each of
+    // kW8MinPartBlocks K blocks or more) for a grid of fewer tiles than CUs; a
+    // forced part count is kept
+    auto big_tile_if_faster = [&](W8Plan p) {
+        if (p.tile != wq::W8_T128 || mpad <= 256 || KB < 32 || forced_w8a8_tile() >= 0) return p;
+        const int64_t t256 = tiles(wq::W8_T256);
+        W8Plan b = p;
+        double bt = 0.95 * w8_estimate_us(wq::W8_T128, tiles(wq::W8_T128), p.kp, KB, M, N, cu);
+        const int kmax = forced_kp || !ws ? p.kp : t256 < cu ? std::min(3, std::max(1, std::min(max_kp, KB / kW8MinPartBlocks))) : 1;
+        for (int k = forced_kp || !ws ? p.kp : 1; k <= kmax; ++k) {
+            const double e = w8_estimate_us(wq::W8_T256, t256, k, KB, M, N, cu);
+            if (e < bt) {
+                bt = e;
+                b = {wq::W8_T256, k};
+            }
+        }
+        return b;
+    };
     W8Plan best{cand[0], 1};
     if (!ws || forced_kp) {                          // the part count is given: the tile that fills best
         const int kp = ws ? std::min(forced_kp, max_kp) : 1;
@@ -755,7 +813,7 @@ W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
                 best = {cand[i], kp};
             }
         }
-        return best;
+        return big_tile_if_faster(best);
     }
     if (cand[0] == wq::W8_T256) return best;
     const int64_t t0 = tiles(cand[0]);
@@ -763,7 +821,7 @@ W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
         if (t0 < 4 * (int64_t)cu)
             best.kp = std::max(1, (int)std::min<int64_t>({(int64_t)KB / kW8PartBlocks, (4 * cu + t0 - 1) / t0,
                                                           (int64_t)max_kp}));
-        return best;
+        return big_tile_if_faster(best);
     }
     // equal fills: fewer parts while the tile has at most 128 rows (the
     // stream binds); more work-groups above (two per CU hide the longer
@@ -782,7 +840,7 @@ W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
             }
         }
     }
-    return best;
+    return big_tile_if_faster(best);
 }
 
 size_t w8a8_workspace_bytes(int64_t M, int64_t N, int kp) { return kp > 1 ? (size_t)kp * M * N * 4 : 0; }
