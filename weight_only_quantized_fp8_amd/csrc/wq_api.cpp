@@ -791,8 +791,12 @@ W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
         const int64_t t256 = tiles(wq::W8_T256);
         W8Plan b = p;
         double bt = 0.95 * w8_estimate_us(wq::W8_T128, tiles(wq::W8_T128), p.kp, KB, M, N, cu);
-        const int kmax = forced_kp || !ws ? p.kp : t256 < cu ? std::min(3, std::max(1, std::min(max_kp, KB / kW8MinPartBlocks))) : 1;
-        for (int k = forced_kp || !ws ? p.kp : 1; k <= kmax; ++k) {
+        const bool fixed_kp = forced_kp || !ws;
+        const int kmin = fixed_kp ? p.kp : 1;
+        const int kmax = fixed_kp ? p.kp
+                         : t256 < cu ? std::min(3, std::max(1, std::min(max_kp, KB / kW8MinPartBlocks)))
+                                     : 1;
+        for (int k = kmin; k <= kmax; ++k) {
             const double e = w8_estimate_us(wq::W8_T256, t256, k, KB, M, N, cu);
             if (e < bt) {
                 bt = e;
