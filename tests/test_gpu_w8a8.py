@@ -393,6 +393,30 @@ def test_w8a8_automatic_split(name, M, kp, kparts_reset):
     check_w8a8(r)
 
 
+@pytest.mark.parametrize("N,K,M,kp", [(1408, 4608, 1500, 3), (2432, 4096, 1000, 2), (3200, 4096, 3000, 1)])
+def test_w8a8_automatic_big_tile(N, K, M, kp):
+    """Ragged shapes (N not a multiple of 256, M not of 16) on which the
+    automatic plan takes the 256 x 256 tile below M = 4097, in 3, 2 and 1 K
+    parts: sampled columns against the oracle, and the same bits on a repeat
+    (NaN-filled workspace)."""
+    wq = U.wqmod()
+    U.note("w8a8 big tile N=%d K=%d M=%d kp=%d" % (N, K, M, kp))
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if cu == 256:
+        assert wq.wq_query_w8a8_plan(M, N, K, cu, True) == {"tile": (256, 256), "kparts": kp}
+    codes, scales = synth.fp8_weights(N, K, 2100 + N)
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(M, K, 2200 + M)
+    xq, xc, xs = quantize(xb, K)
+    y, _ = run(packed, N, K, xq, M, ws="auto")
+    cols = U.sample_cols(N, 69, 160)
+    y64 = oracle.gemm_w8a8(xc, xs, codes, scales, cols=cols)
+    r = compare.grade(y[:, cols], y64, floor_w8a8(xc, xs, codes, scales, K), "bf16")
+    U.note("  %s" % r)
+    check_w8a8(r)
+    assert np.array_equal(run(packed, N, K, xq, M, ws="auto")[0], y)
+
+
 def test_w8a8_workspace_errors(kparts_reset):
     wq = U.wqmod()
     wq.wq_set_kparts(3)
