@@ -994,7 +994,11 @@ __global__ void unpack_lut3_kernel(const uint8_t* __restrict__ packed, int64_t N
 // ----------------------------------------------------------- K-part sum
 // y[m][n] = the sum of the K parts' FP32 partials ws[p][m][n] taken in order
 // p = 0, 1, .., kp-1, rounded once (RNE) to BF16 or FP16.  A thread takes 4
-// consecutive columns (N is a multiple of 16).
+// consecutive columns (N is a multiple of 16).  The parts are loaded
+// kSumBatch at a time, all of a batch's loads in flight together, and then
+// added in order: one memory round trip per batch rather than per part.
+constexpr int kSumBatch = 8;
+
 __global__ void __launch_bounds__(256) reduce_parts_kernel(const float* __restrict__ ws, int kp, int rows, int N,
                                                            uint16_t* __restrict__ y, int64_t ldy, int f16_out)
 {
@@ -1003,11 +1007,19 @@ __global__ void __launch_bounds__(256) reduce_parts_kernel(const float* __restri
     if (q >= (int64_t)rows * groups) return;
     const int64_t m = q / groups, n = (q - m * groups) * 4;
     const float* p = ws + m * N + n;
+    const int64_t part = (int64_t)rows * N;
     f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
-    for (int k = 1; k < kp; ++k) {
-        const f32x4_t w = *reinterpret_cast<const f32x4_t*>(p + (int64_t)k * rows * N);
+    for (int k0 = 1; k0 < kp; k0 += kSumBatch) {
+        f32x4_t w[kSumBatch];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += w[i];
+        for (int j = 0; j < kSumBatch; ++j)
+            if (k0 + j < kp) w[j] = *reinterpret_cast<const f32x4_t*>(p + (k0 + j) * part);
+#pragma unroll
+        for (int j = 0; j < kSumBatch; ++j)
+            if (k0 + j < kp) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] += w[j][i];
+            }
     }
     uint16_t* yp = y + m * ldy + n;
 #pragma unroll
