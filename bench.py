@@ -319,7 +319,8 @@ def time_w8a8(name: str, M: int, steps: int = 20, copies: int = 4) -> dict:
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     k_parts = ws_bytes // (M * N * 4) if ws_bytes else 1
     cu = torch.cuda.get_device_properties(0).multi_processor_count
-    tile = wq.wq_query_w8a8_plan(M, N, K, cu, ws is not None)["tile"]
+    plan = wq.wq_query_w8a8_plan(M, N, K, cu, ws is not None)
+    tile = "%dx%d%s" % (plan["tile"] + (" streaming" if plan["streaming"] else "",))
 
     def step(i):
         wq.wq_quantize_x_fp8(x, M, K, xq)
@@ -358,7 +359,7 @@ def time_w8a8(name: str, M: int, steps: int = 20, copies: int = 4) -> dict:
     torch.cuda.empty_cache()
     return {"us_per_call": round(us, 2), "quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2),
             "gemm_TFLOPs": round(tf, 1), "pct_of_fp8_mfma_peak": round(100 * tf / FP8_MFMA_PEAK_TFLOPS, 1),
-            "k_parts": k_parts, "tile": "%dx%d" % tile}
+            "k_parts": k_parts, "tile": tile}
 
 
 def graph_time_us(step, steps: int = 100, windows: int = 9) -> dict:

@@ -456,7 +456,9 @@ wq_status wq_query_gemm_plan(int fmt, int path, int64_t M, int64_t N, int64_t K,
                              int with_workspace, int* plan);
 
 /* W8A8 (wq_gemm_fp8_w8a8; any M the activation packer accepts):
- * plan[3] = { output tile rows, tile columns, K parts across work-groups }.
+ * plan[4] = { output tile rows, tile columns, K parts across work-groups,
+ * kernel: 0 = the LDS-staged tile kernel, 1 = the weight-streaming tile of up
+ * to 64 rows (then the columns are those of one work-group) }.
  * Source: atlas docs "Module m16_tc", ARM ORDER rung 6 (the W8A8 prefill
  * rung) and "WHY THE FFN ARM LOSES" (grids against the machine's slots). */
 wq_status wq_query_w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, int with_workspace, int* plan);

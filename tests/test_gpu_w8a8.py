@@ -319,13 +319,16 @@ def test_w8a8_depth_boundary(M, stages_reset):
     check_w8a8(compare.grade(y[:, cols], y64, floor_w8a8(xc, xs, codes, scales, K), "bf16"))
 
 
-@pytest.mark.parametrize("name", ["gate_up", "down"])
-def test_w8a8_small_grid_rows_equal_large_grid(name, stages_reset):
+@pytest.mark.parametrize("name,small", [("gate_up", (16, 48, 128, 512)), ("down", (128,))])
+def test_w8a8_small_grid_rows_equal_large_grid(name, small, stages_reset):
     """At the FFN sizes M = 2048 runs 128 x 128 tiles on the two-stage
-    pipeline; M = 48 runs 64-row tiles and M = 128 the four-stage pipeline (at
-    most one work-group per CU), and gate/up M = 512 the 256 x 256 tile.  Rows
-    depend only on their own activations, so the smaller calls equal the first
-    rows of the large one bit for bit."""
+    pipeline; gate/up M = 16 and 48 run the weight-streaming tile (one K group,
+    so the same fold order), M = 128 the four-stage pipeline (at most one
+    work-group per CU), and gate/up M = 512 the 256 x 256 tile.  Rows depend
+    only on their own activations, so the smaller calls equal the first rows
+    of the large one bit for bit.  (FFN down at M <= 64 without a workspace
+    streams with 3 K groups, another summation order: graded against the
+    oracle by the parity tests.)"""
     wq = U.wqmod()
     fmt, N, K, Ms, (codes, scales) = U.config_inputs(name)
     packed = U.pack_fp8(codes, scales)
@@ -334,7 +337,7 @@ def test_w8a8_small_grid_rows_equal_large_grid(name, stages_reset):
     U.note("w8a8 %s M=2048 (two stages)" % name)
     assert wq.wq_query_w8a8_plan(2048, N, K, 256, False)["tile"] == (128, 128)
     ybig, _ = run(packed, N, K, xq, 2048)
-    for M in (48, 128, 512):
+    for M in small:
         U.note("w8a8 %s M=%d (plan %s)" % (name, M, wq.wq_query_w8a8_plan(M, N, K, 256, False)))
         xq2, _, _ = quantize(xb[:M], K)
         y, _ = run(packed, N, K, xq2, M)
@@ -368,18 +371,18 @@ def test_w8a8_parts_match_oracle(N, K, M, kp, kparts_reset):
         assert np.array_equal(run(packed, N, K, xq, M, ws="auto")[0], y)
 
 
-@pytest.mark.parametrize("name,M,kp", [("down", 256, 6), ("down", 128, 6), ("down", 64, 3), ("gate_up", 64, 3),
+@pytest.mark.parametrize("name,M,kp", [("down", 256, 6), ("down", 128, 6), ("down", 64, 4), ("gate_up", 64, 1),
                                        ("gate_up", 128, 3), ("down", 1024, 3)])
 def test_w8a8_automatic_split(name, M, kp, kparts_reset):
     """The automatic plan at the FFN sizes: FFN down at M = 256 in 6 K parts
     (80 128 x 128 tiles, two work-groups per CU), at M = 128 in 6 (40 tiles),
-    at M = 64 in 3 (80 64 x 64 tiles), at M = 1024 in 3 on 256 x 256 tiles
-    (80 tiles, one work-group per CU); gate/up at M = 64 in 3 (136 64 x 128
-    tiles, two work-groups per CU), at M = 128 in 3 and with K whole from
-    M = 256 on (sampled columns against the oracle)."""
+    at M = 64 on the weight-streaming tile in 4 (the FP8 decode tile's plan),
+    at M = 1024 in 3 on 256 x 256 tiles (80 tiles, one work-group per CU);
+    gate/up at M = 64 on the streaming tile with K whole, at M = 128 in 3 and
+    with K whole from M = 256 on (sampled columns against the oracle)."""
     wq = U.wqmod()
     fmt, N, K, Ms, (codes, scales) = U.config_inputs(name)
-    assert wq.wq_w8a8_workspace_bytes(M, N, K) == kp * M * N * 4
+    assert wq.wq_w8a8_workspace_bytes(M, N, K) == (kp * M * N * 4 if kp > 1 else 0)
     assert wq.wq_w8a8_workspace_bytes(256, 17408, 5120) == 0        # gate/up keeps K whole
     U.note("w8a8 %s M=%d with a workspace (%d parts)" % (name, M, kp))
     packed = U.pack_fp8(codes, scales)
@@ -403,7 +406,7 @@ def test_w8a8_automatic_big_tile(N, K, M, kp):
     U.note("w8a8 big tile N=%d K=%d M=%d kp=%d" % (N, K, M, kp))
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     if cu == 256:
-        assert wq.wq_query_w8a8_plan(M, N, K, cu, True) == {"tile": (256, 256), "kparts": kp}
+        assert wq.wq_query_w8a8_plan(M, N, K, cu, True) == {"tile": (256, 256), "kparts": kp, "streaming": False}
     codes, scales = synth.fp8_weights(N, K, 2100 + N)
     packed = U.pack_fp8(codes, scales)
     xb = synth.x_bf16(M, K, 2200 + M)
@@ -415,6 +418,31 @@ def test_w8a8_automatic_big_tile(N, K, M, kp):
     U.note("  %s" % r)
     check_w8a8(r)
     assert np.array_equal(run(packed, N, K, xq, M, ws="auto")[0], y)
+
+
+def test_w8a8_streaming_tile_bits(kparts_reset):
+    """The weight-streaming tile with one K group runs the tile kernel's
+    arithmetic: FFN down in 4 K parts at M = 48 (streaming tile, 5
+    column-waves) equals the first 48 rows of M = 128 in 4 parts (128 x 128
+    tiles) bit for bit, NaN-filled workspaces both; and M = 48 against the
+    oracle on sampled columns."""
+    wq = U.wqmod()
+    fmt, N, K, Ms, (codes, scales) = U.config_inputs("down")
+    wq.wq_set_kparts(4)
+    assert wq.wq_query_w8a8_plan(48, N, K, 256, True)["streaming"]
+    assert not wq.wq_query_w8a8_plan(128, N, K, 256, True)["streaming"]
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(128, K, 2301)
+    xq, xc, xs = quantize(xb, K)
+    U.note("w8a8 down M=128 in 4 parts (tile kernel)")
+    ybig, _ = run(packed, N, K, xq, 128, ws="auto")
+    U.note("w8a8 down M=48 in 4 parts (streaming tile)")
+    xq48, xc48, xs48 = quantize(xb[:48], K)
+    y, _ = run(packed, N, K, xq48, 48, ws="auto")
+    assert np.array_equal(y, ybig[:48])
+    cols = U.sample_cols(N, 71, 256)
+    y64 = oracle.gemm_w8a8(xc48, xs48, codes, scales, cols=cols)
+    check_w8a8(compare.grade(y[:, cols], y64, floor_w8a8(xc48, xs48, codes, scales, K), "bf16"))
 
 
 def test_w8a8_workspace_errors(kparts_reset):

@@ -172,21 +172,23 @@ def test_query_validation():
 
 
 # W8A8 on 256 CUs, FFN gate/up (17408 x 5120) and down (5120 x 17408):
-# M -> (tile rows, tile columns, K parts) with a workspace, and the tile
-# without one (K whole) -- the choices of the timed sweeps: 64-row tiles in
-# 3 parts for small M; 128 x 128 split while the grid is short; one part for
-# gate/up from M = 192 on; 256 x 256 where its coarser rounds still come out
-# ahead (gate/up M = 512 and 4096, down M = 1024 and 2048 in 3 parts) and
-# above M = 4096.
+# M -> (tile rows, tile columns, K parts) with a workspace, and the tile rows
+# without one (K whole) -- the choices of the timed sweeps: up to 64 rows the
+# weight-streaming tile with the FP8 decode tile's plan (16 / 32 / 64 rows,
+# 5 column-waves of 16 columns; down in 4 K parts, or 2 column-waves and K
+# whole without a workspace); 128 x 128 split while the grid is short; one
+# part for gate/up from M = 192 on; 256 x 256 where its coarser rounds still
+# come out ahead (gate/up M = 512 and 4096, down M = 1024 and 2048 in 3
+# parts) and above M = 4096.
 W8A8_PLANS = {
-    "gate_up": {1: ((64, 128, 3), 64), 16: ((64, 128, 3), 64), 64: ((64, 128, 3), 64),
+    "gate_up": {1: ((16, 80, 1), 16), 16: ((16, 80, 1), 16), 32: ((32, 80, 1), 32), 64: ((64, 80, 1), 64),
                 96: ((128, 128, 3), 128), 128: ((128, 128, 3), 128), 192: ((128, 128, 1), 128),
                 256: ((128, 128, 1), 128), 512: ((256, 256, 1), 256), 1024: ((128, 128, 1), 128),
                 2048: ((128, 128, 1), 128), 4096: ((256, 256, 1), 256), 8192: ((256, 256, 1), 256)},
-    "down": {1: ((64, 64, 3), 64), 16: ((64, 64, 3), 64), 64: ((64, 64, 3), 64), 96: ((128, 128, 6), 128),
-             128: ((128, 128, 6), 128), 192: ((128, 128, 6), 128), 256: ((128, 128, 6), 128),
-             512: ((128, 128, 3), 128), 1024: ((256, 256, 3), 128), 2048: ((256, 256, 3), 128),
-             4096: ((128, 128, 1), 128), 8192: ((256, 256, 1), 256)},
+    "down": {1: ((16, 80, 4), 16), 16: ((16, 80, 4), 16), 48: ((64, 80, 4), 64), 64: ((64, 80, 4), 64),
+             96: ((128, 128, 6), 128), 128: ((128, 128, 6), 128), 192: ((128, 128, 6), 128),
+             256: ((128, 128, 6), 128), 512: ((128, 128, 3), 128), 1024: ((256, 256, 3), 128),
+             2048: ((256, 256, 3), 128), 4096: ((128, 128, 1), 128), 8192: ((256, 256, 1), 256)},
 }
 FFN = {"gate_up": (17408, 5120), "down": (5120, 17408)}
 
@@ -197,8 +199,26 @@ def test_measured_w8a8_plans(name):
     for M, (want, rows_no_ws) in W8A8_PLANS[name].items():
         p = wq.wq_query_w8a8_plan(M, N, K, CU, True)
         assert p["tile"] + (p["kparts"],) == want, (name, M, p)
+        assert p["streaming"] == (M <= 64), (name, M, p)
         q = wq.wq_query_w8a8_plan(M, N, K, CU, False)
         assert q["kparts"] == 1 and q["tile"][0] == rows_no_ws, (name, M, q)
+    # the streaming tile's columns without a workspace: FFN down's one-part plan (2 column-waves)
+    if name == "down":
+        assert wq.wq_query_w8a8_plan(16, N, K, CU, False)["tile"] == (16, 32)
+
+
+def test_w8a8_streaming_only_while_staging_is_small():
+    """The streaming tile takes M <= 64 while a work-group's staged activations
+    (Mpad x K) are at most twice its weight bytes (16 column-waves x 16 x K):
+    attention K/V (one column-wave a work-group) up to 32 rows, then the
+    64-row tile kernel."""
+    for M in (1, 16, 32):
+        assert wq.wq_query_w8a8_plan(M, 1024, 5120, CU, True)["streaming"]
+    for M in (33, 48, 64):
+        p = wq.wq_query_w8a8_plan(M, 1024, 5120, CU, True)
+        assert not p["streaming"] and p["tile"][0] == 64
+    for M in (33, 64):
+        assert wq.wq_query_w8a8_plan(M, 6144, 5120, CU, True)["streaming"]      # 2 column-waves
 
 
 def test_w8a8_big_tile_only_where_fitted(levers_reset):
@@ -240,6 +260,14 @@ def test_w8a8_rule_invariants():
         (r, c), kp = p["tile"], p["kparts"]
         where = (M, N, K, cu, ws, p)
         mpad = -(-M // 16) * 16
+        if p["streaming"]:
+            # the weight-streaming tile: the FP8 decode tile's rules (16-row tiles
+            # covering Mpad, 1..8 column-waves of 16 columns, parts only with a
+            # workspace), staging at most twice a work-group's weight bytes
+            assert mpad <= 64 and r == (16 if mpad <= 16 else 32 if mpad <= 32 else 64), where
+            assert c % 16 == 0 and 16 <= c <= 128 and mpad <= 2 * c, where
+            assert 1 <= kp <= 32 and (ws or kp == 1), where
+            continue
         if mpad <= 64:
             assert r == 64, where
         elif mpad > 4096:

@@ -183,24 +183,27 @@ Plan make_plan(int kind, int64_t N, int64_t K, int cu, const Options& o, bool ws
     p.n_tiles = (int)(N / 16);
     p.KB = (int)(K / 128);
     ws = ws && kind != wq::KIND_GEMV_FP8;      // the GEMV keeps its K split inside the work-group
+    // the W8A8 streaming tile streams the FP8 tile's units: it takes that tile's measured plans
+    const int tkind = kind == wq::KIND_W8A8_STREAM ? wq::KIND_MFMA_FP8 : kind;
     const TableEntry* te = nullptr;
     if (cu == 256) {
         if (ws)
             for (const TableEntry& e : kSplitTable)
-                if (e.kind == kind && e.N == N && e.K == K) te = &e;
+                if (e.kind == tkind && e.N == N && e.K == K) te = &e;
         if (!te)
             for (const TableEntry& e : kTable)
-                if (e.kind == kind && e.N == N && e.K == K) te = &e;
+                if (e.kind == tkind && e.N == N && e.K == K) te = &e;
         // the GEMV streams the same one-tile units as the FP8 MFMA tile
         if (!te && kind == wq::KIND_GEMV_FP8)
             for (const TableEntry& e : kTable)
                 if (e.kind == wq::KIND_MFMA_FP8 && e.N == N && e.K == K) te = &e;
     }
+    const bool one_tile = kind == wq::KIND_GEMV_FP8 || kind == wq::KIND_W8A8_STREAM;
     if (o.nt || o.sn) {
-        p.nt = kind == wq::KIND_GEMV_FP8 ? 1 : (o.nt ? o.nt : 1);
+        p.nt = one_tile ? 1 : (o.nt ? o.nt : 1);
         p.sn = o.sn ? std::min(o.sn, 8) : 1;
     } else if (te) {
-        p.nt = kind == wq::KIND_GEMV_FP8 ? 1 : te->nt;
+        p.nt = one_tile ? 1 : te->nt;
         p.sn = te->sn;
     } else {
         // one tile per wave; as many column-waves per work-group as leaves at
@@ -768,6 +771,22 @@ W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
     const int KB = (int)(K / 128);
     const int max_kp = std::max(1, std::min(KB, wq::kMaxKParts));
     const int64_t mpad = (M + 15) / 16 * 16;
+    // Up to 64 rows the product runs on the weight-streaming tile with the FP8
+    // decode tile's plan for the shape (unless a tile is forced), while each
+    // work-group's staged activations (Mpad x K codes) are at most twice its
+    // weight bytes (16 sn x K): measured against the 64-row tiles (GEMM and
+    // parts sum, quantised activations prepared), gate/up M = 1 / 16 / 32 /
+    // 48 / 64 16.3 / 16.5 / 17.4 / 19.9 / 20.2 us against 20.6 / 21.5 /
+    // 23.1 / 25.0 / 26.7; FFN down (4 parts) 18.4 / 18.9 / 19.9 / 22.0 /
+    // 23.1 against 21.0 / 21.6 / 22.1 / 22.5 / 23.2; attention Q 8.5 / 8.7 /
+    // 10.0 / 12.6 / 13.0 against 11.6 / 12.0 / 12.6 / 12.9 / 13.1; attention
+    // K/V (one column-wave a work-group) 5.7 / 6.0 / 7.4 at M <= 32 against
+    // 8.6 / 9.2 / 9.7, but 10.8 / 11.0 at M = 48 / 64 against 9.8 -- there
+    // every work-group stages four times its weight bytes.
+    if (mpad <= 64 && forced_w8a8_tile() < 0) {
+        const Plan sp = cached_plan(wq::KIND_W8A8_STREAM, N, K, cu, ws);
+        if (mpad <= 32 * sp.sn) return {wq::W8_STREAM, sp.kp};
+    }
     int cand[2], nc = 0;
     if (forced_w8a8_tile() >= 0) cand[nc++] = forced_w8a8_tile();
     else if (mpad <= 64) {
@@ -868,9 +887,16 @@ wq_status wq_query_w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, int with_w
         (uint64_t)N * (uint64_t)K >= ((uint64_t)1 << 32) || !wq_x_fp8_packed_bytes(M, K))
         return WQ_ERR_SHAPE;
     const W8Plan p = w8a8_plan(M, N, K, cu, with_workspace != 0);
-    plan[0] = wq::w8_tile_rows(p.tile);
-    plan[1] = wq::w8_tile_cols(p.tile);
+    if (p.tile == wq::W8_STREAM) {   // rows of the row tiles, columns of a work-group
+        const int64_t mpad = (M + 15) / 16 * 16;
+        plan[0] = mpad <= 16 ? 16 : mpad <= 32 ? 32 : 64;
+        plan[1] = 16 * cached_plan(wq::KIND_W8A8_STREAM, N, K, cu, with_workspace != 0).sn;
+    } else {
+        plan[0] = wq::w8_tile_rows(p.tile);
+        plan[1] = wq::w8_tile_cols(p.tile);
+    }
     plan[2] = p.kp;
+    plan[3] = p.tile == wq::W8_STREAM ? 1 : 0;
     return WQ_OK;
 }
 
@@ -923,6 +949,29 @@ wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void*
     if (kp > 1) {
         if (workspace_bytes < w8a8_workspace_bytes(M, N, kp)) return WQ_ERR_WORKSPACE;
         if (!aligned16(workspace)) return WQ_ERR_ALIGN;
+    }
+    if (plan.tile == wq::W8_STREAM) {
+        const Plan p = cached_plan(wq::KIND_W8A8_STREAM, N, K, dev.cu, workspace != nullptr);
+        wq::GemmArgs a{};
+        a.codes = static_cast<const uint8_t*>(packed);
+        a.scales = static_cast<const uint8_t*>(packed) + N * K;
+        a.qmap = nullptr;
+        a.x = static_cast<const uint16_t*>(xq);
+        a.ldx = (M + 15) / 16 * 16;
+        a.y = y;
+        a.ldy = ldy;
+        a.rows = (int)M;
+        a.N = (int)N;
+        a.KB = p.KB;
+        a.n_tiles = p.n_tiles;
+        a.n_cg = p.n_cg;
+        a.sn = p.sn;
+        a.kp = p.kp;
+        a.ws = p.kp > 1 ? static_cast<float*>(workspace) : nullptr;
+        return wq::launch_gemm(wq::KIND_W8A8_STREAM, 1, 0, a, p.split, static_cast<hipStream_t>(hip_stream)) ==
+                       hipSuccess
+                   ? WQ_OK
+                   : WQ_ERR_HIP;
     }
     return wq::launch_w8a8(static_cast<const uint8_t*>(packed), (int)N, (int)K, static_cast<const uint8_t*>(xq),
                            (int)M, y, ldy, plan.tile, kp, kp > 1 ? static_cast<float*>(workspace) : nullptr, dev.cu,

@@ -137,6 +137,27 @@ __device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16) += A(16x128) * B(128x16) on E4M3 codes (the W8A8 product): lane l
+// supplies its 32 codes of A row (l % 16) and of B column (l % 16), as the
+// packed 2 KiB units lay them out (16 bytes of each 1 KiB chunk); lane l
+// receives D rows 4*(l/16) .. 4*(l/16)+3 of column (l % 16).
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma_fp8(i32x8_t a, i32x8_t b, f32x4_t c)
+{
+    // scale operands 0: the unscaled v_mfma_f32_16x16x128_f8f6f4, both sides E4M3
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// A 16-row x 128-K operand from a 2 KB unit staged in LDS: lane l takes its
+// 16 bytes of chunk 0 and of chunk 1.
+__device__ __forceinline__ i32x8_t lds_frag(const uint8_t* unit, int lane)
+{
+    const uint4 p = *reinterpret_cast<const uint4*>(unit + lane * 16);
+    const uint4 q = *reinterpret_cast<const uint4*>(unit + 1024 + lane * 16);
+    return i32x8_t{(int)p.x, (int)p.y, (int)p.z, (int)p.w, (int)q.x, (int)q.y, (int)q.z, (int)q.w};
+}
+
 // --------------------------------------------------------------- epilogue
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v)
 {

@@ -28,6 +28,8 @@ enum Kind : int {
     KIND_MFMA_LUT = 1,   // 16-row FP16 MFMA tile, 3-bit LUT weights
     KIND_GEMV_FP8 = 2,   // strict-K-order FP32 GEMV, M <= 4, FP8 weights, one tile per wave
     KIND_MFMA_LUT3D = 3, // 16-row FP16 MFMA tile, 3-bit LUT weights stored densely (3 bits a code)
+    KIND_W8A8_STREAM = 4, // W8A8 product on the weight-streaming tile (M <= 64): FP8 weights through
+                          // the register ring, packed FP8 activations and their scales staged in LDS
 };
 
 constexpr bool is_lut_kind(int kind) { return kind == KIND_MFMA_LUT || kind == KIND_MFMA_LUT3D; }
@@ -45,7 +47,7 @@ constexpr int k_align(int kind) { return is_lut_kind(kind) ? 8 : 1; }
 // stages four 4-row blocks.
 constexpr int chunk_blocks16(int kind, int mt)
 {
-    return kind == KIND_MFMA_FP8 ? 2 * mt : is_lut_kind(kind) ? 4 * mt : 4;
+    return kind == KIND_MFMA_FP8 || kind == KIND_W8A8_STREAM ? 2 * mt : is_lut_kind(kind) ? 4 * mt : 4;
 }
 
 // LDS bytes of one staged activation chunk (16-row blocks, rows padded to 272 bytes)
@@ -63,10 +65,13 @@ constexpr int kMaxKParts = 32;
 
 // 16-byte activation pieces each lane loads per chunk when SN column-waves
 // share it: ceil(chunk pieces / (64 * SN)); a chunk is chunk_blocks16 blocks
-// x 16 rows x 16 pieces for the MFMA tiles, x 4 rows x 16 pieces for the GEMV.
+// x 16 rows x 16 pieces for the BF16/FP16 MFMA tiles, x 4 rows x 16 pieces for
+// the GEMV, and x one 2 KiB FP8 unit (128 pieces) for the W8A8 streaming tile
+// (whose activation scales are loaded apart).
 constexpr int x_pieces_per_lane(int kind, int sn, int mt = 1)
 {
-    const int pieces = chunk_blocks16(kind, mt) * (kind == KIND_GEMV_FP8 ? 4 : 16) * 16;
+    const int per_block = kind == KIND_GEMV_FP8 ? 4 * 16 : kind == KIND_W8A8_STREAM ? 128 : 16 * 16;
+    const int pieces = chunk_blocks16(kind, mt) * per_block;
     return (pieces + 64 * sn - 1) / (64 * sn);
 }
 
@@ -103,7 +108,7 @@ constexpr bool split_ok(int kind, int nt, int sn, int split)
 {
     if (sn < 1 || split < 1 || split % sn || split > max_split(kind, nt, sn)) return false;
     if (sn > 8 || split / sn > kMaxKGroups) return false;
-    if (kind == KIND_GEMV_FP8) return nt == 1;
+    if (kind == KIND_GEMV_FP8 || kind == KIND_W8A8_STREAM) return nt == 1;
     return nt == 1 || nt == 2;
 }
 
@@ -113,8 +118,8 @@ struct GemmArgs {
     const uint8_t* codes;     // packed code units
     const void* scales;       // FP8: float [N/128][KB]; LUT: half [n_tiles][KB/8][16][8]
     const uint16_t* qmap;     // LUT: 8 FP16 map entries (4-byte aligned)
-    const uint16_t* x;        // activations [rows][ldx]
-    int64_t ldx;
+    const uint16_t* x;        // activations [rows][ldx]; W8A8 streaming tile: the packed FP8 activations
+    int64_t ldx;              //   (units, then scales) and ldx = their padded row count
     uint16_t* y;              // outputs [rows][ldy]
     int64_t ldy;
     int rows;                 // rows in this launch: 1..16, or 17..32 (one-tile MFMA waves)
@@ -154,6 +159,7 @@ enum W8Tile : int {
     W8_T256 = 1,      // 256 x 256: 8 waves of 64 x 128
     W8_T64x128 = 2,   // 64 x 128: 4 waves of 64 x 32
     W8_T64x64 = 3,    // 64 x 64: 4 waves of 32 x 32
+    W8_STREAM = 4,    // Mpad <= 64: the weight-streaming tile (KIND_W8A8_STREAM, launched by launch_gemm)
 };
 constexpr int w8_tile_rows(int t) { return t == W8_T256 ? 256 : t == W8_T128 ? 128 : 64; }
 constexpr int w8_tile_cols(int t) { return t == W8_T256 ? 256 : t == W8_T64x64 ? 64 : 128; }

@@ -587,6 +587,159 @@ struct MfmaLut {
     }
 };
 
+// ---- W8A8 product on the weight-streaming tile (M <= 64) --------------------
+// Activation staging for it: a chunk holds two K blocks, each the packed FP8
+// activation units of MT row tiles (2 KiB each, in the operand order the
+// MFMA reads: lane l's 16 bytes of each 1 KiB half) followed by the 16 MT
+// rows' FP32 scales of that block.  The unit pieces are dealt over the K
+// group's SN*64 lanes as in XChunk; the scale pieces (16 bytes = 4 rows)
+// over the lanes of column-wave 0.  Blocks past the K range, row tiles past
+// the padded rows and rows past them read zeros.
+template <int XPL, int MT>
+struct XqChunk {
+    static constexpr int kBlocks = 2;                         // K blocks per chunk
+    static constexpr int kUnitPieces = MT * 128;              // 16-byte pieces of one block's units
+    static constexpr int kScalePieces = MT * 4;               // ... of one block's row scales
+    static constexpr int kBlockBytes = MT * 2048 + MT * 64;
+    static constexpr int kChunkBytes = kBlocks * kBlockBytes;
+    static constexpr int kXChunkPieces = kBlocks * kUnitPieces;
+    static_assert(kBlocks * kScalePieces <= 64, "the scale pieces fit one wave");
+    buf_t rx;                 // activation units [Mpad/16][KB] x 2 KiB
+    buf_t rs;                 // activation scales [KB][Mpad] FP32
+    uint32_t sstride;         // bytes of one K block's scales (Mpad * 4)
+    uint32_t vo[XPL];         // byte offset of unit piece i at K block 0, or out of range
+    int blk[XPL];             // K block of piece i inside the chunk (large: no piece)
+    int dst[XPL];             // LDS offset of piece i inside a chunk buffer (-1: no piece)
+    uint4 r[XPL];
+    uint32_t svo;             // the lane's scale piece, as vo
+    int sblk, sdst;
+    uint4 sr;
+
+    __device__ void init(const GemmArgs& a, int lane, int cw, int sn)
+    {
+        const int mpad = (int)a.ldx;
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x);
+        rx = make_buf(base, (uint32_t)((int64_t)mpad * a.KB * 128));
+        rs = make_buf(base + (int64_t)mpad * a.KB * 128, (uint32_t)((int64_t)a.KB * mpad * 4));
+        sstride = (uint32_t)mpad * 4u;
+#pragma unroll
+        for (int i = 0; i < XPL; ++i) {
+            const int q = cw * 64 + lane + i * sn * 64;
+            const int b = q / kUnitPieces, rem = q % kUnitPieces, h = rem >> 7, off = rem & 127;
+            const bool ok = q < kXChunkPieces && 16 * h < mpad;
+            blk[i] = ok ? b : (1 << 29);
+            vo[i] = ok ? (uint32_t)((h * a.KB + b) * 2048 + off * 16) : kBufOutOfRange;
+            dst[i] = q < kXChunkPieces ? b * kBlockBytes + h * 2048 + off * 16 : -1;
+        }
+        const int q = cw * 64 + lane;
+        const int b = q / kScalePieces, sp = q % kScalePieces;
+        const bool ok = q < kBlocks * kScalePieces && 4 * sp < mpad;
+        sblk = ok ? b : (1 << 29);
+        svo = ok ? (uint32_t)b * sstride + (uint32_t)sp * 16u : kBufOutOfRange;
+        sdst = q < kBlocks * kScalePieces ? b * kBlockBytes + MT * 2048 + sp * 16 : -1;
+    }
+
+    __device__ __forceinline__ void load(int kb, int kb_end)
+    {
+        const int lim = kb_end - kb;
+#pragma unroll
+        for (int i = 0; i < XPL; ++i) r[i] = buf_load16(rx, blk[i] < lim ? vo[i] : kBufOutOfRange, (uint32_t)kb * 2048u);
+        sr = buf_load16(rs, sblk < lim ? svo : kBufOutOfRange, (uint32_t)kb * sstride);
+    }
+
+    __device__ __forceinline__ void stage(uint8_t* buf) const
+    {
+#pragma unroll
+        for (int i = 0; i < XPL; ++i)
+            if (dst[i] >= 0) *reinterpret_cast<uint4*>(buf + dst[i]) = r[i];
+        if (sdst >= 0) *reinterpret_cast<uint4*>(buf + sdst) = sr;
+    }
+};
+
+// One 16-column weight tile per wave, streamed as in the FP8 decode tile; per
+// K block one v_mfma_f32_16x16x128_f8f6f4 per row tile (A = the activation
+// unit, B = the weight unit: D[m][n] over the block's 128 codes) folded onto
+// FP32 outer accumulators times sx[m][kb] * sw[n/128][kb].  Operands,
+// products and fold are those of the W8A8 tile kernel, in the same order, so
+// a plan with one K group gives its bits for the same K parts.  Lane l holds
+// rows 16h + 4(l/16) .. +3 of column l % 16 of row tile h.
+template <int MT>
+struct MfmaW8A8 : Fp8Stream<1> {
+    static constexpr int KIND = KIND_W8A8_STREAM;
+    static constexpr bool kSumInRegisters = true;   // K groups combine through add_partial
+    static constexpr int NTILES = 1;
+    static constexpr int ROWS = 16 * MT;
+    static constexpr int KALIGN = k_align(KIND);
+    template <int XPL> using Stage = XqChunk<XPL, MT>;
+    using typename Fp8Stream<1>::Unit;
+    using Fp8Stream<1>::lane;
+    using Fp8Stream<1>::ntiles;
+    f32x4_t outer[MT];
+
+    __device__ MfmaW8A8(const GemmArgs& a, int l, int tile0) : Fp8Stream<1>(a, l, tile0)
+    {
+#pragma unroll
+        for (int h = 0; h < MT; ++h) outer[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    __device__ __forceinline__ void compute(const Unit& r, const uint8_t* xblk, int)
+    {
+        const i32x8_t bw = i32x8_t{(int)r.w[0][0].x, (int)r.w[0][0].y, (int)r.w[0][0].z, (int)r.w[0][0].w,
+                                   (int)r.w[0][1].x, (int)r.w[0][1].y, (int)r.w[0][1].z, (int)r.w[0][1].w};
+        f32x4_t blk[MT];
+#pragma unroll
+        for (int h = 0; h < MT; ++h) blk[h] = mfma_fp8(lds_frag(xblk + h * 2048, lane), bw, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const f32x4_t sx =
+                *reinterpret_cast<const f32x4_t*>(xblk + MT * 2048 + (16 * h + 4 * (lane >> 4)) * 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) outer[h][q] = __builtin_fmaf(blk[h][q], sx[q] * r.s, outer[h][q]);
+        }
+    }
+
+    template <bool F16_OUT>
+    __device__ __forceinline__ void store_direct(const GemmArgs& a, int tile0) const
+    {
+        if (ntiles < 1) return;
+        const int n = tile0 * 16 + (lane & 15);
+#pragma unroll
+        for (int h = 0; h < MT; ++h)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = 16 * h + 4 * (lane >> 4) + q;
+                if (m < a.rows)
+                    a.y[(int64_t)m * a.ldy + n] = F16_OUT ? f32_to_f16_rne(outer[h][q]) : f32_to_bf16_rne(outer[h][q]);
+            }
+    }
+
+    // slot: [ROWS][16] FP32 partial tile of this wave, lane-major
+    __device__ __forceinline__ void store_partial(float* slot) const
+    {
+#pragma unroll
+        for (int h = 0; h < MT; ++h) *reinterpret_cast<f32x4_t*>(slot + h * 256 + lane * 4) = outer[h];
+    }
+
+    __device__ __forceinline__ void add_partial(const float* slot)
+    {
+#pragma unroll
+        for (int h = 0; h < MT; ++h) outer[h] += *reinterpret_cast<const f32x4_t*>(slot + h * 256 + lane * 4);
+    }
+
+    __device__ __forceinline__ void store_part(float* dst, const GemmArgs& a, int tile0) const
+    {
+        if (ntiles < 1) return;
+        const int n = tile0 * 16 + (lane & 15);
+#pragma unroll
+        for (int h = 0; h < MT; ++h)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = 16 * h + 4 * (lane >> 4) + q;
+                if (m < a.rows) dst[(int64_t)m * a.N + n] = outer[h][q];
+            }
+    }
+};
+
 // ---- FP8 weights, strict-K-order GEMV (MR <= 4 rows) ------------------------
 // One tile per wave, loaded exactly as the MFMA tile loads it: lane l holds
 // column c = l%16 and, within each 32-wide MFMA step s of a K block, the
@@ -756,7 +909,7 @@ gemm_kernel(GemmArgs a)
         // ahead of the weight ring's first burst, which they would otherwise
         // queue behind (~256 cycles; attention K/V 7.7 -> 7.2 us, the large
         // shapes within 1%; the LUT tile measured no gain from it)
-        if constexpr (Pol::KIND == KIND_MFMA_FP8) __builtin_amdgcn_s_sleep(4);
+        if constexpr (Pol::KIND == KIND_MFMA_FP8 || Pol::KIND == KIND_W8A8_STREAM) __builtin_amdgcn_s_sleep(4);
 #pragma unroll
         for (int i = 0; i < D; ++i) pol.load(r[i], kb0 + i, i < len, i);
         xc.stage(xb);
@@ -1136,10 +1289,35 @@ hipError_t launch_sum_parts(const float* ws, int kp, int rows, int N, uint16_t* 
     return hipGetLastError();
 }
 
+// W8A8 streaming tile: MT row tiles cover the padded rows (1, 2 or 4)
+template <int MT>
+static hipError_t launch_w8s(const GemmArgs& a, int split, hipStream_t s)
+{
+    const int d = split == a.sn ? kDepthMfmaFp8Solo : kDepthMfmaFp8;
+    switch (x_pieces_per_lane(KIND_W8A8_STREAM, a.sn, MT)) {
+#define WQ_W8S_CASE(X)                                                                              \
+    case X:                                                                                         \
+        if constexpr (xpl_used(KIND_W8A8_STREAM, MT, X))                                            \
+            return d == kDepthMfmaFp8Solo ? launch_one<MfmaW8A8<MT>, kDepthMfmaFp8Solo, X, false>(a, split, s) \
+                                          : launch_one<MfmaW8A8<MT>, kDepthMfmaFp8, X, false>(a, split, s);   \
+        return hipErrorInvalidValue;
+        WQ_W8S_CASE(16) WQ_W8S_CASE(8) WQ_W8S_CASE(6) WQ_W8S_CASE(5) WQ_W8S_CASE(4) WQ_W8S_CASE(3)
+        WQ_W8S_CASE(2) WQ_W8S_CASE(1)
+#undef WQ_W8S_CASE
+    default: return hipErrorInvalidValue;
+    }
+}
+
 static hipError_t launch_gemm_parts(int kind, int nt, int gemv_rows, const GemmArgs& a, int split,
                                     hipStream_t stream)
 {
     if (!split_ok(kind, nt, a.sn, split)) return hipErrorInvalidValue;
+    if (kind == KIND_W8A8_STREAM) {
+        if (a.rows <= 16) return launch_w8s<1>(a, split, stream);
+        if (a.rows <= 32) return launch_w8s<2>(a, split, stream);
+        if (a.rows <= 64) return launch_w8s<4>(a, split, stream);
+        return hipErrorInvalidValue;
+    }
     if (kind == KIND_GEMV_FP8) {
         switch (gemv_rows) {
         case 1: return launch_gemv<1>(a, split, stream);

@@ -160,23 +160,6 @@ struct W8Args {
     float* ws;              // kp > 1: partial outputs [kp][M][N]
 };
 
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ f32x4_t mfma_fp8(i32x8_t a, i32x8_t b, f32x4_t c)
-{
-    // scale operands 0: the unscaled v_mfma_f32_16x16x128_f8f6f4, both sides E4M3
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// A 16-row x 128-K operand from a 2 KB unit staged in LDS: lane l takes its
-// 16 bytes of chunk 0 and of chunk 1.
-__device__ __forceinline__ i32x8_t lds_frag(const uint8_t* unit, int lane)
-{
-    const uint4 p = *reinterpret_cast<const uint4*>(unit + lane * 16);
-    const uint4 q = *reinterpret_cast<const uint4*>(unit + 1024 + lane * 16);
-    return i32x8_t{(int)p.x, (int)p.y, (int)p.z, (int)p.w, (int)q.x, (int)q.y, (int)q.z, (int)q.w};
-}
-
 // Wait until at most n vector-memory operations of this wave are outstanding
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
 // left at their maxima, i.e. not waited for).

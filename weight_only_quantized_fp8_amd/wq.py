@@ -251,9 +251,9 @@ def wq_query_gemm_plan(fmt: int, M: int, N: int, K: int, cu: int, with_workspace
 def wq_query_w8a8_plan(M: int, N: int, K: int, cu: int, with_workspace: bool = False) -> dict:
     """Host-only: the tile and K parts a W8A8 call would take on a device with
     `cu` compute units (no device is touched)."""
-    out = (_INT * 3)()
+    out = (_INT * 4)()
     _check(lib.wq_query_w8a8_plan(M, N, K, cu, int(bool(with_workspace)), out), "wq_query_w8a8_plan")
-    return dict(tile=(out[0], out[1]), kparts=out[2])
+    return dict(tile=(out[0], out[1]), kparts=out[2], streaming=bool(out[3]))
 
 
 def wq_unpack_x_fp8(xq, M: int, K: int, codes, scales, stream=None) -> None:
