@@ -430,7 +430,7 @@ def crossover() -> dict:
         out["gemv_vs_mfma"][name] = row
         if name in ("gate_up", "down"):
             r2 = {}
-            for M in (16, 32, 40, 48, 64, 96, 128):
+            for M in (16, 32, 33, 40, 48, 64, 96, 128):
                 x = torch.from_numpy(synth.x_bf16(M, K, synth.SEEDS[name] + 100).view(np.int16)).to(dev).view(
                     torch.bfloat16)
                 y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
