@@ -328,7 +328,7 @@ wq_status wq_gemm_lut3_dense(const void* packed, int64_t N, int64_t K,
  * of that row is NaN (the weight-only paths give NaN or an infinity there).
  *
  * Measured on MI355X at the FFN sizes, quantiser + GEMM with the workspace
- * overtake the decode GEMM run as 32-row calls from M = 40 on. */
+ * overtake the decode GEMM run as 32-row calls from M = 33 on. */
 
 /* Workspace bytes of a W8A8 GEMM of this M, N, K that splits K across
  * work-groups (kp * M * N * 4 for kp parts, following wq_set_kparts); 0 when
