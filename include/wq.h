@@ -357,7 +357,11 @@ size_t wq_x_fp8_packed_bytes(int64_t M, int64_t K);
 wq_status wq_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int64_t K,
                             void* xq, void* hip_stream);
 
-/* y = dequant(xq) . dequant(W)^T with both operands FP8.
+/* y = dequant(xq) . dequant(W)^T with both operands FP8.  Up to 64 rows it
+ * runs on the weight-streaming tile of the decode GEMM (FP8 weight units
+ * through a register ring, the packed activations staged in LDS) where that
+ * stages at most twice a work-group's weight bytes; otherwise, and above, on
+ * an LDS-staged tile kernel (64-row, 128 x 128 or 256 x 256 tiles).
  *   packed  device, from wq_pack_fp8_block with the same N, K (the same packed
  *           matrix serves wq_gemm_fp8_block); N*K < 2^32
  *   xq      device, from wq_quantize_x_fp8 with the same M, K
@@ -370,7 +374,9 @@ wq_status wq_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int6
  *   workspace  NULL, or device scratch of at least wq_w8a8_workspace_bytes(M, N, K)
  *           bytes, 16-byte aligned, contents on entry irrelevant.  With NULL
  *           every output is reduced inside one work-group and row r of the result
- *           depends only on row r of xq.  With a workspace, an M whose output
+ *           depends only on row r of xq (its summation order may still differ
+ *           between Ms that take different kernels, e.g. the streaming tile's K
+ *           groups up to 64 rows).  With a workspace, an M whose output
  *           tiles leave CUs idle also splits K across work-groups: FP32 partial
  *           sums go to the workspace and a second kernel on the same stream adds
  *           them in a fixed order (results stay deterministic for a given M, N, K;
