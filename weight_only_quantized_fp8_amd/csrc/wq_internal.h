@@ -11,7 +11,8 @@ namespace wq {
 // Prefetch depth: weight units in flight per wave beyond the one being
 // computed (the register ring has depth + 1 slots).  FP8 16-row tile: 4 where
 // each wave streams its K range alone (one K group per work-group: gate/up
-// 17.45 -> 17.24 us, FFN down in 4 parts 19.61 -> 19.56), 3 where K groups
+// 17.45 -> 17.24 us, FFN down in 4 parts 19.61 -> 19.56; at 5 and 6 units
+// gate/up 17.31 / 17.37 and down 19.54 / 19.86 against 17.15 / 19.38), 3 where K groups
 // split it (attention output 9.84 us at 3, 10.01 at 4, 10.20 at 5).  GEMV
 // and 32-row tiles: 3.  LUT tile with the quad schedule, 28672 x 8192, M = 16
 // (medians of 15 interleaved windows of 200 graph-replayed calls): one-tile
