@@ -191,6 +191,13 @@ def test_w8a8_integer_exact():
 
 
 def test_w8a8_rows_determinism_strides():
+    """Row r of the result depends only on row r of the activations, for each
+    kernel: calls of at most 32 rows (here the weight-streaming tile, whose
+    plan does not depend on M) equal the matching rows of a 32-row call, calls
+    of more than 64 (the tile kernels, K whole) those of a 150-row call, and the 256 x 256
+    tile (M > 4096) folds the same MFMA blocks in the same order as 128 x 128;
+    repeats are deterministic and a wider row stride leaves the pad alone."""
+    wq = U.wqmod()
     U.note("w8a8 invariants")
     N, K, M = 384, 768, 150
     codes, scales = synth.fp8_weights(N, K, 62)
@@ -198,23 +205,29 @@ def test_w8a8_rows_determinism_strides():
     xb = synth.x_bf16(M, K, 63)
     xq, _, _ = quantize(xb, K)
     y, _ = run(packed, N, K, xq, M)
-    # row r depends only on row r: a 20-row call and the rows 130.. of the call
-    for lo, hi in ((0, 20), (130, 150), (16, 17)):
+    xq64, _, _ = quantize(xb[:32], K)
+    assert wq.wq_query_w8a8_plan(32, N, K, 256, False)["streaming"]
+    y64, _ = run(packed, N, K, xq64, 32)
+    for lo, hi in ((0, 20), (20, 32), (16, 17)):
+        xq2, _, _ = quantize(xb[lo:hi], K)
+        y2, _ = run(packed, N, K, xq2, hi - lo)
+        assert np.array_equal(y2, y64[lo:hi]), (lo, hi)
+    for lo, hi in ((0, 100), (70, 150)):
         xq2, _, _ = quantize(xb[lo:hi], K)
         y2, _ = run(packed, N, K, xq2, hi - lo)
         assert np.array_equal(y2, y[lo:hi]), (lo, hi)
     for _ in range(5):
         assert np.array_equal(run(packed, N, K, xq, M)[0], y)
-    # the 256 x 256 tile (M > 4096) folds the same MFMA blocks in the same
-    # order as the 128 x 128 tile: rows agree bit for bit across the two
+        assert np.array_equal(run(packed, N, K, xq64, 32)[0], y64)
     xbig = np.vstack([xb, synth.x_bf16(4200 - M, K, 64)])
     xqb, _, _ = quantize(xbig, K)
     yb, _ = run(packed, N, K, xqb, 4200)
     assert np.array_equal(yb[:M], y)
     ldy = N + 40
-    canary = np.full((M, ldy), 0x7FAB, dtype=np.uint16)
-    ys, full = run(packed, N, K, xq, M, ldy=ldy, y_init=canary)
-    assert np.array_equal(ys, y) and np.all(full[:, N:] == 0x7FAB)
+    for Mc, xqc, ref in ((M, xq, y), (32, xq64, y64)):
+        canary = np.full((Mc, ldy), 0x7FAB, dtype=np.uint16)
+        ys, full = run(packed, N, K, xqc, Mc, ldy=ldy, y_init=canary)
+        assert np.array_equal(ys, ref) and np.all(full[:, N:] == 0x7FAB), Mc
 
 
 def test_w8a8_graph_replay():
