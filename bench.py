@@ -317,10 +317,12 @@ def time_w8a8(name: str, M: int, steps: int = 20, copies: int = 4) -> dict:
     # the workspace lets a thin grid split K across work-groups (FFN down at small M)
     ws_bytes = wq.wq_w8a8_workspace_bytes(M, N, K)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    k_parts = ws_bytes // (M * N * 4) if ws_bytes else 1
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     plan = wq.wq_query_w8a8_plan(M, N, K, cu, ws is not None)
+    k_parts = plan["kparts"]
     tile = "%dx%d%s" % (plan["tile"] + (" streaming" if plan["streaming"] else "",))
+    if plan["tail"]:   # two column bands: the rest of the columns on their own plan
+        tile += ", columns %d-%d on %dx%d in %d parts" % ((plan["band"], N - 1) + plan["tail"])
 
     def step(i):
         wq.wq_quantize_x_fp8(x, M, K, xq)

@@ -331,9 +331,9 @@ wq_status wq_gemm_lut3_dense(const void* packed, int64_t N, int64_t K,
  * overtake the decode GEMM run as 32-row calls from M = 33 on. */
 
 /* Workspace bytes of a W8A8 GEMM of this M, N, K that splits K across
- * work-groups (kp * M * N * 4 for kp parts, following wq_set_kparts); 0 when
- * it keeps K inside one work-group, for an invalid shape, or with no gfx950
- * device current.
+ * work-groups (kp * M * n * 4 for kp parts over the n columns split, following
+ * wq_set_kparts); 0 when it keeps K inside one work-group, for an invalid
+ * shape, or with no gfx950 device current.
  * Source: atlas docs "Module m16_tc", ARM ORDER rung 6 (W8A8 block-scaled
  * prefill); FLUTE PR "Add optimized_w3: 3-bit LUT GEMM on a new mainloop",
  * "Core contributions" (stream-K for thin grids). */
@@ -380,9 +380,12 @@ wq_status wq_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int6
  *           tiles leave CUs idle also splits K across work-groups: FP32 partial
  *           sums go to the workspace and a second kernel on the same stream adds
  *           them in a fixed order (results stay deterministic for a given M, N, K;
- *           the split, and so the rounding of a row, may differ between Ms).  A
- *           workspace smaller than required returns WQ_ERR_WORKSPACE, a misaligned
- *           one WQ_ERR_ALIGN.
+ *           the split, and so the rounding of a row, may differ between Ms).
+ *           And an M whose grid would end in a mostly idle round of work-group
+ *           slots is served in two column bands, a leading band of whole rounds
+ *           in one K part and the remaining columns as a second launch with K
+ *           split.  A workspace smaller than required returns WQ_ERR_WORKSPACE,
+ *           a misaligned one WQ_ERR_ALIGN.
  * Source: atlas docs "Module m16_tc", ARM ORDER rung 6 (W8A8 block-scaled
  * prefill) and NUMERICS (the two-level fold); arc PR "fix(ArcKernels): FP8
  * bank conflict + the dispatch threshold's provenance", "Worth a separate

@@ -234,6 +234,7 @@ def test_plan_query_matches_the_device():
         kp = wq.wq_query_gemm_plan(fmt, 16, N, K, cu, True)["kparts"]
         assert wq.wq_gemm_workspace_bytes(fmt, 16, N, K) == (kp * 32 * N * 4 if kp > 1 else 0), (fmt, N, K, kp)
     for M, N, K in ((16, 17408, 5120), (16, 5120, 17408), (128, 5120, 17408), (1024, 5120, 17408),
-                    (8192, 17408, 5120), (300, 1280, 1152)):
-        kp = wq.wq_query_w8a8_plan(M, N, K, cu, True)["kparts"]
-        assert wq.wq_w8a8_workspace_bytes(M, N, K) == (kp * M * N * 4 if kp > 1 else 0), (M, N, K, kp)
+                    (8192, 17408, 5120), (300, 1280, 1152), (2048, 17408, 5120), (4096, 5120, 17408)):
+        p = wq.wq_query_w8a8_plan(M, N, K, cu, True)
+        kp, n = (p["tail"][2], N - p["band"]) if p["tail"] else (p["kparts"], N)
+        assert wq.wq_w8a8_workspace_bytes(M, N, K) == (kp * M * n * 4 if kp > 1 else 0), (M, N, K, p)

@@ -419,7 +419,8 @@ def test_w8a8_automatic_big_tile(N, K, M, kp):
     U.note("w8a8 big tile N=%d K=%d M=%d kp=%d" % (N, K, M, kp))
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     if cu == 256:
-        assert wq.wq_query_w8a8_plan(M, N, K, cu, True) == {"tile": (256, 256), "kparts": kp, "streaming": False}
+        p = wq.wq_query_w8a8_plan(M, N, K, cu, True)
+        assert (p["tile"], p["kparts"], p["streaming"], p["tail"]) == ((256, 256), kp, False, None)
     codes, scales = synth.fp8_weights(N, K, 2100 + N)
     packed = U.pack_fp8(codes, scales)
     xb = synth.x_bf16(M, K, 2200 + M)
@@ -431,6 +432,45 @@ def test_w8a8_automatic_big_tile(N, K, M, kp):
     U.note("  %s" % r)
     check_w8a8(r)
     assert np.array_equal(run(packed, N, K, xq, M, ws="auto")[0], y)
+
+
+@pytest.mark.parametrize("name,M", [("gate_up", 1024), ("gate_up", 2048), ("gate_up", 3000), ("down", 4096)])
+def test_w8a8_column_bands(name, M):
+    """Calls whose one-band grid would end in a mostly idle round of
+    work-group slots run in two column bands.  The leading band (one K part)
+    equals the call without a workspace (K whole in every tile) bit for bit;
+    the remaining columns equal a call of their own on those columns' packed
+    matrix, whose plan is the band's; sampled columns of both bands, and the
+    columns around the band edge, against the oracle (NaN-filled
+    workspaces)."""
+    wq = U.wqmod()
+    fmt, N, K, Ms, (codes, scales) = U.config_inputs(name)
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    p = wq.wq_query_w8a8_plan(M, N, K, cu, True)
+    U.note("w8a8 %s M=%d bands %s" % (name, M, p))
+    if p["tail"] is None:
+        pytest.skip("one band on a device of %d CUs" % cu)
+    na = p["band"]
+    packed = U.pack_fp8(codes, scales)
+    xb = synth.x_bf16(M, K, 2401 + M)
+    xq, xc, xs = quantize(xb, K)
+    y, _ = run(packed, N, K, xq, M, ws="auto")
+    U.note("  one band, K whole")
+    y1, _ = run(packed, N, K, xq, M)
+    assert np.array_equal(y[:, :na], y1[:, :na])
+    U.note("  the remaining columns alone")
+    q = wq.wq_query_w8a8_plan(M, N - na, K, cu, True)
+    assert q["tail"] is None and q["tile"] + (q["kparts"],) == p["tail"]
+    pt = U.pack_fp8(np.ascontiguousarray(codes[na:]), np.ascontiguousarray(scales[na // 128:]))
+    yt, _ = run(pt, N - na, K, xq, M, ws="auto")
+    assert np.array_equal(y[:, na:], yt)
+    assert np.array_equal(run(packed, N, K, xq, M, ws="auto")[0], y)
+    cols = np.unique(np.concatenate([U.sample_cols(N, 72 + M, 192), np.arange(na - 16, na + 16)]))
+    rows = np.arange(min(M, 4096 * 5120 // K))        # FFN down: the first 1204 rows
+    y64 = oracle.gemm_w8a8(xc[rows], xs[rows], codes, scales, cols=cols)
+    r = compare.grade(y[rows][:, cols], y64, floor_w8a8(xc[rows], xs[rows], codes, scales, K), "bf16")
+    U.note("  %s" % r)
+    check_w8a8(r)
 
 
 def test_w8a8_streaming_tile_bits(kparts_reset):

@@ -263,6 +263,9 @@ PlanKey g_plan_keys[kPlanCache];
 Plan g_plans[kPlanCache];
 int g_plan_count = 0, g_plan_next = 0;
 
+// Forgets the cached W8A8 call plans; the caller holds g_plan_mu.
+void w8_cache_reset();
+
 Plan cached_plan(int kind, int64_t N, int64_t K, int cu, bool ws)
 {
     const PlanKey key{kind, N, K, cu, ws};
@@ -492,6 +495,7 @@ wq_status wq_set_tuning(int nt, int sn, int split, int waves_per_cu)
     g_opts.waves_per_cu = waves_per_cu ? waves_per_cu : 4;
     g_plan_count = 0;
     g_plan_next = 0;
+    w8_cache_reset();
     return WQ_OK;
 }
 
@@ -503,6 +507,7 @@ wq_status wq_set_kparts(int kp)
     g_opts.kp = kp;
     g_plan_count = 0;
     g_plan_next = 0;
+    w8_cache_reset();
     return WQ_OK;
 }
 
@@ -868,6 +873,115 @@ W8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, bool ws)
 
 size_t w8a8_workspace_bytes(int64_t M, int64_t N, int kp) { return kp > 1 ? (size_t)kp * M * N * 4 : 0; }
 
+// Work-group slots of one round of a tile-kernel grid of n work-groups:
+// 256 x 256 tiles run one per CU, 128 x 128 tiles two per CU once the grid has
+// more work-groups than CUs (the two-stage pipeline), else one.
+int64_t w8_round_slots(int tile, int64_t n, int cu)
+{
+    return tile == wq::W8_T128 && n > cu ? 2 * (int64_t)cu : (int64_t)cu;
+}
+
+// Work-groups of a tile-kernel grid over M rows and N columns.
+int64_t w8_grid(const W8Plan& p, int64_t M, int64_t N)
+{
+    const int64_t mpad = (M + 15) / 16 * 16;
+    const int r = wq::w8_tile_rows(p.tile), c = wq::w8_tile_cols(p.tile);
+    return (mpad + r - 1) / r * ((N + c - 1) / c) * p.kp;
+}
+
+// A W8A8 call: output columns [0, na) on `main`, and where na < N the columns
+// [na, N) as a second launch on `tail`, the plan of that band as a call of
+// its own.
+struct W8Call {
+    W8Plan main;
+    int64_t na;
+    W8Plan tail;
+};
+
+// Column bands.  A grid of several rounds of work-group slots whose last
+// round is at most half full leaves most CUs idle for that round.  With a
+// workspace, 64 < Mpad <= kW8BigM and no forced tile or part count, such a
+// call is split by columns: the widest leading band -- a multiple of 256
+// columns, leaving at most a quarter of N -- whose own plan runs in one K
+// part and fills whole rounds takes that plan, and the remaining columns run
+// as a second launch with their own plan, which splits their K over the
+// slots.  Each output is computed by one of the two launches; in the first
+// band in one K part, the same sums as any one-part tile plan.  Measured on
+// MI355X (quantised activations prepared, graph-replayed calls, the same
+// process): gate/up M = 1024 / 2048 / 3000 / 4096 102.4 / 187.9 / 271.8 /
+// 358.6 us against 123.1 / 206.8 / 288.7 / 369.1 in one band, FFN down
+// M = 4096 332.0 against 375.2.  Where the rule keeps one band the split
+// measured slower: gate/up M = 512 (one partial round) 75.0 against 72.7;
+// above kW8BigM, whose plans keep K whole, gate/up M = 5000 / 6144 / 8192
+// 457.7 / 536.0 / 690.1 against 442.6 / 519.5 / 675.2 and FFN down M = 8192
+// 676.3 against 664.5.
+W8Call w8a8_call_uncached(int64_t M, int64_t N, int64_t K, int cu, bool ws)
+{
+    const W8Plan p = w8a8_plan(M, N, K, cu, ws);
+    const W8Call one{p, N, W8Plan{p.tile, 1}};
+    int forced_kp;
+    {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        forced_kp = g_opts.kp;
+    }
+    const int64_t mpad = (M + 15) / 16 * 16;
+    if (!ws || forced_kp || forced_w8a8_tile() >= 0 || mpad > wq::kW8BigM ||
+        (p.tile != wq::W8_T128 && p.tile != wq::W8_T256))
+        return one;
+    const int64_t n = w8_grid(p, M, N), slots = w8_round_slots(p.tile, n, cu), last = n % slots;
+    if (n <= slots || last == 0 || 2 * last > slots) return one;
+    for (int64_t na = (N - 1) / 256 * 256; na >= 256 && 4 * (N - na) <= N; na -= 256) {
+        const W8Plan pm = w8a8_plan(M, na, K, cu, ws);
+        if (pm.kp != 1 || (pm.tile != wq::W8_T128 && pm.tile != wq::W8_T256)) continue;
+        const int64_t nm = w8_grid(pm, M, na);
+        if (nm % w8_round_slots(pm.tile, nm, cu) == 0) return {pm, na, w8a8_plan(M, N - na, K, cu, ws)};
+    }
+    return one;
+}
+
+struct W8Key {
+    int64_t M, N, K;
+    int cu;
+    bool ws;
+    bool operator==(const W8Key& o) const { return M == o.M && N == o.N && K == o.K && cu == o.cu && ws == o.ws; }
+};
+
+constexpr int kW8Cache = 64;
+W8Key g_w8_keys[kW8Cache];
+W8Call g_w8_calls[kW8Cache];
+int g_w8_count = 0, g_w8_next = 0;
+
+void w8_cache_reset()
+{
+    g_w8_count = 0;
+    g_w8_next = 0;
+}
+
+W8Call w8a8_call(int64_t M, int64_t N, int64_t K, int cu, bool ws)
+{
+    const W8Key key{M, N, K, cu, ws};
+    options();   // read the environment once, before the first plan
+    {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        for (int i = 0; i < g_w8_count; ++i)
+            if (g_w8_keys[i] == key) return g_w8_calls[i];
+    }
+    const W8Call c = w8a8_call_uncached(M, N, K, cu, ws);
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    g_w8_keys[g_w8_next] = key;
+    g_w8_calls[g_w8_next] = c;
+    g_w8_next = (g_w8_next + 1) % kW8Cache;
+    g_w8_count = std::min(g_w8_count + 1, kW8Cache);
+    return c;
+}
+
+size_t w8a8_call_workspace_bytes(const W8Call& c, int64_t M, int64_t N)
+{
+    const size_t a = w8a8_workspace_bytes(M, c.na, c.main.kp);
+    const size_t b = c.na < N ? w8a8_workspace_bytes(M, N - c.na, c.tail.kp) : 0;
+    return std::max(a, b);
+}
+
 }  // namespace
 
 extern "C" {
@@ -877,7 +991,7 @@ size_t wq_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K)
     if (M <= 0 || !shape_ok(WQ_FMT_FP8_BLOCK, N, K) || !wq_x_fp8_packed_bytes(M, K)) return 0;
     DevInfo dev;
     if (current_device(&dev) != WQ_OK) return 0;
-    return w8a8_workspace_bytes(M, N, w8a8_plan(M, N, K, dev.cu, true).kp);
+    return w8a8_call_workspace_bytes(w8a8_call(M, N, K, dev.cu, true), M, N);
 }
 
 wq_status wq_query_w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, int with_workspace, int* plan)
@@ -886,7 +1000,8 @@ wq_status wq_query_w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, int with_w
     if (M < 1 || cu < 1 || cu > kMaxQueryCu || !shape_ok(WQ_FMT_FP8_BLOCK, N, K) ||
         (uint64_t)N * (uint64_t)K >= ((uint64_t)1 << 32) || !wq_x_fp8_packed_bytes(M, K))
         return WQ_ERR_SHAPE;
-    const W8Plan p = w8a8_plan(M, N, K, cu, with_workspace != 0);
+    const W8Call c = w8a8_call(M, N, K, cu, with_workspace != 0);
+    const W8Plan p = c.main;
     if (p.tile == wq::W8_STREAM) {   // rows of the row tiles, columns of a work-group
         const int64_t mpad = (M + 15) / 16 * 16;
         plan[0] = mpad <= 16 ? 16 : mpad <= 32 ? 32 : 64;
@@ -897,6 +1012,10 @@ wq_status wq_query_w8a8_plan(int64_t M, int64_t N, int64_t K, int cu, int with_w
     }
     plan[2] = p.kp;
     plan[3] = p.tile == wq::W8_STREAM ? 1 : 0;
+    plan[4] = (int)c.na;
+    plan[5] = c.na < N ? wq::w8_tile_rows(c.tail.tile) : 0;
+    plan[6] = c.na < N ? wq::w8_tile_cols(c.tail.tile) : 0;
+    plan[7] = c.na < N ? c.tail.kp : 0;
     return WQ_OK;
 }
 
@@ -939,15 +1058,16 @@ wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void*
     wq_status st = current_device(&dev);
     if (st != WQ_OK) return st;
     // with a workspace, K may be split across work-groups (FP32 partials there)
-    const W8Plan plan = w8a8_plan(M, N, K, dev.cu, workspace != nullptr);
+    const W8Call call = w8a8_call(M, N, K, dev.cu, workspace != nullptr);
+    const W8Plan plan = call.main;
     const int kp = plan.kp;
     int stages;
     {
         std::lock_guard<std::mutex> lk(g_plan_mu);
         stages = g_opts.w8a8_stages;
     }
-    if (kp > 1) {
-        if (workspace_bytes < w8a8_workspace_bytes(M, N, kp)) return WQ_ERR_WORKSPACE;
+    if (const size_t need = w8a8_call_workspace_bytes(call, M, N)) {
+        if (workspace_bytes < need) return WQ_ERR_WORKSPACE;
         if (!aligned16(workspace)) return WQ_ERR_ALIGN;
     }
     if (plan.tile == wq::W8_STREAM) {
@@ -973,12 +1093,22 @@ wq_status wq_gemm_fp8_w8a8(const void* packed, int64_t N, int64_t K, const void*
                    ? WQ_OK
                    : WQ_ERR_HIP;
     }
-    return wq::launch_w8a8(static_cast<const uint8_t*>(packed), (int)N, (int)K, static_cast<const uint8_t*>(xq),
-                           (int)M, y, ldy, plan.tile, kp, kp > 1 ? static_cast<float*>(workspace) : nullptr, dev.cu,
-                           stages,
-                           static_cast<hipStream_t>(hip_stream)) == hipSuccess
-               ? WQ_OK
-               : WQ_ERR_HIP;
+    // the packed matrix: 16 x K code bytes per 16-column tile, then the block
+    // scales [N/128][K/128]; a band of columns starts at its first tile and
+    // its first scale row
+    const uint8_t* codes = static_cast<const uint8_t*>(packed);
+    const float* sw = reinterpret_cast<const float*>(codes + N * K);
+    const uint8_t* xqb = static_cast<const uint8_t*>(xq);
+    float* ws = static_cast<float*>(workspace);
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = wq::launch_w8a8(codes, sw, (int)call.na, (int)K, xqb, (int)M, y, ldy, plan.tile, kp,
+                                   kp > 1 ? ws : nullptr, dev.cu, stages, s);
+    if (e == hipSuccess && call.na < N) {
+        const int tkp = call.tail.kp;
+        e = wq::launch_w8a8(codes + call.na * K, sw + call.na / 128 * (K / 128), (int)(N - call.na), (int)K, xqb,
+                            (int)M, y + call.na, ldy, call.tail.tile, tkp, tkp > 1 ? ws : nullptr, dev.cu, stages, s);
+    }
+    return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
 }
 
 wq_status wq_unpack_x_fp8(const void* xq, int64_t M, int64_t K, uint8_t* codes, float* scales, void* hip_stream)

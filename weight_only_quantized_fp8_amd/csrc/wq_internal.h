@@ -165,12 +165,15 @@ enum W8Tile : int {
 constexpr int w8_tile_rows(int t) { return t == W8_T256 ? 256 : t == W8_T128 ? 128 : 64; }
 constexpr int w8_tile_cols(int t) { return t == W8_T256 ? 256 : t == W8_T64x64 ? 64 : 128; }
 
+// codes: the packed FP8 code units of the N columns served (16 x K bytes per
+// 16-column tile), sw: their block scales [N/128][K/128]; a band of columns of
+// a packed matrix passes its first tile's units and first scale row.
 // tile: a W8Tile; kp > 1: K split into kp parts across work-groups, FP32
 // partials in ws [kp][M][N] summed in order into y by launch_sum_parts; cu:
 // the device's compute units; stages: the LDS pipeline depth (2 or 4), 0 = 4
 // where the grid has at most one work-group per CU
-hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
-                       int tile, int kp, float* ws, int cu, int stages, hipStream_t stream);
+hipError_t launch_w8a8(const uint8_t* codes, const float* sw, int N, int K, const uint8_t* xq, int M, uint16_t* y,
+                       int64_t ldy, int tile, int kp, float* ws, int cu, int stages, hipStream_t stream);
 
 // y[m][n] = the parts ws[p][m][n] (p = 0 .. kp-1, [kp][rows][N] FP32) added in
 // order and rounded once (RNE) to BF16, or FP16 with f16_out; N % 16 == 0.

@@ -468,8 +468,8 @@ static hipError_t launch_w8a8_tile(W8Args a, int cu, int stages, hipStream_t str
     return hipGetLastError();
 }
 
-hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq, int M, uint16_t* y, int64_t ldy,
-                       int tile, int kp, float* ws, int cu, int stages, hipStream_t stream)
+hipError_t launch_w8a8(const uint8_t* codes, const float* sw, int N, int K, const uint8_t* xq, int M, uint16_t* y,
+                       int64_t ldy, int tile, int kp, float* ws, int cu, int stages, hipStream_t stream)
 {
     if (kp < 1 || kp > K / 128 || kp > kMaxKParts || (kp > 1 && !ws)) return hipErrorInvalidValue;
     W8Args a{};
@@ -479,8 +479,8 @@ hipError_t launch_w8a8(const uint8_t* packed_w, int N, int K, const uint8_t* xq,
     a.N = N;
     a.M = M;
     a.Mpad = (M + 15) & ~15;
-    a.w = packed_w;
-    a.sw = reinterpret_cast<const float*>(packed_w + (int64_t)N * K);
+    a.w = codes;
+    a.sw = sw;
     a.xq = xq;
     a.sx = reinterpret_cast<const float*>(xq + (int64_t)a.Mpad * K);
     a.y = y;

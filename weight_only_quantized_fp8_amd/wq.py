@@ -250,10 +250,14 @@ def wq_query_gemm_plan(fmt: int, M: int, N: int, K: int, cu: int, with_workspace
 
 def wq_query_w8a8_plan(M: int, N: int, K: int, cu: int, with_workspace: bool = False) -> dict:
     """Host-only: the tile and K parts a W8A8 call would take on a device with
-    `cu` compute units (no device is touched)."""
-    out = (_INT * 4)()
+    `cu` compute units (no device is touched).  `band` is the number of leading
+    columns on that plan (N when the call is one launch); the remaining columns
+    run as a second launch on `tail` = (tile rows, tile columns, K parts), else
+    None."""
+    out = (_INT * 8)()
     _check(lib.wq_query_w8a8_plan(M, N, K, cu, int(bool(with_workspace)), out), "wq_query_w8a8_plan")
-    return dict(tile=(out[0], out[1]), kparts=out[2], streaming=bool(out[3]))
+    tail = (out[5], out[6], out[7]) if out[4] < N else None
+    return dict(tile=(out[0], out[1]), kparts=out[2], streaming=bool(out[3]), band=out[4], tail=tail)
 
 
 def wq_unpack_x_fp8(xq, M: int, K: int, codes, scales, stream=None) -> None:
