@@ -381,11 +381,12 @@ wq_status wq_quantize_x_fp8(const uint16_t* x_bf16, int64_t ldx, int64_t M, int6
  *           sums go to the workspace and a second kernel on the same stream adds
  *           them in a fixed order (results stay deterministic for a given M, N, K;
  *           the split, and so the rounding of a row, may differ between Ms).
- *           And an M whose grid would end in a mostly idle round of work-group
- *           slots is served in two column bands, a leading band of whole rounds
- *           in one K part and the remaining columns as a second launch with K
- *           split.  A workspace smaller than required returns WQ_ERR_WORKSPACE,
- *           a misaligned one WQ_ERR_ALIGN.
+ *           With or without a workspace, an M whose grid would end in a mostly
+ *           idle round of work-group slots may be served in two column bands: a
+ *           leading band of whole rounds in one K part, and the remaining
+ *           columns as a second launch (K split there only with a workspace).
+ *           A workspace smaller than required returns WQ_ERR_WORKSPACE, a
+ *           misaligned one WQ_ERR_ALIGN.
  * Source: atlas docs "Module m16_tc", ARM ORDER rung 6 (W8A8 block-scaled
  * prefill) and NUMERICS (the two-level fold); arc PR "fix(ArcKernels): FP8
  * bank conflict + the dispatch threshold's provenance", "Worth a separate

@@ -334,10 +334,12 @@ def test_w8a8_depth_boundary(M, stages_reset):
 
 @pytest.mark.parametrize("name,small", [("gate_up", (16, 48, 128, 512)), ("down", (128,))])
 def test_w8a8_small_grid_rows_equal_large_grid(name, small, stages_reset):
-    """At the FFN sizes M = 2048 runs 128 x 128 tiles on the two-stage
-    pipeline; gate/up M = 16 and 48 run the weight-streaming tile (one K group,
-    so the same fold order), M = 128 the four-stage pipeline (at most one
-    work-group per CU), and gate/up M = 512 the 256 x 256 tile.  Rows depend
+    """At the FFN sizes M = 2048 runs FFN down on 128 x 128 tiles on the
+    two-stage pipeline and gate/up in two column bands (256 x 256 tiles, then
+    the last 1024 columns on 128 x 128, K whole in both); gate/up M = 16 and
+    48 run the weight-streaming tile (one K group, so the same fold order),
+    M = 128 the four-stage pipeline (at most one work-group per CU), and
+    gate/up M = 512 the 256 x 256 tile.  Rows depend
     only on their own activations, so the smaller calls equal the first rows
     of the large one bit for bit.  (FFN down at M <= 64 without a workspace
     streams with 3 K groups, another summation order: graded against the
@@ -348,7 +350,8 @@ def test_w8a8_small_grid_rows_equal_large_grid(name, small, stages_reset):
     xb = synth.x_bf16(2048, K, 1801)
     xq, _, _ = quantize(xb, K)
     U.note("w8a8 %s M=2048 (two stages)" % name)
-    assert wq.wq_query_w8a8_plan(2048, N, K, 256, False)["tile"] == (128, 128)
+    p = wq.wq_query_w8a8_plan(2048, N, K, 256, False)
+    assert (p["tile"], p["tail"]) == (((256, 256), (128, 128, 1)) if name == "gate_up" else ((128, 128), None))
     ybig, _ = run(packed, N, K, xq, 2048)
     for M in small:
         U.note("w8a8 %s M=%d (plan %s)" % (name, M, wq.wq_query_w8a8_plan(M, N, K, 256, False)))
@@ -438,11 +441,12 @@ def test_w8a8_automatic_big_tile(N, K, M, kp):
 def test_w8a8_column_bands(name, M):
     """Calls whose one-band grid would end in a mostly idle round of
     work-group slots run in two column bands.  The leading band (one K part)
-    equals the call without a workspace (K whole in every tile) bit for bit;
-    the remaining columns equal a call of their own on those columns' packed
-    matrix, whose plan is the band's; sampled columns of both bands, and the
-    columns around the band edge, against the oracle (NaN-filled
-    workspaces)."""
+    equals the call without a workspace (K whole in every tile, also in two
+    bands) bit for bit, and that call equals the one-band plan (one K part
+    forced); the remaining columns equal a call of their own on those
+    columns' packed matrix, whose plan is the band's; sampled columns of both
+    bands, and the columns around the band edge, against the oracle
+    (NaN-filled workspaces)."""
     wq = U.wqmod()
     fmt, N, K, Ms, (codes, scales) = U.config_inputs(name)
     cu = torch.cuda.get_device_properties(0).multi_processor_count
@@ -458,6 +462,13 @@ def test_w8a8_column_bands(name, M):
     U.note("  one band, K whole")
     y1, _ = run(packed, N, K, xq, M)
     assert np.array_equal(y[:, :na], y1[:, :na])
+    U.note("  one band, one K part")
+    wq.wq_set_kparts(1)
+    try:
+        assert wq.wq_query_w8a8_plan(M, N, K, cu, False)["tail"] is None
+        assert np.array_equal(run(packed, N, K, xq, M)[0], y1)
+    finally:
+        wq.wq_set_kparts(0)
     U.note("  the remaining columns alone")
     q = wq.wq_query_w8a8_plan(M, N - na, K, cu, True)
     assert q["tail"] is None and q["tile"] + (q["kparts"],) == p["tail"]

@@ -179,29 +179,32 @@ def test_query_validation():
 # whole without a workspace); 128 x 128 split while the grid is short; one
 # part for gate/up from M = 192 on; 256 x 256 where its coarser rounds still
 # come out ahead (gate/up M = 512, down M = 1024 and 2048 in 3 parts) and
-# above M = 4096.  With a workspace, gate/up M = 1024 / 2048 / 3000 / 4096
-# and down M = 4096 run in two column bands (W8A8_BANDS): the plan listed is
-# that of the leading band.
+# above M = 4096.  Gate/up M = 1024 / 2048 / 3000 / 4096 and down M = 4096
+# run in two column bands (W8A8_BANDS), with or without a workspace: the plan
+# listed is that of the leading band.
 W8A8_PLANS = {
     "gate_up": {1: ((16, 80, 1), 16), 16: ((16, 80, 1), 16), 32: ((32, 80, 1), 32), 64: ((64, 80, 1), 64),
                 96: ((128, 128, 3), 128), 128: ((128, 128, 3), 128), 192: ((128, 128, 1), 128),
-                256: ((128, 128, 1), 128), 512: ((256, 256, 1), 256), 1024: ((256, 256, 1), 128),
-                2048: ((256, 256, 1), 128), 3000: ((256, 256, 1), 256), 4096: ((256, 256, 1), 256),
+                256: ((128, 128, 1), 128), 512: ((256, 256, 1), 256), 1024: ((256, 256, 1), 256),
+                2048: ((256, 256, 1), 256), 3000: ((256, 256, 1), 256), 4096: ((256, 256, 1), 256),
                 8192: ((256, 256, 1), 256)},
     "down": {1: ((16, 80, 4), 16), 16: ((16, 80, 4), 16), 48: ((64, 80, 4), 64), 64: ((64, 80, 4), 64),
              96: ((128, 128, 6), 128), 128: ((128, 128, 6), 128), 192: ((128, 128, 6), 128),
              256: ((128, 128, 6), 128), 512: ((128, 128, 3), 128), 1024: ((256, 256, 3), 128),
-             2048: ((256, 256, 3), 128), 4096: ((256, 256, 1), 128), 8192: ((256, 256, 1), 256)},
+             2048: ((256, 256, 3), 128), 4096: ((256, 256, 1), 256), 8192: ((256, 256, 1), 256)},
 }
 # (shape, M) -> (columns of the leading band, (tile rows, tile columns, K
-# parts) of the rest): the calls whose one-band grid would end in a round of
-# work-group slots at most half full (gate/up: 1088 128 x 128 tiles on 512
-# slots at M = 1024, 2176 at 2048; 816 and 1088 256 x 256 tiles on 256 at
-# M = 3000 and 4096; down M = 4096: 1280 128 x 128 tiles on 512), measured
-# 3-17% faster in two bands
-W8A8_BANDS = {("gate_up", 1024): (16384, (128, 128, 3)), ("gate_up", 2048): (16384, (128, 128, 2)),
-              ("gate_up", 3000): (16384, (256, 256, 3)), ("gate_up", 4096): (16384, (256, 256, 3)),
-              ("down", 4096): (4096, (256, 256, 3))}
+# parts) of the rest with a workspace, and without one): the calls whose
+# one-band grid would end in a round of work-group slots at most half full
+# (gate/up: 1088 128 x 128 tiles on 512 slots at M = 1024, 2176 at 2048; 816
+# and 1088 256 x 256 tiles on 256 at M = 3000 and 4096; down M = 4096: 1280
+# 128 x 128 tiles on 512), measured 3-17% faster in two bands (2-10%
+# without a workspace)
+W8A8_BANDS = {("gate_up", 1024): (16384, (128, 128, 3), (128, 128, 1)),
+              ("gate_up", 2048): (16384, (128, 128, 2), (128, 128, 1)),
+              ("gate_up", 3000): (16384, (256, 256, 3), (128, 128, 1)),
+              ("gate_up", 4096): (16384, (256, 256, 3), (128, 128, 1)),
+              ("down", 4096): (4096, (256, 256, 3), (128, 128, 1))}
 FFN = {"gate_up": (17408, 5120), "down": (5120, 17408)}
 
 
@@ -212,11 +215,11 @@ def test_measured_w8a8_plans(name):
         p = wq.wq_query_w8a8_plan(M, N, K, CU, True)
         assert p["tile"] + (p["kparts"],) == want, (name, M, p)
         assert p["streaming"] == (M <= 64), (name, M, p)
-        band, tail = W8A8_BANDS.get((name, M), (N, None))
+        band, tail, tail_no_ws = W8A8_BANDS.get((name, M), (N, None, None))
         assert (p["band"], p["tail"]) == (band, tail), (name, M, p)
         q = wq.wq_query_w8a8_plan(M, N, K, CU, False)
         assert q["kparts"] == 1 and q["tile"][0] == rows_no_ws, (name, M, q)
-        assert q["band"] == N and q["tail"] is None, (name, M, q)
+        assert (q["band"], q["tail"]) == (band, tail_no_ws), (name, M, q)
     # the streaming tile's columns without a workspace: FFN down's one-part plan (2 column-waves)
     if name == "down":
         assert wq.wq_query_w8a8_plan(16, N, K, CU, False)["tile"] == (16, 32)
@@ -314,12 +317,12 @@ def test_w8a8_rule_invariants():
 
 
 def test_w8a8_band_rule_invariants():
-    """Two column bands only with a workspace, 64 < Mpad <= 4096 and no lever
+    """Two column bands only for 64 < Mpad <= 4096, K >= 4096 and no lever
     set; the leading band is a multiple of 256 columns leaving at most a
     quarter of N, runs in one K part on 128 x 128 or 256 x 256 tiles and fills
     whole rounds of work-group slots (256 x 256 one per CU, 128 x 128 two per
     CU once the grid has more work-groups than CUs); the rest runs on the plan
-    of a call over those columns alone."""
+    of a call over those columns alone, in one K part without a workspace."""
     rng = random.Random(12)
     seen = 0
     for _ in range(600):
@@ -336,7 +339,8 @@ def test_w8a8_band_rule_invariants():
             continue
         seen += 1
         (r, c), kp, na = p["tile"], p["kparts"], p["band"]
-        assert ws and 64 < mpad <= 4096 and not p["streaming"], where
+        assert 64 < mpad <= 4096 and K >= 4096 and not p["streaming"], where
+        assert ws or p["tail"][2] == 1, where
         assert na % 256 == 0 and 0 < na < N and 4 * (N - na) <= N, where
         assert kp == 1 and (r, c) in ((128, 128), (256, 256)), where
         n = -(-mpad // r) * (na // c)
@@ -348,10 +352,14 @@ def test_w8a8_band_rule_invariants():
 
 
 def test_w8a8_bands_follow_the_levers(levers_reset):
-    """A forced part count keeps one band; a plan query without a workspace too."""
+    """A forced part count keeps one band, with or without a workspace; FFN
+    down at M = 2048 without a workspace stays in one band (its rest would be
+    a whole extra round of 136 K blocks on half the CUs)."""
     assert wq.wq_query_w8a8_plan(2048, 17408, 5120, CU, True)["tail"] is not None
-    assert wq.wq_query_w8a8_plan(2048, 17408, 5120, CU, False)["tail"] is None
+    assert wq.wq_query_w8a8_plan(2048, 17408, 5120, CU, False)["tail"] == (128, 128, 1)
+    assert wq.wq_query_w8a8_plan(2048, 5120, 17408, CU, False)["tail"] is None
     wq.wq_set_kparts(1)
     assert wq.wq_query_w8a8_plan(2048, 17408, 5120, CU, True)["tail"] is None
+    assert wq.wq_query_w8a8_plan(2048, 17408, 5120, CU, False)["tail"] is None
     wq.wq_set_kparts(0)
     assert wq.wq_query_w8a8_plan(2048, 17408, 5120, CU, True)["tail"] is not None

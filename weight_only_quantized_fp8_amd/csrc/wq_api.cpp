@@ -899,22 +899,30 @@ struct W8Call {
 };
 
 // Column bands.  A grid of several rounds of work-group slots whose last
-// round is at most half full leaves most CUs idle for that round.  With a
-// workspace, 64 < Mpad <= kW8BigM and no forced tile or part count, such a
-// call is split by columns: the widest leading band -- a multiple of 256
-// columns, leaving at most a quarter of N -- whose own plan runs in one K
-// part and fills whole rounds takes that plan, and the remaining columns run
-// as a second launch with their own plan, which splits their K over the
-// slots.  Each output is computed by one of the two launches; in the first
-// band in one K part, the same sums as any one-part tile plan.  Measured on
-// MI355X (quantised activations prepared, graph-replayed calls, the same
-// process): gate/up M = 1024 / 2048 / 3000 / 4096 102.4 / 187.9 / 271.8 /
-// 358.6 us against 123.1 / 206.8 / 288.7 / 369.1 in one band, FFN down
-// M = 4096 332.0 against 375.2.  Where the rule keeps one band the split
-// measured slower: gate/up M = 512 (one partial round) 75.0 against 72.7;
-// above kW8BigM, whose plans keep K whole, gate/up M = 5000 / 6144 / 8192
-// 457.7 / 536.0 / 690.1 against 442.6 / 519.5 / 675.2 and FFN down M = 8192
-// 676.3 against 664.5.
+// round is at most half full leaves most CUs idle for that round.  For
+// 64 < Mpad <= kW8BigM, K >= 4096 (the range w8_estimate_us was fitted on)
+// and no forced tile or part count, such a call is split by columns: the
+// widest leading band -- a multiple of 256 columns, leaving at most a quarter
+// of N -- whose own plan runs in one K part and fills whole rounds takes that
+// plan, and the remaining columns run as a second launch with their own plan
+// (with a workspace, K split over the slots), where the estimates of the two
+// launches (plus ~3 us for the second) come to at least 5% below that of the
+// one-band plan.  Each output is computed by one of the two launches; in the
+// first band in one K part, the same sums as any one-part tile plan (without
+// a workspace both bands keep K whole: the same bits as one band).  Measured
+// on MI355X (quantised activations prepared, graph-replayed calls, the same
+// process), with a workspace: gate/up M = 1024 / 2048 / 3000 / 4096
+// 101.8 / 184.6 / 272.7 / 357.0 us against 122.2 / 207.2 / 288.7 / 368.8
+// in one band, FFN down M = 4096 331.7 against 377.6, attention output
+// M = 4096 135.1 against 138.8; without one: gate/up 113.5 / 189.9 / 272.2
+// / 354.6 against 121.3 / 208.4 / 289.7 / 372.1, down M = 4096 355.1
+// against 384.1, attention output 131.9 against 141.7.  Where the estimate
+// keeps one band the split measured slower: FFN down without a workspace at
+// M = 1921 / 2048 (the rest of the columns a whole extra round of 136 K
+// blocks on half the CUs) 243.3 / 246.4 against 234.7 / 227.5; gate/up
+// M = 512 (one partial round) 75.0 against 72.7; above kW8BigM, whose plans
+// keep K whole, gate/up M = 5000 / 6144 / 8192 457.7 / 536.0 / 690.1
+// against 442.6 / 519.5 / 675.2, FFN down M = 8192 676.3 against 664.5.
 W8Call w8a8_call_uncached(int64_t M, int64_t N, int64_t K, int cu, bool ws)
 {
     const W8Plan p = w8a8_plan(M, N, K, cu, ws);
@@ -925,7 +933,8 @@ W8Call w8a8_call_uncached(int64_t M, int64_t N, int64_t K, int cu, bool ws)
         forced_kp = g_opts.kp;
     }
     const int64_t mpad = (M + 15) / 16 * 16;
-    if (!ws || forced_kp || forced_w8a8_tile() >= 0 || mpad > wq::kW8BigM ||
+    const int KB = (int)(K / 128);
+    if (forced_kp || forced_w8a8_tile() >= 0 || mpad > wq::kW8BigM || KB < 32 ||
         (p.tile != wq::W8_T128 && p.tile != wq::W8_T256))
         return one;
     const int64_t n = w8_grid(p, M, N), slots = w8_round_slots(p.tile, n, cu), last = n % slots;
@@ -934,7 +943,12 @@ W8Call w8a8_call_uncached(int64_t M, int64_t N, int64_t K, int cu, bool ws)
         const W8Plan pm = w8a8_plan(M, na, K, cu, ws);
         if (pm.kp != 1 || (pm.tile != wq::W8_T128 && pm.tile != wq::W8_T256)) continue;
         const int64_t nm = w8_grid(pm, M, na);
-        if (nm % w8_round_slots(pm.tile, nm, cu) == 0) return {pm, na, w8a8_plan(M, N - na, K, cu, ws)};
+        if (nm % w8_round_slots(pm.tile, nm, cu)) continue;
+        const W8Plan pt = w8a8_plan(M, N - na, K, cu, ws);
+        const double two = w8_estimate_us(pm.tile, nm, 1, KB, M, na, cu) +
+                           w8_estimate_us(pt.tile, w8_grid(pt, M, N - na) / pt.kp, pt.kp, KB, M, N - na, cu) + 3.0;
+        if (two < 0.95 * w8_estimate_us(p.tile, n / p.kp, p.kp, KB, M, N, cu)) return {pm, na, pt};
+        return one;
     }
     return one;
 }
