@@ -81,7 +81,45 @@ def three_parts():
 
 def test_concurrent_threads_and_streams_match_serial(three_parts):
     U.note("concurrency: %d threads x %d rounds" % (THREADS, ROUNDS))
-    jobs = _jobs()
+    _run_concurrently(_jobs(), ROUNDS)
+
+
+def _w8a8_job(N, K, M, seed, ws):
+    wq = U.wqmod()
+    codes, scales = synth.fp8_weights(N, K, seed)
+    packed = U.pack_fp8(codes, scales)
+    x = U.t_u16(synth.x_bf16(M, K, seed + 1), torch.bfloat16)
+    nb = wq.wq_w8a8_workspace_bytes(M, N, K) if ws else 0
+
+    def make():
+        return {"y": torch.empty((M, N), dtype=torch.bfloat16, device=U.DEV),
+                "xq": torch.empty(wq.wq_x_fp8_packed_bytes(M, K), dtype=torch.uint8, device=U.DEV),
+                "ws": torch.empty(max(nb, 16), dtype=torch.uint8, device=U.DEV)}
+
+    def call(o, s):
+        wq.wq_quantize_x_fp8(x, M, K, o["xq"], stream=s)
+        wq.wq_gemm_fp8_w8a8(packed, N, K, o["xq"], M, o["y"], o["ws"] if nb else None, stream=s)
+    return ("w8a8-%dx%d-M%d-%s" % (N, K, M, "ws" if ws else "nows"), make, call)
+
+
+def test_concurrent_w8a8_column_bands_match_serial():
+    """W8A8 calls that run in two column bands (on 256 CUs: a leading band of
+    whole rounds, then the rest of the columns as a second launch, with K
+    split there when a workspace is passed), from four threads on their own
+    streams beside one-band calls: every result equals the serial call."""
+    wq = U.wqmod()
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K, M = 16640, 4096, 897
+    U.note("concurrency: W8A8 bands %s / %s" % (wq.wq_query_w8a8_plan(M, N, K, cu, True),
+                                                wq.wq_query_w8a8_plan(M, N, K, cu, False)))
+    if cu == 256:
+        assert wq.wq_query_w8a8_plan(M, N, K, cu, True)["tail"] == (128, 128, 2)
+        assert wq.wq_query_w8a8_plan(M, N, K, cu, False)["tail"] == (128, 128, 1)
+    jobs = [_w8a8_job(N, K, M, 2030, True), _w8a8_job(N, K, M, 2030, False), _w8a8_job(640, 2048, 300, 2040, True)]
+    _run_concurrently(jobs, 4)
+
+
+def _run_concurrently(jobs, rounds):
     ref = {}
     for name, make, call in jobs:                 # serial reference on the current stream
         o = make()
@@ -96,7 +134,7 @@ def test_concurrent_threads_and_streams_match_serial(three_parts):
             s = torch.cuda.Stream()
             outs = {name: make() for name, make, _ in jobs}
             with torch.cuda.stream(s):
-                for r in range(ROUNDS):
+                for r in range(rounds):
                     order = jobs if (r + t) % 2 == 0 else list(reversed(jobs))
                     for name, _, call in order:
                         outs[name]["y"].fill_(float("nan"))

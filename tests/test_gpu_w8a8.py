@@ -530,6 +530,46 @@ def test_w8a8_workspace_errors(kparts_reset):
     assert bool((y.float() == 5.0).all())
 
 
+@pytest.mark.parametrize("ws", [True, False])
+def test_w8a8_graph_replay_with_bands(ws):
+    """Quantiser and a GEMM in two column bands (on 256 CUs: the leading band,
+    the rest of the columns, and with a workspace their parts sum) captured in
+    a HIP graph replay to the eager result, with eager work between replays."""
+    wq = U.wqmod()
+    N, K, M = 16640, 4096, 897
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    U.note("w8a8 graph replay with bands %s" % wq.wq_query_w8a8_plan(M, N, K, cu, ws))
+    if cu == 256:
+        assert wq.wq_query_w8a8_plan(M, N, K, cu, ws)["tail"] is not None
+    codes, scales = synth.fp8_weights(N, K, 1810)
+    packed = U.pack_fp8(codes, scales)
+    x = U.t_u16(synth.x_bf16(M, K, 1811), torch.bfloat16)
+    xq = torch.empty(wq.wq_x_fp8_packed_bytes(M, K), dtype=torch.uint8, device=U.DEV)
+    nb = wq.wq_w8a8_workspace_bytes(M, N, K) if ws else 0
+    wsb = torch.empty(max(nb, 16), dtype=torch.uint8, device=U.DEV)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=U.DEV)
+    wq.wq_quantize_x_fp8(x, M, K, xq)
+    wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y, wsb if nb else None)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            wq.wq_quantize_x_fp8(x, M, K, xq)
+            wq.wq_gemm_fp8_w8a8(packed, N, K, xq, M, y, wsb if nb else None)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        y.fill_(3.0)
+        wsb.fill_(0xFF)
+        xq.fill_(0x11)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), rep
+
+
 def test_w8a8_graph_replay_with_parts(kparts_reset):
     """Quantiser, split GEMM and parts sum captured in a HIP graph replay to the eager result."""
     wq = U.wqmod()
