@@ -437,7 +437,8 @@ def test_w8a8_automatic_big_tile(N, K, M, kp):
     assert np.array_equal(run(packed, N, K, xq, M, ws="auto")[0], y)
 
 
-@pytest.mark.parametrize("name,M", [("gate_up", 1024), ("gate_up", 2048), ("gate_up", 3000), ("down", 4096)])
+@pytest.mark.parametrize("name,M", [("gate_up", 1024), ("gate_up", 2048), ("gate_up", 3000), ("down", 4096),
+                                    ((9600, 4096), 1793)])
 def test_w8a8_column_bands(name, M):
     """Calls whose one-band grid would end in a mostly idle round of
     work-group slots run in two column bands.  The leading band (one K part)
@@ -446,9 +447,15 @@ def test_w8a8_column_bands(name, M):
     forced); the remaining columns equal a call of their own on those
     columns' packed matrix, whose plan is the band's; sampled columns of both
     bands, and the columns around the band edge, against the oracle
-    (NaN-filled workspaces)."""
+    (NaN-filled workspaces).  The 9600-column shape at M = 1793 has ragged
+    rows and ends its second band (1408 columns on 256 x 256 tiles, in 2 K
+    parts) with a half-filled tile."""
     wq = U.wqmod()
-    fmt, N, K, Ms, (codes, scales) = U.config_inputs(name)
+    if isinstance(name, tuple):
+        N, K = name
+        codes, scales = synth.fp8_weights(N, K, 2500)
+    else:
+        fmt, N, K, Ms, (codes, scales) = U.config_inputs(name)
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     p = wq.wq_query_w8a8_plan(M, N, K, cu, True)
     U.note("w8a8 %s M=%d bands %s" % (name, M, p))
