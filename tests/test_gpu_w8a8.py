@@ -124,6 +124,44 @@ def test_quantizer_matches_oracle_bit_exact(M, K, ld):
         assert not last[:, :, lanes, :].any()
 
 
+def test_quantizer_every_bf16_magnitude():
+    """Every finite BF16 value x (both signs, zeros and subnormals included)
+    with |x| <= amax, for amax across the binades -- from the smallest BF16
+    subnormal, through both sides of 2^-80 (below which the quantiser divides
+    by the scale, above which it multiplies by its correctly rounded
+    reciprocal and corrects the remainder), to the largest finite BF16 -- in
+    groups whose amax it is (the group's first value): codes and scales equal
+    the oracle's bit for bit (the oracle divides)."""
+    allx = np.arange(65536, dtype=np.uint32)
+    xs = allx[(allx & 0x7F80) != 0x7F80].astype(np.uint16)   # finite patterns
+    mag = xs & 0x7FFF                                           # BF16 magnitude order = integer order
+    amaxes = [0x0001, 0x0025, 0x0080, 0x0711, 0x0B80, 0x1234, 0x1700, 0x177F, 0x1780, 0x1781, 0x17F3,
+              0x1F00, 0x2A55, 0x3381, 0x3C00, 0x3F80, 0x3FC1, 0x4000, 0x43E0, 0x4B2B, 0x55AA, 0x5F12,
+              0x6C00, 0x7700, 0x7F7F]
+    groups = []
+    for a in amaxes:
+        sel = xs[mag <= a]
+        n = -(-len(sel) // 127)
+        g = np.zeros((n, 128), dtype=np.uint16)
+        g[:, 0] = a
+        flat = np.zeros(n * 127, dtype=np.uint16)
+        flat[:len(sel)] = sel
+        g[:, 1:] = flat.reshape(n, 127)
+        groups.append(g)
+    groups = np.concatenate(groups)
+    K = 4096
+    M = -(-len(groups) // (K // 128))
+    xb = np.zeros((M * (K // 128), 128), dtype=np.uint16)
+    xb[:len(groups)] = groups
+    xb = xb.reshape(M, K)
+    U.note("w8a8 quantize every BF16 magnitude: %d groups, M=%d K=%d" % (len(groups), M, K))
+    xq, codes, scales = quantize(xb, K)
+    oc, osc = oracle.quantize_x_fp8(xb, K=K)
+    assert np.array_equal(scales.view(np.uint32), osc.view(np.uint32)), "scales differ"
+    bad = np.argwhere(codes != oc)
+    assert not len(bad), "codes differ at %s (x %s)" % (bad[:4], [hex(xb[tuple(i)]) for i in bad[:4]])
+
+
 def test_quantizer_nonfinite_groups():
     """A K group holding +Inf, -Inf or NaN quantises to a NaN scale and the
     E4M3 NaN code everywhere, as in the oracle; every output of its row is NaN

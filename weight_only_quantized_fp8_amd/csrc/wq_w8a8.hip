@@ -63,7 +63,8 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v)
 // loads (the four 8-wide runs k = 8g + 32q, q = 0..3, of its row); the four
 // lanes of a row (l = r, r+16, r+32, r+48) hold its whole K group and find
 // the group's amax with two exchanges.  Per value the arithmetic is that of
-// the quantiser rule above: s = amax / 448, code = e4m3_rne(clamp(x / s)).
+// the quantiser rule above: s = amax / 448, code = e4m3_rne(clamp(x / s)),
+// with x / s the correctly rounded binary32 quotient.
 __global__ void __launch_bounds__(256) quantize_x_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                          int Mpad, int KB, uint8_t* __restrict__ xq)
 {
@@ -105,13 +106,35 @@ __global__ void __launch_bounds__(256) quantize_x_kernel(const uint16_t* __restr
     // everywhere, so every product that uses the group is NaN
     const bool nonfinite = expmax == 0xFFu;
     const float s = nonfinite ? __uint_as_float(0x7FC00000u) : amax > 0.f ? amax / 448.0f : 1.0f;
+    // x / s correctly rounded without a division per value: y = RN(1/s) once,
+    // then q = RN(x y), the remainder x - q s exactly (one FMA) and RN(q + r y)
+    // (Markstein's correction step), with x's sign put back so that -0 stays
+    // -0.  Compared on gfx950 against the division for every pair of BF16
+    // values with |x| <= amax: the same E4M3 code wherever amax >= 2^-104;
+    // groups with 0 < amax < 2^-80 keep the division (below 2^-104 1/s nears
+    // the top of the binary32 range and the two differ).
+    if (!(amax > 0.f && amax < 0x1p-80f)) {
+        const float y = 1.0f / s;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xv = v[q][e], q0 = xv * y;
+                v[q][e] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, xv), y, q0), xv);
+            }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[q][e] = v[q][e] / s;
+    }
     uint32_t c[4][2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         c[q][0] = c[q][1] = 0u;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float qv = fminf(fmaxf(v[q][e] / s, -448.0f), 448.0f);
+            const float qv = fminf(fmaxf(v[q][e], -448.0f), 448.0f);
             const uint32_t code = m < M ? (nonfinite ? 0x7Fu : e4m3_rne(qv)) : 0u;
             c[q][e >> 2] |= code << (8 * (e & 3));
         }
